@@ -1,0 +1,264 @@
+"""Seeded synthetic workloads for the drafting path.
+
+This module only draws inputs.  It holds none of the path's arithmetic: it
+never pools, attends, takes an argmax or merges anything.  The target's
+greedy token at each verified position is *planted* (a value above every
+other logit of the row), so draft tokens with a given match probability can
+be drawn without looking at the logits.  Both the HIP path and the CPU
+oracle read the arrays made here.
+
+Storage dtypes: bf16 values are numpy ``uint16`` bit patterns, rounded from
+float32 normals with round-to-nearest-even; f32 values are ``float32``.
+
+Workload shapes follow the paper's settings: Qwen3-4B / Qwen3-8B shaped
+attention layers (32 query heads, 8 KV heads, head dim 128), concurrency 16,
+block B = 16, vocabulary 151936, prefixes of 8K / 32K / 64K / 128K rows
+(LongSpark paper page, Fig. 1 and Table 2: Qwen3-8B at concurrency 16 on
+32K / 64K / 128K contexts).  Values are N(0, 1): the real post-RoPE KV rows,
+queries and logits of those runs are not available, and the path's cost
+depends only on the shapes.
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+# stream identifiers inside a workload's seed tree
+_U, _PREFIX, _ROUND, _LOGITS = 0, 1, 2, 3
+LOGIT_CLIP = 4.0        # ordinary logits are clipped to [-4, 4]
+LOGIT_TOP = 4.5         # the planted greedy token's logit (exact in bf16 and f32)
+TIE_PROB = 0.25         # share of rows with a second, higher-index copy of the top value
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "f32" or "bf16"
+    C: int              # concurrent sequences
+    Hq: int
+    Hkv: int
+    d: int
+    L0: int             # prefix rows per sequence
+    W: int              # recent-window rows
+    S: int              # summary slots
+    B: int              # drafted block length
+    V: int              # vocabulary
+    rounds: int
+    p_match: float      # per-position probability that a draft token equals the target's
+    seed: int
+    lambdas: tuple = () # explicit decays; empty -> 1 - 2**-(j mod 16)
+    logits_pool: int = 0  # 0 -> one logits tensor per round; else cycle this many
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    # tiny fp32 case: 1 sequence, 2 query heads on 1 KV head, d=16
+    "tiny_f32": Workload("tiny_f32", "f32", C=1, Hq=2, Hkv=1, d=16, L0=64, W=16, S=4, B=4,
+                         V=32, rounds=8, p_match=0.7, seed=20260929,
+                         lambdas=(1.0, 0.9, 0.5, 0.1)),
+    # Qwen3-4B-shaped tapped layer, one sequence, 8K prefix
+    "q3_4b_8k": Workload("q3_4b_8k", "bf16", C=1, Hq=32, Hkv=8, d=128, L0=8192, W=512, S=64,
+                         B=16, V=151936, rounds=64, p_match=0.8, seed=20260930,
+                         logits_pool=8),
+    # Qwen3-8B-shaped tapped layer at concurrency 16
+    "q3_8b_32k": Workload("q3_8b_32k", "bf16", C=16, Hq=32, Hkv=8, d=128, L0=32768, W=1024,
+                          S=128, B=16, V=151936, rounds=256, p_match=0.8, seed=20260931,
+                          logits_pool=8),
+    "q3_8b_64k": Workload("q3_8b_64k", "bf16", C=16, Hq=32, Hkv=8, d=128, L0=65536, W=1024,
+                          S=128, B=16, V=151936, rounds=256, p_match=0.75, seed=20260932,
+                          logits_pool=8),
+    "q3_8b_128k": Workload("q3_8b_128k", "bf16", C=16, Hq=32, Hkv=8, d=128, L0=131072,
+                           W=1024, S=128, B=16, V=151936, rounds=256, p_match=0.7,
+                           seed=20260933, logits_pool=8),
+}
+SWEEP_L0 = (4096, 16384, 32768, 65536, 131072)
+
+
+# --------------------------------------------------------------------------
+# primitives
+# --------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even) -> uint16 bits."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (b >> np.uint32(16)) & np.uint32(1)
+    return ((b + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_storage(x32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return f32_to_bf16_bits(x32)
+    if dtype == "f32":
+        return np.ascontiguousarray(x32, dtype=np.float32)
+    raise ValueError(dtype)
+
+
+def storage_dtype(dtype: str):
+    return np.uint16 if dtype == "bf16" else np.float32
+
+
+def _rng(seed: int, *key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=key)))
+
+
+def normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """N(0, 1) float32 draws in storage dtype."""
+    return to_storage(rng.standard_normal(size=shape, dtype=np.float32), dtype)
+
+
+# --------------------------------------------------------------------------
+# model-side parameters
+# --------------------------------------------------------------------------
+def lambdas(wl: Workload) -> np.ndarray:
+    """Per-slot decays: explicit, or 1 - 2**-(j mod 16) (16 scales, lambda=0 at j%16==0)."""
+    if wl.lambdas:
+        assert len(wl.lambdas) == wl.S
+        return np.asarray(wl.lambdas, dtype=np.float64)
+    j = np.arange(wl.S)
+    return 1.0 - np.exp2(-(j % 16).astype(np.float64))
+
+
+def log_lambda(wl: Workload) -> np.ndarray:
+    """ln(lambda_j) as float32, -inf where lambda_j = 0."""
+    lam = lambdas(wl)
+    with np.errstate(divide="ignore"):
+        return np.log(lam).astype(np.float32)
+
+
+def slot_queries(wl: Workload) -> np.ndarray:
+    """u [Hkv, S, d]: seeded N(0, 1) slot queries, shared by all sequences."""
+    return normal(_rng(wl.seed, _U), (wl.Hkv, wl.S, wl.d), wl.dtype)
+
+
+# --------------------------------------------------------------------------
+# prefix
+# --------------------------------------------------------------------------
+def _fill_rows(out: np.ndarray, rng: np.random.Generator, dtype: str, chunk_rows: int):
+    rows = out.shape[0]
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        out[r0:r1] = normal(rng, out[r0:r1].shape, dtype)
+
+
+def prefix(wl: Workload, L0: int | None = None, threads: int = 8, rows_alloc: int | None = None,
+           log=None):
+    """k_prefix, v_prefix [C, rows_alloc, Hkv, d] with rows 0..L0-1 drawn.
+
+    Each (sequence, K|V) has its own stream and rows are drawn in order, so the
+    first L rows of a longer prefix equal a prefix drawn with L0 = L.
+    ``rows_alloc`` (>= L0) leaves room at the end of each sequence (unfilled).
+    """
+    L0 = wl.L0 if L0 is None else L0
+    rows_alloc = L0 if rows_alloc is None else rows_alloc
+    assert rows_alloc >= L0
+    sd = storage_dtype(wl.dtype)
+    K = np.empty((wl.C, rows_alloc, wl.Hkv, wl.d), dtype=sd)
+    V = np.empty((wl.C, rows_alloc, wl.Hkv, wl.d), dtype=sd)
+    jobs = []
+    for c in range(wl.C):
+        jobs.append((K[c, :L0], _rng(wl.seed, _PREFIX, c, 0)))
+        jobs.append((V[c, :L0], _rng(wl.seed, _PREFIX, c, 1)))
+    chunk = max(1, (1 << 22) // (wl.Hkv * wl.d))
+    done = [0]
+
+    def run(job):
+        _fill_rows(job[0], job[1], wl.dtype, chunk)
+        done[0] += 1
+        if log is not None and (done[0] % max(1, len(jobs) // 4) == 0):
+            log(f"prefix: {done[0]}/{len(jobs)} streams drawn")
+
+    if threads <= 1 or len(jobs) == 1:
+        for j in jobs:
+            run(j)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(run, jobs))
+    return K, V
+
+
+# --------------------------------------------------------------------------
+# per-round inputs
+# --------------------------------------------------------------------------
+def logits_entry(wl: Workload, k: int):
+    """One logits tensor [C, B+1, V] and its planted greedy tokens [C, B+1].
+
+    Ordinary logits are N(0, 1) clipped to [-4, 4]; the planted token of each
+    row gets 4.5, so it is the row's maximum.  In about a quarter of the rows
+    a second token with a higher index also gets 4.5, a tie that only the
+    lowest-index rule resolves to the planted token.
+    """
+    rng = _rng(wl.seed, _LOGITS, k)
+    shape = (wl.C, wl.B + 1, wl.V)
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    np.clip(x, -LOGIT_CLIP, LOGIT_CLIP, out=x)
+    g = rng.integers(0, wl.V, size=shape[:2])
+    tie = rng.random(size=shape[:2]) < TIE_PROB
+    off = rng.integers(0, np.iinfo(np.int64).max, size=shape[:2])
+    for c in range(wl.C):
+        for i in range(wl.B + 1):
+            x[c, i, g[c, i]] = LOGIT_TOP
+            room = wl.V - 1 - g[c, i]
+            if tie[c, i] and room > 0:
+                x[c, i, g[c, i] + 1 + off[c, i] % room] = LOGIT_TOP
+    return to_storage(x, wl.dtype), g.astype(np.int32)
+
+
+def pool_size(wl: Workload) -> int:
+    return wl.logits_pool if wl.logits_pool > 0 else wl.rounds
+
+
+def round_inputs(wl: Workload, r: int, planted: np.ndarray):
+    """Inputs of round r (except the logits, which come from the pool).
+
+    ``planted`` [C, B+1] are the greedy tokens of the logits this round uses.
+    Draft token i equals planted[:, i] with probability p_match, otherwise it
+    is uniform over the other V-1 tokens.
+    """
+    rng = _rng(wl.seed, _ROUND, r)
+    C, B, Hq, Hkv, d, V = wl.C, wl.B, wl.Hq, wl.Hkv, wl.d, wl.V
+    k_new = normal(rng, (C, B + 1, Hkv, d), wl.dtype)
+    v_new = normal(rng, (C, B + 1, Hkv, d), wl.dtype)
+    match = rng.random(size=(C, B)) < wl.p_match
+    other = rng.integers(0, V - 1, size=(C, B))
+    g = planted[:, :B].astype(np.int64)
+    other = other + (other >= g)
+    draft = np.where(match, g, other).astype(np.int32)
+    q = normal(rng, (C, B, Hq, d), wl.dtype)
+    k_blk = normal(rng, (C, B, Hkv, d), wl.dtype)
+    v_blk = normal(rng, (C, B, Hkv, d), wl.dtype)
+    return dict(k_new=k_new, v_new=v_new, draft=draft, q=q, k_blk=k_blk, v_blk=v_blk)
+
+
+def expected_tau(wl: Workload) -> float:
+    """E[tau] = 1 + sum_{k=1..B} p^k for independent per-position matches."""
+    return 1.0 + sum(wl.p_match ** k for k in range(1, wl.B + 1))
+
+
+def state_bytes(wl: Workload) -> int:
+    """Bytes of one sequence's drafter context state (ring + fp32 summary + slots)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    ring = 2 * wl.Hkv * wl.W * wl.d * e + 4 * wl.W
+    summ = wl.Hkv * wl.S * (2 * wl.d + 2) * 4
+    slots = 2 * wl.Hkv * wl.S * wl.d * e
+    return ring + summ + slots + 4
+
+
+def describe(wl: Workload) -> dict:
+    return dict(workload=wl.name, dtype=wl.dtype, C=wl.C, Hq=wl.Hq, Hkv=wl.Hkv, d=wl.d,
+                L0=wl.L0, W=wl.W, S=wl.S, B=wl.B, V=wl.V, p_match=wl.p_match, seed=wl.seed)
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
