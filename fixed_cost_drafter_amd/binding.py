@@ -1,0 +1,241 @@
+"""ctypes binding of liblongspark.so (argument marshalling only).
+
+The functions here carry the C ABI's names and do nothing but turn torch
+tensors (device memory owned by the caller) and streams into pointers, call
+the library and raise on a non-zero status.  Every step of the drafting path
+runs in the library's HIP kernels; there is no fallback.  Importing this
+module fails loudly when the library has not been built.
+
+``DrafterState`` allocates the fixed-size context state with torch (device
+memory and streams are torch's job here) and hands the library its pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblongspark.so")
+
+LS_F32, LS_BF16 = 0, 1
+STATUS = {0: "LS_OK", 1: "LS_ERR_NULL", 2: "LS_ERR_SHAPE", 3: "LS_ERR_DTYPE",
+          4: "LS_ERR_WORKSPACE", 5: "LS_ERR_ALIGN", 6: "LS_ERR_HIP"}
+EXPORTS = ("ls_workspace_bytes", "ls_summary_init", "ls_verify_greedy", "ls_append_accepted",
+           "ls_draft_attention", "ls_status_string", "ls_version")
+
+
+class LsDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("C", "Hq", "Hkv", "d", "W", "S", "B", "V", "dtype")]
+
+
+class LsState(ctypes.Structure):
+    _fields_ = [("ring_k", ctypes.c_void_p), ("ring_v", ctypes.c_void_p),
+                ("ring_pos", ctypes.c_void_p), ("seq_len", ctypes.c_void_p),
+                ("sum_m", ctypes.c_void_p), ("sum_l", ctypes.c_void_p),
+                ("sum_n", ctypes.c_void_p), ("slot_k", ctypes.c_void_p),
+                ("slot_v", ctypes.c_void_p), ("u", ctypes.c_void_p),
+                ("log_lambda", ctypes.c_void_p), ("err_flag", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class LsError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} "
+                         f"({_lib.ls_status_string(status).decode()})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m fixed_cost_drafter_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    D, S = ctypes.POINTER(LsDims), ctypes.POINTER(LsState)
+    lib.ls_workspace_bytes.argtypes = [D, I32]
+    lib.ls_workspace_bytes.restype = SZ
+    lib.ls_summary_init.argtypes = [D, S, P, P, I32, I64, P]
+    lib.ls_verify_greedy.argtypes = [D, P, P, P, P, P, SZ, P]
+    lib.ls_append_accepted.argtypes = [D, S, P, P, P, P]
+    lib.ls_draft_attention.argtypes = [D, S, P, P, P, P, P]
+    for f in ("ls_summary_init", "ls_verify_greedy", "ls_append_accepted", "ls_draft_attention"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.ls_status_string.argtypes = [ctypes.c_int]
+    lib.ls_status_string.restype = ctypes.c_char_p
+    lib.ls_version.argtypes = []
+    lib.ls_version.restype = I32
+    return lib
+
+
+_lib = _load()
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, torch.Tensor):
+        if not x.is_contiguous():
+            raise ValueError("tensors passed to liblongspark must be contiguous")
+        return x.data_ptr()
+    raise TypeError(f"expected a torch tensor or a raw pointer, got {type(x)}")
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise LsError(fn, status)
+
+
+def make_dims(C, Hq, Hkv, d, W, S, B, V, dtype) -> LsDims:
+    dt = {"f32": LS_F32, "bf16": LS_BF16}.get(dtype, dtype)
+    return LsDims(C, Hq, Hkv, d, W, S, B, V, dt)
+
+
+def torch_dtype(dtype: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Copy a storage array (uint16 bf16 bits or float32 / int32) to the device."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    """Device tensor -> numpy (bf16 as uint16 bit patterns)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+# --------------------------------------------------------------------------
+# the C ABI, one wrapper per entry point
+# --------------------------------------------------------------------------
+def ls_workspace_bytes(dims: LsDims, max_L0: int) -> int:
+    return int(_lib.ls_workspace_bytes(ctypes.byref(dims), int(max_L0)))
+
+
+def ls_summary_init(dims: LsDims, state: LsState, k_prefix, v_prefix, L0: int,
+                    prefix_rows_stride: int, stream=None):
+    _check("ls_summary_init", _lib.ls_summary_init(
+        ctypes.byref(dims), ctypes.byref(state), _ptr(k_prefix), _ptr(v_prefix), int(L0),
+        int(prefix_rows_stride), _stream(stream)))
+
+
+def ls_verify_greedy(dims: LsDims, logits, draft, target_tok, tau, workspace, workspace_bytes,
+                     stream=None):
+    _check("ls_verify_greedy", _lib.ls_verify_greedy(
+        ctypes.byref(dims), _ptr(logits), _ptr(draft), _ptr(target_tok), _ptr(tau),
+        _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def ls_append_accepted(dims: LsDims, state: LsState, k_new, v_new, tau, stream=None):
+    _check("ls_append_accepted", _lib.ls_append_accepted(
+        ctypes.byref(dims), ctypes.byref(state), _ptr(k_new), _ptr(v_new), _ptr(tau),
+        _stream(stream)))
+
+
+def ls_draft_attention(dims: LsDims, state: LsState, q, k_blk, v_blk, out, stream=None):
+    _check("ls_draft_attention", _lib.ls_draft_attention(
+        ctypes.byref(dims), ctypes.byref(state), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(out),
+        _stream(stream)))
+
+
+def ls_status_string(status: int) -> str:
+    return _lib.ls_status_string(int(status)).decode()
+
+
+def ls_version() -> int:
+    return int(_lib.ls_version())
+
+
+# --------------------------------------------------------------------------
+# device state (torch-allocated)
+# --------------------------------------------------------------------------
+class DrafterState:
+    """The drafter's fixed-size context state plus workspace, on one device.
+
+    ``u`` [Hkv, S, d] and ``log_lambda`` [S] are the slot parameters (storage
+    arrays from numpy or tensors).  ``max_L0`` sizes the workspace for the
+    longest prefix that ``summary_init`` will be called with.
+    """
+
+    def __init__(self, C, Hq, Hkv, d, W, S, B, V, dtype, u, log_lambda, max_L0,
+                 device="cuda"):
+        self.dtype = dtype
+        self.dims = make_dims(C, Hq, Hkv, d, W, S, B, V, dtype)
+        td = torch_dtype(dtype)
+        z = lambda *shape, dt=td: torch.zeros(shape, dtype=dt, device=device)
+        self.ring_k = z(C, Hkv, W, d)
+        self.ring_v = z(C, Hkv, W, d)
+        self.ring_pos = torch.full((C, W), -1, dtype=torch.int32, device=device)
+        self.seq_len = z(C, dt=torch.int32)
+        self.sum_m = z(C, Hkv, S, dt=torch.float32)
+        self.sum_l = z(C, Hkv, S, dt=torch.float32)
+        self.sum_n = z(C, Hkv, S, 2 * d, dt=torch.float32)
+        self.slot_k = z(C, Hkv, S, d)
+        self.slot_v = z(C, Hkv, S, d)
+        self.u = u if isinstance(u, torch.Tensor) else to_device(u, device)
+        lg = log_lambda if isinstance(log_lambda, torch.Tensor) else to_device(
+            np.asarray(log_lambda, dtype=np.float32), device)
+        self.log_lambda = lg.to(torch.float32).contiguous()
+        self.err_flag = z(1, dt=torch.int32)
+        nbytes = ls_workspace_bytes(self.dims, max_L0)
+        if nbytes == 0:
+            raise LsError("ls_workspace_bytes", 2)
+        # zero-filled once: it holds counters that the kernels keep at zero
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.c_state = LsState(
+            _ptr(self.ring_k), _ptr(self.ring_v), _ptr(self.ring_pos), _ptr(self.seq_len),
+            _ptr(self.sum_m), _ptr(self.sum_l), _ptr(self.sum_n), _ptr(self.slot_k),
+            _ptr(self.slot_v), _ptr(self.u), _ptr(self.log_lambda), _ptr(self.err_flag),
+            _ptr(self.workspace), nbytes)
+
+    @classmethod
+    def for_workload(cls, wl, u, log_lambda, max_L0=None, device="cuda"):
+        return cls(wl.C, wl.Hq, wl.Hkv, wl.d, wl.W, wl.S, wl.B, wl.V, wl.dtype, u, log_lambda,
+                   wl.L0 if max_L0 is None else max_L0, device)
+
+    # the four calls of the path, on this state
+    def summary_init(self, k_prefix, v_prefix, L0=None, prefix_rows_stride=None, stream=None):
+        rows = k_prefix.shape[1]
+        L0 = rows if L0 is None else L0
+        ls_summary_init(self.dims, self.c_state, k_prefix, v_prefix, L0,
+                        rows if prefix_rows_stride is None else prefix_rows_stride, stream)
+
+    def verify_greedy(self, logits, draft, target_tok, tau, stream=None):
+        ls_verify_greedy(self.dims, logits, draft, target_tok, tau, self.workspace,
+                         self.workspace.numel(), stream)
+
+    def append_accepted(self, k_new, v_new, tau, stream=None):
+        ls_append_accepted(self.dims, self.c_state, k_new, v_new, tau, stream)
+
+    def draft_attention(self, q, k_blk, v_blk, out, stream=None):
+        ls_draft_attention(self.dims, self.c_state, q, k_blk, v_blk, out, stream)
+
+    def state_bytes(self) -> int:
+        ts = (self.ring_k, self.ring_v, self.ring_pos, self.seq_len, self.sum_m, self.sum_l,
+              self.sum_n, self.slot_k, self.slot_v)
+        return sum(t.numel() * t.element_size() for t in ts)

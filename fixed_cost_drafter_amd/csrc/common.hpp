@@ -1,0 +1,144 @@
+// Shared device helpers and the workspace layout of liblongspark.
+//
+// Element access for the two storage types (IEEE float32 and bfloat16 bit
+// patterns), the MFMA operand vector types of gfx950, wave-level reductions
+// for 64-lane wavefronts, and where each kernel keeps its scratch inside the
+// caller's workspace.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/longspark.h"
+
+namespace ls {
+
+// ---------------------------------------------------------------------------
+// storage types
+// ---------------------------------------------------------------------------
+struct F32 {
+  using T = float;
+  static constexpr int kBytes = 4;
+  __device__ static inline float load(const T* p, int64_t i) { return p[i]; }
+  __device__ static inline void store(T* p, int64_t i, float x) { p[i] = x; }
+};
+
+__device__ inline float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// round to nearest, ties to even (inputs are finite)
+__device__ inline uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+struct BF16 {
+  using T = uint16_t;
+  static constexpr int kBytes = 2;
+  __device__ static inline float load(const T* p, int64_t i) { return bf16_to_f32(p[i]); }
+  __device__ static inline void store(T* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+};
+
+// MFMA operand / accumulator vectors
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline bf16x8 as_bf16x8(u16x8 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// wave (64 lanes) reductions
+// ---------------------------------------------------------------------------
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ inline uint64_t shfl_xor_u64(uint64_t x, int o) {
+  uint32_t lo = __shfl_xor(uint32_t(x), o, 64);
+  uint32_t hi = __shfl_xor(uint32_t(x >> 32), o, 64);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// e^(x) for the online softmax; e^(-inf) = 0
+__device__ inline float exp_f(float x) { return __expf(x); }
+
+// ---------------------------------------------------------------------------
+// workspace layout (bytes), shared by the host code and the kernels
+// ---------------------------------------------------------------------------
+constexpr int kVerifyChunk = 8192;     // logits per verify workgroup
+constexpr int kDraftSplitsMax = 8;     // key splits of the MFMA draft attention
+constexpr int kInitTargetBlocks = 512; // aim of the init grid size
+constexpr int kInitRowTile = 64;       // rows per init tile (MFMA path)
+
+inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct WsLayout {
+  int64_t cnt_verify, cnt_append, cnt_draft;  // uint32 counters
+  int64_t verify_part;                        // uint64 keys [C*(B+1)*vsplit]
+  int64_t draft_part;                         // float [C*Hkv*dsplit * Mpad*(d+2)]
+  int64_t init_part;                          // float [isplit*C*Hkv*S*(2d+2)]
+  int64_t total;
+  int vsplit, dsplit, isplit, init_rows;
+};
+
+inline int verify_splits(const ls_dims& d) { return int(cdiv(d.V, kVerifyChunk)); }
+
+inline int init_rows_per_split(const ls_dims& d, int32_t L0) {
+  // split each (sequence, head) prefix so the grid has ~kInitTargetBlocks blocks
+  int64_t units = int64_t(d.C) * d.Hkv;
+  int64_t want = cdiv(kInitTargetBlocks, units);
+  int64_t rows = cdiv(L0, want);
+  rows = cdiv(rows, kInitRowTile) * kInitRowTile;
+  if (rows < kInitRowTile) rows = kInitRowTile;
+  return int(rows);
+}
+
+inline int draft_splits(const ls_dims& d) {
+  if (d.dtype != LS_BF16) return 1;
+  // about 4 key tiles of 64 per split, at most kDraftSplitsMax splits
+  int64_t nkeys = int64_t(d.W) + d.S + d.B;
+  int64_t s = cdiv(nkeys, 4 * 64);
+  if (s > kDraftSplitsMax) s = kDraftSplitsMax;
+  if (s < 1) s = 1;
+  return int(s);
+}
+
+inline WsLayout ws_layout(const ls_dims& d, int32_t max_L0) {
+  WsLayout w{};
+  int64_t off = 0;
+  w.cnt_verify = off;  off = align256(off + 4 * int64_t(d.C));
+  w.cnt_append = off;  off = align256(off + 4 * int64_t(d.C));
+  w.cnt_draft = off;   off = align256(off + 4 * int64_t(d.C) * d.Hkv);
+  w.vsplit = verify_splits(d);
+  w.verify_part = off; off = align256(off + 8 * int64_t(d.C) * (d.B + 1) * w.vsplit);
+  w.dsplit = draft_splits(d);
+  const int64_t M = int64_t(d.B) * (d.Hq / d.Hkv);
+  const int64_t Mpad = cdiv(M, 16) * 16;
+  w.draft_part = off;
+  if (w.dsplit > 1) off = align256(off + 4 * int64_t(d.C) * d.Hkv * w.dsplit * Mpad * (d.d + 2));
+  // the split count of a call with L0 <= max_L0 never exceeds this bound
+  const int64_t L = max_L0 < 1 ? 1 : max_L0;
+  const int64_t want = cdiv(kInitTargetBlocks, int64_t(d.C) * d.Hkv);
+  const int64_t by_rows = cdiv(L, kInitRowTile);
+  w.init_rows = init_rows_per_split(d, int32_t(L));
+  w.isplit = int(want < by_rows ? want : by_rows);
+  w.init_part = off;
+  off = align256(off + 4 * int64_t(w.isplit) * d.C * d.Hkv * d.S * (2 * d.d + 2));
+  w.total = off;
+  return w;
+}
+
+}  // namespace ls

@@ -1,0 +1,25 @@
+// Internal launchers, one per kernel family.  The C ABI (abi.cpp) validates
+// arguments and calls these; they compute launch shapes and enqueue kernels
+// on `stream`, never synchronising and never allocating.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/longspark.h"
+
+namespace ls {
+
+ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* draft,
+                        int32_t* target_tok, int32_t* tau, char* ws, hipStream_t stream);
+
+ls_status launch_append(const ls_dims& d, const ls_state& st, const void* k_new,
+                        const void* v_new, const int32_t* tau, hipStream_t stream);
+
+ls_status launch_init(const ls_dims& d, const ls_state& st, const void* k_prefix,
+                      const void* v_prefix, int32_t L0, int64_t rows_stride,
+                      hipStream_t stream);
+
+ls_status launch_draft(const ls_dims& d, const ls_state& st, const void* q, const void* k_blk,
+                       const void* v_blk, void* out, hipStream_t stream);
+
+}  // namespace ls

@@ -1,0 +1,175 @@
+// Greedy verification of a drafted block (LongSpark paper page, Fig. 2 (a);
+// Table 3: greedy decoding, T = 0; Table 1: accepted length tau).
+//
+// g_i = argmax_v logits[c, i, v] with the lowest index on ties; M = longest
+// prefix with draft[c, i] == g_i; tau = M + 1.
+//
+// One launch.  Each workgroup scans one chunk of one logits row with 16-byte
+// loads and reduces (value, index) to a 64-bit key whose unsigned order is
+// "larger value first, then lower index": the high word is the value's bits
+// mapped to an order-preserving unsigned integer (+0 and -0 merged), the low
+// word is ~index.  Keys go to the workspace; the last workgroup of a sequence
+// to finish (a device-scope counter) reduces its (B+1) x splits keys, counts
+// the accepted prefix and writes target_tok and tau, then resets the counter.
+// The logits are streamed once (HBM-bound: 2 bytes per bf16 logit).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ls {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline uint32_t ordered_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;  // -0 compares equal to +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ inline uint64_t make_key(float x, uint32_t idx) {
+  return (uint64_t(ordered_bits(x)) << 32) | uint64_t(~idx);
+}
+
+template <typename Ty>
+struct Vec16;  // 16 bytes of logits
+template <>
+struct Vec16<F32> {
+  static constexpr int N = 4;
+  using V = float __attribute__((ext_vector_type(4)));
+  __device__ static inline float get(const V& v, int i) { return v[i]; }
+};
+template <>
+struct Vec16<BF16> {
+  static constexpr int N = 8;
+  using V = u16x8;
+  __device__ static inline float get(const V& v, int i) { return bf16_to_f32(v[i]); }
+};
+
+template <typename Ty>
+__global__ __launch_bounds__(kThreads) void verify_kernel(
+    const typename Ty::T* __restrict__ logits, const int32_t* __restrict__ draft,
+    int32_t* __restrict__ target_tok, int32_t* __restrict__ tau, uint64_t* __restrict__ part,
+    uint32_t* __restrict__ counter, int V, int B, int nsplit, int chunk, int vec_ok) {
+  using VT = Vec16<Ty>;
+  const int split = blockIdx.x;
+  const int row = blockIdx.y;  // c * (B+1) + i
+  const int c = row / (B + 1);
+  const int tid = threadIdx.x;
+  const typename Ty::T* x = logits + int64_t(row) * V;
+  const int begin = split * chunk;
+  const int end = min(V, begin + chunk);
+
+  float best = -INFINITY;
+  uint32_t best_i = 0xFFFFFFFFu;
+  if (vec_ok) {
+    // 16-byte loads; each thread walks its vectors in increasing index order,
+    // so a strict '>' keeps the lowest index among equal values.
+    const typename VT::V* xv = reinterpret_cast<const typename VT::V*>(x + begin);
+    const int nvec = (end - begin) / VT::N;
+    constexpr int U = 4;
+    for (int base = 0; base < nvec; base += kThreads * U) {
+      typename VT::V buf[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int v = base + u * kThreads + tid;
+        if (v < nvec) buf[u] = __builtin_nontemporal_load(xv + v);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int v = base + u * kThreads + tid;
+        if (v < nvec) {
+#pragma unroll
+          for (int e = 0; e < VT::N; ++e) {
+            float f = VT::get(buf[u], e);
+            if (f > best) {
+              best = f;
+              best_i = uint32_t(begin + v * VT::N + e);
+            }
+          }
+        }
+      }
+    }
+    // tail that does not fill a vector (only in the last chunk)
+    for (int i = begin + nvec * VT::N + tid; i < end; i += kThreads) {
+      float f = Ty::load(x, i);
+      if (f > best) { best = f; best_i = uint32_t(i); }
+    }
+  } else {
+    for (int i = begin + tid; i < end; i += kThreads) {
+      float f = Ty::load(x, i);
+      if (f > best) { best = f; best_i = uint32_t(i); }
+    }
+  }
+
+  uint64_t key = (best_i == 0xFFFFFFFFu) ? 0ull : make_key(best, best_i);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint64_t other = shfl_xor_u64(key, o);
+    key = other > key ? other : key;
+  }
+  __shared__ uint64_t wkeys[kThreads / 64];
+  __shared__ int is_last;
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) wkeys[wave] = key;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t k = wkeys[0];
+    for (int w = 1; w < kThreads / 64; ++w) k = wkeys[w] > k ? wkeys[w] : k;
+    part[int64_t(row) * nsplit + split] = k;
+    __threadfence();
+    const uint32_t blocks_per_seq = uint32_t(B + 1) * uint32_t(nsplit);
+    uint32_t ticket = atomicAdd(&counter[c], 1u);
+    is_last = (ticket == blocks_per_seq - 1);
+  }
+  __syncthreads();
+  if (!is_last) return;
+
+  // last workgroup of sequence c: reduce the keys of its B+1 rows
+  __threadfence();
+  __shared__ int32_t g[kThreads];
+  for (int i = tid; i <= B; i += kThreads) {
+    const uint64_t* p = part + (int64_t(c) * (B + 1) + i) * nsplit;
+    uint64_t k = 0;
+    for (int s = 0; s < nsplit; ++s) {
+      uint64_t ks = __atomic_load_n(p + s, __ATOMIC_RELAXED);
+      k = ks > k ? ks : k;
+    }
+    int32_t gi = int32_t(~uint32_t(k));
+    g[i] = gi;
+    target_tok[int64_t(c) * (B + 1) + i] = gi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int M = 0;
+    while (M < B && draft[int64_t(c) * B + M] == g[M]) ++M;
+    tau[c] = M + 1;
+    counter[c] = 0u;
+  }
+}
+
+}  // namespace
+
+ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* draft,
+                        int32_t* target_tok, int32_t* tau, char* ws, hipStream_t stream) {
+  const WsLayout lay = ws_layout(d, 1);
+  const int nsplit = lay.vsplit;
+  const int chunk = kVerifyChunk;
+  const int esz = d.dtype == LS_BF16 ? 2 : 4;
+  // 16-byte loads need every row start (and chunk start) 16-byte aligned
+  const int vec_ok = ((int64_t(d.V) * esz) % 16 == 0) && ((uintptr_t(logits) & 15) == 0);
+  dim3 grid(nsplit, d.C * (d.B + 1));
+  uint64_t* part = reinterpret_cast<uint64_t*>(ws + lay.verify_part);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + lay.cnt_verify);
+  if (d.dtype == LS_BF16) {
+    hipLaunchKernelGGL(verify_kernel<BF16>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(logits), draft, target_tok, tau, part, cnt,
+                       d.V, d.B, nsplit, chunk, vec_ok);
+  } else {
+    hipLaunchKernelGGL(verify_kernel<F32>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const float*>(logits), draft, target_tok, tau, part, cnt, d.V,
+                       d.B, nsplit, chunk, vec_ok);
+  }
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+}
+
+}  // namespace ls

@@ -1,0 +1,159 @@
+/*
+ * longspark.h -- C ABI of the LongSpark fixed-cost drafting path on MI355X.
+ *
+ * Source: the paper page "LongSpark: Efficient speculative decoding with a
+ * fixed-cost parallel drafter" (arXiv 2609.37029).  One decoding round
+ * (Fig. 2): (a) the target verifies the drafted block; (b) fixed-size views
+ * of the target's state are kept -- a recent KV window and a global context
+ * summary; (c) the drafter attends over those views to propose the next
+ * block, at a cost that does not depend on the prefix length.  The summary is
+ * initialised over the whole prefix at prefill and then updated with only the
+ * newly retained rows, at most B+1 per round (Fig. 3).
+ *
+ * The pages print no formula for the summary.  This library implements S
+ * slots per KV head: slot j pools retained rows p = 0..t (t = newest) with
+ * weight w_jp = exp(u_j . k_p / sqrt(d)) * lambda_j^(t-p) (0^0 = 1); its key
+ * is sum w k / sum w and its value sum w v / sum w.  The state is kept as an
+ * online-softmax triple per slot: a_jp = u_j.k_p/sqrt(d) + (t-p) ln lambda_j,
+ * m = max_p a_jp, l = sum_p exp(a_jp - m), n = sum_p exp(a_jp - m) [k_p ; v_p].
+ *
+ * Conventions for every entry point
+ *   - All array pointers are DEVICE memory owned by the caller.  The library
+ *     never allocates, frees or keeps a pointer after a call returns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream) and never synchronises with the host.
+ *   - Arrays are dense row-major in the shapes given below.  "dtype" arrays
+ *     hold IEEE float32 (LS_F32) or bfloat16 (LS_BF16) per `ls_dims.dtype`.
+ *   - Errors that the host can see (NULL pointer, bad size, unsupported
+ *     shape or dtype, workspace too small, misaligned pointer) are returned
+ *     BEFORE anything is launched.  LS_ERR_HIP means a launch failed.
+ *     Device-side faults surface at the caller's next synchronisation.
+ *   - Calls that share one workspace or one state must not overlap (same
+ *     stream, or ordered with events).
+ *
+ * Supported shapes: Hq % Hkv == 0; 1 <= B, B+1 <= W; V >= 1; S >= 1.
+ *   LS_F32 : d in {16, 32, 64, 128}, S <= 256, B*Hq/Hkv <= 64.
+ *   LS_BF16: d == 128, S in {64, 128}, B*Hq/Hkv <= 64.
+ * Pointers to dtype arrays and to sum_n must be 16-byte aligned.
+ */
+#ifndef LONGSPARK_H
+#define LONGSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ls_dtype { LS_F32 = 0, LS_BF16 = 1 } ls_dtype;
+
+typedef enum ls_status {
+  LS_OK = 0,
+  LS_ERR_NULL = 1,      /* a required pointer is NULL                        */
+  LS_ERR_SHAPE = 2,     /* a size is out of range or not supported           */
+  LS_ERR_DTYPE = 3,     /* dtype is neither LS_F32 nor LS_BF16               */
+  LS_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
+  LS_ERR_ALIGN = 5,     /* a pointer lacks the required 16-byte alignment    */
+  LS_ERR_HIP = 6        /* the HIP runtime reported an error at launch       */
+} ls_status;
+
+/* A hipStream_t; NULL selects the default stream. */
+typedef void* ls_stream;
+
+/* Sizes shared by every call. */
+typedef struct ls_dims {
+  int32_t C;     /* concurrent sequences                                  */
+  int32_t Hq;    /* query heads of the drafter's attention                */
+  int32_t Hkv;   /* KV heads (GQA: query head hq reads KV head hq/(Hq/Hkv)) */
+  int32_t d;     /* head dimension                                        */
+  int32_t W;     /* rows of the recent-KV ring window                     */
+  int32_t S;     /* summary slots per KV head                             */
+  int32_t B;     /* drafted block length; B+1 positions are verified      */
+  int32_t V;     /* vocabulary size                                       */
+  int32_t dtype; /* ls_dtype of every "dtype" array                       */
+} ls_dims;
+
+/* The drafter's fixed-size context state (Fig. 2 (b)) plus parameters.
+ * Its size is independent of the prefix length. */
+typedef struct ls_state {
+  void* ring_k;             /* [C, Hkv, W, d] dtype: window keys            */
+  void* ring_v;             /* [C, Hkv, W, d] dtype: window values          */
+  int32_t* ring_pos;        /* [C, W] absolute position held, -1 = empty     */
+  int32_t* seq_len;         /* [C] retained rows per sequence                */
+  float* sum_m;             /* [C, Hkv, S] running max m (natural log units) */
+  float* sum_l;             /* [C, Hkv, S] denominator l                     */
+  float* sum_n;             /* [C, Hkv, S, 2d] numerator n: keys | values    */
+  void* slot_k;             /* [C, Hkv, S, d] dtype: n[:d] / l               */
+  void* slot_v;             /* [C, Hkv, S, d] dtype: n[d:] / l               */
+  const void* u;            /* [Hkv, S, d] dtype: slot queries               */
+  const float* log_lambda;  /* [S] ln(lambda_j); -INFINITY for lambda_j = 0  */
+  int32_t* err_flag;        /* [1] sticky device error word, 0 = no error    */
+  void* workspace;          /* scratch, see ls_workspace_bytes               */
+  size_t workspace_bytes;
+} ls_state;
+
+/* Bytes of workspace that every call below needs for prefixes of up to
+ * `max_L0` rows.  The workspace must be ZERO-FILLED ONCE after allocation:
+ * it holds completion counters that each kernel returns to zero before it
+ * ends.  Returns 0 if `dims` is invalid. */
+size_t ls_workspace_bytes(const ls_dims* dims, int32_t max_L0);
+
+/* Prefill view (Fig. 3: the summary is initialised over the full prefix).
+ *   k_prefix, v_prefix: [C, prefix_rows_stride, Hkv, d] dtype, token-major
+ *     (the serving KV-cache layout); rows 0..L0-1 of each sequence are read.
+ *   L0 >= 1, prefix_rows_stride >= L0.
+ * Writes sum_m, sum_l, sum_n, slot_k, slot_v over all L0 rows (t = L0-1);
+ * the ring gets rows max(0, L0-W)..L0-1 at slot p mod W with ring_pos = p,
+ * other ring slots get zero rows and position -1; seq_len = L0; err_flag = 0.
+ * Cost O(L0): the only call that reads the prefix. */
+ls_status ls_summary_init(const ls_dims* dims, const ls_state* state, const void* k_prefix,
+                          const void* v_prefix, int32_t L0, int64_t prefix_rows_stride,
+                          ls_stream stream);
+
+/* Greedy verification (Fig. 2 (a); Table 3, T = 0).
+ *   logits:     [C, B+1, V] dtype, the target's scores at the B+1 verified
+ *               positions (last committed token, drafts 1..B); no NaN.
+ *   draft:      [C, B] int32 drafted tokens.
+ *   target_tok: [C, B+1] int32 out, g_i = argmax_v logits[c,i,v], lowest
+ *               index on ties (+0 and -0 compare equal).
+ *   tau:        [C] int32 out, M+1 where M is the longest prefix with
+ *               draft[c,i] == g_i; tau is in [1, B+1].
+ *   workspace:  as sized by ls_workspace_bytes (any max_L0). */
+ls_status ls_verify_greedy(const ls_dims* dims, const void* logits, const int32_t* draft,
+                           int32_t* target_tok, int32_t* tau, void* workspace,
+                           size_t workspace_bytes, ls_stream stream);
+
+/* Per-round update (Fig. 2 (b), Fig. 3: only the newly retained rows).
+ *   k_new, v_new: [C, B+1, Hkv, d] dtype, KV rows of the verified positions.
+ *   tau: [C] int32 in DEVICE memory (e.g. from ls_verify_greedy): rows
+ *        0..tau[c]-1 are retained.  Values outside [1, B+1] are clamped into
+ *        it and set bit 0 of *err_flag.
+ * Appends the rows to the ring at slot (L+i) mod W (ring_pos = L+i), shifts
+ * every slot's m by tau*ln(lambda_j), merges the new rows into (m, l, n),
+ * rewrites slot_k/slot_v and sets seq_len += tau.  O(tau*S*d) work per
+ * (sequence, KV head); the prefix is never read. */
+ls_status ls_append_accepted(const ls_dims* dims, const ls_state* state, const void* k_new,
+                             const void* v_new, const int32_t* tau, ls_stream stream);
+
+/* Drafter block attention (Fig. 2 (c)).
+ *   q:            [C, B, Hq, d] dtype, block queries.
+ *   k_blk, v_blk: [C, B, Hkv, d] dtype, block keys/values.
+ *   out:          [C, B, Hq, d] dtype.
+ * out = softmax(q k^T / sqrt(d)) v over the occupied ring rows, the S slots
+ * and the B block rows of the query's KV head; bidirectional (no mask).
+ * Reads W + S + B rows per KV head whatever the prefix length. */
+ls_status ls_draft_attention(const ls_dims* dims, const ls_state* state, const void* q,
+                             const void* k_blk, const void* v_blk, void* out, ls_stream stream);
+
+/* Static description of a status code. */
+const char* ls_status_string(ls_status status);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t ls_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LONGSPARK_H */

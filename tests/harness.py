@@ -1,0 +1,160 @@
+"""Lockstep runs of the HIP path and the CPU oracle on the same seeded inputs.
+
+Test infrastructure.  Both sides read the arrays from
+fixed_cost_drafter_amd.workload; the oracle never sees a value produced by the
+GPU.  Comparisons:
+  * bit-exact: tau, target_tok, ring_k/ring_v contents, ring_pos, seq_len;
+  * f32 workloads: normwise relative error max|x-y| / max|y| <= 1e-5;
+  * bf16 workloads: max|x-y| <= 2e-2 on unit-scale outputs (slots, out,
+    the pooled means n/l), relative 2e-2 on l, absolute 2e-2 on m.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+from fixed_cost_drafter_amd import workload as WLM
+from oracle import longspark_oracle as O
+
+F32_REL = 1e-5
+BF16_ABS = 2e-2
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def as_f64(a):
+    return O.decode(a)
+
+
+def close(name, got, ref, dtype, mask=None):
+    """Assert the stated tolerance; return the error figure."""
+    g = as_f64(got)
+    r = np.asarray(ref, dtype=np.float64)
+    if mask is not None:
+        g, r = g[mask], r[mask]
+    assert g.shape == r.shape, (name, g.shape, r.shape)
+    assert np.all(np.isfinite(g)), f"{name}: non-finite GPU values"
+    err = np.max(np.abs(g - r)) if g.size else 0.0
+    if dtype == "f32":
+        scale = max(np.max(np.abs(r)) if r.size else 0.0, 1e-30)
+        rel = err / scale
+        assert rel <= F32_REL, f"{name}: normwise rel err {rel:.3e} > {F32_REL}"
+        return rel
+    assert err <= BF16_ABS, f"{name}: max abs err {err:.3e} > {BF16_ABS}"
+    return err
+
+
+def exact(name, got, ref):
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    if not np.array_equal(got, ref):
+        bad = np.argwhere(got != ref)
+        raise AssertionError(f"{name}: {len(bad)} mismatches, first at {bad[:3].tolist()}: "
+                             f"got {got[tuple(bad[0])]} want {ref[tuple(bad[0])]}")
+
+
+def compare_state(runner, ost: O.OracleState, dtype, heads=None):
+    """GPU state vs oracle state; ``heads`` restricts the float checks."""
+    snap = runner.snapshot()
+    exact("seq_len", snap["seq_len"].astype(np.int64), ost.seq_len)
+    exact("ring_pos", snap["ring_pos"], ost.ring_pos)
+    exact("ring_k", snap["ring_k"], ost.ring_k)
+    exact("ring_v", snap["ring_v"], ost.ring_v)
+    d = ost.d
+    todo = heads if heads is not None else [(c, h) for c in range(ost.m.shape[0])
+                                            for h in range(ost.m.shape[1])]
+    errs = {}
+    for c, h in todo:
+        if dtype == "f32":
+            errs["m"] = close("sum_m", snap["sum_m"][c, h], ost.m[c, h], dtype)
+            errs["l"] = close("sum_l", snap["sum_l"][c, h], ost.l[c, h], dtype)
+            errs["n"] = close("sum_n", snap["sum_n"][c, h], ost.n[c, h], dtype)
+        else:
+            em = np.max(np.abs(snap["sum_m"][c, h].astype(np.float64) - ost.m[c, h]))
+            assert em <= BF16_ABS, f"sum_m ({c},{h}) err {em}"
+            rl = np.max(np.abs(snap["sum_l"][c, h] / ost.l[c, h] - 1.0))
+            assert rl <= BF16_ABS, f"sum_l ({c},{h}) rel err {rl}"
+            mean = snap["sum_n"][c, h].astype(np.float64) / snap["sum_l"][c, h][:, None].astype(np.float64)
+            close("n/l", mean, ost.n[c, h] / ost.l[c, h][:, None], dtype)
+        errs["slot_k"] = close("slot_k", snap["slot_k"][c, h], ost.slot_k[c, h], dtype)
+        errs["slot_v"] = close("slot_v", snap["slot_v"][c, h], ost.slot_v[c, h], dtype)
+    return errs
+
+
+def lockstep(wl: WLM.Workload, rounds: int, k_prefix=None, v_prefix=None, heads=None,
+             check_state_every=1, runner=None, tau_override=None, device="cuda"):
+    """Run ``rounds`` rounds on both sides and compare after each.
+
+    ``heads`` samples (c, h) pairs for the float checks of large workloads
+    (the oracle's summary and attention are computed only there).
+    ``tau_override`` (round -> tau array) replaces the verified tau on both
+    sides before the append (device-side clamping and the error flag).
+    Returns (runner, oracle_state, stats).
+    """
+    import torch
+    from fixed_cost_drafter_amd import binding as LB
+    from fixed_cost_drafter_amd.runner import PathRunner, upload_round
+
+    t0 = time.time()
+    if k_prefix is None:
+        k_prefix, v_prefix = WLM.prefix(wl, threads=16)
+    if runner is None:
+        runner = PathRunner(wl, k_prefix, v_prefix, device=device)
+        runner.init()
+    log(f"[{wl.name}] init launched ({time.time() - t0:.1f}s)")
+    u = WLM.slot_queries(wl)
+    logl = WLM.log_lambda(wl)
+    L0 = k_prefix.shape[1]
+    ost = O.summary_init(u, logl, np.ascontiguousarray(k_prefix[:, :L0]),
+                         np.ascontiguousarray(v_prefix[:, :L0]), wl.W, heads=heads)
+    torch.cuda.synchronize()
+    compare_state(runner, ost, wl.dtype, heads)
+    log(f"[{wl.name}] init parity ok ({time.time() - t0:.1f}s)")
+    stats = dict(tau=[])
+    pool = {}
+    G = wl.G
+    pairs = None
+    if heads is not None:
+        pairs = [(c, h * G + g) for c, h in heads for g in range(G)]
+    for r in range(rounds):
+        k = r % WLM.pool_size(wl)
+        if k not in pool:
+            logits, planted = WLM.logits_entry(wl, k)
+            pool[k] = (logits, planted, LB.to_device(logits, device))
+        logits, planted, logits_dev = pool[k]
+        inp = WLM.round_inputs(wl, r, planted)
+        dev = upload_round(inp, device)
+        b = runner.buf
+        s = runner.state
+        s.verify_greedy(logits_dev, dev["draft"], b.target_tok, b.tau)
+        tgt_ref, tau_ref = O.verify_greedy(logits, inp["draft"])
+        torch.cuda.synchronize()
+        exact("target_tok", LB.to_host(b.target_tok), tgt_ref)
+        exact("tau", LB.to_host(b.tau), tau_ref)
+        exact("target_tok==planted", tgt_ref, planted)
+        tau_use = tau_ref
+        if tau_override is not None and r in tau_override:
+            forced = np.asarray(tau_override[r], dtype=np.int32)
+            b.tau.copy_(LB.to_device(forced, device))
+            tau_use = np.clip(forced, 1, wl.B + 1)
+        s.append_accepted(dev["k_new"], dev["v_new"], b.tau)
+        s.draft_attention(dev["q"], dev["k_blk"], dev["v_blk"], b.out)
+        O.append_accepted(ost, inp["k_new"], inp["v_new"], tau_use, heads=heads)
+        out_ref = O.draft_attention(ost, inp["q"], inp["k_blk"], inp["v_blk"], pairs=pairs)
+        torch.cuda.synchronize()
+        stats["tau"].append(tau_ref.copy())
+        if check_state_every and (r % check_state_every == 0 or r == rounds - 1):
+            compare_state(runner, ost, wl.dtype, heads)
+        out = LB.to_host(b.out)
+        if pairs is None:
+            close("out", out, out_ref, wl.dtype)
+        else:
+            for c, hq in pairs:
+                close("out", out[c, :, hq], out_ref[c, :, hq], wl.dtype)
+    log(f"[{wl.name}] {rounds} rounds parity ok ({time.time() - t0:.1f}s)")
+    return runner, ost, stats

@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI (no GPU: nothing here launches a kernel).
+
+The library must load, export every function that include/longspark.h
+declares, size workspaces, and reject bad arguments with the documented
+status codes before touching the device.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "longspark.h")
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+# Tests that pass never-dereferenced fake addresses run only where no GPU is
+# visible: validation must reject them before any launch, and on a machine
+# without a device a validation bug shows up as LS_ERR_HIP instead of a fault.
+no_device = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation tests run without a GPU")
+
+
+@pytest.fixture(scope="module")
+def LB():
+    from fixed_cost_drafter_amd import binding
+    return binding
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ls_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_path_calls():
+    names = _declared_functions()
+    for n in ("ls_summary_init", "ls_append_accepted", "ls_draft_attention", "ls_verify_greedy"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(LB):
+    names = _declared_functions()
+    for n in names:
+        assert hasattr(LB.lib(), n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", LB.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ls_\w+)", out))
+    assert set(names) <= exported
+    assert set(LB.EXPORTS) == set(names)
+
+
+def test_header_compiles_as_plain_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "longspark.h"\nint main(void){ls_dims d={0};(void)d;return 0;}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    "-c", str(src), "-o", str(tmp_path / "t.o")], check=True)
+
+
+def test_version_and_status_strings(LB):
+    assert LB.ls_version() == 100
+    assert LB.ls_status_string(0) == "ok"
+    for s in range(1, 7):
+        assert LB.ls_status_string(s) and LB.ls_status_string(s) != "unknown status"
+    assert LB.ls_status_string(99) == "unknown status"
+
+
+def _dims(LB, **kw):
+    base = dict(C=16, Hq=32, Hkv=8, d=128, W=1024, S=128, B=16, V=151936, dtype="bf16")
+    base.update(kw)
+    return LB.make_dims(**base)
+
+
+def test_workspace_bytes(LB):
+    d = _dims(LB)
+    small = LB.ls_workspace_bytes(d, 1024)
+    big = LB.ls_workspace_bytes(d, 131072)
+    assert 0 < small <= big
+    # init partials dominate: splits * C*Hkv*S*(2d+2) floats
+    assert big >= 4 * 16 * 8 * 128 * 258
+    # monotone in the prefix bound (a call with a shorter prefix always fits)
+    prev = 0
+    for L in (1, 63, 64, 65, 255, 256, 257, 4096, 5000, 131072):
+        w = LB.ls_workspace_bytes(d, L)
+        assert w >= prev
+        prev = w
+    # invalid dims -> 0
+    assert LB.ls_workspace_bytes(_dims(LB, Hq=30), 100) == 0
+
+
+@no_device
+@pytest.mark.parametrize("bad,status", [
+    (dict(dtype=7), 3),
+    (dict(C=0), 2), (dict(Hq=0), 2), (dict(V=0), 2), (dict(S=0), 2),
+    (dict(Hq=30), 2),                 # Hq % Hkv != 0
+    (dict(B=48), 2),                  # B > 47
+    (dict(W=16, B=16), 2),            # B+1 > W
+    (dict(d=64), 2),                  # bf16 needs d = 128
+    (dict(S=96), 2),                  # bf16 needs S in {64, 128}
+    (dict(Hq=64, Hkv=8, B=16), 2),    # B*G = 128 > 64
+    (dict(dtype="f32", d=48), 2),     # f32 d not supported
+    (dict(dtype="f32", d=16, S=300), 2),
+])
+def test_bad_dims_are_rejected_before_any_launch(LB, bad, status):
+    d = _dims(LB, **bad)
+    rc = LB.lib().ls_verify_greedy(ctypes.byref(d), 16, 16, 16, 16, 256, 1 << 30, None)
+    assert rc == status
+    st = LB.LsState()
+    rc = LB.lib().ls_draft_attention(ctypes.byref(d), ctypes.byref(st), 16, 16, 16, 16, None)
+    assert rc == status
+
+
+@no_device
+def test_null_state_and_pointers(LB):
+    d = _dims(LB)
+    L = LB.lib()
+    assert L.ls_summary_init(ctypes.byref(d), None, 16, 16, 100, 100, None) == 1
+    assert L.ls_append_accepted(None, None, 16, 16, 16, None) == 1
+    st = LB.LsState()  # all NULL
+    assert L.ls_append_accepted(ctypes.byref(d), ctypes.byref(st), 16, 16, 16, None) == 1
+    assert L.ls_verify_greedy(ctypes.byref(d), None, 16, 16, 16, 256, 1 << 30, None) == 1
+
+
+def _fake_state(LB, d, ws_bytes, align=16):
+    # distinct, never-dereferenced addresses: validation must reject or accept
+    # without touching them (no call below reaches a launch)
+    p = [0x10000 * (i + 1) for i in range(13)]
+    st = LB.LsState(*p, ws_bytes)
+    if align != 16:
+        st.ring_k = p[0] + align
+    return st
+
+
+@no_device
+def test_shape_workspace_and_alignment_errors(LB):
+    d = _dims(LB)
+    L = LB.lib()
+    need = LB.ls_workspace_bytes(d, 32768)
+    st = _fake_state(LB, d, need)
+    # L0 < 1 and stride < L0
+    assert L.ls_summary_init(ctypes.byref(d), ctypes.byref(st), 16, 16, 0, 10, None) == 2
+    assert L.ls_summary_init(ctypes.byref(d), ctypes.byref(st), 16, 16, 100, 99, None) == 2
+    # workspace one byte short
+    small = _fake_state(LB, d, need - 1)
+    assert L.ls_summary_init(ctypes.byref(d), ctypes.byref(small), 16, 16, 32768, 32768,
+                             None) == 4
+    # misaligned ring
+    bad = _fake_state(LB, d, need, align=8)
+    assert L.ls_append_accepted(ctypes.byref(d), ctypes.byref(bad), 16, 16, 16, None) == 5
+    # misaligned round inputs
+    assert L.ls_append_accepted(ctypes.byref(d), ctypes.byref(st), 18, 16, 16, None) == 5
+    assert L.ls_draft_attention(ctypes.byref(d), ctypes.byref(st), 16, 16, 16, 24, None) == 5
+    # verify: workspace too small
+    assert L.ls_verify_greedy(ctypes.byref(d), 16, 16, 16, 16, 256, 8, None) == 4
