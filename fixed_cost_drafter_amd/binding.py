@@ -205,8 +205,7 @@ class DrafterState:
         nbytes = ls_workspace_bytes(self.dims, max_L0)
         if nbytes == 0:
             raise LsError("ls_workspace_bytes", 2)
-        # zero-filled once: it holds counters that the kernels keep at zero
-        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.c_state = LsState(
             _ptr(self.ring_k), _ptr(self.ring_v), _ptr(self.ring_pos), _ptr(self.seq_len),
             _ptr(self.sum_m), _ptr(self.sum_l), _ptr(self.sum_n), _ptr(self.slot_k),

@@ -27,6 +27,7 @@ ls_status check_dims(const ls_dims* d) {
   if (d->Hq % d->Hkv != 0) return LS_ERR_SHAPE;
   if (d->B > kMaxB || d->B + 1 > d->W) return LS_ERR_SHAPE;
   if (int64_t(d->C) * (d->B + 1) > 65535) return LS_ERR_SHAPE;
+  if (d->V > (1 << 20)) return LS_ERR_SHAPE;  // verify keeps (B+1) x V/16384 keys in LDS
   if (int64_t(d->C) * d->Hkv * d->S > (int64_t(1) << 30)) return LS_ERR_SHAPE;
   const int G = d->Hq / d->Hkv;
   if (d->dtype == LS_F32) {

@@ -9,7 +9,9 @@
 //   a_jp grows by tau*ln(lambda_j), so m' = m + tau*ln(lambda_j) and l, n
 //   keep their values; the new rows a_ji = u_j.k_i/sqrt(d) + (tau-1-i) ln
 //   lambda_j are merged by the online-softmax rule; slot = n / l.
-//   seq_len[c] += tau (by the last workgroup of the sequence).
+//   seq_len[c] += tau (a second, one-workgroup launch: every workgroup of
+//   the first launch reads the old L, and the kernel boundary orders the
+//   reads before the update without a device-scope fence).
 //
 // Grid: one workgroup per (sequence, KV head, tile of 16 slots).  Each
 // workgroup stages the tau rows (and its 16 slot queries) in LDS, computes
@@ -30,14 +32,17 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
     const typename Ty::T* __restrict__ k_new, const typename Ty::T* __restrict__ v_new,
     const int32_t* __restrict__ tau_in, typename Ty::T* __restrict__ ring_k,
     typename Ty::T* __restrict__ ring_v, int32_t* __restrict__ ring_pos,
-    int32_t* __restrict__ seq_len, float* __restrict__ sum_m, float* __restrict__ sum_l,
+    const int32_t* __restrict__ seq_len, float* __restrict__ sum_m, float* __restrict__ sum_l,
     float* __restrict__ sum_n, typename Ty::T* __restrict__ slot_k,
     typename Ty::T* __restrict__ slot_v, const typename Ty::T* __restrict__ u,
-    const float* __restrict__ log_lambda, int32_t* __restrict__ err_flag,
-    uint32_t* __restrict__ counter, int Hkv, int W, int S, int B, int NT) {
-  constexpr int RS = 2 * D + 1;  // LDS row stride (floats): +1 avoids bank conflicts
-  constexpr int US = D + 1;
-  extern __shared__ float smem[];
+    const float* __restrict__ log_lambda, int32_t* __restrict__ err_flag, int Hkv, int W,
+    int S, int B, int NT) {
+  constexpr int RS = 2 * D + 4;  // LDS row stride (floats): 16-byte rows, banks offset by 4
+  constexpr int US = D + 4;
+  constexpr int Q = 2 * D / 4;   // float4 per slot of n
+  constexpr int NQ = (kSlotsPerBlock * Q + kThreads - 1) / kThreads;  // float4 of n per thread
+  extern __shared__ float4 smem4[];
+  float* smem = reinterpret_cast<float*>(smem4);
   float* rows = smem;                              // [B+1][RS]  k | v
   float* ush = rows + (B + 1) * RS;                // [16][US]   slot queries
   float* w = ush + kSlotsPerBlock * US;            // [16][B+1]  scores -> weights
@@ -49,6 +54,25 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   const int c = ch / Hkv;
   const int tid = threadIdx.x;
   const int B1 = B + 1;
+  const int j0 = tile * kSlotsPerBlock;
+  const int nj = min(kSlotsPerBlock, S - j0);
+  const int64_t slot0 = (int64_t(c) * Hkv + h) * S + j0;  // first slot of this tile
+
+  // issue the state loads first: they do not depend on tau, and their
+  // latency then overlaps the staging below
+  float4 nreg[NQ];
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int p = tid + k * kThreads, jj = p / Q;
+    nreg[k] = jj < nj ? reinterpret_cast<const float4*>(sum_n + slot0 * 2 * D)[p]
+                      : float4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m_old = 0.f, l_old = 0.f, lnl_t = 0.f;
+  if (tid < nj) {
+    m_old = sum_m[slot0 + tid];
+    l_old = sum_l[slot0 + tid];
+    lnl_t = log_lambda[j0 + tid];
+  }
 
   int T = tau_in[c];
   if (T < 1 || T > B1) {
@@ -56,8 +80,6 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
     T = T < 1 ? 1 : B1;
   }
   const int L = seq_len[c];
-  const int j0 = tile * kSlotsPerBlock;
-  const int nj = min(kSlotsPerBlock, S - j0);
 
   // stage the new rows and this tile's slot queries
   for (int idx = tid; idx < T * 2 * D; idx += kThreads) {
@@ -69,14 +91,16 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
     const int jj = idx / D, e = idx % D;
     ush[jj * US + e] = Ty::load(u, (int64_t(h) * S + j0 + jj) * D + e);
   }
-  // ring window: this tile copies rows i = tile, tile + NT, ...
+  // ring window: this tile copies rows i = tile, tile + NT, ... in 16-byte pieces
+  constexpr int V16 = D * Ty::kBytes / 16;  // 16-byte pieces per row
   for (int i = tile; i < T; i += NT) {
     const int slot = int((int64_t(L) + i) % W);
     const int64_t dst = ((int64_t(c) * Hkv + h) * W + slot) * D;
     const int64_t src = ((int64_t(c) * B1 + i) * Hkv + h) * D;
-    for (int e = tid; e < D; e += kThreads) {
-      ring_k[dst + e] = k_new[src + e];
-      ring_v[dst + e] = v_new[src + e];
+    for (int e = tid; e < 2 * V16; e += kThreads) {
+      const typename Ty::T* sp = (e < V16 ? k_new : v_new) + src;
+      typename Ty::T* dp = (e < V16 ? ring_k : ring_v) + dst;
+      reinterpret_cast<uint4*>(dp)[e % V16] = reinterpret_cast<const uint4*>(sp)[e % V16];
     }
     if (h == 0 && tid == 0) ring_pos[int64_t(c) * W + slot] = L + i;
   }
@@ -86,23 +110,27 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   const float inv_sqrt_d = 1.0f / sqrtf(float(D));
   for (int p = tid; p < nj * T; p += kThreads) {
     const int jj = p / T, i = p % T;
-    float acc = 0.f;
-#pragma unroll 16
-    for (int e = 0; e < D; ++e) acc = fmaf(ush[jj * US + e], rows[i * RS + e], acc);
+    const float4* ur = reinterpret_cast<const float4*>(ush + jj * US);
+    const float4* kr = reinterpret_cast<const float4*>(rows + i * RS);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll 8
+    for (int e = 0; e < D / 4; ++e) {
+      const float4 x = ur[e], y = kr[e];
+      a0 = fmaf(x.x, y.x, a0);
+      a1 = fmaf(x.y, y.y, a1);
+      a0 = fmaf(x.z, y.z, a0);
+      a1 = fmaf(x.w, y.w, a1);
+    }
     const float lnl = log_lambda[j0 + jj];
     const int dist = T - 1 - i;
     const float bias = dist == 0 ? 0.f : float(dist) * lnl;
-    w[jj * B1 + i] = acc * inv_sqrt_d + bias;
+    w[jj * B1 + i] = (a0 + a1) * inv_sqrt_d + bias;
   }
   __syncthreads();
 
   // per-slot merge of (m, l) with the new rows
   if (tid < nj) {
-    const int j = j0 + tid;
-    const int64_t sidx = (int64_t(c) * Hkv + h) * S + j;
-    const float lnl = log_lambda[j];
-    const float m_old = sum_m[sidx];
-    const float m_shift = (lnl == -INFINITY) ? -INFINITY : fmaf(float(T), lnl, m_old);
+    const float m_shift = (lnl_t == -INFINITY) ? -INFINITY : fmaf(float(T), lnl_t, m_old);
     float mx = m_shift;
     for (int i = 0; i < T; ++i) mx = fmaxf(mx, w[tid * B1 + i]);
     const float scale = (m_shift == -INFINITY) ? 0.f : exp_f(m_shift - mx);
@@ -112,50 +140,49 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
       w[tid * B1 + i] = pw;
       lsum += pw;
     }
-    const float l_new = fmaf(sum_l[sidx], scale, lsum);
-    sum_m[sidx] = mx;
-    sum_l[sidx] = l_new;
+    const float l_new = fmaf(l_old, scale, lsum);
+    sum_m[slot0 + tid] = mx;
+    sum_l[slot0 + tid] = l_new;
     s_scale[tid] = scale;
     s_inv_l[tid] = 1.0f / l_new;
   }
   __syncthreads();
 
   // numerator n = n * scale + sum_i w_i [k_i ; v_i]; slots = n / l
-  constexpr int Q = 2 * D / 4;  // float4 per slot
-  for (int p = tid; p < nj * Q; p += kThreads) {
-    const int jj = p / Q, e4 = (p % Q) * 4;
-    float4* np = reinterpret_cast<float4*>(sum_n + ((int64_t(c) * Hkv + h) * S + j0 + jj) * 2 * D + e4);
-    float4 acc = *np;
+#pragma unroll
+  for (int k = 0; k < NQ; ++k) {
+    const int p = tid + k * kThreads, jj = p / Q, e4 = (p % Q) * 4;
+    if (jj >= nj) continue;
+    float4 acc = nreg[k];
     const float sc = s_scale[jj];
     acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
     for (int i = 0; i < T; ++i) {
       const float wi = w[jj * B1 + i];
-      const float* r = rows + i * RS + e4;
-      acc.x = fmaf(wi, r[0], acc.x);
-      acc.y = fmaf(wi, r[1], acc.y);
-      acc.z = fmaf(wi, r[2], acc.z);
-      acc.w = fmaf(wi, r[3], acc.w);
+      const float4 r = *reinterpret_cast<const float4*>(rows + i * RS + e4);
+      acc.x = fmaf(wi, r.x, acc.x);
+      acc.y = fmaf(wi, r.y, acc.y);
+      acc.z = fmaf(wi, r.z, acc.z);
+      acc.w = fmaf(wi, r.w, acc.w);
     }
-    *np = acc;
+    reinterpret_cast<float4*>(sum_n + slot0 * 2 * D)[p] = acc;
     const float il = s_inv_l[jj];
-    const int64_t so = ((int64_t(c) * Hkv + h) * S + j0 + jj) * D + (e4 % D);
+    const int64_t so = (slot0 + jj) * D + (e4 % D);
     typename Ty::T* dst = e4 < D ? slot_k : slot_v;
     Ty::store(dst, so + 0, acc.x * il);
     Ty::store(dst, so + 1, acc.y * il);
     Ty::store(dst, so + 2, acc.z * il);
     Ty::store(dst, so + 3, acc.w * il);
   }
+}
 
-  // the last workgroup of sequence c advances seq_len (all have read L)
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const uint32_t ticket = atomicAdd(&counter[c], 1u);
-    if (ticket == uint32_t(Hkv * NT - 1)) {
-      seq_len[c] = L + T;
-      counter[c] = 0u;
-    }
-  }
+// seq_len[c] += clamp(tau[c], 1, B+1), after every append workgroup read it
+__global__ void append_commit(const int32_t* __restrict__ tau_in, int32_t* __restrict__ seq_len,
+                              int C, int B) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= C) return;
+  int T = tau_in[c];
+  T = T < 1 ? 1 : (T > B + 1 ? B + 1 : T);
+  seq_len[c] += T;
 }
 
 template <typename Ty, int D>
@@ -163,17 +190,18 @@ ls_status run(const ls_dims& d, const ls_state& st, const void* k_new, const voi
               const int32_t* tau, hipStream_t stream) {
   using T = typename Ty::T;
   const int NT = int(cdiv(d.S, kSlotsPerBlock));
-  const WsLayout lay = ws_layout(d, 1);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(st.workspace) + lay.cnt_append);
-  const size_t shmem = sizeof(float) * (size_t(d.B + 1) * (2 * D + 1) +
-                                        size_t(kSlotsPerBlock) * (D + 1) +
+  const size_t shmem = sizeof(float) * (size_t(d.B + 1) * (2 * D + 4) +
+                                        size_t(kSlotsPerBlock) * (D + 4) +
                                         size_t(kSlotsPerBlock) * (d.B + 1));
   hipLaunchKernelGGL((append_kernel<Ty, D>), dim3(d.C * d.Hkv * NT), dim3(kThreads), shmem, stream,
                      static_cast<const T*>(k_new), static_cast<const T*>(v_new), tau,
                      static_cast<T*>(st.ring_k), static_cast<T*>(st.ring_v), st.ring_pos,
                      st.seq_len, st.sum_m, st.sum_l, st.sum_n, static_cast<T*>(st.slot_k),
                      static_cast<T*>(st.slot_v), static_cast<const T*>(st.u), st.log_lambda,
-                     st.err_flag, cnt, d.Hkv, d.W, d.S, d.B, NT);
+                     st.err_flag, d.Hkv, d.W, d.S, d.B, NT);
+  if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
+  hipLaunchKernelGGL(append_commit, dim3(unsigned(cdiv(d.C, 256))), dim3(256), 0, stream, tau,
+                     st.seq_len, d.C, d.B);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
 

@@ -77,8 +77,10 @@ __device__ inline float exp_f(float x) { return __expf(x); }
 // ---------------------------------------------------------------------------
 // workspace layout (bytes), shared by the host code and the kernels
 // ---------------------------------------------------------------------------
-constexpr int kVerifyChunk = 8192;     // logits per verify workgroup
-constexpr int kDraftSplitsMax = 8;     // key splits of the MFMA draft attention
+#ifndef LS_VERIFY_CHUNK
+#define LS_VERIFY_CHUNK 16384
+#endif
+constexpr int kVerifyChunk = LS_VERIFY_CHUNK;  // logits per verify workgroup
 constexpr int kInitTargetBlocks = 512; // aim of the init grid size
 constexpr int kInitRowTile = 64;       // rows per init tile (MFMA path)
 
@@ -86,12 +88,10 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct WsLayout {
-  int64_t cnt_verify, cnt_append, cnt_draft;  // uint32 counters
   int64_t verify_part;                        // uint64 keys [C*(B+1)*vsplit]
-  int64_t draft_part;                         // float [C*Hkv*dsplit * Mpad*(d+2)]
   int64_t init_part;                          // float [isplit*C*Hkv*S*(2d+2)]
   int64_t total;
-  int vsplit, dsplit, isplit, init_rows;
+  int vsplit, isplit, init_rows;
 };
 
 inline int verify_splits(const ls_dims& d) { return int(cdiv(d.V, kVerifyChunk)); }
@@ -106,29 +106,11 @@ inline int init_rows_per_split(const ls_dims& d, int32_t L0) {
   return int(rows);
 }
 
-inline int draft_splits(const ls_dims& d) {
-  if (d.dtype != LS_BF16) return 1;
-  // about 4 key tiles of 64 per split, at most kDraftSplitsMax splits
-  int64_t nkeys = int64_t(d.W) + d.S + d.B;
-  int64_t s = cdiv(nkeys, 4 * 64);
-  if (s > kDraftSplitsMax) s = kDraftSplitsMax;
-  if (s < 1) s = 1;
-  return int(s);
-}
-
 inline WsLayout ws_layout(const ls_dims& d, int32_t max_L0) {
   WsLayout w{};
   int64_t off = 0;
-  w.cnt_verify = off;  off = align256(off + 4 * int64_t(d.C));
-  w.cnt_append = off;  off = align256(off + 4 * int64_t(d.C));
-  w.cnt_draft = off;   off = align256(off + 4 * int64_t(d.C) * d.Hkv);
   w.vsplit = verify_splits(d);
   w.verify_part = off; off = align256(off + 8 * int64_t(d.C) * (d.B + 1) * w.vsplit);
-  w.dsplit = draft_splits(d);
-  const int64_t M = int64_t(d.B) * (d.Hq / d.Hkv);
-  const int64_t Mpad = cdiv(M, 16) * 16;
-  w.draft_part = off;
-  if (w.dsplit > 1) off = align256(off + 4 * int64_t(d.C) * d.Hkv * w.dsplit * Mpad * (d.d + 2));
   // the split count of a call with L0 <= max_L0 never exceeds this bound
   const int64_t L = max_L0 < 1 ? 1 : max_L0;
   const int64_t want = cdiv(kInitTargetBlocks, int64_t(d.C) * d.Hkv);

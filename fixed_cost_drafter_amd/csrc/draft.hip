@@ -8,13 +8,11 @@
 // bidirectional (no mask inside the block).  The B*G query rows of one KV
 // head (G = Hq/Hkv) share its keys, so they form one query tile.
 //
-// bf16, d = 128: one workgroup per (KV head unit, key split).  4 waves own 16
-// query rows each; key tiles of 64 are staged in LDS (row-major K for the
-// S^T = K Q^T MFMA, transposed V for the O^T += V^T P^T MFMA); the online
-// softmax lives in registers (per query row, per lane).  Splits write
-// (m, l, O) partials and the last split of a unit to finish merges them.
-// Workgroup index = split * units + unit, so with units % 8 == 0 all splits
-// of one unit land on the same XCD and share its L2.
+// bf16, d = 128: one workgroup per (KV head unit, 32 query rows), so a
+// Qwen3-8B-shaped layer at C = 16 (128 units x 64 rows) fills 256 CUs.  Its
+// waves split the key range in parts that stream through LDS in parallel and
+// merge (m, l, O) in LDS at the end: no partials leave the workgroup, no
+// second launch.  The online softmax lives in registers (per query row).
 // f32: one workgroup per query row, plain LDS loop (small shapes).
 #include "common.hpp"
 #include "launch.hpp"
@@ -24,38 +22,97 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads, 2) void draft_mfma(
+// launch shape of the bf16 kernel: query row groups of 16 per workgroup, key
+// parts per workgroup, keys per part per step (overridable for tuning builds)
+#ifndef LS_DRAFT_RG
+#define LS_DRAFT_RG 2
+#endif
+#ifndef LS_DRAFT_KQ
+#define LS_DRAFT_KQ 4
+#endif
+#ifndef LS_DRAFT_TK
+#define LS_DRAFT_TK 32
+#endif
+
+// Where the keys of one (sequence, KV head) live: [ring | slots | block].
+struct KeySources {
+  const uint16_t *ring_k, *ring_v;
+  const int32_t* ring_pos;
+  const uint16_t *slot_k, *slot_v, *kb, *vb;
+  int W, S, B, Hkv, c, h, unit;
+};
+
+// Branch-free staging loads of NL keys (pairs 2rp, 2rp+1 every STEP keys from
+// t0): each key's source row is chosen with integer selects and all loads
+// issue back to back.  A key past `end` reads row 0 of the unit's window
+// (valid memory).  Validity is NOT decided here: `kpos` keeps the raw ring
+// position (or a marker) and `key_state` says how to read it, so nothing
+// waits on these loads until the tile is staged into LDS one step later.
+// An empty ring row holds zeros (written by init) and is masked there.
+template <int NL, int STEP>
+__device__ __forceinline__ void load_keys(u16x8 (&kr)[NL], u16x8 (&vr)[NL], int (&kpos)[NL],
+                                          int (&key_state)[NL], const KeySources s, int t0,
+                                          int end, int rp, int dg) {
+  constexpr int D = 128;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int key_raw = t0 + (i >> 1) * STEP + 2 * rp + (i & 1);
+    const bool live = key_raw < end;
+    const int key = live ? key_raw : 0;
+    const bool in_ring = key < s.W, in_slots = !in_ring && key < s.W + s.S;
+    const int row = in_ring ? s.unit * s.W + key
+                  : in_slots ? s.unit * s.S + (key - s.W)
+                             : (s.c * s.B + (key - s.W - s.S)) * s.Hkv + s.h;
+    const int64_t off = int64_t(row) * D + dg * 8;
+    const uint16_t* kbase = in_ring ? s.ring_k : (in_slots ? s.slot_k : s.kb);
+    const uint16_t* vbase = in_ring ? s.ring_v : (in_slots ? s.slot_v : s.vb);
+    kr[i] = *reinterpret_cast<const u16x8*>(kbase + off);
+    vr[i] = *reinterpret_cast<const u16x8*>(vbase + off);
+    kpos[i] = s.ring_pos[s.c * s.W + (in_ring ? key : 0)];
+    key_state[i] = !live ? 0 : (in_ring ? 1 : 2);  // 0 dead, 1 ring (check pos), 2 always valid
+  }
+}
+
+// bf16, d = 128.  Workgroup = (KV head unit, half of the query tile: 32 rows
+// = 2 row groups of 16).  Its 8 waves are 2 row groups x KQ key parts; part
+// q streams keys [q*Np, (q+1)*Np) in tiles of TK through its own LDS tile
+// (row-major K, transposed V), then the parts' (m, l, O) merge in LDS.
+// 128 threads stage one part's tile: 16 lanes cover one 256-byte key row.
+template <int RG, int KQ, int TK>
+__global__ __launch_bounds__(64 * RG * KQ, 1) void draft_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, const uint16_t* __restrict__ ring_k,
     const uint16_t* __restrict__ ring_v, const int32_t* __restrict__ ring_pos,
     const uint16_t* __restrict__ slot_k, const uint16_t* __restrict__ slot_v,
-    uint16_t* __restrict__ out, float* __restrict__ part, uint32_t* __restrict__ counter,
-    int Hq, int Hkv, int W, int S, int B, int nsplit, int keys_per_split) {
-  constexpr int D = 128, TK = 64;
+    uint16_t* __restrict__ out, int Hq, int Hkv, int W, int S, int B, int units) {
+  constexpr int D = 128;
   constexpr int KLS = D + 8, VTS = TK + 4;
-  __shared__ __attribute__((aligned(16))) uint16_t KL[TK * KLS];
-  __shared__ __attribute__((aligned(16))) uint16_t VT[D * VTS];
-  __shared__ int kvalid[TK];
-  __shared__ int is_last;
+  constexpr int MB = TK / 16, KS = TK / 32;
+  constexpr int PT = 64 * RG;               // threads staging one part's tile
+  constexpr int PAIRS = TK / (8 * RG);      // key pairs staged per thread
+  static_assert(PAIRS >= 1 && TK % (8 * RG) == 0, "tile must cover the staging threads");
+  constexpr int PART_ELEMS = TK * KLS + D * VTS;  // bf16 elements of one part's tile
+  static_assert(TK % 32 == 0, "tile must hold whole 32-key MFMA k-steps");
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[KQ * PART_ELEMS];
+  __shared__ int kvalid[KQ][TK];
 
-  const int units = gridDim.x / nsplit;
-  const int split = blockIdx.x / units;
+  const int rh = blockIdx.x / units;  // which (16*RG)-row slice of the query tile
   const int unit = blockIdx.x % units;
   const int c = unit / Hkv, h = unit % Hkv;
   const int G = Hq / Hkv, M = B * G;
   const int N = W + S + B;
-  const int k_begin = split * keys_per_split;
-  const int k_end = min(N, k_begin + keys_per_split);
+  const int Np = ((N + KQ - 1) / KQ + TK - 1) / TK * TK;  // keys per part, whole tiles
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, kg = lane >> 4;
+  const int rg = wave % RG, part = wave / RG;
   const float sm_scale = 0.08838834764831845f;  // 1/sqrt(128)
 
-  // query operand: lane (row ln of this wave, kg) holds q[row][ks*32+kg*8..+7]
-  const int row = wave * 16 + ln;
+  // query operand: lane (row ln of this wave's group, kg) holds q[row][ks*32+kg*8..+7]
+  const int row = (rh * RG + rg) * 16 + ln;
   const bool row_ok = row < M;
   const int b = row_ok ? row / G : 0;
   const int hq = h * G + (row_ok ? row % G : 0);
-  const bool wave_active = wave * 16 < M;
+  const bool group_active = (rh * RG + rg) * 16 < M;
   bf16x8 qb[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -71,73 +128,52 @@ __global__ __launch_bounds__(kThreads, 2) void draft_mfma(
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int dg = tid & 15, rp = tid >> 4;
-  u16x8 kr[4], vr[4];
-  int kv_ok[4];
-  auto load_tile = [&](int t0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = t0 + (i >> 1) * 32 + 2 * rp + (i & 1);
-      const uint16_t* ks = nullptr;
-      const uint16_t* vs = nullptr;
-      bool ok = false;
-      if (key < k_end) {
-        if (key < W) {
-          ok = ring_pos[int64_t(c) * W + key] >= 0;
-          const int64_t off = (int64_t(unit) * W + key) * D;
-          ks = ring_k + off;
-          vs = ring_v + off;
-        } else if (key < W + S) {
-          ok = true;
-          const int64_t off = (int64_t(unit) * S + (key - W)) * D;
-          ks = slot_k + off;
-          vs = slot_v + off;
-        } else {
-          ok = true;
-          const int64_t off = ((int64_t(c) * B + (key - W - S)) * Hkv + h) * D;
-          ks = kb + off;
-          vs = vb + off;
-        }
-      }
-      kv_ok[i] = ok;
-      if (ok) {
-        kr[i] = *reinterpret_cast<const u16x8*>(ks + dg * 8);
-        vr[i] = *reinterpret_cast<const u16x8*>(vs + dg * 8);
-      } else {
-        kr[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        vr[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
-    }
-  };
+  // staging: thread (lpart, dg, rp) loads keys 2rp, 2rp+1 (+ 8*RG*k) of part lpart
+  const int lpart = tid / PT;
+  const int dg = tid & 15, rp = (tid % PT) >> 4;
+  const int p_begin = lpart * Np;
+  const int p_end = min(N, p_begin + Np);
+  u16x8 kr[2 * PAIRS] = {}, vr[2 * PAIRS] = {};
+  int kpos[2 * PAIRS] = {}, kstate[2 * PAIRS] = {};
+  const KeySources src{ring_k, ring_v, ring_pos, slot_k, slot_v, kb, vb, W, S, B, Hkv, c, h, unit};
 
-  if (k_begin < k_end) load_tile(k_begin);
-  for (int t0 = k_begin; t0 < k_end; t0 += TK) {
-    __syncthreads();
+  uint16_t* myKL = tiles + lpart * PART_ELEMS;   // staged by this thread
+  uint16_t* myVT = myKL + TK * KLS;
+  const uint16_t* KL = tiles + part * PART_ELEMS;  // read by this wave
+  const uint16_t* VT = KL + TK * KLS;
+  const int steps = Np / TK;
+  const int w_begin = part * Np;
+
+  load_keys<2 * PAIRS, 8 * RG>(kr, vr, kpos, kstate, src, p_begin, p_end, rp, dg);
+  for (int st = 0; st < steps; ++st) {
+    __syncthreads();  // the previous tiles' LDS reads are done
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (i >> 1) * 32 + 2 * rp + (i & 1);
-      *reinterpret_cast<u16x8*>(&KL[r * KLS + dg * 8]) = kr[i];
-      if (dg == 0) kvalid[r] = kv_ok[i];
+    for (int i = 0; i < 2 * PAIRS; ++i) {
+      const int r = (i >> 1) * (8 * RG) + 2 * rp + (i & 1);
+      *reinterpret_cast<u16x8*>(&myKL[r * KLS + dg * 8]) = kr[i];
+      if (dg == 0) kvalid[lpart][r] = kstate[i] == 2 || (kstate[i] == 1 && kpos[i] >= 0);
     }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int r0 = half * 32 + 2 * rp;
+    for (int pp = 0; pp < PAIRS; ++pp) {
+      const int r0 = pp * (8 * RG) + 2 * rp;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t vv = uint32_t(vr[2 * half][e]) | (uint32_t(vr[2 * half + 1][e]) << 16);
-        *reinterpret_cast<uint32_t*>(&VT[(dg * 8 + e) * VTS + r0]) = vv;
+        const uint32_t vv = uint32_t(vr[2 * pp][e]) | (uint32_t(vr[2 * pp + 1][e]) << 16);
+        *reinterpret_cast<uint32_t*>(&myVT[(dg * 8 + e) * VTS + r0]) = vv;
       }
     }
     __syncthreads();
-    if (t0 + TK < k_end) load_tile(t0 + TK);
-    if (!wave_active) continue;
+    if (st + 1 < steps)  // next tile in flight during compute
+      load_keys<2 * PAIRS, 8 * RG>(kr, vr, kpos, kstate, src, p_begin + (st + 1) * TK, p_end,
+                                   rp, dg);
+    if (!group_active || w_begin + st * TK >= N) continue;
 
     // S^T[key][row]: lane (row ln, kg) holds keys mb*16 + kg*4 + r
-    f32x4 s[4];
+    f32x4 s[MB];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < MB; ++mb) s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 a = as_bf16x8(
@@ -147,12 +183,11 @@ __global__ __launch_bounds__(kThreads, 2) void draft_mfma(
 
     float tmax = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = mb * 16 + kg * 4 + r;
         float a = s[mb][r] * sm_scale;
-        if (!kvalid[key]) a = -INFINITY;
+        if (!kvalid[part][mb * 16 + kg * 4 + r]) a = -INFINITY;
         s[mb][r] = a;
         tmax = fmaxf(tmax, a);
       }
@@ -163,9 +198,9 @@ __global__ __launch_bounds__(kThreads, 2) void draft_mfma(
     const float scale = m_run == -INFINITY ? 0.f : exp_f(m_run - m_use);
     m_run = m_new;
     float lsum = 0.f;
-    u16x8 pv[2];
+    u16x8 pv[KS];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint16_t pb = f32_to_bf16(exp_f(s[mb][r] - m_use));
@@ -173,87 +208,70 @@ __global__ __launch_bounds__(kThreads, 2) void draft_mfma(
         pv[mb >> 1][(mb & 1) * 4 + r] = pb;
       }
     l_run = fmaf(l_run, scale, lsum);
-    const bf16x8 pk0 = as_bf16x8(pv[0]), pk1 = as_bf16x8(pv[1]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] *= scale;
 
-    // O^T[dim][row] += V^T[dim][key] P^T[key][row]
+    // O^T[dim][row] += V^T[dim][key] P^T[key][row]; the A operand's k order
+    // (keys 32ks+4kg..+3, 32ks+16+4kg..+3) matches pv's element order
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 pk = as_bf16x8(pv[ks]);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int mb = 0; mb < 8; ++mb) {
         const uint16_t* base = &VT[(mb * 16 + ln) * VTS + ks * 32 + kg * 4];
         const u16x4 lo = *reinterpret_cast<const u16x4*>(base);
         const u16x4 hi = *reinterpret_cast<const u16x4*>(base + 16);
         const bf16x8 a = as_bf16x8(u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        o[mb] = mfma16x16x32(a, ks == 0 ? pk0 : pk1, o[mb]);
+        o[mb] = mfma16x16x32(a, pk, o[mb]);
       }
+    }
   }
 
   float lt = l_run;
   lt += __shfl_xor(lt, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
 
-  if (nsplit == 1) {
-    if (row_ok) {
-      const float il = 1.0f / lt;
-      uint16_t* orow = out + ((int64_t(c) * B + b) * Hq + hq) * D;
+  // merge the key parts in LDS (reusing the tile buffers): parts 1..KQ-1
+  // publish (m, l, O) in the same lane layout, part 0 combines and writes
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(tiles);  // [KQ-1][RG groups][64 lanes][34]
+  static_assert((KQ - 1) * RG * 64 * 34 * 4 <= KQ * PART_ELEMS * 2, "merge area fits the tiles");
+  if (part > 0 && group_active) {
+    float* dst = red + (((part - 1) * RG + rg) * 64 + lane) * 34;
+    dst[0] = m_run;
+    dst[1] = lt;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[2 + mb * 4 + r] = o[mb][r];
+  }
+  __syncthreads();
+  if (part == 0 && row_ok) {
+    float mx = m_run;
+#pragma unroll
+    for (int p2 = 1; p2 < KQ; ++p2) mx = fmaxf(mx, red[(((p2 - 1) * RG + rg) * 64 + lane) * 34]);
+    const float w0 = m_run == -INFINITY ? 0.f : exp_f(m_run - mx);
+    float l = lt * w0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= w0;
+#pragma unroll
+    for (int p2 = 1; p2 < KQ; ++p2) {
+      const float* src = red + (((p2 - 1) * RG + rg) * 64 + lane) * 34;
+      const float wq = src[0] == -INFINITY ? 0.f : exp_f(src[0] - mx);
+      l = fmaf(src[1], wq, l);
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) orow[mb * 16 + kg * 4 + r] = f32_to_bf16(o[mb][r] * il);
-    }
-    return;
-  }
-
-  // partial of this split: pm[Mpad] | pl[Mpad] | po[Mpad][D]
-  const int Mpad = (M + 15) & ~15;
-  const int64_t pstride = int64_t(Mpad) * (D + 2);
-  float* pb = part + (int64_t(unit) * nsplit + split) * pstride;
-  if (wave_active) {
-    if (kg == 0) {
-      pb[row] = m_run;
-      pb[Mpad + row] = lt;
-    }
-    float* po = pb + 2 * Mpad + int64_t(row) * D;
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f32x4*>(po + mb * 16 + kg * 4) = o[mb];
-  }
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    const uint32_t ticket = atomicAdd(&counter[unit], 1u);
-    is_last = ticket == uint32_t(nsplit - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-
-  // merge the splits of this unit
-  const float* ub = part + int64_t(unit) * nsplit * pstride;
-  for (int p = tid; p < M * (D / 4); p += kThreads) {
-    const int r = p / (D / 4), e4 = (p % (D / 4)) * 4;
-    float mx = -INFINITY;
-    for (int s2 = 0; s2 < nsplit; ++s2) mx = fmaxf(mx, __builtin_nontemporal_load(ub + s2 * pstride + r));
-    float l = 0.f;
-    f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < nsplit; ++s2) {
-      const float* sp = ub + s2 * pstride;
-      const float ms = __builtin_nontemporal_load(sp + r);
-      const float wgt = ms == -INFINITY ? 0.f : exp_f(ms - mx);
-      l = fmaf(__builtin_nontemporal_load(sp + Mpad + r), wgt, l);
-      const f32x4 ov = __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4*>(sp + 2 * Mpad + int64_t(r) * D + e4));
-      a += ov * wgt;
+        for (int r = 0; r < 4; ++r) o[mb][r] = fmaf(src[2 + mb * 4 + r], wq, o[mb][r]);
     }
     const float il = 1.0f / l;
-    const int bb = r / G, hh = h * G + r % G;
-    uint16_t* orow = out + ((int64_t(c) * B + bb) * Hq + hh) * D + e4;
-    u16x4 ob = u16x4{f32_to_bf16(a[0] * il), f32_to_bf16(a[1] * il), f32_to_bf16(a[2] * il),
-                     f32_to_bf16(a[3] * il)};
-    *reinterpret_cast<u16x4*>(orow) = ob;
+    uint16_t* orow = out + ((int64_t(c) * B + b) * Hq + hq) * D;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      *reinterpret_cast<u16x4*>(orow + mb * 16 + kg * 4) =
+          u16x4{f32_to_bf16(o[mb][0] * il), f32_to_bf16(o[mb][1] * il),
+                f32_to_bf16(o[mb][2] * il), f32_to_bf16(o[mb][3] * il)};
   }
-  if (tid == 0) counter[unit] = 0u;
 }
 
 // generic path: one workgroup per (sequence, block row, query head)
@@ -352,21 +370,18 @@ ls_status run_generic(const ls_dims& d, const ls_state& st, const void* q, const
 ls_status launch_draft(const ls_dims& d, const ls_state& st, const void* q, const void* kb,
                        const void* vb, void* out, hipStream_t stream) {
   if (d.dtype == LS_BF16) {
-    const WsLayout lay = ws_layout(d, 1);
-    const int N = d.W + d.S + d.B;
-    const int kps = int(cdiv(cdiv(N, lay.dsplit), 64) * 64);
-    const int nsplit = int(cdiv(N, kps));  // <= lay.dsplit
+    constexpr int RG = LS_DRAFT_RG, KQ = LS_DRAFT_KQ, TK = LS_DRAFT_TK;
     const int units = d.C * d.Hkv;
-    char* ws = static_cast<char*>(st.workspace);
-    hipLaunchKernelGGL(draft_mfma, dim3(units * nsplit), dim3(kThreads), 0, stream,
+    const int M = d.B * (d.Hq / d.Hkv);
+    const int slices = int(cdiv(M, 16 * RG));
+    hipLaunchKernelGGL((draft_mfma<RG, KQ, TK>), dim3(units * slices), dim3(64 * RG * KQ), 0,
+                       stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kb),
                        static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(st.ring_k),
                        static_cast<const uint16_t*>(st.ring_v), st.ring_pos,
                        static_cast<const uint16_t*>(st.slot_k),
-                       static_cast<const uint16_t*>(st.slot_v), static_cast<uint16_t*>(out),
-                       reinterpret_cast<float*>(ws + lay.draft_part),
-                       reinterpret_cast<uint32_t*>(ws + lay.cnt_draft), d.Hq, d.Hkv, d.W, d.S,
-                       d.B, nsplit, kps);
+                       static_cast<const uint16_t*>(st.slot_v), static_cast<uint16_t*>(out), d.Hq,
+                       d.Hkv, d.W, d.S, d.B, units);
     return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
   }
   switch (d.d) {

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
   // pairs rp + k*(NT/16); 16 lanes cover one 256-byte row segment
   const int dg = tid & 15, rp = tid >> 4;
   u16x8 kr[2 * PAIRS], vr[2 * PAIRS];
-  auto load_tile = [&](int t0) {
+  auto load_tile = [&](int t0) __attribute__((always_inline)) {
     const int nrows = min(TR, r_end - t0);
 #pragma unroll
     for (int i = 0; i < 2 * PAIRS; ++i) {

@@ -4,13 +4,14 @@
 // g_i = argmax_v logits[c, i, v] with the lowest index on ties; M = longest
 // prefix with draft[c, i] == g_i; tau = M + 1.
 //
-// One launch.  Each workgroup scans one chunk of one logits row with 16-byte
-// loads and reduces (value, index) to a 64-bit key whose unsigned order is
-// "larger value first, then lower index": the high word is the value's bits
-// mapped to an order-preserving unsigned integer (+0 and -0 merged), the low
-// word is ~index.  Keys go to the workspace; the last workgroup of a sequence
-// to finish (a device-scope counter) reduces its (B+1) x splits keys, counts
-// the accepted prefix and writes target_tok and tau, then resets the counter.
+// Two launches.  (1) Each workgroup scans one chunk of one logits row with
+// 16-byte non-temporal loads and reduces (value, index) to a 64-bit key whose
+// unsigned order is "larger value first, then lower index": the high word is
+// the value's bits mapped to an order-preserving unsigned integer (+0 and -0
+// merged), the low word is ~index.  (2) One workgroup per sequence reduces
+// its (B+1) x splits keys, counts the accepted prefix and writes target_tok
+// and tau.  The kernel boundary orders (1) before (2): no device-scope fence
+// is needed, which on a multi-XCD GPU would write back and invalidate L2.
 // The logits are streamed once (HBM-bound: 2 bytes per bf16 logit).
 #include "common.hpp"
 #include "launch.hpp"
@@ -46,14 +47,12 @@ struct Vec16<BF16> {
 };
 
 template <typename Ty>
-__global__ __launch_bounds__(kThreads) void verify_kernel(
-    const typename Ty::T* __restrict__ logits, const int32_t* __restrict__ draft,
-    int32_t* __restrict__ target_tok, int32_t* __restrict__ tau, uint64_t* __restrict__ part,
-    uint32_t* __restrict__ counter, int V, int B, int nsplit, int chunk, int vec_ok) {
+__global__ __launch_bounds__(kThreads) void verify_partial(
+    const typename Ty::T* __restrict__ logits, uint64_t* __restrict__ part, int V, int nsplit,
+    int chunk, int vec_ok) {
   using VT = Vec16<Ty>;
   const int split = blockIdx.x;
   const int row = blockIdx.y;  // c * (B+1) + i
-  const int c = row / (B + 1);
   const int tid = threadIdx.x;
   const typename Ty::T* x = logits + int64_t(row) * V;
   const int begin = split * chunk;
@@ -66,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
     // so a strict '>' keeps the lowest index among equal values.
     const typename VT::V* xv = reinterpret_cast<const typename VT::V*>(x + begin);
     const int nvec = (end - begin) / VT::N;
-    constexpr int U = 4;
+    constexpr int U = (kVerifyChunk / VT::N + kThreads - 1) / kThreads;  // loads in flight
     for (int base = 0; base < nvec; base += kThreads * U) {
       typename VT::V buf[U];
 #pragma unroll
@@ -108,7 +107,6 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
     key = other > key ? other : key;
   }
   __shared__ uint64_t wkeys[kThreads / 64];
-  __shared__ int is_last;
   const int lane = tid & 63, wave = tid >> 6;
   if (lane == 0) wkeys[wave] = key;
   __syncthreads();
@@ -116,25 +114,25 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
     uint64_t k = wkeys[0];
     for (int w = 1; w < kThreads / 64; ++w) k = wkeys[w] > k ? wkeys[w] : k;
     part[int64_t(row) * nsplit + split] = k;
-    __threadfence();
-    const uint32_t blocks_per_seq = uint32_t(B + 1) * uint32_t(nsplit);
-    uint32_t ticket = atomicAdd(&counter[c], 1u);
-    is_last = (ticket == blocks_per_seq - 1);
   }
-  __syncthreads();
-  if (!is_last) return;
+}
 
-  // last workgroup of sequence c: reduce the keys of its B+1 rows
-  __threadfence();
-  __shared__ int32_t g[kThreads];
+// one workgroup per sequence: keys -> g_i -> accepted prefix -> tau
+__global__ __launch_bounds__(kThreads) void verify_finalize(
+    const uint64_t* __restrict__ part, const int32_t* __restrict__ draft,
+    int32_t* __restrict__ target_tok, int32_t* __restrict__ tau, int B, int nsplit) {
+  extern __shared__ uint64_t keys[];  // [(B+1) * nsplit]
+  __shared__ int32_t g[64];
+  const int c = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = (B + 1) * nsplit;
+  const uint64_t* p = part + int64_t(c) * n;
+  for (int i = tid; i < n; i += kThreads) keys[i] = p[i];
+  __syncthreads();
   for (int i = tid; i <= B; i += kThreads) {
-    const uint64_t* p = part + (int64_t(c) * (B + 1) + i) * nsplit;
     uint64_t k = 0;
-    for (int s = 0; s < nsplit; ++s) {
-      uint64_t ks = __atomic_load_n(p + s, __ATOMIC_RELAXED);
-      k = ks > k ? ks : k;
-    }
-    int32_t gi = int32_t(~uint32_t(k));
+    for (int s = 0; s < nsplit; ++s) k = keys[i * nsplit + s] > k ? keys[i * nsplit + s] : k;
+    const int32_t gi = int32_t(~uint32_t(k));
     g[i] = gi;
     target_tok[int64_t(c) * (B + 1) + i] = gi;
   }
@@ -143,7 +141,6 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(
     int M = 0;
     while (M < B && draft[int64_t(c) * B + M] == g[M]) ++M;
     tau[c] = M + 1;
-    counter[c] = 0u;
   }
 }
 
@@ -159,16 +156,16 @@ ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* dra
   const int vec_ok = ((int64_t(d.V) * esz) % 16 == 0) && ((uintptr_t(logits) & 15) == 0);
   dim3 grid(nsplit, d.C * (d.B + 1));
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + lay.verify_part);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + lay.cnt_verify);
-  if (d.dtype == LS_BF16) {
-    hipLaunchKernelGGL(verify_kernel<BF16>, grid, dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(logits), draft, target_tok, tau, part, cnt,
-                       d.V, d.B, nsplit, chunk, vec_ok);
-  } else {
-    hipLaunchKernelGGL(verify_kernel<F32>, grid, dim3(kThreads), 0, stream,
-                       static_cast<const float*>(logits), draft, target_tok, tau, part, cnt, d.V,
-                       d.B, nsplit, chunk, vec_ok);
-  }
+  if (d.dtype == LS_BF16)
+    hipLaunchKernelGGL(verify_partial<BF16>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(logits), part, d.V, nsplit, chunk, vec_ok);
+  else
+    hipLaunchKernelGGL(verify_partial<F32>, grid, dim3(kThreads), 0, stream,
+                       static_cast<const float*>(logits), part, d.V, nsplit, chunk, vec_ok);
+  if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
+  const size_t shmem = sizeof(uint64_t) * size_t(d.B + 1) * nsplit;
+  hipLaunchKernelGGL(verify_finalize, dim3(d.C), dim3(kThreads), shmem, stream, part, draft,
+                     target_tok, tau, d.B, nsplit);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
 

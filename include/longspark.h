@@ -31,7 +31,8 @@
  *   - Calls that share one workspace or one state must not overlap (same
  *     stream, or ordered with events).
  *
- * Supported shapes: Hq % Hkv == 0; 1 <= B, B+1 <= W; V >= 1; S >= 1.
+ * Supported shapes: Hq % Hkv == 0; 1 <= B <= 47, B+1 <= W; 1 <= V <= 2^20;
+ *   C*(B+1) <= 65535; S >= 1.
  *   LS_F32 : d in {16, 32, 64, 128}, S <= 256, B*Hq/Hkv <= 64.
  *   LS_BF16: d == 128, S in {64, 128}, B*Hq/Hkv <= 64.
  * Pointers to dtype arrays and to sum_n must be 16-byte aligned.
@@ -94,9 +95,9 @@ typedef struct ls_state {
 } ls_state;
 
 /* Bytes of workspace that every call below needs for prefixes of up to
- * `max_L0` rows.  The workspace must be ZERO-FILLED ONCE after allocation:
- * it holds completion counters that each kernel returns to zero before it
- * ends.  Returns 0 if `dims` is invalid. */
+ * `max_L0` rows.  The workspace is scratch that each call overwrites before
+ * reading (split partials); it needs no initialisation and carries nothing
+ * from one call to the next.  Returns 0 if `dims` is invalid. */
 size_t ls_workspace_bytes(const ls_dims* dims, int32_t max_L0);
 
 /* Prefill view (Fig. 3: the summary is initialised over the full prefix).

@@ -109,6 +109,7 @@ def test_workspace_bytes(LB):
     (dict(Hq=64, Hkv=8, B=16), 2),    # B*G = 128 > 64
     (dict(dtype="f32", d=48), 2),     # f32 d not supported
     (dict(dtype="f32", d=16, S=300), 2),
+    (dict(V=(1 << 20) + 1), 2),       # vocabulary above 2^20
 ])
 def test_bad_dims_are_rejected_before_any_launch(LB, bad, status):
     d = _dims(LB, **bad)

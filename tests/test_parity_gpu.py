@@ -90,7 +90,7 @@ def test_tau_out_of_range_is_clamped_and_flagged():
     assert int(LB.to_host(runner.state.err_flag)[0]) == 0
 
 
-def test_counters_return_to_zero_and_runs_are_deterministic():
+def test_runs_are_deterministic():
     import torch
     from fixed_cost_drafter_amd import binding as LB
     from fixed_cost_drafter_amd.runner import PathRunner, upload_round
@@ -109,9 +109,6 @@ def test_counters_return_to_zero_and_runs_are_deterministic():
         snap = rn.snapshot()
         snap["out"] = LB.to_host(rn.buf.out)
         outs.append(snap)
-        ws = LB.to_host(rn.state.workspace)
-        from_layout = 3 * 256  # the three counter blocks lead the workspace
-        assert not ws[:from_layout].any(), "completion counters must be back at zero"
     for k in outs[0]:
         H.exact(f"rerun {k}", outs[1][k], outs[0][k])
 
