@@ -168,6 +168,30 @@ def run_gpu(args, wl):
             res["draft_s"] = statistics.mean(x[2].elapsed_time(x[3]) for x in ev) * 1e-3
         return res
 
+    def run_graph(L0):
+        """K rounds captured once in a HIP graph, replayed; the same inputs as run_rounds."""
+        runner.init(L0)
+        for r in range(args.warmup):
+            runner.round(pool[r % len(pool)][0], rounds[r])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            g.capture_begin()
+            for r in range(args.warmup, n_rounds):
+                runner.round(pool[r % len(pool)][0], rounds[r])
+            g.capture_end()
+        torch.cuda.current_stream().wait_stream(side)
+        runner.init(L0)  # capture does not execute: replay from the same state
+        for r in range(args.warmup):
+            runner.round(pool[r % len(pool)][0], rounds[r])
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        return dict(wall_s=time.perf_counter() - t_start)
+
     out = {}
     # headline: the workload's own prefix
     out["init_s"] = time_init(wl.L0)
@@ -175,6 +199,9 @@ def run_gpu(args, wl):
     taus = LB.to_host(runner.buf.tau)
     kern = run_rounds(wl.L0, per_call_events=True)
     out.update(main=main, kern=kern)
+    if args.graph:
+        out["graph"] = run_graph(wl.L0)
+        log(f"graph replay: {args.steps / out['graph']['wall_s']:.0f} rounds/s")
     sweep = {}
     if args.sweep:
         for L0 in WLM.SWEEP_L0:
@@ -240,6 +267,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", dest="cpu", action="store_false")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the K rounds captured in one HIP graph")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the drafting "
@@ -297,6 +326,7 @@ def main(argv=None):
         "round_gb_per_s": round(alg["round"] * value / 1e9, 1),
         "gpu_event_ms_per_step": round(main_r["gpu_s"] / args.steps * 1e3, 5),
         "sweep": g["sweep"],
+        "graph_rounds_per_s": (round(args.steps / g["graph"]["wall_s"], 1) if "graph" in g else None),
         "state_bytes_per_seq": g["state_bytes_per_seq"],
     }
     if args.cpu:

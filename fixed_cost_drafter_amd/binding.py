@@ -110,6 +110,17 @@ def make_dims(C, Hq, Hkv, d, W, S, B, V, dtype) -> LsDims:
     return LsDims(C, Hq, Hkv, d, W, S, B, V, dt)
 
 
+def value_tile(rows: int) -> int:
+    """Key-tile width of the window / slot value layout [rows/tw][d][tw]."""
+    return 32 if rows % 32 == 0 else rows
+
+
+def values_to_rows(a: np.ndarray) -> np.ndarray:
+    """Host copy of key-tiled values [..., rows/tw, d, tw] -> [..., rows, d]."""
+    *lead, nt, d, tw = a.shape
+    return np.ascontiguousarray(np.swapaxes(a, -1, -2).reshape(*lead, nt * tw, d))
+
+
 def torch_dtype(dtype: str) -> torch.dtype:
     return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
 
@@ -189,14 +200,15 @@ class DrafterState:
         td = torch_dtype(dtype)
         z = lambda *shape, dt=td: torch.zeros(shape, dtype=dt, device=device)
         self.ring_k = z(C, Hkv, W, d)
-        self.ring_v = z(C, Hkv, W, d)
+        tw, ts = value_tile(W), value_tile(S)
+        self.ring_v = z(C, Hkv, W // tw, d, tw)  # key-tiled values
         self.ring_pos = torch.full((C, W), -1, dtype=torch.int32, device=device)
         self.seq_len = z(C, dt=torch.int32)
         self.sum_m = z(C, Hkv, S, dt=torch.float32)
         self.sum_l = z(C, Hkv, S, dt=torch.float32)
         self.sum_n = z(C, Hkv, S, 2 * d, dt=torch.float32)
         self.slot_k = z(C, Hkv, S, d)
-        self.slot_v = z(C, Hkv, S, d)
+        self.slot_v = z(C, Hkv, S // ts, d, ts)  # key-tiled values
         self.u = u if isinstance(u, torch.Tensor) else to_device(u, device)
         lg = log_lambda if isinstance(log_lambda, torch.Tensor) else to_device(
             np.asarray(log_lambda, dtype=np.float32), device)

@@ -36,6 +36,7 @@ ls_status check_dims(const ls_dims* d) {
   } else {
     if (d->d != 128) return LS_ERR_SHAPE;
     if (d->S != 64 && d->S != 128) return LS_ERR_SHAPE;
+    if (d->W % 32 != 0) return LS_ERR_SHAPE;  // 32-key chunks never straddle window | slots
     if (d->B * G > 64) return LS_ERR_SHAPE;
   }
   return LS_OK;
@@ -48,6 +49,7 @@ ls_status check_state(const ls_state* s, const ls_dims& d, int32_t L0) {
       !s->workspace)
     return LS_ERR_NULL;
   if (!aligned16(s->ring_k) || !aligned16(s->ring_v) || !aligned16(s->sum_n) ||
+      !aligned16(s->ring_pos) ||
       !aligned16(s->slot_k) || !aligned16(s->slot_v) || !aligned16(s->u) ||
       !aligned16(s->workspace))
     return LS_ERR_ALIGN;

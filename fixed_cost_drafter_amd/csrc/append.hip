@@ -9,15 +9,17 @@
 //   a_jp grows by tau*ln(lambda_j), so m' = m + tau*ln(lambda_j) and l, n
 //   keep their values; the new rows a_ji = u_j.k_i/sqrt(d) + (tau-1-i) ln
 //   lambda_j are merged by the online-softmax rule; slot = n / l.
-//   seq_len[c] += tau (a second, one-workgroup launch: every workgroup of
-//   the first launch reads the old L, and the kernel boundary orders the
-//   reads before the update without a device-scope fence).
+//   seq_len[c] += tau (a second, tiny launch: every workgroup of the first
+//   launch reads the old L, and the kernel boundary orders those reads
+//   before the update without a device-scope fence).
 //
 // Grid: one workgroup per (sequence, KV head, tile of 16 slots).  Each
 // workgroup stages the tau rows (and its 16 slot queries) in LDS, computes
 // the 16 x tau scores, and streams its slots' fp32 state once (coalesced
 // float4), so the per-round traffic is the state read + write + slot write,
-// independent of the prefix length.
+// independent of the prefix length.  The tiles share the ring copy of the
+// tau rows.  Values of the window and of the slots are written in key tiles
+// of 32 ([rows/32][d][32]), the layout the drafter's P.V product reads.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -46,14 +48,16 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   float* rows = smem;                              // [B+1][RS]  k | v
   float* ush = rows + (B + 1) * RS;                // [16][US]   slot queries
   float* w = ush + kSlotsPerBlock * US;            // [16][B+1]  scores -> weights
+  constexpr int SVS = kSlotsPerBlock + 1;          // slot-value staging stride
+  float* svals = w + kSlotsPerBlock * (B + 1);     // [d][SVS]   slot values
   __shared__ float s_scale[kSlotsPerBlock], s_inv_l[kSlotsPerBlock];
 
+  const int tid = threadIdx.x;
+  const int B1 = B + 1;
   const int tile = blockIdx.x % NT;
   const int ch = blockIdx.x / NT;
   const int h = ch % Hkv;
   const int c = ch / Hkv;
-  const int tid = threadIdx.x;
-  const int B1 = B + 1;
   const int j0 = tile * kSlotsPerBlock;
   const int nj = min(kSlotsPerBlock, S - j0);
   const int64_t slot0 = (int64_t(c) * Hkv + h) * S + j0;  // first slot of this tile
@@ -91,18 +95,27 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
     const int jj = idx / D, e = idx % D;
     ush[jj * US + e] = Ty::load(u, (int64_t(h) * S + j0 + jj) * D + e);
   }
-  // ring window: this tile copies rows i = tile, tile + NT, ... in 16-byte pieces
-  constexpr int V16 = D * Ty::kBytes / 16;  // 16-byte pieces per row
-  for (int i = tile; i < T; i += NT) {
-    const int slot = int((int64_t(L) + i) % W);
-    const int64_t dst = ((int64_t(c) * Hkv + h) * W + slot) * D;
-    const int64_t src = ((int64_t(c) * B1 + i) * Hkv + h) * D;
-    for (int e = tid; e < 2 * V16; e += kThreads) {
-      const typename Ty::T* sp = (e < V16 ? k_new : v_new) + src;
-      typename Ty::T* dp = (e < V16 ? ring_k : ring_v) + dst;
-      reinterpret_cast<uint4*>(dp)[e % V16] = reinterpret_cast<const uint4*>(sp)[e % V16];
+  // ring window, shared by the NT tiles of (c, h): tile t copies the key
+  // pieces p = t, t + NT, ... (16 bytes of one new row each) and the values
+  // of dimensions t, t + NT, ...; lanes run over the tau rows, so their
+  // 2-byte stores land on consecutive slots of the key-tiled value layout
+  {
+    constexpr int V16 = D * Ty::kBytes / 16;  // 16-byte pieces per key row
+    const int64_t unit = int64_t(c) * Hkv + h;
+    for (int p = tile + NT * tid; p < T * V16; p += NT * kThreads) {
+      const int i = p / V16, e = p % V16;
+      const int slot = int((int64_t(L) + i) % W);
+      reinterpret_cast<uint4*>(ring_k + (unit * W + slot) * D)[e] =
+          reinterpret_cast<const uint4*>(k_new + ((int64_t(c) * B1 + i) * Hkv + h) * D)[e];
     }
-    if (h == 0 && tid == 0) ring_pos[int64_t(c) * W + slot] = L + i;
+    const int ndim = (D - tile + NT - 1) / NT;  // dimensions tile, tile+NT, ...
+    for (int p = tid; p < ndim * T; p += kThreads) {
+      const int dim = tile + NT * (p / T), i = p % T;
+      const int slot = int((int64_t(L) + i) % W);
+      ring_v[value_index(unit, W, D, slot, dim)] = v_new[((int64_t(c) * B1 + i) * Hkv + h) * D + dim];
+    }
+    if (h == 0 && tile == 0)
+      for (int i = tid; i < T; i += kThreads) ring_pos[int64_t(c) * W + int((int64_t(L) + i) % W)] = L + i;
   }
   __syncthreads();
 
@@ -166,12 +179,29 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
     }
     reinterpret_cast<float4*>(sum_n + slot0 * 2 * D)[p] = acc;
     const float il = s_inv_l[jj];
-    const int64_t so = (slot0 + jj) * D + (e4 % D);
-    typename Ty::T* dst = e4 < D ? slot_k : slot_v;
-    Ty::store(dst, so + 0, acc.x * il);
-    Ty::store(dst, so + 1, acc.y * il);
-    Ty::store(dst, so + 2, acc.z * il);
-    Ty::store(dst, so + 3, acc.w * il);
+    if (e4 < D) {  // pooled key, [S][d]
+      const int64_t so = (slot0 + jj) * D + e4;
+      Ty::store(slot_k, so + 0, acc.x * il);
+      Ty::store(slot_k, so + 1, acc.y * il);
+      Ty::store(slot_k, so + 2, acc.z * il);
+      Ty::store(slot_k, so + 3, acc.w * il);
+    } else {  // pooled value: staged [dim][slot] in LDS, written below
+      float* sv = svals + (e4 - D) * SVS + jj;
+      sv[0 * SVS] = acc.x * il;
+      sv[1 * SVS] = acc.y * il;
+      sv[2 * SVS] = acc.z * il;
+      sv[3 * SVS] = acc.w * il;
+    }
+  }
+  // slot values to the key-tiled layout: per dimension the tile's nj slots
+  // are consecutive, so each thread stores a run of slots of one dimension
+  __syncthreads();
+  {
+    const int64_t unit = int64_t(c) * Hkv + h;
+    for (int p = tid; p < D * nj; p += kThreads) {
+      const int dim = p / nj, jj = p % nj;
+      Ty::store(slot_v, value_index(unit, S, D, j0 + jj, dim), svals[dim * SVS + jj]);
+    }
   }
 }
 
@@ -192,7 +222,8 @@ ls_status run(const ls_dims& d, const ls_state& st, const void* k_new, const voi
   const int NT = int(cdiv(d.S, kSlotsPerBlock));
   const size_t shmem = sizeof(float) * (size_t(d.B + 1) * (2 * D + 4) +
                                         size_t(kSlotsPerBlock) * (D + 4) +
-                                        size_t(kSlotsPerBlock) * (d.B + 1));
+                                        size_t(kSlotsPerBlock) * (d.B + 1) +
+                                        size_t(D) * (kSlotsPerBlock + 1));
   hipLaunchKernelGGL((append_kernel<Ty, D>), dim3(d.C * d.Hkv * NT), dim3(kThreads), shmem, stream,
                      static_cast<const T*>(k_new), static_cast<const T*>(v_new), tau,
                      static_cast<T*>(st.ring_k), static_cast<T*>(st.ring_v), st.ring_pos,

@@ -75,6 +75,18 @@ __device__ inline uint64_t shfl_xor_u64(uint64_t x, int o) {
 __device__ inline float exp_f(float x) { return __expf(x); }
 
 // ---------------------------------------------------------------------------
+// value layout of the window and of the slots: key tiles of 32,
+// [unit][rows/32][d][32], so the 32 keys of a tile are contiguous for each
+// dimension and a whole tile is one contiguous block; when rows is not a
+// multiple of 32 the tile is the whole row range ([unit][d][rows]).
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int value_tile(int rows) { return rows % 32 == 0 ? 32 : rows; }
+__host__ __device__ inline int64_t value_index(int64_t unit, int rows, int d, int key, int dim) {
+  const int tw = value_tile(rows);
+  return ((unit * (rows / tw) + key / tw) * d + dim) * tw + key % tw;
+}
+
+// ---------------------------------------------------------------------------
 // workspace layout (bytes), shared by the host code and the kernels
 // ---------------------------------------------------------------------------
 #ifndef LS_VERIFY_CHUNK
@@ -88,6 +100,7 @@ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct WsLayout {
+  int64_t draft_part;                         // float [C*Hkv*halves * Mpad*(d+2)]
   int64_t verify_part;                        // uint64 keys [C*(B+1)*vsplit]
   int64_t init_part;                          // float [isplit*C*Hkv*S*(2d+2)]
   int64_t total;
@@ -106,9 +119,23 @@ inline int init_rows_per_split(const ls_dims& d, int32_t L0) {
   return int(rows);
 }
 
+// key halves of the bf16 draft attention: two workgroups per KV head unit
+// when there are too few units to fill the GPU with one, and enough keys
+inline int draft_halves(const ls_dims& d) {
+  if (d.dtype != LS_BF16) return 1;
+  const int64_t chunks = (int64_t(d.W) + d.S) / 32 + cdiv(d.B, 32);
+  return (int64_t(d.C) * d.Hkv < 256 && chunks >= 16) ? 2 : 1;
+}
+
 inline WsLayout ws_layout(const ls_dims& d, int32_t max_L0) {
   WsLayout w{};
   int64_t off = 0;
+  {
+    const int64_t Mpad = 64;  // draft partials hold 4 row groups of 16
+    w.draft_part = off;
+    const int halves = draft_halves(d);
+    if (halves > 1) off = align256(off + 4 * int64_t(d.C) * d.Hkv * halves * Mpad * (d.d + 2));
+  }
   w.vsplit = verify_splits(d);
   w.verify_part = off; off = align256(off + 8 * int64_t(d.C) * (d.B + 1) * w.vsplit);
   // the split count of a call with L0 <= max_L0 never exceeds this bound

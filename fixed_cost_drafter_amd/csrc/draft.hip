@@ -8,12 +8,26 @@
 // bidirectional (no mask inside the block).  The B*G query rows of one KV
 // head (G = Hq/Hkv) share its keys, so they form one query tile.
 //
-// bf16, d = 128: one workgroup per (KV head unit, 32 query rows), so a
-// Qwen3-8B-shaped layer at C = 16 (128 units x 64 rows) fills 256 CUs.  Its
-// waves split the key range in parts that stream through LDS in parallel and
-// merge (m, l, O) in LDS at the end: no partials leave the workgroup, no
-// second launch.  The online softmax lives in registers (per query row).
-// f32: one workgroup per query row, plain LDS loop (small shapes).
+// bf16, d = 128 (draft_mfma).  One workgroup per (KV head unit, 32 query
+// rows), so a Qwen3-8B-shaped layer at C = 16 (128 units x 64 rows) fills the
+// 256 CUs.  Its 4 waves are 4 key parts, each for all 32 rows (2 row groups
+// of 16, one wave per SIMD with the full register file).  The keys are cut
+// in 32-key chunks that never straddle two views (W and S are multiples of
+// 32; the block gets its own chunks); each wave streams its part's chunks
+// with every MFMA operand loaded straight from memory into registers in
+// operand layout, two chunks in flight, with no LDS staging and no barrier
+// in the loop:
+//   S^T = K Q^T : A = key rows (row-major [key][d]: 16 contiguous bytes per
+//                 lane), B = the wave's 16 query rows (registers);
+//   O^T += V^T P^T : A = values, which the state keeps in key tiles of 32
+//                 ([rows/32][d][32]) so a lane's keys of one dimension are
+//                 16 contiguous bytes and a chunk is one 8 KB block; B = the
+//                 softmax weights from the S^T output layout, rounded to bf16.
+// Each loaded operand serves both row groups of the wave.  The block's
+// values arrive token-major from the caller and are transposed through LDS
+// once per workgroup.  The online softmax lives in registers (per query row,
+// per lane); the key parts merge (m, l, O) in LDS at the end.
+// f32 (draft_generic): one workgroup per query row, plain loop (small shapes).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -21,257 +35,316 @@ namespace ls {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kParts = 4;  // waves of the bf16 kernel's workgroup
+constexpr float kRescale = 8.f;  // e-folds the running max may lag the true max
 
-// launch shape of the bf16 kernel: query row groups of 16 per workgroup, key
-// parts per workgroup, keys per part per step (overridable for tuning builds)
-#ifndef LS_DRAFT_RG
-#define LS_DRAFT_RG 2
-#endif
-#ifndef LS_DRAFT_KQ
-#define LS_DRAFT_KQ 4
-#endif
-#ifndef LS_DRAFT_TK
-#define LS_DRAFT_TK 32
-#endif
+__device__ inline uint16_t bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // v_cvt, nearest-even
+}
 
-// Where the keys of one (sequence, KV head) live: [ring | slots | block].
-struct KeySources {
-  const uint16_t *ring_k, *ring_v;
-  const int32_t* ring_pos;
-  const uint16_t *slot_k, *slot_v, *kb, *vb;
-  int W, S, B, Hkv, c, h, unit;
+// Keys are permuted inside a 32-key chunk so that the S^T output puts keys
+// 8kg..8kg+7 in lane group kg: A-row m of score block mb holds key
+// 8*(m/4) + 4*mb + m%4.  Then the P^T operand, the V^T operand (one 16-byte
+// read per dimension block) and the positions all see the lane's 8 keys in
+// natural order.
+__device__ __forceinline__ int chunk_key(int m, int mb) { return 8 * (m >> 2) + 4 * mb + (m & 3); }
+
+// LDS image of one staged 32-key chunk: keys row-major (padded rows), values
+// [d][32] (padded), positions.  Reads of both are conflict-free ds_read_b128.
+constexpr int kKS = 128 + 8;   // key row stride (bf16)
+constexpr int kVS = 32 + 8;    // value row stride (bf16)
+constexpr int kStageElems = 32 * kKS + 128 * kVS + 64;  // bf16 elements (+ 32 int positions)
+
+struct Stage {  // pointers into one stage buffer
+  uint16_t* k;
+  uint16_t* v;
+  int* pos;
+  __device__ explicit Stage(uint16_t* base)
+      : k(base), v(base + 32 * kKS), pos(reinterpret_cast<int*>(base + 32 * kKS + 128 * kVS)) {}
 };
 
-// Branch-free staging loads of NL keys (pairs 2rp, 2rp+1 every STEP keys from
-// t0): each key's source row is chosen with integer selects and all loads
-// issue back to back.  A key past `end` reads row 0 of the unit's window
-// (valid memory).  Validity is NOT decided here: `kpos` keeps the raw ring
-// position (or a marker) and `key_state` says how to read it, so nothing
-// waits on these loads until the tile is staged into LDS one step later.
-// An empty ring row holds zeros (written by init) and is masked there.
-template <int NL, int STEP>
-__device__ __forceinline__ void load_keys(u16x8 (&kr)[NL], u16x8 (&vr)[NL], int (&kpos)[NL],
-                                          int (&key_state)[NL], const KeySources s, int t0,
-                                          int end, int rp, int dg) {
+// One thread's share of a chunk: 4 pieces of 16 bytes (2 of keys, 2 of
+// values) out of the chunk's 1024, plus one ring position for t < 32.
+struct Piece {
+  u16x8 d[4];
+  int pos;
+};
+
+// Source of chunk ch of one unit: [window W/32 | slots S/32 | block].
+struct Views {
+  const uint16_t *rk, *rv, *sk, *sv, *kb, *vb;
+  const int32_t* rp;
+  int W, S, B, Hkv, c, h, nring, ngl;
+};
+
+// loads for staging chunk ch (thread t of the 256 staging threads of a part)
+__device__ __forceinline__ void load_piece(Piece& x, const Views& s, int ch, int t) {
   constexpr int D = 128;
+  if (ch < s.ngl) {  // window or slots: K rows [key][d], V tile [d][32], contiguous
+    const bool ring = ch < s.nring;
+    const int key0 = (ring ? ch : ch - s.nring) * 32;
+    const uint16_t* kt = (ring ? s.rk : s.sk) + int64_t(key0) * D;
+    const uint16_t* vt = (ring ? s.rv : s.sv) + int64_t(ring ? ch : ch - s.nring) * D * 32;
 #pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int key_raw = t0 + (i >> 1) * STEP + 2 * rp + (i & 1);
-    const bool live = key_raw < end;
-    const int key = live ? key_raw : 0;
-    const bool in_ring = key < s.W, in_slots = !in_ring && key < s.W + s.S;
-    const int row = in_ring ? s.unit * s.W + key
-                  : in_slots ? s.unit * s.S + (key - s.W)
-                             : (s.c * s.B + (key - s.W - s.S)) * s.Hkv + s.h;
-    const int64_t off = int64_t(row) * D + dg * 8;
-    const uint16_t* kbase = in_ring ? s.ring_k : (in_slots ? s.slot_k : s.kb);
-    const uint16_t* vbase = in_ring ? s.ring_v : (in_slots ? s.slot_v : s.vb);
-    kr[i] = *reinterpret_cast<const u16x8*>(kbase + off);
-    vr[i] = *reinterpret_cast<const u16x8*>(vbase + off);
-    kpos[i] = s.ring_pos[s.c * s.W + (in_ring ? key : 0)];
-    key_state[i] = !live ? 0 : (in_ring ? 1 : 2);  // 0 dead, 1 ring (check pos), 2 always valid
+    for (int j = 0; j < 2; ++j) {
+      x.d[j] = *reinterpret_cast<const u16x8*>(kt + (t + 256 * j) * 8);
+      x.d[2 + j] = *reinterpret_cast<const u16x8*>(vt + (t + 256 * j) * 8);
+    }
+    const int p = s.rp[(ring ? key0 : 0) + (t & 31)];
+    x.pos = ring ? p : 0;
+  } else {  // block: K and V rows are the caller's token-major [b][Hkv][d]
+    const int key0 = (ch - s.ngl) * 32;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int piece = t + 256 * j, row = piece >> 4, col = (piece & 15) * 8;
+      const int64_t off = ((int64_t(s.c) * s.B + min(key0 + row, s.B - 1)) * s.Hkv + s.h) * D + col;
+      x.d[j] = *reinterpret_cast<const u16x8*>(s.kb + off);
+      x.d[2 + j] = *reinterpret_cast<const u16x8*>(s.vb + off);
+    }
+    x.pos = key0 + (t & 31) < s.B ? 0 : -1;
   }
 }
 
-// bf16, d = 128.  Workgroup = (KV head unit, half of the query tile: 32 rows
-// = 2 row groups of 16).  Its 8 waves are 2 row groups x KQ key parts; part
-// q streams keys [q*Np, (q+1)*Np) in tiles of TK through its own LDS tile
-// (row-major K, transposed V), then the parts' (m, l, O) merge in LDS.
-// 128 threads stage one part's tile: 16 lanes cover one 256-byte key row.
-template <int RG, int KQ, int TK>
-__global__ __launch_bounds__(64 * RG * KQ, 1) void draft_mfma(
+__device__ __forceinline__ void store_piece(const Piece& x, Stage st, bool block_chunk, int t) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int piece = t + 256 * j, row = piece >> 4, col = (piece & 15) * 8;
+    *reinterpret_cast<u16x8*>(st.k + row * kKS + col) = x.d[j];
+    if (!block_chunk) {  // value tile piece: dim = piece / 4, keys (piece % 4) * 8 ..
+      *reinterpret_cast<u16x8*>(st.v + (piece >> 2) * kVS + (piece & 3) * 8) = x.d[2 + j];
+    } else {  // token-major value row -> [d][32]
+#pragma unroll
+      for (int e = 0; e < 8; ++e) st.v[(col + e) * kVS + row] = x.d[2 + j][e];
+    }
+  }
+  if (t < 32) st.pos[t] = x.pos;
+}
+
+// Online softmax state of one row group of 16 query rows.
+struct Softmax {
+  float m, l;
+  f32x4 o[8];
+};
+
+// one staged chunk for the wave's row group: scores, masking, lazy online
+// softmax update, P.V
+__device__ __forceinline__ void compute_chunk(Softmax& st, Stage sg, const bf16x8 (&qb)[4], int ln,
+                                              int kg) {
+  const float sm_scale = 0.08838834764831845f;  // 1/sqrt(128)
+  f32x4 s[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const uint16_t* krow = sg.k + chunk_key(ln, mb) * kKS + kg * 8;
+    s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      s[mb] = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u16x8*>(krow + ks * 32)), qb[ks], s[mb]);
+  }
+  const int4 p0 = *reinterpret_cast<const int4*>(sg.pos + 8 * kg);
+  const int4 p1 = *reinterpret_cast<const int4*>(sg.pos + 8 * kg + 4);
+  const int pos[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+  // s[mb][r] is key 8kg + 4mb + r of the chunk
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = pos[mb * 4 + r] >= 0 ? s[mb][r] * sm_scale : -INFINITY;
+      s[mb][r] = a;
+      tmax = fmaxf(tmax, a);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  // lazy rescale: the reference max moves only when some row's max grows by
+  // more than kRescale, so weights stay <= e^kRescale and the O / l rescale
+  // is skipped in the steady state
+  if (__any(tmax > st.m + kRescale)) {
+    const float m_new = fmaxf(st.m, tmax);
+    const float scale = st.m == -INFINITY ? 0.f : exp_f(st.m - m_new);
+    st.m = m_new;
+    st.l *= scale;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) st.o[mb] *= scale;
+  }
+  const float m_use = st.m == -INFINITY ? 0.f : st.m;
+  float lsum = 0.f;
+  u16x8 pv;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint16_t pb = bf16_bits(exp_f(s[mb][r] - m_use));
+      lsum += bf16_to_f32(pb);
+      pv[mb * 4 + r] = pb;
+    }
+  st.l += lsum;
+  const bf16x8 pk = as_bf16x8(pv);
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) {
+    const u16x8 v = *reinterpret_cast<const u16x8*>(sg.v + (mb * 16 + ln) * kVS + kg * 8);
+    st.o[mb] = mfma16x16x32(as_bf16x8(v), pk, st.o[mb]);
+  }
+}
+
+// Workgroup = (KV head unit, one of `halves` key ranges); 8 waves = 4 row
+// groups of 16 query rows x 2 key parts.  Each part stages its chunks into
+// its own double-buffered LDS stages (two chunks in flight in registers) and
+// its 4 row-group waves read them.  The parts merge in LDS; the halves' (m,
+// l, O) go to the workspace for draft_combine (a kernel boundary, no fence),
+// or with a single range the output is written here.
+__global__ __launch_bounds__(512, 1) void draft_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, const uint16_t* __restrict__ ring_k,
     const uint16_t* __restrict__ ring_v, const int32_t* __restrict__ ring_pos,
     const uint16_t* __restrict__ slot_k, const uint16_t* __restrict__ slot_v,
-    uint16_t* __restrict__ out, int Hq, int Hkv, int W, int S, int B, int units) {
-  constexpr int D = 128;
-  constexpr int KLS = D + 8, VTS = TK + 4;
-  constexpr int MB = TK / 16, KS = TK / 32;
-  constexpr int PT = 64 * RG;               // threads staging one part's tile
-  constexpr int PAIRS = TK / (8 * RG);      // key pairs staged per thread
-  static_assert(PAIRS >= 1 && TK % (8 * RG) == 0, "tile must cover the staging threads");
-  constexpr int PART_ELEMS = TK * KLS + D * VTS;  // bf16 elements of one part's tile
-  static_assert(TK % 32 == 0, "tile must hold whole 32-key MFMA k-steps");
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[KQ * PART_ELEMS];
-  __shared__ int kvalid[KQ][TK];
+    uint16_t* __restrict__ out, float* __restrict__ part_out, int Hq, int Hkv, int W, int S,
+    int B, int units, int halves) {
+  constexpr int D = 128, RG = 4, KPW = 2;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[KPW * 2 * kStageElems];
 
-  const int rh = blockIdx.x / units;  // which (16*RG)-row slice of the query tile
+  const int half = blockIdx.x / units;
   const int unit = blockIdx.x % units;
   const int c = unit / Hkv, h = unit % Hkv;
   const int G = Hq / Hkv, M = B * G;
-  const int N = W + S + B;
-  const int Np = ((N + KQ - 1) / KQ + TK - 1) / TK * TK;  // keys per part, whole tiles
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, kg = lane >> 4;
-  const int rg = wave % RG, part = wave / RG;
-  const float sm_scale = 0.08838834764831845f;  // 1/sqrt(128)
+  const int g = wave % RG, kq = wave / RG;   // row group, key part
+  const int t = tid % 256;                   // staging thread within the part
 
-  // query operand: lane (row ln of this wave's group, kg) holds q[row][ks*32+kg*8..+7]
-  const int row = (rh * RG + rg) * 16 + ln;
+  // query operand: lane (row ln of group g, kg) holds q[row][ks*32+kg*8..+7]
+  const int row = g * 16 + ln;
   const bool row_ok = row < M;
-  const int b = row_ok ? row / G : 0;
-  const int hq = h * G + (row_ok ? row % G : 0);
-  const bool group_active = (rh * RG + rg) * 16 < M;
   bf16x8 qb[4];
+  {
+    const int bq = row_ok ? row / G : 0, hq = h * G + (row_ok ? row % G : 0);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    if (row_ok)
-      v = *reinterpret_cast<const u16x8*>(q + ((int64_t(c) * B + b) * Hq + hq) * D + ks * 32 +
-                                          kg * 8);
-    qb[ks] = as_bf16x8(v);
+    for (int ks = 0; ks < 4; ++ks) {
+      u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (row_ok)
+        v = *reinterpret_cast<const u16x8*>(q + ((int64_t(c) * B + bq) * Hq + hq) * D + ks * 32 + kg * 8);
+      qb[ks] = as_bf16x8(v);
+    }
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nring = W / 32, ngl = nring + S / 32, nch = ngl + (B + 31) / 32;
+  const Views views{ring_k + int64_t(unit) * W * D, ring_v + int64_t(unit) * D * W,
+                    slot_k + int64_t(unit) * S * D, slot_v + int64_t(unit) * D * S, kb, vb,
+                    ring_pos + int64_t(c) * W, W, S, B, Hkv, c, h, nring, ngl};
+  const int nparts = halves * KPW, pidx = half * KPW + kq;
+  const int per = (nch + nparts - 1) / nparts;
+  const int ch0 = pidx * per, ch1 = min(nch, ch0 + per);
+  const int steps = per;  // same count in every part (empty chunks are skipped)
+  uint16_t* mine = lds + kq * 2 * kStageElems;
+  const bool active = (g * 16 < M);
 
-  // staging: thread (lpart, dg, rp) loads keys 2rp, 2rp+1 (+ 8*RG*k) of part lpart
-  const int lpart = tid / PT;
-  const int dg = tid & 15, rp = (tid % PT) >> 4;
-  const int p_begin = lpart * Np;
-  const int p_end = min(N, p_begin + Np);
-  u16x8 kr[2 * PAIRS] = {}, vr[2 * PAIRS] = {};
-  int kpos[2 * PAIRS] = {}, kstate[2 * PAIRS] = {};
-  const KeySources src{ring_k, ring_v, ring_pos, slot_k, slot_v, kb, vb, W, S, B, Hkv, c, h, unit};
+  Softmax st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint16_t* myKL = tiles + lpart * PART_ELEMS;   // staged by this thread
-  uint16_t* myVT = myKL + TK * KLS;
-  const uint16_t* KL = tiles + part * PART_ELEMS;  // read by this wave
-  const uint16_t* VT = KL + TK * KLS;
-  const int steps = Np / TK;
-  const int w_begin = part * Np;
-
-  load_keys<2 * PAIRS, 8 * RG>(kr, vr, kpos, kstate, src, p_begin, p_end, rp, dg);
-  for (int st = 0; st < steps; ++st) {
-    __syncthreads();  // the previous tiles' LDS reads are done
+  Piece pa, pb;
+  if (ch0 < ch1) load_piece(pa, views, ch0, t);
+  if (ch0 + 1 < ch1) load_piece(pb, views, ch0 + 1, t);
+  for (int i = 0; i < steps; i += 2) {
 #pragma unroll
-    for (int i = 0; i < 2 * PAIRS; ++i) {
-      const int r = (i >> 1) * (8 * RG) + 2 * rp + (i & 1);
-      *reinterpret_cast<u16x8*>(&myKL[r * KLS + dg * 8]) = kr[i];
-      if (dg == 0) kvalid[lpart][r] = kstate[i] == 2 || (kstate[i] == 1 && kpos[i] >= 0);
-    }
-#pragma unroll
-    for (int pp = 0; pp < PAIRS; ++pp) {
-      const int r0 = pp * (8 * RG) + 2 * rp;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t vv = uint32_t(vr[2 * pp][e]) | (uint32_t(vr[2 * pp + 1][e]) << 16);
-        *reinterpret_cast<uint32_t*>(&myVT[(dg * 8 + e) * VTS + r0]) = vv;
-      }
-    }
-    __syncthreads();
-    if (st + 1 < steps)  // next tile in flight during compute
-      load_keys<2 * PAIRS, 8 * RG>(kr, vr, kpos, kstate, src, p_begin + (st + 1) * TK, p_end,
-                                   rp, dg);
-    if (!group_active || w_begin + st * TK >= N) continue;
-
-    // S^T[key][row]: lane (row ln, kg) holds keys mb*16 + kg*4 + r
-    f32x4 s[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = as_bf16x8(
-            *reinterpret_cast<const u16x8*>(&KL[(mb * 16 + ln) * KLS + ks * 32 + kg * 8]));
-        s[mb] = mfma16x16x32(a, qb[ks], s[mb]);
-      }
-
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float a = s[mb][r] * sm_scale;
-        if (!kvalid[part][mb * 16 + kg * 4 + r]) a = -INFINITY;
-        s[mb][r] = a;
-        tmax = fmaxf(tmax, a);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float scale = m_run == -INFINITY ? 0.f : exp_f(m_run - m_use);
-    m_run = m_new;
-    float lsum = 0.f;
-    u16x8 pv[KS];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint16_t pb = f32_to_bf16(exp_f(s[mb][r] - m_use));
-        lsum += bf16_to_f32(pb);
-        pv[mb >> 1][(mb & 1) * 4 + r] = pb;
-      }
-    l_run = fmaf(l_run, scale, lsum);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= scale;
-
-    // O^T[dim][row] += V^T[dim][key] P^T[key][row]; the A operand's k order
-    // (keys 32ks+4kg..+3, 32ks+16+4kg..+3) matches pv's element order
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 pk = as_bf16x8(pv[ks]);
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const uint16_t* base = &VT[(mb * 16 + ln) * VTS + ks * 32 + kg * 4];
-        const u16x4 lo = *reinterpret_cast<const u16x4*>(base);
-        const u16x4 hi = *reinterpret_cast<const u16x4*>(base + 16);
-        const bf16x8 a = as_bf16x8(u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        o[mb] = mfma16x16x32(a, pk, o[mb]);
+    for (int u = 0; u < 2; ++u) {  // step i + u, registers pa (u = 0) / pb (u = 1)
+      const int ch = ch0 + i + u;
+      Piece& x = u == 0 ? pa : pb;
+      Stage sg(mine + u * kStageElems);
+      if (i + u < steps) {
+        if (ch < ch1) store_piece(x, sg, ch >= ngl, t);
+        __syncthreads();  // stage ready; the stage written two steps ago was read before
+        if (ch + 2 < ch1) load_piece(x, views, ch + 2, t);
+        if (active && ch < ch1) compute_chunk(st, sg, qb, ln, kg);
       }
     }
   }
 
-  float lt = l_run;
+  // merge the 2 key parts in LDS (reusing the stages), then write
+  float lt = st.l;
   lt += __shfl_xor(lt, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
-
-  // merge the key parts in LDS (reusing the tile buffers): parts 1..KQ-1
-  // publish (m, l, O) in the same lane layout, part 0 combines and writes
   __syncthreads();
-  float* red = reinterpret_cast<float*>(tiles);  // [KQ-1][RG groups][64 lanes][34]
-  static_assert((KQ - 1) * RG * 64 * 34 * 4 <= KQ * PART_ELEMS * 2, "merge area fits the tiles");
-  if (part > 0 && group_active) {
-    float* dst = red + (((part - 1) * RG + rg) * 64 + lane) * 34;
-    dst[0] = m_run;
+  float* red = reinterpret_cast<float*>(lds);  // [RG][64 lanes][34]
+  if (kq == 1) {
+    float* dst = red + (g * 64 + lane) * 34;
+    dst[0] = st.m;
     dst[1] = lt;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[2 + mb * 4 + r] = o[mb][r];
+      for (int r = 0; r < 4; ++r) dst[2 + mb * 4 + r] = st.o[mb][r];
   }
   __syncthreads();
-  if (part == 0 && row_ok) {
-    float mx = m_run;
+  if (kq != 0) return;
+  const float* src = red + (g * 64 + lane) * 34;
+  const float mx = fmaxf(st.m, src[0]);
+  const float w0 = st.m == -INFINITY ? 0.f : exp_f(st.m - mx);
+  const float w1 = src[0] == -INFINITY ? 0.f : exp_f(src[0] - mx);
+  const float l = lt * w0 + src[1] * w1;
+  f32x4 o[8];
 #pragma unroll
-    for (int p2 = 1; p2 < KQ; ++p2) mx = fmaxf(mx, red[(((p2 - 1) * RG + rg) * 64 + lane) * 34]);
-    const float w0 = m_run == -INFINITY ? 0.f : exp_f(m_run - mx);
-    float l = lt * w0;
+  for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= w0;
-#pragma unroll
-    for (int p2 = 1; p2 < KQ; ++p2) {
-      const float* src = red + (((p2 - 1) * RG + rg) * 64 + lane) * 34;
-      const float wq = src[0] == -INFINITY ? 0.f : exp_f(src[0] - mx);
-      l = fmaf(src[1], wq, l);
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[mb][r] = fmaf(src[2 + mb * 4 + r], wq, o[mb][r]);
-    }
+    for (int r = 0; r < 4; ++r) o[mb][r] = st.o[mb][r] * w0 + src[2 + mb * 4 + r] * w1;
+  if (halves == 1) {  // the whole key range: write the output
+    if (!row_ok) return;
     const float il = 1.0f / l;
-    uint16_t* orow = out + ((int64_t(c) * B + b) * Hq + hq) * D;
+    uint16_t* orow = out + ((int64_t(c) * B + row / G) * Hq + h * G + row % G) * D;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
       *reinterpret_cast<u16x4*>(orow + mb * 16 + kg * 4) =
-          u16x4{f32_to_bf16(o[mb][0] * il), f32_to_bf16(o[mb][1] * il),
-                f32_to_bf16(o[mb][2] * il), f32_to_bf16(o[mb][3] * il)};
+          u16x4{bf16_bits(o[mb][0] * il), bf16_bits(o[mb][1] * il), bf16_bits(o[mb][2] * il),
+                bf16_bits(o[mb][3] * il)};
+  } else {  // partial of this range: m[64] | l[64] | O[64][D]
+    constexpr int Mpad = 16 * RG;
+    float* pbuf = part_out + (int64_t(unit) * halves + half) * int64_t(Mpad) * (D + 2);
+    if (kg == 0) {
+      pbuf[row] = mx;
+      pbuf[Mpad + row] = l;
+    }
+    float* po = pbuf + 2 * Mpad + int64_t(row) * D;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f32x4*>(po + mb * 16 + kg * 4) = o[mb];
   }
+}
+
+// merge the key halves: one thread per (unit, query row, 4 dimensions)
+__global__ __launch_bounds__(kThreads) void draft_combine(
+    const float* __restrict__ part, uint16_t* __restrict__ out, int Hq, int Hkv, int B,
+    int halves, int Mpad, int units) {
+  constexpr int D = 128;
+  const int G = Hq / Hkv, M = B * G;
+  const int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int e4 = int(idx % (D / 4)) * 4;
+  const int row = int((idx / (D / 4)) % Mpad);
+  const int unit = int(idx / (int64_t(D / 4) * Mpad));
+  if (unit >= units || row >= M) return;
+  const int c = unit / Hkv, h = unit % Hkv;
+  const int64_t pstride = int64_t(Mpad) * (D + 2);
+  const float* ub = part + int64_t(unit) * halves * pstride;
+  float ms[4], ls[4];
+  f32x4 os[4];
+  float mx = -INFINITY;
+  for (int s2 = 0; s2 < halves; ++s2) {
+    const float* sp = ub + s2 * pstride;
+    ms[s2] = sp[row];
+    ls[s2] = sp[Mpad + row];
+    os[s2] = *reinterpret_cast<const f32x4*>(sp + 2 * Mpad + int64_t(row) * D + e4);
+    mx = fmaxf(mx, ms[s2]);
+  }
+  float l = 0.f;
+  f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s2 = 0; s2 < halves; ++s2) {
+    const float wgt = ms[s2] == -INFINITY ? 0.f : exp_f(ms[s2] - mx);
+    l = fmaf(ls[s2], wgt, l);
+    a += os[s2] * wgt;
+  }
+  const float il = 1.0f / l;
+  uint16_t* orow = out + ((int64_t(c) * B + row / G) * Hq + h * G + row % G) * D + e4;
+  *reinterpret_cast<u16x4*>(orow) = u16x4{bf16_bits(a[0] * il), bf16_bits(a[1] * il),
+                                          bf16_bits(a[2] * il), bf16_bits(a[3] * il)};
 }
 
 // generic path: one workgroup per (sequence, block row, query head)
@@ -296,29 +369,24 @@ __global__ __launch_bounds__(kThreads) void draft_generic(
   const int64_t qo = ((int64_t(c) * B + b) * Hq + hq) * D;
   for (int e = tid; e < D; e += kThreads) qs[e] = Ty::load(q, qo + e);
 
-  auto key_ptr = [&](int key, bool vals, bool& ok) -> const typename Ty::T* {
-    ok = true;
-    if (key < W) {
-      ok = ring_pos[int64_t(c) * W + key] >= 0;
-      return (vals ? ring_v : ring_k) + (int64_t(unit) * W + key) * D;
-    }
-    if (key < W + S) return (vals ? slot_v : slot_k) + (int64_t(unit) * S + key - W) * D;
-    return (vals ? vb : kb) + ((int64_t(c) * B + key - W - S) * Hkv + h) * D;
-  };
-
   float m_run = -INFINITY, l_run = 0.f, o = 0.f;
   __syncthreads();
   for (int k0 = 0; k0 < N; k0 += kThreads) {
     const int key = k0 + tid;
     float a = -INFINITY;
-    if (key < N) {
-      bool ok;
-      const typename Ty::T* kp = key_ptr(key, false, ok);
-      if (ok) {
-        float dot = 0.f;
-        for (int e = 0; e < D; ++e) dot = fmaf(qs[e], Ty::load(kp, e), dot);
-        a = dot * sm_scale;
+    if (key < N && (key >= W || ring_pos[int64_t(c) * W + key] >= 0)) {
+      float dot = 0.f;
+      if (key < W) {
+        for (int e = 0; e < D; ++e)
+          dot = fmaf(qs[e], Ty::load(ring_k, (int64_t(unit) * W + key) * D + e), dot);
+      } else if (key < W + S) {
+        for (int e = 0; e < D; ++e)
+          dot = fmaf(qs[e], Ty::load(slot_k, (int64_t(unit) * S + key - W) * D + e), dot);
+      } else {
+        for (int e = 0; e < D; ++e)
+          dot = fmaf(qs[e], Ty::load(kb, ((int64_t(c) * B + key - W - S) * Hkv + h) * D + e), dot);
       }
+      a = dot * sm_scale;
     }
     float mx = wave_max(a);
     if ((tid & 63) == 0) red[tid >> 6] = mx;
@@ -341,11 +409,16 @@ __global__ __launch_bounds__(kThreads) void draft_generic(
       const int nk = min(kThreads, N - k0);
       for (int k = 0; k < nk; ++k) {
         const float pk = sc[k];
-        if (pk != 0.f) {
-          bool ok;
-          const typename Ty::T* vp = key_ptr(k0 + k, true, ok);
-          o = fmaf(pk, Ty::load(vp, tid), o);
-        }
+        if (pk == 0.f) continue;
+        const int kk = k0 + k;
+        float v;  // values of the window and of the slots are key-tiled
+        if (kk < W)
+          v = Ty::load(ring_v, value_index(unit, W, D, kk, tid));
+        else if (kk < W + S)
+          v = Ty::load(slot_v, value_index(unit, S, D, kk - W, tid));
+        else
+          v = Ty::load(vb, ((int64_t(c) * B + kk - W - S) * Hkv + h) * D + tid);
+        o = fmaf(pk, v, o);
       }
     }
     __syncthreads();
@@ -370,18 +443,25 @@ ls_status run_generic(const ls_dims& d, const ls_state& st, const void* q, const
 ls_status launch_draft(const ls_dims& d, const ls_state& st, const void* q, const void* kb,
                        const void* vb, void* out, hipStream_t stream) {
   if (d.dtype == LS_BF16) {
-    constexpr int RG = LS_DRAFT_RG, KQ = LS_DRAFT_KQ, TK = LS_DRAFT_TK;
     const int units = d.C * d.Hkv;
     const int M = d.B * (d.Hq / d.Hkv);
-    const int slices = int(cdiv(M, 16 * RG));
-    hipLaunchKernelGGL((draft_mfma<RG, KQ, TK>), dim3(units * slices), dim3(64 * RG * KQ), 0,
-                       stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kb),
-                       static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(st.ring_k),
-                       static_cast<const uint16_t*>(st.ring_v), st.ring_pos,
-                       static_cast<const uint16_t*>(st.slot_k),
-                       static_cast<const uint16_t*>(st.slot_v), static_cast<uint16_t*>(out), d.Hq,
-                       d.Hkv, d.W, d.S, d.B, units);
+    const int halves = draft_halves(d);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(st.workspace) + ws_layout(d, 1).draft_part);
+    const dim3 grid(units * halves), block(512);
+    hipLaunchKernelGGL(draft_mfma, grid, block, 0, stream, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(kb), static_cast<const uint16_t*>(vb),
+                       static_cast<const uint16_t*>(st.ring_k), static_cast<const uint16_t*>(st.ring_v),
+                       st.ring_pos, static_cast<const uint16_t*>(st.slot_k),
+                       static_cast<const uint16_t*>(st.slot_v), static_cast<uint16_t*>(out), part,
+                       d.Hq, d.Hkv, d.W, d.S, d.B, units, halves);
+    if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
+    if (halves > 1) {
+      const int Mpad = 64;
+      const int64_t threads = int64_t(units) * Mpad * (128 / 4);
+      hipLaunchKernelGGL(draft_combine, dim3(unsigned(cdiv(threads, kThreads))), dim3(kThreads), 0,
+                         stream, part, static_cast<uint16_t*>(out), d.Hq, d.Hkv, d.B, halves,
+                         Mpad, units);
+    }
     return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
   }
   switch (d.d) {

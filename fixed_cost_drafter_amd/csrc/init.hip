@@ -71,7 +71,8 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
     ub[ks] = as_bf16x8(
         *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + slot) * D + ks * 32 + kg * 8));
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // reference max (may lag) and weight sum
+  float m_true = -INFINITY;               // exact running max
   f32x4 acc[16];  // n^T: lane (slot ln, kg) holds dims mb*16 + kg*4 + r
 #pragma unroll
   for (int mb = 0; mb < 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -147,10 +148,19 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float scale = m_run == -INFINITY ? 0.f : exp_f(m_run - m_use);
-    m_run = m_new;
+    // lazy rescale: the reference max moves only when some slot's max grows
+    // by more than 8 e-folds (weights stay <= e^8), so the 64-register
+    // accumulator rescale is skipped in the steady state
+    m_true = fmaxf(m_true, tmax);
+    if (__any(tmax > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float scale = m_run == -INFINITY ? 0.f : exp_f(m_run - m_new);
+      m_run = m_new;
+      l_run *= scale;
+#pragma unroll
+      for (int mb = 0; mb < 16; ++mb) acc[mb] *= scale;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float lsum = 0.f;
     u16x8 pv[KS2];
 #pragma unroll
@@ -162,9 +172,7 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
         pv[mb >> 1][(mb & 1) * 4 + r] = pb;
       }
     }
-    l_run = fmaf(l_run, scale, lsum);
-#pragma unroll
-    for (int mb = 0; mb < 16; ++mb) acc[mb] *= scale;
+    l_run += lsum;
 
     // n^T[dim][slot] += [K|V]^T[dim][row] P^T[row][slot]; the k order of the
     // A operand (rows 32ks+4kg..+3, 32ks+16+4kg..+3) matches pv's element order
@@ -180,6 +188,15 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
         acc[mb] = mfma16x16x32(a, pk, acc[mb]);
       }
     }
+  }
+
+  // the state's m is the exact max: move the reference there once
+  if (m_true > m_run) {
+    const float scale = exp_f(m_run - m_true);
+    m_run = m_true;
+    l_run *= scale;
+#pragma unroll
+    for (int mb = 0; mb < 16; ++mb) acc[mb] *= scale;
   }
 
   // write the partial: lane (slot ln, kg) holds n[slot][mb*16 + kg*4 + r]
@@ -335,20 +352,22 @@ __global__ __launch_bounds__(kThreads) void init_finalize(
     }
     const int64_t ni = (int64_t(unit) * S + j0 + jj) * 2 * D + e;
     sum_n[ni] = a;
-    const int64_t so = (int64_t(unit) * S + j0 + jj) * D + (e % D);
-    Ty::store(e < D ? slot_k : slot_v, so, a * s_inv_l[jj]);
+    if (e < D)
+      Ty::store(slot_k, (int64_t(unit) * S + j0 + jj) * D + e, a * s_inv_l[jj]);
+    else  // values in key tiles
+      Ty::store(slot_v, value_index(unit, S, D, j0 + jj, e - D), a * s_inv_l[jj]);
   }
 
   // ring window: slots ws = tile, tile + NT, ... ; slot ws holds the newest
-  // prefix position p with p mod W == ws, if p >= max(0, L0-W)
+  // prefix position p with p mod W == ws, if p >= max(0, L0-W).  Keys are
+  // copied row by row; values go to the key-tiled layout.
   for (int wsl = tile; wsl < W; wsl += NT) {
     const int64_t newest = int64_t(L0) - 1 - ((int64_t(L0) - 1 - wsl) % W + W) % W;
     const bool occ = newest >= 0;
-    const int64_t dst = (int64_t(unit) * W + wsl) * D;
     const int64_t src = ((int64_t(c) * rows_stride + (occ ? newest : 0)) * Hkv + h) * D;
     for (int e = tid; e < D; e += kThreads) {
-      ring_k[dst + e] = occ ? kp[src + e] : typename Ty::T(0);
-      ring_v[dst + e] = occ ? vp[src + e] : typename Ty::T(0);
+      ring_k[(int64_t(unit) * W + wsl) * D + e] = occ ? kp[src + e] : typename Ty::T(0);
+      ring_v[value_index(unit, W, D, wsl, e)] = occ ? vp[src + e] : typename Ty::T(0);
     }
     if (h == 0 && tid == 0) ring_pos[int64_t(c) * W + wsl] = occ ? int32_t(newest) : -1;
   }

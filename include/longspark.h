@@ -34,8 +34,11 @@
  * Supported shapes: Hq % Hkv == 0; 1 <= B <= 47, B+1 <= W; 1 <= V <= 2^20;
  *   C*(B+1) <= 65535; S >= 1.
  *   LS_F32 : d in {16, 32, 64, 128}, S <= 256, B*Hq/Hkv <= 64.
- *   LS_BF16: d == 128, S in {64, 128}, B*Hq/Hkv <= 64.
- * Pointers to dtype arrays and to sum_n must be 16-byte aligned.
+ *   LS_BF16: d == 128, S in {64, 128}, W % 32 == 0, B*Hq/Hkv <= 64.
+ * Pointers to dtype arrays, ring_pos and sum_n must be 16-byte aligned.
+ * The values of the window and of the slots are kept in key tiles of 32
+ * (per tile: [d][32]) so that the drafter's P.V product reads contiguous
+ * keys per dimension and each 32-key tile is one contiguous block.
  */
 #ifndef LONGSPARK_H
 #define LONGSPARK_H
@@ -79,14 +82,18 @@ typedef struct ls_dims {
  * Its size is independent of the prefix length. */
 typedef struct ls_state {
   void* ring_k;             /* [C, Hkv, W, d] dtype: window keys            */
-  void* ring_v;             /* [C, Hkv, W, d] dtype: window values          */
+  void* ring_v;             /* dtype window values in key tiles of 32:
+                               [C, Hkv, W/32, d, 32] ([C, Hkv, d, W] when
+                               W % 32 != 0)                                 */
   int32_t* ring_pos;        /* [C, W] absolute position held, -1 = empty     */
   int32_t* seq_len;         /* [C] retained rows per sequence                */
   float* sum_m;             /* [C, Hkv, S] running max m (natural log units) */
   float* sum_l;             /* [C, Hkv, S] denominator l                     */
   float* sum_n;             /* [C, Hkv, S, 2d] numerator n: keys | values    */
   void* slot_k;             /* [C, Hkv, S, d] dtype: n[:d] / l               */
-  void* slot_v;             /* [C, Hkv, S, d] dtype: n[d:] / l               */
+  void* slot_v;             /* dtype n[d:] / l in key tiles of 32:
+                               [C, Hkv, S/32, d, 32] ([C, Hkv, d, S] when
+                               S % 32 != 0)                                 */
   const void* u;            /* [Hkv, S, d] dtype: slot queries               */
   const float* log_lambda;  /* [S] ln(lambda_j); -INFINITY for lambda_j = 0  */
   int32_t* err_flag;        /* [1] sticky device error word, 0 = no error    */

@@ -61,6 +61,10 @@ def exact(name, got, ref):
 def compare_state(runner, ost: O.OracleState, dtype, heads=None):
     """GPU state vs oracle state; ``heads`` restricts the float checks."""
     snap = runner.snapshot()
+    # the library keeps window and slot values in key tiles [rows/tw][d][tw]
+    from fixed_cost_drafter_amd.binding import values_to_rows
+    snap["ring_v"] = values_to_rows(snap["ring_v"])
+    snap["slot_v"] = values_to_rows(snap["slot_v"])
     exact("seq_len", snap["seq_len"].astype(np.int64), ost.seq_len)
     exact("ring_pos", snap["ring_pos"], ost.ring_pos)
     exact("ring_k", snap["ring_k"], ost.ring_k)

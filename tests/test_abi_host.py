@@ -106,6 +106,7 @@ def test_workspace_bytes(LB):
     (dict(W=16, B=16), 2),            # B+1 > W
     (dict(d=64), 2),                  # bf16 needs d = 128
     (dict(S=96), 2),                  # bf16 needs S in {64, 128}
+    (dict(W=1000), 2),                # bf16 needs W % 32 == 0
     (dict(Hq=64, Hkv=8, B=16), 2),    # B*G = 128 > 64
     (dict(dtype="f32", d=48), 2),     # f32 d not supported
     (dict(dtype="f32", d=16, S=300), 2),

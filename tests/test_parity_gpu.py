@@ -32,21 +32,31 @@ SMALL = {
     "f32_d32_wrap": WLM.WORKLOADS["tiny_f32"].with_(
         name="f32_d32_wrap", C=3, Hq=6, Hkv=3, d=32, L0=77, W=9, S=5, B=6, V=300, rounds=12,
         lambdas=(1.0, 0.999, 0.9, 0.5, 0.0), seed=11),
-    # bf16, S=64, ragged prefix (300 rows: tiles of 64 + tail), V spans 3 chunks + tail
+    # bf16, S=64, ragged prefix (300 rows: tiles of 64 + tail), V spans 2 chunks + tail
     "bf16_s64_ragged": WLM.Workload(
-        "bf16_s64_ragged", "bf16", C=2, Hq=8, Hkv=2, d=128, L0=300, W=40, S=64, B=5, V=20001,
+        "bf16_s64_ragged", "bf16", C=2, Hq=8, Hkv=2, d=128, L0=300, W=64, S=64, B=5, V=20001,
         rounds=6, p_match=0.8, seed=12),
-    # bf16, S=128, prefix shorter than the window (empty ring slots are masked)
+    # bf16, S=128, prefix shorter than the window (empty ring slots are masked),
+    # B*G = 48 (a 16-row tail in the second 32-row slice)
     "bf16_s128_short": WLM.Workload(
         "bf16_s128_short", "bf16", C=3, Hq=16, Hkv=4, d=128, L0=37, W=128, S=128, B=12,
         V=4096, rounds=10, p_match=0.85, seed=13),
-    # bf16, single-row prefix, B*G = 64 exactly, odd vocabulary (scalar verify path)
+    # bf16, single-row prefix, B*G = 32, odd vocabulary (scalar verify path)
     "bf16_l1": WLM.Workload(
         "bf16_l1", "bf16", C=2, Hq=32, Hkv=8, d=128, L0=1, W=64, S=128, B=8, V=1001,
         rounds=5, p_match=0.9, seed=14),
+    # bf16, B = 40: two block chunks (one ragged), B*G = 40 (ragged 32-row slice)
+    "bf16_b40": WLM.Workload(
+        "bf16_b40", "bf16", C=2, Hq=8, Hkv=8, d=128, L0=500, W=96, S=64, B=40, V=3000,
+        rounds=6, p_match=0.9, seed=16),
+    # bf16, keys split over two workgroups per KV head + combine (W = 512),
+    # 64 query rows per KV head, prefix shorter than the window
+    "bf16_halves": WLM.Workload(
+        "bf16_halves", "bf16", C=2, Hq=8, Hkv=2, d=128, L0=300, W=512, S=64, B=16, V=2000,
+        rounds=5, p_match=0.8, seed=17),
     # bf16, ring wraps inside the round loop, G=1, B=16 at C=5
     "bf16_wrap": WLM.Workload(
-        "bf16_wrap", "bf16", C=5, Hq=4, Hkv=4, d=128, L0=130, W=20, S=64, B=16, V=9000,
+        "bf16_wrap", "bf16", C=5, Hq=4, Hkv=4, d=128, L0=130, W=32, S=64, B=16, V=9000,
         rounds=14, p_match=0.75, seed=15),
 }
 
