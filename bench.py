@@ -74,20 +74,96 @@ def algorithmic(wl, mean_tau: float, L0: int) -> dict:
                 init=init, init_flop=init_flop, round=verify + append + draft)
 
 
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+# kernels that make up one call of each entry point (substrings of their names)
+ENTRY_KERNELS = {
+    "verify": ("verify_partial", "verify_finalize"),
+    "append": ("append_kernel", "append_commit"),
+    "draft": ("draft_mfma", "draft_combine", "draft_generic"),
+    "init": ("init_mfma_partial", "init_generic_partial", "init_finalize"),
+}
+CALIB_BYTES = 512 << 20        # the streaming copy used to scale the counters
+CALIB_KERNEL = "neg_kernel"
+
+
+def copy_calibration(dev):
+    """One plain streaming copy of known size (reads and writes CALIB_BYTES).
+
+    Run before timing so that a rocprofv3 --pmc pass over this program sees it
+    and can scale FETCH_SIZE / WRITE_SIZE to bytes.
+    """
+    import torch
+    src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def load_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 PMC summary, if current."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(p):
+    """HBM bytes per call of an entry point from the committed PMC summary, if current."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
     try:
-        with open(p) as f:
+        with open(TRAFFIC_JSON) as f:
             t = json.load(f)
-        ent = t.get("kernels", {}).get(kernel)
+        ent = t.get("entry_points", {}).get(kernel)
         if not ent or ent.get("source_hash") != source_hash(KERNEL_SOURCES[kernel]):
             return None
-        return ent["fetch_bytes"] + ent["write_bytes"]
-    except Exception:
+        return int(ent["fetch_bytes"] + ent["write_bytes"])
+    except (OSError, ValueError, KeyError, TypeError):
         return None
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> dict:
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; csv) into bytes per call.
+
+    Both counters are KiB per dispatch.  They are scaled by what the same
+    counter reads for the calibration copy (CALIB_BYTES read and written), so
+    the figures are bytes as a plain copy would count them.
+    """
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals = {}
+        for fn in files:
+            with open(fn, newline="") as f:
+                for row in csv.DictReader(f):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]) * 1024)
+        return vals
+
+    out = {"command": command, "entry_points": {}, "kernels": {}}
+    for key, d, counter in (("fetch", fetch_dir, "FETCH_SIZE"), ("write", write_dir, "WRITE_SIZE")):
+        vals = per_kernel(d, counter)
+        calib = [v for n, vs in vals.items() if CALIB_KERNEL in n for v in vs]
+        if not calib:
+            raise SystemExit(f"calibration copy not found in the {counter} run")
+        factor = CALIB_BYTES / max(calib)
+        out[f"{key}_scale"] = round(factor, 4)
+        out[f"{key}_calibration_raw_bytes"] = max(calib)
+        for name, vs in vals.items():
+            short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            ent = out["kernels"].setdefault(short, {})
+            ent["dispatches"] = len(vs)
+            ent[f"{key}_bytes"] = statistics.mean(vs) * factor
+    for entry, parts in ENTRY_KERNELS.items():
+        f = w = 0.0
+        seen = []
+        for short, ent in out["kernels"].items():
+            if any(p in short for p in parts):
+                f += ent.get("fetch_bytes", 0.0)
+                w += ent.get("write_bytes", 0.0)
+                seen.append(short)
+        if seen:
+            out["entry_points"][entry] = dict(fetch_bytes=round(f), write_bytes=round(w), kernels=seen,
+                                              source_hash=source_hash(KERNEL_SOURCES[entry]))
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -101,6 +177,7 @@ def run_gpu(args, wl):
 
     dev = "cuda"
     torch.cuda.set_device(0)
+    copy_calibration(dev)
     rows = max(WLM.SWEEP_L0) if args.sweep else wl.L0
     rows = max(rows, wl.L0)
     t0 = time.time()
@@ -269,7 +346,18 @@ def main(argv=None):
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--graph", action="store_true",
                     help="also time the K rounds captured in one HIP graph")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc csv runs into the traffic table and exit")
+    ap.add_argument("--traffic-command", default="",
+                    help="the command the counter runs were made with (recorded in the table)")
     args = ap.parse_args(argv)
+    if args.traffic:
+        t = summarize_traffic(args.traffic[0], args.traffic[1], args.traffic_command)
+        os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+        with open(TRAFFIC_JSON, "w") as f:
+            json.dump(t, f, indent=1, sort_keys=True)
+        print(json.dumps(t["entry_points"]))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the drafting "
               "state shards by sequence or KV head with no exchange; see the design notes). "
