@@ -78,7 +78,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 # kernels that make up one call of each entry point (substrings of their names)
 ENTRY_KERNELS = {
     "verify": ("verify_partial", "verify_finalize"),
-    "append": ("append_kernel", "append_commit"),
+    "append": ("append_kernel",),
     "draft": ("draft_mfma", "draft_combine", "draft_generic"),
     "init": ("init_mfma_partial", "init_generic_partial", "init_finalize"),
 }

@@ -9,230 +9,414 @@
 //   a_jp grows by tau*ln(lambda_j), so m' = m + tau*ln(lambda_j) and l, n
 //   keep their values; the new rows a_ji = u_j.k_i/sqrt(d) + (tau-1-i) ln
 //   lambda_j are merged by the online-softmax rule; slot = n / l.
-//   seq_len[c] += tau (a second, tiny launch: every workgroup of the first
-//   launch reads the old L, and the kernel boundary orders those reads
-//   before the update without a device-scope fence).
+//   seq_len[c] += tau.
 //
-// Grid: one workgroup per (sequence, KV head, tile of 16 slots).  Each
-// workgroup stages the tau rows (and its 16 slot queries) in LDS, computes
-// the 16 x tau scores, and streams its slots' fp32 state once (coalesced
-// float4), so the per-round traffic is the state read + write + slot write,
-// independent of the prefix length.  The tiles share the ring copy of the
-// tau rows.  Values of the window and of the slots are written in key tiles
-// of 32 ([rows/32][d][32]), the layout the drafter's P.V product reads.
+// Grid: C window workgroups (one per sequence: the only reader and writer of
+// seq_len in the launch, so the update needs no second kernel and no
+// device-scope fence), then one workgroup per (sequence, KV head, 32 slots).
+//
+// Summary workgroups: 32 slots, LPS lanes per slot (32; at most d for f32).
+// Lane g of a slot owns 2d/LPS consecutive entries of the slot's [k | v]
+// numerator n (the first half of the lanes the key half, the rest the value
+// half) and keeps them in registers from the first load to the last store,
+// so the fp32 state crosses HBM once each way.  All B+1 verified rows of the
+// (sequence, KV head) are staged once in LDS as fp32, whatever tau is, so no
+// load waits for tau.  The tau new rows are merged two at a time: the key
+// lanes form partial dot products with the slot query, a DPP butterfly over
+// the slot's lanes completes the scores, and one rescale per batch folds them
+// into (m, l, n).  The slots n / l leave as pooled keys (row-major, one slot
+// row per lane group) and pooled values; the values of the workgroup's 32
+// slots are one key tile ([d][32]) of the value layout the drafter reads,
+// assembled in LDS and stored contiguously.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace ls {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kSlotsPerBlock = 16;
+#ifndef LS_APPEND_LPS
+#define LS_APPEND_LPS 32
+#endif
+#ifndef LS_APPEND_BATCH
+#define LS_APPEND_BATCH 2
+#endif
+constexpr int kSlotsPerBlock = 32;     // one value key tile
+constexpr int kBatch = LS_APPEND_BATCH;  // new rows merged per rescale
 
-template <typename Ty, int D>
-__global__ __launch_bounds__(kThreads) void append_kernel(
-    const typename Ty::T* __restrict__ k_new, const typename Ty::T* __restrict__ v_new,
-    const int32_t* __restrict__ tau_in, typename Ty::T* __restrict__ ring_k,
-    typename Ty::T* __restrict__ ring_v, int32_t* __restrict__ ring_pos,
-    const int32_t* __restrict__ seq_len, float* __restrict__ sum_m, float* __restrict__ sum_l,
-    float* __restrict__ sum_n, typename Ty::T* __restrict__ slot_k,
-    typename Ty::T* __restrict__ slot_v, const typename Ty::T* __restrict__ u,
-    const float* __restrict__ log_lambda, int32_t* __restrict__ err_flag, int Hkv, int W,
-    int S, int B, int NT) {
-  constexpr int RS = 2 * D + 4;  // LDS row stride (floats): 16-byte rows, banks offset by 4
-  constexpr int US = D + 4;
-  constexpr int Q = 2 * D / 4;   // float4 per slot of n
-  constexpr int NQ = (kSlotsPerBlock * Q + kThreads - 1) / kThreads;  // float4 of n per thread
-  extern __shared__ float4 smem4[];
-  float* smem = reinterpret_cast<float*>(smem4);
-  float* rows = smem;                              // [B+1][RS]  k | v
-  float* ush = rows + (B + 1) * RS;                // [16][US]   slot queries
-  float* w = ush + kSlotsPerBlock * US;            // [16][B+1]  scores -> weights
-  constexpr int SVS = kSlotsPerBlock + 1;          // slot-value staging stride
-  float* svals = w + kSlotsPerBlock * (B + 1);     // [d][SVS]   slot values
-  __shared__ float s_scale[kSlotsPerBlock], s_inv_l[kSlotsPerBlock];
+// lanes per slot: the 2d entries of a slot's [k | v] numerator over LPS lanes,
+// EPL = 2d / LPS entries each (2 at least, so every access is 8 bytes or more)
+template <int D>
+constexpr int lanes_per_slot() { return D >= LS_APPEND_LPS ? LS_APPEND_LPS : D; }
+// one lane group per slot of the tile
+template <int D>
+constexpr int block_threads() { return kSlotsPerBlock * lanes_per_slot<D>(); }
 
-  const int tid = threadIdx.x;
-  const int B1 = B + 1;
-  const int tile = blockIdx.x % NT;
-  const int ch = blockIdx.x / NT;
-  const int h = ch % Hkv;
-  const int c = ch / Hkv;
-  const int j0 = tile * kSlotsPerBlock;
-  const int nj = min(kSlotsPerBlock, S - j0);
-  const int64_t slot0 = (int64_t(c) * Hkv + h) * S + j0;  // first slot of this tile
-
-  // issue the state loads first: they do not depend on tau, and their
-  // latency then overlaps the staging below
-  float4 nreg[NQ];
+// EPL consecutive elements starting at p (EPL * element size is a multiple
+// of 8 bytes and p is aligned to it) -> fp32
+template <typename Ty, int EPL>
+__device__ __forceinline__ void load_elems(const typename Ty::T* p, float (&out)[EPL]) {
+  if constexpr (Ty::kBytes == 2) {
+    static_assert(EPL % 8 == 0, "bf16 lanes hold whole 16-byte pieces");
 #pragma unroll
-  for (int k = 0; k < NQ; ++k) {
-    const int p = tid + k * kThreads, jj = p / Q;
-    nreg[k] = jj < nj ? reinterpret_cast<const float4*>(sum_n + slot0 * 2 * D)[p]
-                      : float4{0.f, 0.f, 0.f, 0.f};
-  }
-  float m_old = 0.f, l_old = 0.f, lnl_t = 0.f;
-  if (tid < nj) {
-    m_old = sum_m[slot0 + tid];
-    l_old = sum_l[slot0 + tid];
-    lnl_t = log_lambda[j0 + tid];
-  }
-
-  int T = tau_in[c];
-  if (T < 1 || T > B1) {
-    if (tid == 0 && h == 0 && tile == 0) atomicOr(err_flag, 1);
-    T = T < 1 ? 1 : B1;
-  }
-  const int L = seq_len[c];
-
-  // stage the new rows and this tile's slot queries
-  for (int idx = tid; idx < T * 2 * D; idx += kThreads) {
-    const int i = idx / (2 * D), e = idx % (2 * D);
-    const int64_t src = ((int64_t(c) * B1 + i) * Hkv + h) * D + (e % D);
-    rows[i * RS + e] = Ty::load(e < D ? k_new : v_new, src);
-  }
-  for (int idx = tid; idx < nj * D; idx += kThreads) {
-    const int jj = idx / D, e = idx % D;
-    ush[jj * US + e] = Ty::load(u, (int64_t(h) * S + j0 + jj) * D + e);
-  }
-  // ring window, shared by the NT tiles of (c, h): tile t copies the key
-  // pieces p = t, t + NT, ... (16 bytes of one new row each) and the values
-  // of dimensions t, t + NT, ...; lanes run over the tau rows, so their
-  // 2-byte stores land on consecutive slots of the key-tiled value layout
-  {
-    constexpr int V16 = D * Ty::kBytes / 16;  // 16-byte pieces per key row
-    const int64_t unit = int64_t(c) * Hkv + h;
-    for (int p = tile + NT * tid; p < T * V16; p += NT * kThreads) {
-      const int i = p / V16, e = p % V16;
-      const int slot = int((int64_t(L) + i) % W);
-      reinterpret_cast<uint4*>(ring_k + (unit * W + slot) * D)[e] =
-          reinterpret_cast<const uint4*>(k_new + ((int64_t(c) * B1 + i) * Hkv + h) * D)[e];
-    }
-    const int ndim = (D - tile + NT - 1) / NT;  // dimensions tile, tile+NT, ...
-    for (int p = tid; p < ndim * T; p += kThreads) {
-      const int dim = tile + NT * (p / T), i = p % T;
-      const int slot = int((int64_t(L) + i) % W);
-      ring_v[value_index(unit, W, D, slot, dim)] = v_new[((int64_t(c) * B1 + i) * Hkv + h) * D + dim];
-    }
-    if (h == 0 && tile == 0)
-      for (int i = tid; i < T; i += kThreads) ring_pos[int64_t(c) * W + int((int64_t(L) + i) % W)] = L + i;
-  }
-  __syncthreads();
-
-  // scores a_ji = u_j . k_i / sqrt(d) + (tau-1-i) ln lambda_j
-  const float inv_sqrt_d = 1.0f / sqrtf(float(D));
-  for (int p = tid; p < nj * T; p += kThreads) {
-    const int jj = p / T, i = p % T;
-    const float4* ur = reinterpret_cast<const float4*>(ush + jj * US);
-    const float4* kr = reinterpret_cast<const float4*>(rows + i * RS);
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll 8
-    for (int e = 0; e < D / 4; ++e) {
-      const float4 x = ur[e], y = kr[e];
-      a0 = fmaf(x.x, y.x, a0);
-      a1 = fmaf(x.y, y.y, a1);
-      a0 = fmaf(x.z, y.z, a0);
-      a1 = fmaf(x.w, y.w, a1);
-    }
-    const float lnl = log_lambda[j0 + jj];
-    const int dist = T - 1 - i;
-    const float bias = dist == 0 ? 0.f : float(dist) * lnl;
-    w[jj * B1 + i] = (a0 + a1) * inv_sqrt_d + bias;
-  }
-  __syncthreads();
-
-  // per-slot merge of (m, l) with the new rows
-  if (tid < nj) {
-    const float m_shift = (lnl_t == -INFINITY) ? -INFINITY : fmaf(float(T), lnl_t, m_old);
-    float mx = m_shift;
-    for (int i = 0; i < T; ++i) mx = fmaxf(mx, w[tid * B1 + i]);
-    const float scale = (m_shift == -INFINITY) ? 0.f : exp_f(m_shift - mx);
-    float lsum = 0.f;
-    for (int i = 0; i < T; ++i) {
-      const float pw = exp_f(w[tid * B1 + i] - mx);
-      w[tid * B1 + i] = pw;
-      lsum += pw;
-    }
-    const float l_new = fmaf(l_old, scale, lsum);
-    sum_m[slot0 + tid] = mx;
-    sum_l[slot0 + tid] = l_new;
-    s_scale[tid] = scale;
-    s_inv_l[tid] = 1.0f / l_new;
-  }
-  __syncthreads();
-
-  // numerator n = n * scale + sum_i w_i [k_i ; v_i]; slots = n / l
+    for (int q = 0; q < EPL / 8; ++q) {
+      const uint4 w = reinterpret_cast<const uint4*>(p)[q];
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-  for (int k = 0; k < NQ; ++k) {
-    const int p = tid + k * kThreads, jj = p / Q, e4 = (p % Q) * 4;
-    if (jj >= nj) continue;
-    float4 acc = nreg[k];
-    const float sc = s_scale[jj];
-    acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
-    for (int i = 0; i < T; ++i) {
-      const float wi = w[jj * B1 + i];
-      const float4 r = *reinterpret_cast<const float4*>(rows + i * RS + e4);
-      acc.x = fmaf(wi, r.x, acc.x);
-      acc.y = fmaf(wi, r.y, acc.y);
-      acc.z = fmaf(wi, r.z, acc.z);
-      acc.w = fmaf(wi, r.w, acc.w);
+      for (int e = 0; e < 4; ++e) {
+        out[q * 8 + 2 * e] = __uint_as_float(ws[e] << 16);
+        out[q * 8 + 2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
+      }
     }
-    reinterpret_cast<float4*>(sum_n + slot0 * 2 * D)[p] = acc;
-    const float il = s_inv_l[jj];
-    if (e4 < D) {  // pooled key, [S][d]
-      const int64_t so = (slot0 + jj) * D + e4;
-      Ty::store(slot_k, so + 0, acc.x * il);
-      Ty::store(slot_k, so + 1, acc.y * il);
-      Ty::store(slot_k, so + 2, acc.z * il);
-      Ty::store(slot_k, so + 3, acc.w * il);
-    } else {  // pooled value: staged [dim][slot] in LDS, written below
-      float* sv = svals + (e4 - D) * SVS + jj;
-      sv[0 * SVS] = acc.x * il;
-      sv[1 * SVS] = acc.y * il;
-      sv[2 * SVS] = acc.z * il;
-      sv[3 * SVS] = acc.w * il;
+  } else if constexpr (EPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < EPL / 4; ++q) {
+      const float4 w = reinterpret_cast<const float4*>(p)[q];
+      out[4 * q] = w.x; out[4 * q + 1] = w.y; out[4 * q + 2] = w.z; out[4 * q + 3] = w.w;
     }
-  }
-  // slot values to the key-tiled layout: per dimension the tile's nj slots
-  // are consecutive, so each thread stores a run of slots of one dimension
-  __syncthreads();
-  {
-    const int64_t unit = int64_t(c) * Hkv + h;
-    for (int p = tid; p < D * nj; p += kThreads) {
-      const int dim = p / nj, jj = p % nj;
-      Ty::store(slot_v, value_index(unit, S, D, j0 + jj, dim), svals[dim * SVS + jj]);
-    }
+  } else {
+    static_assert(EPL == 2, "f32 lanes hold 2, 4, 8 or 16 elements");
+    const float2 w = *reinterpret_cast<const float2*>(p);
+    out[0] = w.x; out[1] = w.y;
   }
 }
 
-// seq_len[c] += clamp(tau[c], 1, B+1), after every append workgroup read it
-__global__ void append_commit(const int32_t* __restrict__ tau_in, int32_t* __restrict__ seq_len,
-                              int C, int B) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= C) return;
-  int T = tau_in[c];
-  T = T < 1 ? 1 : (T > B + 1 ? B + 1 : T);
-  seq_len[c] += T;
+template <typename Ty, int EPL>
+__device__ __forceinline__ void store_elems(typename Ty::T* p, const float (&v)[EPL], float s) {
+  if constexpr (Ty::kBytes == 2) {
+#pragma unroll
+    for (int q = 0; q < EPL / 8; ++q) {
+      uint32_t ws[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        ws[e] = uint32_t(f32_to_bf16(v[q * 8 + 2 * e] * s)) |
+                (uint32_t(f32_to_bf16(v[q * 8 + 2 * e + 1] * s)) << 16);
+      reinterpret_cast<uint4*>(p)[q] = uint4{ws[0], ws[1], ws[2], ws[3]};
+    }
+  } else if constexpr (EPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < EPL / 4; ++q)
+      reinterpret_cast<float4*>(p)[q] =
+          float4{v[4 * q] * s, v[4 * q + 1] * s, v[4 * q + 2] * s, v[4 * q + 3] * s};
+  } else {
+    *reinterpret_cast<float2*>(p) = float2{v[0] * s, v[1] * s};
+  }
+}
+
+// EPL consecutive elements of one row as loaded (bf16 stays packed until use)
+template <typename Ty, int EPL>
+struct Frag {
+  float v[EPL];
+  __device__ __forceinline__ void load(const typename Ty::T* p) { load_elems<Ty, EPL>(p, v); }
+  __device__ __forceinline__ float operator[](int e) const { return v[e]; }
+  __device__ __forceinline__ float dot(const Frag& o, float acc) const {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = fmaf(v[e], o.v[e], acc);
+    return acc;
+  }
+};
+template <int EPL>
+struct Frag<BF16, EPL> {
+  uint32_t w[EPL / 2];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+#pragma unroll
+    for (int q = 0; q < EPL / 8; ++q) {
+      const uint4 x = reinterpret_cast<const uint4*>(p)[q];
+      w[4 * q] = x.x; w[4 * q + 1] = x.y; w[4 * q + 2] = x.z; w[4 * q + 3] = x.w;
+    }
+  }
+  __device__ __forceinline__ float operator[](int e) const {
+    return (e & 1) ? __uint_as_float(w[e >> 1] & 0xFFFF0000u) : __uint_as_float(w[e >> 1] << 16);
+  }
+  // packed bf16 pairs straight into the fp32 dot product (v_dot2_f32_bf16),
+  // so the rows need not stay unpacked in registers
+  __device__ __forceinline__ float dot(const Frag& o, float acc) const {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int q = 0; q < EPL / 2; ++q)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[q]),
+                                            __builtin_bit_cast(bf16x2, o.w[q]), acc, false);
+    return acc;
+  }
+};
+
+// fp32 state entries: EPL consecutive floats, aligned to 8 * EPL bytes at most 16
+template <int EPL>
+__device__ __forceinline__ void load_state(const float* p, float (&out)[EPL]) {
+  if constexpr (EPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < EPL / 4; ++q) {
+      const float4 w = reinterpret_cast<const float4*>(p)[q];
+      out[4 * q] = w.x; out[4 * q + 1] = w.y; out[4 * q + 2] = w.z; out[4 * q + 3] = w.w;
+    }
+  } else {
+    const float2 w = *reinterpret_cast<const float2*>(p);
+    out[0] = w.x; out[1] = w.y;
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void store_state(float* p, const float (&v)[EPL]) {
+  if constexpr (EPL % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < EPL / 4; ++q)
+      reinterpret_cast<float4*>(p)[q] = float4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  } else {
+    *reinterpret_cast<float2*>(p) = float2{v[0], v[1]};
+  }
+}
+
+// x + (x taken from another lane of the same 16-lane DPP row)
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the LPS (16 or 32) lanes of a slot group, left in every lane of it:
+// within a 16-lane row by DPP (quad swaps, then rotations by 4 and 8), across
+// the two rows of a 32-lane group by one lane shuffle
+template <int LPS>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPS == 16 || LPS == 32, "slot groups are one or two DPP rows");
+  x = dpp_add<0xB1>(x);   // quad_perm [1,0,3,2]
+  x = dpp_add<0x4E>(x);   // quad_perm [2,3,0,1]
+  x = dpp_add<0x124>(x);  // row_ror:4
+  x = dpp_add<0x128>(x);  // row_ror:8
+  if constexpr (LPS == 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+// The window part of one sequence: rows 0..tau-1 of the verified block go to
+// window slots (L + i) mod W of every KV head, their positions to ring_pos,
+// and seq_len advances by tau.  One workgroup per sequence does all of it, so
+// it is the only reader of seq_len in the launch and may update it in place.
+// Keys and values are staged in LDS (a group of heads at a time, 16-byte
+// loads), keys leave as 16-byte pieces and values go into the key-tiled
+// layout with lanes over rows, so neighbouring lanes store neighbouring
+// window slots.
+template <typename Ty, int D>
+__device__ __forceinline__ void append_window(
+    const typename Ty::T* __restrict__ k_new, const typename Ty::T* __restrict__ v_new,
+    const int32_t* __restrict__ tau_in, typename Ty::T* __restrict__ ring_k,
+    typename Ty::T* __restrict__ ring_v, int32_t* __restrict__ ring_pos,
+    int32_t* __restrict__ seq_len, int32_t* __restrict__ err_flag, typename Ty::T* stage,
+    int stage_elems, int c, int Hkv, int W, int B) {
+  constexpr int kThreads = block_threads<D>();
+  constexpr int E16 = 16 / Ty::kBytes;      // elements per 16-byte piece
+  constexpr int V16 = D / E16;              // 16-byte pieces per key row
+  const int tid = threadIdx.x;
+  const int B1 = B + 1;
+  int Tn = tau_in[c];
+  if (Tn < 1 || Tn > B1) {
+    if (tid == 0) atomicOr(err_flag, 1);
+    Tn = Tn < 1 ? 1 : B1;
+  }
+  const int L = seq_len[c];
+  const int slot0 = L % W;                  // window slot of row 0; row i -> slot0 + i (mod W)
+  const bool tiled = value_tile(W) == 32;   // values in 32-key tiles (else one tile of W keys)
+  // a group of HG heads at a time: stage the group's tau rows [head][row][k | v]
+  // in LDS (every 16-byte load in flight at once: LDS stores never alias the
+  // global loads), then store keys as 16-byte pieces and values into the
+  // key tiles.  Index arithmetic stays 32-bit with divisions by constants:
+  // this workgroup's work grows with tau and must not be ALU-bound.
+  const int HG = max(1, min(Hkv, stage_elems / (B1 * 2 * D)));
+  for (int h0 = 0; h0 < Hkv; h0 += HG) {
+    const int hg = min(HG, Hkv - h0);
+    const int rows = hg * Tn;                 // (head, row) pairs, row fastest
+    for (int p = tid; p < rows * 2 * V16; p += kThreads) {
+      const int e = p % V16, half = (p / V16) & 1, pr = p / (2 * V16);
+      const int hl = pr / Tn, i = pr - hl * Tn;
+      reinterpret_cast<uint4*>(stage + (pr * 2 + half) * D)[e] =
+          reinterpret_cast<const uint4*>((half ? v_new : k_new) +
+                                         ((int64_t(c) * B1 + i) * Hkv + h0 + hl) * D)[e];
+    }
+    __syncthreads();
+    for (int p = tid; p < rows * V16; p += kThreads) {
+      const int e = p % V16, pr = p / V16;
+      const int hl = pr / Tn, i = pr - hl * Tn;
+      const int slot = slot0 + i >= W ? slot0 + i - W : slot0 + i;
+      reinterpret_cast<uint4*>(ring_k + ((int64_t(c) * Hkv + h0 + hl) * W + slot) * D)[e] =
+          reinterpret_cast<const uint4*>(stage + pr * 2 * D)[e];
+    }
+    // values: D lanes per (head, row) pair, one dimension each
+    constexpr int PAIRS = kThreads / D;       // pairs per pass
+    for (int pr = tid / D; pr < rows; pr += PAIRS) {
+      const int dim = tid % D;
+      const int hl = pr / Tn, i = pr - hl * Tn;
+      const int slot = slot0 + i >= W ? slot0 + i - W : slot0 + i;
+      const int64_t unit = int64_t(c) * Hkv + h0 + hl;
+      const int64_t idx = tiled ? ((unit * (W >> 5) + (slot >> 5)) * D + dim) * 32 + (slot & 31)
+                                : (unit * D + dim) * W + slot;
+      ring_v[idx] = stage[(pr * 2 + 1) * D + dim];
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < Tn; i += kThreads) {
+    const int slot = slot0 + i >= W ? slot0 + i - W : slot0 + i;
+    ring_pos[int64_t(c) * W + slot] = L + i;
+  }
+  if (tid == 0) seq_len[c] = L + Tn;
+}
+
+template <typename Ty, int D>
+__global__ __launch_bounds__(block_threads<D>()) void append_kernel(
+    const typename Ty::T* __restrict__ k_new, const typename Ty::T* __restrict__ v_new,
+    const int32_t* __restrict__ tau_in, typename Ty::T* __restrict__ ring_k,
+    typename Ty::T* __restrict__ ring_v, int32_t* __restrict__ ring_pos,
+    int32_t* __restrict__ seq_len, float* __restrict__ sum_m, float* __restrict__ sum_l,
+    float* __restrict__ sum_n, typename Ty::T* __restrict__ slot_k,
+    typename Ty::T* __restrict__ slot_v, const typename Ty::T* __restrict__ u,
+    const float* __restrict__ log_lambda, int32_t* __restrict__ err_flag, int C, int Hkv, int W,
+    int S, int B, int stage_elems) {
+  using T = typename Ty::T;
+  extern __shared__ float4 smem4[];
+  T* lds = reinterpret_cast<T*>(smem4);
+  if (int(blockIdx.x) < C) {
+    append_window<Ty, D>(k_new, v_new, tau_in, ring_k, ring_v, ring_pos, seq_len, err_flag, lds,
+                         stage_elems, int(blockIdx.x), Hkv, W, B);
+    return;
+  }
+  constexpr int LPS = lanes_per_slot<D>();
+  constexpr int EPL = 2 * D / LPS;       // n entries per lane
+  constexpr int HALF = LPS / 2;          // lanes of the key half
+  const int tid = threadIdx.x;
+  const int g = tid % LPS;               // entry group: g < HALF key half, else value half
+  const int js = tid / LPS;              // slot within the tile
+  const int ntile = (S + kSlotsPerBlock - 1) / kSlotsPerBlock;
+  const int bid = int(blockIdx.x) - C;
+  const int tile = bid % ntile;
+  constexpr int kThreads = block_threads<D>();
+  const int unit = bid / ntile;          // c * Hkv + h
+  const int c = unit / Hkv, h = unit % Hkv;
+  const int j = tile * kSlotsPerBlock + js;
+  const bool active = j < S;
+  const int jc = active ? j : S - 1;     // idle lanes (S % 32 != 0) load in bounds
+  const int64_t sidx = int64_t(unit) * S + jc;
+  const bool key_lane = g < HALF;
+  const int col = (key_lane ? g : g - HALF) * EPL;  // first dimension of this lane's entries
+
+  // Issue the state and slot-query loads, then stage all B+1 verified rows
+  // of this (c, h) ([k | v] per row) in LDS with 16-byte pieces.  Rows past
+  // tau exist in the buffer, so nothing here waits for tau, and the merge
+  // below reads rows from LDS whatever the number of batches.
+  const int B1 = B + 1;
+  // [B+1][2d] fp32 after the value tile (16-byte aligned: the tile is d*32 elements)
+  float* rows = reinterpret_cast<float*>(lds + D * kSlotsPerBlock);
+  float n[EPL], uq[EPL];
+  load_state<EPL>(sum_n + sidx * 2 * D + g * EPL, n);
+  const float m_old = sum_m[sidx], l_old = sum_l[sidx], lnl = log_lambda[jc];
+  load_elems<Ty, EPL>(u + (int64_t(h) * S + jc) * D + col, uq);
+  {
+    // rows are widened to fp32 once here, so the merge reads them ready to use
+    constexpr int E16 = 16 / Ty::kBytes, V16 = D / E16;
+    for (int p = tid; p < B1 * 2 * V16; p += kThreads) {
+      const int e = p % V16, half = (p / V16) & 1, i = p / (2 * V16);
+      float x[E16];
+      load_elems<Ty, E16>((half ? v_new : k_new) + ((int64_t(c) * B1 + i) * Hkv + h) * D + e * E16, x);
+      float4* dst = reinterpret_cast<float4*>(rows + i * 2 * D + half * D + e * E16);
+#pragma unroll
+      for (int q = 0; q < E16 / 4; ++q) dst[q] = float4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+    }
+  }
+  int Tn = tau_in[c];
+  Tn = Tn < 1 ? 1 : (Tn > B1 ? B1 : Tn);
+  __syncthreads();
+
+  const float inv_sqrt_d = 1.0f / sqrtf(float(D));
+  // every old score grows by tau*ln(lambda); lambda = 0 drops the old state
+  float m_run = (lnl == -INFINITY) ? -INFINITY : fmaf(float(Tn), lnl, m_old);
+  float l_run = l_old;
+  for (int i0 = 0; i0 < Tn; i0 += kBatch) {
+    float r[kBatch][EPL], a[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) load_state<EPL>(rows + min(i0 + q, Tn - 1) * 2 * D + g * EPL, r[q]);
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      // every lane forms the product (no branch); only the key half counts
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part = fmaf(uq[e], r[q][e], part);
+      const float dot = group_sum<LPS>(key_lane ? part : 0.f);
+      const int i = i0 + q, dist = Tn - 1 - i;
+      const float bias = dist == 0 ? 0.f : float(dist) * lnl;
+      a[q] = i < Tn ? dot * inv_sqrt_d + bias : -INFINITY;
+    }
+    float mb = m_run;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) mb = fmaxf(mb, a[q]);
+    const float sc = (m_run == -INFINITY) ? 0.f : exp_f(m_run - mb);
+    float wq[kBatch], lsum = 0.f;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      wq[q] = (a[q] == -INFINITY) ? 0.f : exp_f(a[q] - mb);
+      lsum += wq[q];
+    }
+    l_run = fmaf(l_run, sc, lsum);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float x = n[e] * sc;
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) x = fmaf(wq[q], r[q][e], x);
+      n[e] = x;
+    }
+    m_run = mb;
+  }
+
+  const float il = 1.0f / l_run;
+  if (active) {
+    store_state<EPL>(sum_n + sidx * 2 * D + g * EPL, n);
+    if (g == 0) {
+      sum_m[sidx] = m_run;
+      sum_l[sidx] = l_run;
+    }
+    if (key_lane) store_elems<Ty, EPL>(slot_k + sidx * D + col, n, il);
+  }
+  // pooled values -> the tile [d][32] in LDS -> slot_v
+  if (!key_lane) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float x = n[e] * il;
+      T t;
+      if constexpr (Ty::kBytes == 2) t = f32_to_bf16(x); else t = x;
+      lds[(col + e) * kSlotsPerBlock + js] = t;
+    }
+  }
+  __syncthreads();
+  if (value_tile(S) == kSlotsPerBlock) {
+    // the tile is contiguous in slot_v: D * 32 elements as 16-byte pieces
+    constexpr int P16 = D * kSlotsPerBlock * Ty::kBytes / 16;
+    uint4* dst = reinterpret_cast<uint4*>(slot_v + value_index(unit, S, D, tile * kSlotsPerBlock, 0));
+    const uint4* srcv = reinterpret_cast<const uint4*>(lds);
+    for (int p = tid; p < P16; p += kThreads) dst[p] = srcv[p];
+  } else {
+    for (int p = tid; p < D * kSlotsPerBlock; p += kThreads) {
+      const int dim = p / kSlotsPerBlock, jt = p % kSlotsPerBlock;
+      const int jj = tile * kSlotsPerBlock + jt;
+      if (jj < S) slot_v[value_index(unit, S, D, jj, dim)] = lds[p];
+    }
+  }
 }
 
 template <typename Ty, int D>
 ls_status run(const ls_dims& d, const ls_state& st, const void* k_new, const void* v_new,
               const int32_t* tau, hipStream_t stream) {
   using T = typename Ty::T;
-  const int NT = int(cdiv(d.S, kSlotsPerBlock));
-  const size_t shmem = sizeof(float) * (size_t(d.B + 1) * (2 * D + 4) +
-                                        size_t(kSlotsPerBlock) * (D + 4) +
-                                        size_t(kSlotsPerBlock) * (d.B + 1) +
-                                        size_t(D) * (kSlotsPerBlock + 1));
-  hipLaunchKernelGGL((append_kernel<Ty, D>), dim3(d.C * d.Hkv * NT), dim3(kThreads), shmem, stream,
-                     static_cast<const T*>(k_new), static_cast<const T*>(v_new), tau,
+  const int ntile = int(cdiv(d.S, kSlotsPerBlock));
+  // LDS: the summary value tile [d][32] and the B+1 staged rows [B+1][2d]
+  // (fp32), or the window's staging (up to all heads' B+1 rows of k and v,
+  // capped at 40 KB; the window loops over head groups)
+  const size_t tile_bytes = size_t(D) * kSlotsPerBlock * sizeof(T) + size_t(d.B + 1) * 2 * D * sizeof(float);
+  const size_t head_bytes = size_t(d.B + 1) * 2 * D * sizeof(T);
+  const size_t heads = std::max<size_t>(1, std::min<size_t>(size_t(d.Hkv), (size_t(40) << 10) / head_bytes));
+  const size_t shmem = std::max(tile_bytes, heads * head_bytes);
+  const int stage_elems = int(shmem / sizeof(T));
+  hipLaunchKernelGGL((append_kernel<Ty, D>), dim3(d.C + d.C * d.Hkv * ntile), dim3(block_threads<D>()), shmem,
+                     stream, static_cast<const T*>(k_new), static_cast<const T*>(v_new), tau,
                      static_cast<T*>(st.ring_k), static_cast<T*>(st.ring_v), st.ring_pos,
                      st.seq_len, st.sum_m, st.sum_l, st.sum_n, static_cast<T*>(st.slot_k),
                      static_cast<T*>(st.slot_v), static_cast<const T*>(st.u), st.log_lambda,
-                     st.err_flag, d.Hkv, d.W, d.S, d.B, NT);
-  if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
-  hipLaunchKernelGGL(append_commit, dim3(unsigned(cdiv(d.C, 256))), dim3(256), 0, stream, tau,
-                     st.seq_len, d.C, d.B);
+                     st.err_flag, d.C, d.Hkv, d.W, d.S, d.B, stage_elems);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
 
