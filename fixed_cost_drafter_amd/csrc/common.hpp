@@ -121,8 +121,15 @@ inline int init_rows_per_split(const ls_dims& d, int32_t L0) {
 
 // key halves of the bf16 draft attention: two workgroups per KV head unit
 // when there are too few units to fill the GPU with one, and enough keys
+// bf16 draft attention with more than 32 query rows per KV head: the rows
+// are split over workgroups (each reads all keys, no partials)
+inline bool draft_row_split(const ls_dims& d) {
+  return d.dtype == LS_BF16 && int64_t(d.B) * (d.Hq / d.Hkv) > 32;
+}
+// otherwise the keys may be split over two workgroups (partials + combine)
+// when the units alone do not fill the chip
 inline int draft_halves(const ls_dims& d) {
-  if (d.dtype != LS_BF16) return 1;
+  if (d.dtype != LS_BF16 || draft_row_split(d)) return 1;
   const int64_t chunks = (int64_t(d.W) + d.S) / 32 + cdiv(d.B, 32);
   return (int64_t(d.C) * d.Hkv < 256 && chunks >= 16) ? 2 : 1;
 }

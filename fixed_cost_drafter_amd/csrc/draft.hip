@@ -35,8 +35,15 @@ namespace ls {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kParts = 4;  // waves of the bf16 kernel's workgroup
-constexpr float kRescale = 8.f;  // e-folds the running max may lag the true max
+#ifndef LS_DRAFT_INFLIGHT
+#define LS_DRAFT_INFLIGHT 2
+#endif
+constexpr int kInFlight = LS_DRAFT_INFLIGHT;  // chunks loading into registers per thread
+// Scores are kept in base-2 units (log2(e) folded into the 1/sqrt(d) scale),
+// so every softmax weight is one v_exp_f32 (2^x).
+constexpr float kScale2 = 0.08838834764831845f * 1.4426950408889634f;  // log2(e)/sqrt(128)
+constexpr float kRescale = 8.f * 1.4426950408889634f;  // the running max may lag by e^8
+__device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline uint16_t bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));  // v_cvt, nearest-even
@@ -50,7 +57,8 @@ __device__ inline uint16_t bf16_bits(float f) {
 __device__ __forceinline__ int chunk_key(int m, int mb) { return 8 * (m >> 2) + 4 * mb + (m & 3); }
 
 // LDS image of one staged 32-key chunk: keys row-major (padded rows), values
-// [d][32] (padded), positions.  Reads of both are conflict-free ds_read_b128.
+// [d][32] (padded), and a score bias per key (0, or -inf for an empty window
+// slot or a block row past B).
 constexpr int kKS = 128 + 8;   // key row stride (bf16)
 constexpr int kVS = 32 + 8;    // value row stride (bf16)
 constexpr int kStageElems = 32 * kKS + 128 * kVS + 64;  // bf16 elements (+ 32 int positions)
@@ -58,16 +66,18 @@ constexpr int kStageElems = 32 * kKS + 128 * kVS + 64;  // bf16 elements (+ 32 i
 struct Stage {  // pointers into one stage buffer
   uint16_t* k;
   uint16_t* v;
-  int* pos;
+  float* bias;
   __device__ explicit Stage(uint16_t* base)
-      : k(base), v(base + 32 * kKS), pos(reinterpret_cast<int*>(base + 32 * kKS + 128 * kVS)) {}
+      : k(base), v(base + 32 * kKS), bias(reinterpret_cast<float*>(base + 32 * kKS + 128 * kVS)) {}
 };
 
-// One thread's share of a chunk: 4 pieces of 16 bytes (2 of keys, 2 of
-// values) out of the chunk's 1024, plus one ring position for t < 32.
+// One thread's share of a chunk: PPT pieces of 16 bytes of keys and PPT of
+// values out of the chunk's 512 + 512 (TPP = 512 / PPT staging threads per
+// key part), plus one key's score bias for t < 32.
+template <int PPT>
 struct Piece {
-  u16x8 d[4];
-  int pos;
+  u16x8 d[2 * PPT];
+  float bias;
 };
 
 // Source of chunk ch of one unit: [window W/32 | slots S/32 | block].
@@ -77,47 +87,50 @@ struct Views {
   int W, S, B, Hkv, c, h, nring, ngl;
 };
 
-// loads for staging chunk ch (thread t of the 256 staging threads of a part)
-__device__ __forceinline__ void load_piece(Piece& x, const Views& s, int ch, int t) {
-  constexpr int D = 128;
+// loads for staging chunk ch (thread t of the part's 512 / PPT staging threads)
+template <int PPT>
+__device__ __forceinline__ void load_piece(Piece<PPT>& x, const Views& s, int ch, int t) {
+  constexpr int D = 128, TPP = 512 / PPT;
   if (ch < s.ngl) {  // window or slots: K rows [key][d], V tile [d][32], contiguous
     const bool ring = ch < s.nring;
     const int key0 = (ring ? ch : ch - s.nring) * 32;
     const uint16_t* kt = (ring ? s.rk : s.sk) + int64_t(key0) * D;
     const uint16_t* vt = (ring ? s.rv : s.sv) + int64_t(ring ? ch : ch - s.nring) * D * 32;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      x.d[j] = *reinterpret_cast<const u16x8*>(kt + (t + 256 * j) * 8);
-      x.d[2 + j] = *reinterpret_cast<const u16x8*>(vt + (t + 256 * j) * 8);
+    for (int j = 0; j < PPT; ++j) {
+      x.d[j] = *reinterpret_cast<const u16x8*>(kt + (t + TPP * j) * 8);
+      x.d[PPT + j] = *reinterpret_cast<const u16x8*>(vt + (t + TPP * j) * 8);
     }
     const int p = s.rp[(ring ? key0 : 0) + (t & 31)];
-    x.pos = ring ? p : 0;
+    x.bias = (ring && p < 0) ? -INFINITY : 0.f;
   } else {  // block: K and V rows are the caller's token-major [b][Hkv][d]
     const int key0 = (ch - s.ngl) * 32;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int piece = t + 256 * j, row = piece >> 4, col = (piece & 15) * 8;
+    for (int j = 0; j < PPT; ++j) {
+      const int piece = t + TPP * j, row = piece >> 4, col = (piece & 15) * 8;
       const int64_t off = ((int64_t(s.c) * s.B + min(key0 + row, s.B - 1)) * s.Hkv + s.h) * D + col;
       x.d[j] = *reinterpret_cast<const u16x8*>(s.kb + off);
-      x.d[2 + j] = *reinterpret_cast<const u16x8*>(s.vb + off);
+      x.d[PPT + j] = *reinterpret_cast<const u16x8*>(s.vb + off);
     }
-    x.pos = key0 + (t & 31) < s.B ? 0 : -1;
+    x.bias = key0 + (t & 31) < s.B ? 0.f : -INFINITY;
   }
 }
 
-__device__ __forceinline__ void store_piece(const Piece& x, Stage st, bool block_chunk, int t) {
+template <int PPT>
+__device__ __forceinline__ void store_piece(const Piece<PPT>& x, Stage st, bool block_chunk, int t) {
+  constexpr int TPP = 512 / PPT;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int piece = t + 256 * j, row = piece >> 4, col = (piece & 15) * 8;
+  for (int j = 0; j < PPT; ++j) {
+    const int piece = t + TPP * j, row = piece >> 4, col = (piece & 15) * 8;
     *reinterpret_cast<u16x8*>(st.k + row * kKS + col) = x.d[j];
     if (!block_chunk) {  // value tile piece: dim = piece / 4, keys (piece % 4) * 8 ..
-      *reinterpret_cast<u16x8*>(st.v + (piece >> 2) * kVS + (piece & 3) * 8) = x.d[2 + j];
+      *reinterpret_cast<u16x8*>(st.v + (piece >> 2) * kVS + (piece & 3) * 8) = x.d[PPT + j];
     } else {  // token-major value row -> [d][32]
 #pragma unroll
-      for (int e = 0; e < 8; ++e) st.v[(col + e) * kVS + row] = x.d[2 + j][e];
+      for (int e = 0; e < 8; ++e) st.v[(col + e) * kVS + row] = x.d[PPT + j][e];
     }
   }
-  if (t < 32) st.pos[t] = x.pos;
+  if (t < 32) st.bias[t] = x.bias;
 }
 
 // Online softmax state of one row group of 16 query rows.
@@ -126,11 +139,12 @@ struct Softmax {
   f32x4 o[8];
 };
 
-// one staged chunk for the wave's row group: scores, masking, lazy online
-// softmax update, P.V
+// one staged chunk for the wave's row group: scores (base 2, biased), lazy
+// online softmax update, P.V
 __device__ __forceinline__ void compute_chunk(Softmax& st, Stage sg, const bf16x8 (&qb)[4], int ln,
                                               int kg) {
-  const float sm_scale = 0.08838834764831845f;  // 1/sqrt(128)
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
   f32x4 s[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -140,44 +154,52 @@ __device__ __forceinline__ void compute_chunk(Softmax& st, Stage sg, const bf16x
     for (int ks = 0; ks < 4; ++ks)
       s[mb] = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u16x8*>(krow + ks * 32)), qb[ks], s[mb]);
   }
-  const int4 p0 = *reinterpret_cast<const int4*>(sg.pos + 8 * kg);
-  const int4 p1 = *reinterpret_cast<const int4*>(sg.pos + 8 * kg + 4);
-  const int pos[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-  // s[mb][r] is key 8kg + 4mb + r of the chunk
+  // s[mb][r] is key 8kg + 4mb + r of the chunk: score = s * log2(e)/sqrt(d) + bias
+  const f32x4 b0 = *reinterpret_cast<const f32x4*>(sg.bias + 8 * kg);
+  const f32x4 b1 = *reinterpret_cast<const f32x4*>(sg.bias + 8 * kg + 4);
   float tmax = -INFINITY;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float a = pos[mb * 4 + r] >= 0 ? s[mb][r] * sm_scale : -INFINITY;
-      s[mb][r] = a;
-      tmax = fmaxf(tmax, a);
-    }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  for (int r = 0; r < 4; ++r) {
+    s[0][r] = fmaf(s[0][r], kScale2, b0[r]);
+    s[1][r] = fmaf(s[1][r], kScale2, b1[r]);
+    tmax = fmaxf(tmax, fmaxf(s[0][r], s[1][r]));
+  }
+  // the row's max over the 4 lane groups (lanes ln, ln+16, ln+32, ln+48):
+  // swapping a register with itself across row pairs / halves leaves the
+  // partner's value in one of the two results
+  {
+    const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    tmax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+    const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+    tmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+  }
   // lazy rescale: the reference max moves only when some row's max grows by
-  // more than kRescale, so weights stay <= e^kRescale and the O / l rescale
-  // is skipped in the steady state
+  // more than kRescale, so weights stay <= e^8 and the O / l rescale is
+  // skipped in the steady state
   if (__any(tmax > st.m + kRescale)) {
     const float m_new = fmaxf(st.m, tmax);
-    const float scale = st.m == -INFINITY ? 0.f : exp_f(st.m - m_new);
+    const float scale = st.m == -INFINITY ? 0.f : exp2_f(st.m - m_new);
     st.m = m_new;
     st.l *= scale;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) st.o[mb] *= scale;
   }
   const float m_use = st.m == -INFINITY ? 0.f : st.m;
-  float lsum = 0.f;
-  u16x8 pv;
+  // weights rounded to bf16 in pairs; l sums the same rounded weights
+  uint32_t pw[4];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint16_t pb = bf16_bits(exp_f(s[mb][r] - m_use));
-      lsum += bf16_to_f32(pb);
-      pv[mb * 4 + r] = pb;
+    for (int r = 0; r < 4; r += 2) {
+      const f32x2 e2 = {exp2_f(s[mb][r] - m_use), exp2_f(s[mb][r + 1] - m_use)};
+      pw[mb * 2 + r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(e2, bf16x2));
     }
+  const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
+  float lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[w]), ones, lsum, false);
   st.l += lsum;
+  const u16x8 pv = __builtin_bit_cast(u16x8, uint4{pw[0], pw[1], pw[2], pw[3]});
   const bf16x8 pk = as_bf16x8(pv);
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
@@ -186,33 +208,38 @@ __device__ __forceinline__ void compute_chunk(Softmax& st, Stage sg, const bf16x
   }
 }
 
-// Workgroup = (KV head unit, one of `halves` key ranges); 8 waves = 4 row
-// groups of 16 query rows x 2 key parts.  Each part stages its chunks into
-// its own double-buffered LDS stages (two chunks in flight in registers) and
-// its 4 row-group waves read them.  The parts merge in LDS; the halves' (m,
-// l, O) go to the workspace for draft_combine (a kernel boundary, no fence),
-// or with a single range the output is written here.
-__global__ __launch_bounds__(512, 1) void draft_mfma(
+// Workgroup = (KV head unit, split); 64*RG*KPW threads = RG row groups of 16
+// query rows x KPW key parts.  A split is either one of `ksplit` key ranges
+// (all rows; the ranges' (m, l, O) go to the workspace for draft_combine, a
+// kernel boundary, no fence) or, with ksplit = 1, one range of 16*RG query
+// rows over all keys (the output is written here).  The splits of a unit are
+// blockIdx = unit + k * units, on one XCD when units is a multiple of 8, so
+// the keys they share are fetched from HBM once.  Each key part stages its
+// chunks into its own double-buffered LDS stages (kInFlight chunks loading
+// in registers) and its RG row-group waves read them; the parts merge in LDS.
+template <int RG, int KPW>
+__global__ __launch_bounds__(64 * RG * KPW, 1) void draft_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, const uint16_t* __restrict__ ring_k,
     const uint16_t* __restrict__ ring_v, const int32_t* __restrict__ ring_pos,
     const uint16_t* __restrict__ slot_k, const uint16_t* __restrict__ slot_v,
     uint16_t* __restrict__ out, float* __restrict__ part_out, int Hq, int Hkv, int W, int S,
-    int B, int units, int halves) {
-  constexpr int D = 128, RG = 4, KPW = 2;
+    int B, int units, int ksplit) {
+  constexpr int D = 128, TPP = 64 * RG, PPT = 512 / TPP;
   __shared__ __attribute__((aligned(16))) uint16_t lds[KPW * 2 * kStageElems];
 
-  const int half = blockIdx.x / units;
+  const int split = blockIdx.x / units;
   const int unit = blockIdx.x % units;
+  const int kidx = split % ksplit, ridx = split / ksplit;
   const int c = unit / Hkv, h = unit % Hkv;
   const int G = Hq / Hkv, M = B * G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, kg = lane >> 4;
   const int g = wave % RG, kq = wave / RG;   // row group, key part
-  const int t = tid % 256;                   // staging thread within the part
+  const int t = tid % TPP;                   // staging thread within the part
 
   // query operand: lane (row ln of group g, kg) holds q[row][ks*32+kg*8..+7]
-  const int row = g * 16 + ln;
+  const int row = ridx * 16 * RG + g * 16 + ln;
   const bool row_ok = row < M;
   bf16x8 qb[4];
   {
@@ -230,12 +257,12 @@ __global__ __launch_bounds__(512, 1) void draft_mfma(
   const Views views{ring_k + int64_t(unit) * W * D, ring_v + int64_t(unit) * D * W,
                     slot_k + int64_t(unit) * S * D, slot_v + int64_t(unit) * D * S, kb, vb,
                     ring_pos + int64_t(c) * W, W, S, B, Hkv, c, h, nring, ngl};
-  const int nparts = halves * KPW, pidx = half * KPW + kq;
+  const int nparts = ksplit * KPW, pidx = kidx * KPW + kq;
   const int per = (nch + nparts - 1) / nparts;
   const int ch0 = pidx * per, ch1 = min(nch, ch0 + per);
   const int steps = per;  // same count in every part (empty chunks are skipped)
   uint16_t* mine = lds + kq * 2 * kStageElems;
-  const bool active = (g * 16 < M);
+  const bool active = ridx * 16 * RG + g * 16 < M;
 
   Softmax st;
   st.m = -INFINITY;
@@ -243,32 +270,36 @@ __global__ __launch_bounds__(512, 1) void draft_mfma(
 #pragma unroll
   for (int i = 0; i < 8; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Piece pa, pb;
-  if (ch0 < ch1) load_piece(pa, views, ch0, t);
-  if (ch0 + 1 < ch1) load_piece(pb, views, ch0 + 1, t);
-  for (int i = 0; i < steps; i += 2) {
+  // kInFlight chunks are loading into registers while one is computed; the
+  // LDS holds two stages (written at step k, read at step k, rewritten at
+  // step k + 2 after the barrier of step k + 1)
+  Piece<PPT> pc[kInFlight];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {  // step i + u, registers pa (u = 0) / pb (u = 1)
-      const int ch = ch0 + i + u;
-      Piece& x = u == 0 ? pa : pb;
-      Stage sg(mine + u * kStageElems);
-      if (i + u < steps) {
-        if (ch < ch1) store_piece(x, sg, ch >= ngl, t);
+  for (int u = 0; u < kInFlight; ++u)
+    if (ch0 + u < ch1) load_piece(pc[u], views, ch0 + u, t);
+  for (int i = 0; i < steps; i += kInFlight) {
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {  // step i + u uses registers pc[u]
+      const int stp = i + u, ch = ch0 + stp;
+      Stage sg(mine + (stp & 1) * kStageElems);
+      if (stp < steps) {
+        if (ch < ch1) store_piece(pc[u], sg, ch >= ngl, t);
         __syncthreads();  // stage ready; the stage written two steps ago was read before
-        if (ch + 2 < ch1) load_piece(x, views, ch + 2, t);
+        if (ch + kInFlight < ch1) load_piece(pc[u], views, ch + kInFlight, t);
         if (active && ch < ch1) compute_chunk(st, sg, qb, ln, kg);
       }
     }
   }
 
-  // merge the 2 key parts in LDS (reusing the stages), then write
+  // merge the KPW key parts in LDS (reusing the stages), then write
   float lt = st.l;
   lt += __shfl_xor(lt, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);  // [RG][64 lanes][34]
-  if (kq == 1) {
-    float* dst = red + (g * 64 + lane) * 34;
+  float* red = reinterpret_cast<float*>(lds);  // [KPW-1][RG][64 lanes][34]
+  static_assert((KPW - 1) * RG * 64 * 34 * 4 <= KPW * 2 * kStageElems * 2, "merge buffer fits the stages");
+  if (kq > 0) {
+    float* dst = red + (((kq - 1) * RG + g) * 64 + lane) * 34;
     dst[0] = st.m;
     dst[1] = lt;
 #pragma unroll
@@ -278,17 +309,25 @@ __global__ __launch_bounds__(512, 1) void draft_mfma(
   }
   __syncthreads();
   if (kq != 0) return;
-  const float* src = red + (g * 64 + lane) * 34;
-  const float mx = fmaxf(st.m, src[0]);
-  const float w0 = st.m == -INFINITY ? 0.f : exp_f(st.m - mx);
-  const float w1 = src[0] == -INFINITY ? 0.f : exp_f(src[0] - mx);
-  const float l = lt * w0 + src[1] * w1;
+  float mx = st.m;
+#pragma unroll
+  for (int k = 1; k < KPW; ++k) mx = fmaxf(mx, red[(((k - 1) * RG + g) * 64 + lane) * 34]);
+  const float w0 = st.m == -INFINITY ? 0.f : exp2_f(st.m - mx);
+  float l = lt * w0;
   f32x4 o[8];
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
+  for (int mb = 0; mb < 8; ++mb) o[mb] = st.o[mb] * w0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o[mb][r] = st.o[mb][r] * w0 + src[2 + mb * 4 + r] * w1;
-  if (halves == 1) {  // the whole key range: write the output
+  for (int k = 1; k < KPW; ++k) {
+    const float* src = red + (((k - 1) * RG + g) * 64 + lane) * 34;
+    const float wk = src[0] == -INFINITY ? 0.f : exp2_f(src[0] - mx);
+    l = fmaf(src[1], wk, l);
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[mb][r] = fmaf(src[2 + mb * 4 + r], wk, o[mb][r]);
+  }
+  if (ksplit == 1) {  // the whole key range: write the output
     if (!row_ok) return;
     const float il = 1.0f / l;
     uint16_t* orow = out + ((int64_t(c) * B + row / G) * Hq + h * G + row % G) * D;
@@ -297,9 +336,9 @@ __global__ __launch_bounds__(512, 1) void draft_mfma(
       *reinterpret_cast<u16x4*>(orow + mb * 16 + kg * 4) =
           u16x4{bf16_bits(o[mb][0] * il), bf16_bits(o[mb][1] * il), bf16_bits(o[mb][2] * il),
                 bf16_bits(o[mb][3] * il)};
-  } else {  // partial of this range: m[64] | l[64] | O[64][D]
-    constexpr int Mpad = 16 * RG;
-    float* pbuf = part_out + (int64_t(unit) * halves + half) * int64_t(Mpad) * (D + 2);
+  } else {  // partial of this key range: m[64] | l[64] | O[64][D] (m in base 2)
+    constexpr int Mpad = 64;
+    float* pbuf = part_out + (int64_t(unit) * ksplit + kidx) * int64_t(Mpad) * (D + 2);
     if (kg == 0) {
       pbuf[row] = mx;
       pbuf[Mpad + row] = l;
@@ -337,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void draft_combine(
   float l = 0.f;
   f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s2 = 0; s2 < halves; ++s2) {
-    const float wgt = ms[s2] == -INFINITY ? 0.f : exp_f(ms[s2] - mx);
+    const float wgt = ms[s2] == -INFINITY ? 0.f : exp2_f(ms[s2] - mx);
     l = fmaf(ls[s2], wgt, l);
     a += os[s2] * wgt;
   }
@@ -445,22 +484,28 @@ ls_status launch_draft(const ls_dims& d, const ls_state& st, const void* q, cons
   if (d.dtype == LS_BF16) {
     const int units = d.C * d.Hkv;
     const int M = d.B * (d.Hq / d.Hkv);
-    const int halves = draft_halves(d);
+    const int ksplit = draft_halves(d);  // 1 under the row split
     float* part = reinterpret_cast<float*>(static_cast<char*>(st.workspace) + ws_layout(d, 1).draft_part);
-    const dim3 grid(units * halves), block(512);
-    hipLaunchKernelGGL(draft_mfma, grid, block, 0, stream, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(kb), static_cast<const uint16_t*>(vb),
-                       static_cast<const uint16_t*>(st.ring_k), static_cast<const uint16_t*>(st.ring_v),
-                       st.ring_pos, static_cast<const uint16_t*>(st.slot_k),
-                       static_cast<const uint16_t*>(st.slot_v), static_cast<uint16_t*>(out), part,
-                       d.Hq, d.Hkv, d.W, d.S, d.B, units, halves);
+    const uint16_t *q16 = static_cast<const uint16_t*>(q), *kb16 = static_cast<const uint16_t*>(kb),
+                   *vb16 = static_cast<const uint16_t*>(vb);
+    const uint16_t *rk = static_cast<const uint16_t*>(st.ring_k), *rv = static_cast<const uint16_t*>(st.ring_v),
+                   *sk = static_cast<const uint16_t*>(st.slot_k), *sv = static_cast<const uint16_t*>(st.slot_v);
+    uint16_t* o16 = static_cast<uint16_t*>(out);
+    if (draft_row_split(d)) {
+      // query rows in two halves of 32 (2 row groups x 4 key parts), all keys each
+      const int rsplit = int(cdiv(M, 32));
+      hipLaunchKernelGGL((draft_mfma<2, 4>), dim3(units * rsplit), dim3(512), 0, stream, q16, kb16, vb16,
+                         rk, rv, st.ring_pos, sk, sv, o16, part, d.Hq, d.Hkv, d.W, d.S, d.B, units, 1);
+      return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+    }
+    hipLaunchKernelGGL((draft_mfma<4, 2>), dim3(units * ksplit), dim3(512), 0, stream, q16, kb16, vb16,
+                       rk, rv, st.ring_pos, sk, sv, o16, part, d.Hq, d.Hkv, d.W, d.S, d.B, units, ksplit);
     if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
-    if (halves > 1) {
+    if (ksplit > 1) {
       const int Mpad = 64;
       const int64_t threads = int64_t(units) * Mpad * (128 / 4);
       hipLaunchKernelGGL(draft_combine, dim3(unsigned(cdiv(threads, kThreads))), dim3(kThreads), 0,
-                         stream, part, static_cast<uint16_t*>(out), d.Hq, d.Hkv, d.B, halves,
-                         Mpad, units);
+                         stream, part, o16, d.Hq, d.Hkv, d.B, ksplit, Mpad, units);
     }
     return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
   }
