@@ -352,24 +352,75 @@ __global__ __launch_bounds__(kThreads) void init_finalize(
     }
     const int64_t ni = (int64_t(unit) * S + j0 + jj) * 2 * D + e;
     sum_n[ni] = a;
+    const int j = j0 + jj;
     if (e < D)
-      Ty::store(slot_k, (int64_t(unit) * S + j0 + jj) * D + e, a * s_inv_l[jj]);
-    else  // values in key tiles
-      Ty::store(slot_v, value_index(unit, S, D, j0 + jj, e - D), a * s_inv_l[jj]);
+      Ty::store(slot_k, (int64_t(unit) * S + j) * D + e, a * s_inv_l[jj]);
+    else  // values in key tiles of 32 (one tile of S keys when S % 32 != 0)
+      Ty::store(slot_v,
+                S % 32 == 0 ? ((int64_t(unit) * (S >> 5) + (j >> 5)) * D + (e - D)) * 32 + (j & 31)
+                            : (int64_t(unit) * D + (e - D)) * S + j,
+                a * s_inv_l[jj]);
   }
 
-  // ring window: slots ws = tile, tile + NT, ... ; slot ws holds the newest
-  // prefix position p with p mod W == ws, if p >= max(0, L0-W).  Keys are
-  // copied row by row; values go to the key-tiled layout.
-  for (int wsl = tile; wsl < W; wsl += NT) {
-    const int64_t newest = int64_t(L0) - 1 - ((int64_t(L0) - 1 - wsl) % W + W) % W;
-    const bool occ = newest >= 0;
-    const int64_t src = ((int64_t(c) * rows_stride + (occ ? newest : 0)) * Hkv + h) * D;
-    for (int e = tid; e < D; e += kThreads) {
-      ring_k[(int64_t(unit) * W + wsl) * D + e] = occ ? kp[src + e] : typename Ty::T(0);
-      ring_v[value_index(unit, W, D, wsl, e)] = occ ? vp[src + e] : typename Ty::T(0);
+  // ring window: window slot ws holds the newest prefix position p with
+  // p mod W == ws, if p >= max(0, L0 - W) (else it is empty: zeros, -1).
+  // This workgroup fills the 32-slot key tiles kt = tile, tile + NT, ...:
+  // every key and value piece of a tile is loaded first (several 16-byte
+  // loads in flight per thread), keys are stored as they are, values pass
+  // through LDS and leave as 16-byte pieces of the tile [d][32].
+  auto newest_of = [&](int ws) -> int {  // -1: empty slot
+    const int back = ((L0 - 1 - ws) % W + W) % W;
+    return max(L0 - 1 - back, -1);
+  };
+  if (W % 32 == 0) {
+    using T = typename Ty::T;
+    constexpr int E16 = 16 / Ty::kBytes, P16 = D / E16;  // 16-byte pieces per row
+    constexpr int NP = 32 * P16;                         // pieces per tile (in and out)
+    constexpr int NPT = (NP + kThreads - 1) / kThreads;  // pieces per thread per tile
+    constexpr int VS = D + E16;                          // LDS row stride (elements)
+    T* vls = reinterpret_cast<T*>(wsm + nsplit * SPB);   // [32][VS]
+    for (int kt = tile; kt < W / 32; kt += NT) {
+      uint4 kr[NPT], vr[NPT];
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        const int pc = min(tid + q * kThreads, NP - 1), i = pc / P16, e = pc % P16;
+        const int p = newest_of(kt * 32 + i);
+        const int64_t src = ((int64_t(c) * rows_stride + max(p, 0)) * Hkv + h) * D;
+        kr[q] = p >= 0 ? reinterpret_cast<const uint4*>(kp + src)[e] : uint4{0, 0, 0, 0};
+        vr[q] = p >= 0 ? reinterpret_cast<const uint4*>(vp + src)[e] : uint4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        const int pc = tid + q * kThreads, i = pc / P16, e = pc % P16;
+        if (pc >= NP) break;
+        reinterpret_cast<uint4*>(ring_k + (int64_t(unit) * W + kt * 32 + i) * D)[e] = kr[q];
+        reinterpret_cast<uint4*>(vls + i * VS)[e] = vr[q];
+      }
+      if (h == 0 && tid < 32) ring_pos[int64_t(c) * W + kt * 32 + tid] = newest_of(kt * 32 + tid);
+      __syncthreads();
+      // output piece (dim, kq): keys kq*E16 .. +E16-1 of one dimension
+      T* tile_v = ring_v + (int64_t(unit) * (W / 32) + kt) * D * 32;
+#pragma unroll
+      for (int q = 0; q < NPT; ++q) {
+        const int pc = tid + q * kThreads, dim = pc / (32 / E16), kq = pc % (32 / E16);
+        if (pc >= NP) break;
+        T x[E16];
+#pragma unroll
+        for (int e = 0; e < E16; ++e) x[e] = vls[(kq * E16 + e) * VS + dim];
+        reinterpret_cast<uint4*>(tile_v + dim * 32)[kq] = *reinterpret_cast<const uint4*>(x);
+      }
+      __syncthreads();
     }
-    if (h == 0 && tid == 0) ring_pos[int64_t(c) * W + wsl] = occ ? int32_t(newest) : -1;
+  } else {  // W % 32 != 0 (small f32 windows): values in one tile [d][W]
+    for (int wsl = tile; wsl < W; wsl += NT) {
+      const int p = newest_of(wsl);
+      const int64_t src = ((int64_t(c) * rows_stride + max(p, 0)) * Hkv + h) * D;
+      for (int e = tid; e < D; e += kThreads) {
+        ring_k[(int64_t(unit) * W + wsl) * D + e] = p >= 0 ? kp[src + e] : typename Ty::T(0);
+        ring_v[(int64_t(unit) * D + e) * W + wsl] = p >= 0 ? vp[src + e] : typename Ty::T(0);
+      }
+      if (h == 0 && tid == 0) ring_pos[int64_t(c) * W + wsl] = p;
+    }
   }
   if (h == 0 && tile == 0 && tid == 0) seq_len[c] = L0;
   if (blockIdx.x == 0 && tid == 0) *err_flag = 0;
@@ -382,7 +433,8 @@ ls_status finalize(const ls_dims& d, const ls_state& st, const float* part, int 
   using T = typename Ty::T;
   const int NT = int(cdiv(d.S, 16));
   const int units = d.C * d.Hkv;
-  const size_t shmem = sizeof(float) * size_t(nsplit) * 16;
+  // merge weights [nsplit][16], then the value staging tile [32][d + 16 bytes]
+  const size_t shmem = sizeof(float) * size_t(nsplit) * 16 + 32 * (D * sizeof(T) + 16);
   hipLaunchKernelGGL((init_finalize<Ty, D>), dim3(units * NT), dim3(kThreads), shmem, stream,
                      part, nsplit, units, L0, static_cast<const T*>(kp),
                      static_cast<const T*>(vp), rows_stride, d.Hkv, d.S, d.W, NT, st.sum_m,
