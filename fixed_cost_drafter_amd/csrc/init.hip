@@ -25,6 +25,10 @@ namespace ls {
 namespace {
 
 constexpr int kThreads = 256;
+__device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
+#ifndef LS_INIT_PREFETCH
+#define LS_INIT_PREFETCH 2
+#endif
 
 // partial block of (split, unit): m[S] | l[S] | n[S][2d]
 __device__ __host__ inline int64_t part_off(int split, int units, int unit, int S, int D) {
@@ -47,6 +51,9 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
   constexpr int KS2 = TR / 32; // 32-row k-steps of the PV product
   constexpr int PAIRS = TR / (8 * NW);  // row pairs staged per thread
   static_assert(PAIRS >= 1 && TR % (8 * NW) == 0, "tile rows must cover the threads");
+  // prefix tiles loading in registers per thread (deeper when a thread's
+  // share of a tile is one row pair, so the registers still fit two waves)
+  constexpr int kInitPrefetch = PAIRS == 1 ? LS_INIT_PREFETCH : 1;
   __shared__ __attribute__((aligned(16))) uint16_t KL[TR * KLS];
   __shared__ __attribute__((aligned(16))) uint16_t KVT[2 * D * VTS];
 
@@ -59,12 +66,14 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
   const int r_begin = split * rows_per_split;
   const int r_end = min(L0, r_begin + rows_per_split);
   const int t_newest = L0 - 1;
-  const float inv_sqrt_d = 0.08838834764831845f;  // 1/sqrt(128)
+  // scores in base 2 (one v_exp_f32 per weight): a2 = a * log2(e)
+  constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+  const float k2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
 
   // slot queries as the B operand of S^T = K U^T: lane (slot ln, kg) holds
   // u[slot][ks*32 + kg*8 .. +7]
   const int slot = wave * 16 + ln;
-  const float lnl = log_lambda[slot];
+  const float lnl2 = log_lambda[slot] * kLog2e;  // -inf stays -inf (lambda = 0)
   bf16x8 ub[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
@@ -80,42 +89,57 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
   // global -> register staging: thread (dg = tid%16, rp = tid/16) loads row
   // pairs rp + k*(NT/16); 16 lanes cover one 256-byte row segment
   const int dg = tid & 15, rp = tid >> 4;
-  u16x8 kr[2 * PAIRS], vr[2 * PAIRS];
-  auto load_tile = [&](int t0) __attribute__((always_inline)) {
+  // kInitPrefetch tiles are loading into registers while one is computed
+  u16x8 kr[kInitPrefetch][2 * PAIRS], vr[kInitPrefetch][2 * PAIRS];
+  auto load_tile = [&](int t0, u16x8 (&kd)[2 * PAIRS], u16x8 (&vd)[2 * PAIRS])
+                       __attribute__((always_inline)) {
     const int nrows = min(TR, r_end - t0);
 #pragma unroll
     for (int i = 0; i < 2 * PAIRS; ++i) {
       const int row = 2 * (rp + (i >> 1) * (NT / 16)) + (i & 1);
       if (row < nrows) {
         const int64_t off = ((int64_t(c) * rows_stride + t0 + row) * Hkv + h) * D + dg * 8;
-        kr[i] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(kp + off));
-        vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(vp + off));
+        kd[i] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(kp + off));
+        vd[i] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(vp + off));
       } else {
-        kr[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        vr[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        kd[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        vd[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
       }
     }
   };
 
-  if (r_begin < r_end) load_tile(r_begin);
-  for (int t0 = r_begin; t0 < r_end; t0 += TR) {
+#pragma unroll
+  for (int u = 0; u < kInitPrefetch; ++u)
+    if (r_begin + u * TR < r_end) load_tile(r_begin + u * TR, kr[u], vr[u]);
+  for (int tb = r_begin; tb < r_end; tb += kInitPrefetch * TR) {
+#pragma unroll
+  for (int u = 0; u < kInitPrefetch; ++u) {  // tile t0 uses registers kr[u], vr[u]
+    const int t0 = tb + u * TR;
+    if (t0 >= r_end) break;
     const int nrows = min(TR, r_end - t0);
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int pp = 0; pp < PAIRS; ++pp) {
       const int row0 = 2 * (rp + pp * (NT / 16));  // even row of the pair
-      *reinterpret_cast<u16x8*>(&KL[row0 * KLS + dg * 8]) = kr[2 * pp];
-      *reinterpret_cast<u16x8*>(&KL[(row0 + 1) * KLS + dg * 8]) = kr[2 * pp + 1];
+      *reinterpret_cast<u16x8*>(&KL[row0 * KLS + dg * 8]) = kr[u][2 * pp];
+      *reinterpret_cast<u16x8*>(&KL[(row0 + 1) * KLS + dg * 8]) = kr[u][2 * pp + 1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t kk = uint32_t(kr[2 * pp][e]) | (uint32_t(kr[2 * pp + 1][e]) << 16);
-        const uint32_t vv = uint32_t(vr[2 * pp][e]) | (uint32_t(vr[2 * pp + 1][e]) << 16);
+        // (row0, row0 + 1) of one dimension as one dword: v_perm of the two rows
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        const uint4 k0 = __builtin_bit_cast(uint4, kr[u][2 * pp]), k1 = __builtin_bit_cast(uint4, kr[u][2 * pp + 1]);
+        const uint4 v0 = __builtin_bit_cast(uint4, vr[u][2 * pp]), v1 = __builtin_bit_cast(uint4, vr[u][2 * pp + 1]);
+        const uint32_t k0w[4] = {k0.x, k0.y, k0.z, k0.w}, k1w[4] = {k1.x, k1.y, k1.z, k1.w};
+        const uint32_t v0w[4] = {v0.x, v0.y, v0.z, v0.w}, v1w[4] = {v1.x, v1.y, v1.z, v1.w};
+        const uint32_t kk = __builtin_amdgcn_perm(k1w[e >> 1], k0w[e >> 1], sel);
+        const uint32_t vv = __builtin_amdgcn_perm(v1w[e >> 1], v0w[e >> 1], sel);
         *reinterpret_cast<uint32_t*>(&KVT[(dg * 8 + e) * VTS + row0]) = kk;
         *reinterpret_cast<uint32_t*>(&KVT[(D + dg * 8 + e) * VTS + row0]) = vv;
       }
     }
     __syncthreads();
-    if (t0 + TR < r_end) load_tile(t0 + TR);  // next tile in flight during compute
+    if (t0 + kInitPrefetch * TR < r_end)  // refill: that tile loads during the next computes
+      load_tile(t0 + kInitPrefetch * TR, kr[u], vr[u]);
 
     // S^T[row][slot]: lane (slot ln, kg) holds rows mb*16 + kg*4 + r
     f32x4 s[MB];
@@ -131,48 +155,77 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
       }
     }
 
-    // online softmax per slot over this tile
+    // online softmax per slot over this tile (base 2).  Row r of the tile
+    // sits at distance t_newest - t0 - r >= 1 from the newest row except in
+    // the tile holding the newest row or the ragged tail, which take the
+    // exact per-row path (distance 0 has no bias; rows past the end are out).
     float tmax = -INFINITY;
+    if (t0 + TR <= t_newest && nrows == TR) {
+      const float dk = float(t_newest - t0 - kg * 4);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = mb * 16 + kg * 4 + r;
-        const int dist = t_newest - (t0 + row);
-        const float bias = dist == 0 ? 0.f : float(dist) * lnl;
-        float a = fmaf(s[mb][r], inv_sqrt_d, bias);
-        if (row >= nrows) a = -INFINITY;
-        s[mb][r] = a;
-        tmax = fmaxf(tmax, a);
-      }
+        for (int r = 0; r < 4; ++r) {
+          const float bias = (dk - float(mb * 16 + r)) * lnl2;
+          const float a = fmaf(s[mb][r], k2, bias);
+          s[mb][r] = a;
+          tmax = fmaxf(tmax, a);
+        }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = mb * 16 + kg * 4 + r;
+          const int dist = t_newest - (t0 + row);
+          const float bias = dist == 0 ? 0.f : float(dist) * lnl2;
+          float a = fmaf(s[mb][r], k2, bias);
+          if (row >= nrows) a = -INFINITY;
+          s[mb][r] = a;
+          tmax = fmaxf(tmax, a);
+        }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // the slot's max over the 4 lane groups (rows): swapping a register with
+    // itself across row pairs / halves leaves the partner's value in one result
+    {
+      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+      tmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+    }
     // lazy rescale: the reference max moves only when some slot's max grows
     // by more than 8 e-folds (weights stay <= e^8), so the 64-register
     // accumulator rescale is skipped in the steady state
     m_true = fmaxf(m_true, tmax);
-    if (__any(tmax > m_run + 8.f)) {
+    if (__any(tmax > m_run + 8.f * kLog2e)) {
       const float m_new = fmaxf(m_run, tmax);
-      const float scale = m_run == -INFINITY ? 0.f : exp_f(m_run - m_new);
+      const float scale = m_run == -INFINITY ? 0.f : exp2_f(m_run - m_new);
       m_run = m_new;
       l_run *= scale;
 #pragma unroll
       for (int mb = 0; mb < 16; ++mb) acc[mb] *= scale;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    // weights rounded to bf16 in pairs; l sums the same rounded weights
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
+    uint32_t pw[MB * 2];
     float lsum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2) {
+        const f32x2 e2 = {exp2_f(s[mb][r] - m_use), exp2_f(s[mb][r + 1] - m_use)};
+        const bf16x2 b2 = __builtin_convertvector(e2, bf16x2);
+        pw[mb * 2 + r / 2] = __builtin_bit_cast(uint32_t, b2);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(b2, ones, lsum, false);
+      }
+    l_run += lsum;
     u16x8 pv[KS2];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint16_t pb = f32_to_bf16(exp_f(s[mb][r] - m_use));
-        lsum += bf16_to_f32(pb);
-        pv[mb >> 1][(mb & 1) * 4 + r] = pb;
-      }
-    }
-    l_run += lsum;
+    for (int ks = 0; ks < KS2; ++ks)  // rows of 16-row blocks 2ks and 2ks+1
+      pv[ks] = __builtin_bit_cast(u16x8, uint4{pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]});
 
     // n^T[dim][slot] += [K|V]^T[dim][row] P^T[row][slot]; the k order of the
     // A operand (rows 32ks+4kg..+3, 32ks+16+4kg..+3) matches pv's element order
@@ -189,10 +242,11 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
       }
     }
   }
+  }
 
   // the state's m is the exact max: move the reference there once
   if (m_true > m_run) {
-    const float scale = exp_f(m_run - m_true);
+    const float scale = exp2_f(m_run - m_true);
     m_run = m_true;
     l_run *= scale;
 #pragma unroll
@@ -205,7 +259,7 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
   lt += __shfl_xor(lt, 16, 64);
   lt += __shfl_xor(lt, 32, 64);
   if (kg == 0) {
-    pb[slot] = m_run;
+    pb[slot] = m_run * kLn2;  // natural units, as the state keeps m
     pb[S + slot] = lt;
   }
   float* nrow = pb + 2 * S + int64_t(slot) * 2 * D;
