@@ -38,6 +38,9 @@ Parity status of each function (what pins it is in tests/test_oracle.py):
   summary_reference, summary_init, append_accepted, full_recompute,
   verify_greedy, draft_attention: pinned (closed forms, brute force, SDPA
   special cases, worked examples under tests/golden/).
+  draft_argmax, boundary_row, verify_attention, and the S = 0 / W = 0 views:
+  pinned in tests/test_oracle_next.py (brute force, SDPA with an explicit
+  mask, worked examples).
   Parity with the pages' own LongSpark numbers: unpinned -- the pages print
   no formula and no per-step output for this path.
 """
@@ -57,6 +60,9 @@ __all__ = [
     "append_accepted",
     "full_recompute",
     "draft_attention",
+    "draft_argmax",
+    "boundary_row",
+    "verify_attention",
 ]
 
 
@@ -263,7 +269,7 @@ def append_accepted(state: OracleState, k_new, v_new, tau, heads=None) -> Oracle
     for c in range(C):
         T = int(tau[c])
         L = int(state.seq_len[c])
-        for i in range(T):
+        for i in range(T if W > 0 else 0):         # W = 0: no window view
             state.ring_k[c, :, (L + i) % W, :] = k_new[c, i, :, :]
             state.ring_v[c, :, (L + i) % W, :] = v_new[c, i, :, :]
             state.ring_pos[c, (L + i) % W] = L + i
@@ -308,6 +314,79 @@ def draft_attention(state: OracleState, q, k_blk, v_blk, pairs=None):
         keys = np.concatenate([decode(state.ring_k[c, h][valid]), slot_k[c, h], kb[c, :, h, :]])
         vals = np.concatenate([decode(state.ring_v[c, h][valid]), slot_v[c, h], vb[c, :, h, :]])
         s = qq[c, :, hq, :] @ keys.T / np.sqrt(d)  # [B, nkeys]
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p /= p.sum(axis=1, keepdims=True)
+        out[c, :, hq, :] = p @ vals
+    return out
+
+
+# --------------------------------------------------------------------------
+# drafter proposal at T = 0 (Fig. 1 caption: drafting time counts the
+# proposal and sampling of the drafted tokens; Table 3: greedy decoding)
+# --------------------------------------------------------------------------
+def draft_argmax(logits):
+    """Greedy proposal of the drafted block.
+
+    logits [C, B, V]: the drafter's scores at the B block positions.  Returns
+    int32 [C, B]: the argmax over V of each row, lowest index on ties (+0 and
+    -0 compare equal, as the decoded float64 values do).
+    """
+    x = decode(logits)
+    return np.argmax(x, axis=-1).astype(np.int32)   # first occurrence of the max
+
+
+# --------------------------------------------------------------------------
+# boundary state view (Fig. 2 (b))
+# --------------------------------------------------------------------------
+def boundary_row(hidden, tau):
+    """The target state at the accepted boundary.
+
+    hidden [C, B+1, H]: the target's states at the B+1 verified positions.
+    After verification tau[c] of them are committed; the boundary is the
+    newest committed position, row tau[c] - 1 of the block.  Returns the raw
+    rows [C, H] (a copy: same dtype, same bits).
+    """
+    hidden = np.asarray(hidden)
+    tau = np.asarray(tau).astype(np.int64)
+    C, B1 = hidden.shape[:2]
+    if np.any(tau < 1) or np.any(tau > B1):
+        raise ValueError("tau must lie in [1, B+1]")
+    out = np.empty((C,) + hidden.shape[2:], dtype=hidden.dtype)
+    for c in range(C):
+        out[c] = hidden[c, tau[c] - 1]
+    return out
+
+
+# --------------------------------------------------------------------------
+# target-side verification attention (Fig. 2 (a)): the prefix-dependent cost
+# the drafter avoids
+# --------------------------------------------------------------------------
+def verify_attention(k_cache, v_cache, q, L, pairs=None):
+    """Causal GQA attention of the B+1 verified positions over the whole context.
+
+    k_cache, v_cache [C, R, Hkv, d]: the target's KV rows of one layer; rows
+    0..L[c]-1 are the context before the block and rows L[c]..L[c]+B hold the
+    B+1 verified positions.  q [C, B+1, Hq, d]: their queries.  Query i (at
+    position L[c] + i) attends to rows 0..L[c]+i; query head hq reads KV head
+    hq // (Hq / Hkv); scale 1/sqrt(d).  Returns float64 [C, B+1, Hq, d].
+    ``pairs`` restricts the work to (c, hq) pairs (others NaN).
+    """
+    C, B1, Hq, d = q.shape
+    Hkv = k_cache.shape[2]
+    G = Hq // Hkv
+    L = np.asarray(L).astype(np.int64)
+    qq = decode(q)
+    out = np.full((C, B1, Hq, d), np.nan)
+    todo = pairs if pairs is not None else [(c, hq) for c in range(C) for hq in range(Hq)]
+    for c, hq in todo:
+        h = hq // G
+        n = int(L[c]) + B1
+        keys = decode(k_cache[c, :n, h, :])          # [n, d]
+        vals = decode(v_cache[c, :n, h, :])
+        s = qq[c, :, hq, :] @ keys.T / np.sqrt(d)    # [B+1, n]
+        visible = np.arange(n)[None, :] <= (int(L[c]) + np.arange(B1))[:, None]
+        s = np.where(visible, s, -np.inf)
         s = s - s.max(axis=1, keepdims=True)
         p = np.exp(s)
         p /= p.sum(axis=1, keepdims=True)
