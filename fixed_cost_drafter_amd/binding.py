@@ -24,7 +24,8 @@ LS_F32, LS_BF16 = 0, 1
 STATUS = {0: "LS_OK", 1: "LS_ERR_NULL", 2: "LS_ERR_SHAPE", 3: "LS_ERR_DTYPE",
           4: "LS_ERR_WORKSPACE", 5: "LS_ERR_ALIGN", 6: "LS_ERR_HIP"}
 EXPORTS = ("ls_workspace_bytes", "ls_summary_init", "ls_verify_greedy", "ls_append_accepted",
-           "ls_draft_attention", "ls_status_string", "ls_version")
+           "ls_draft_attention", "ls_draft_argmax", "ls_gather_boundary", "ls_status_string",
+           "ls_version")
 
 
 class LsDims(ctypes.Structure):
@@ -61,7 +62,10 @@ def _load() -> ctypes.CDLL:
     lib.ls_verify_greedy.argtypes = [D, P, P, P, P, P, SZ, P]
     lib.ls_append_accepted.argtypes = [D, S, P, P, P, P]
     lib.ls_draft_attention.argtypes = [D, S, P, P, P, P, P]
-    for f in ("ls_summary_init", "ls_verify_greedy", "ls_append_accepted", "ls_draft_attention"):
+    lib.ls_draft_argmax.argtypes = [D, P, P, P, SZ, P]
+    lib.ls_gather_boundary.argtypes = [D, P, I32, P, P, P, P]
+    for f in ("ls_summary_init", "ls_verify_greedy", "ls_append_accepted", "ls_draft_attention",
+              "ls_draft_argmax", "ls_gather_boundary"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ls_status_string.argtypes = [ctypes.c_int]
     lib.ls_status_string.restype = ctypes.c_char_p
@@ -174,6 +178,18 @@ def ls_draft_attention(dims: LsDims, state: LsState, q, k_blk, v_blk, out, strea
         _stream(stream)))
 
 
+def ls_draft_argmax(dims: LsDims, logits, draft_tok, workspace, workspace_bytes, stream=None):
+    _check("ls_draft_argmax", _lib.ls_draft_argmax(
+        ctypes.byref(dims), _ptr(logits), _ptr(draft_tok), _ptr(workspace), int(workspace_bytes),
+        _stream(stream)))
+
+
+def ls_gather_boundary(dims: LsDims, hidden, H: int, tau, out, err_flag=None, stream=None):
+    _check("ls_gather_boundary", _lib.ls_gather_boundary(
+        ctypes.byref(dims), _ptr(hidden), int(H), _ptr(tau), _ptr(out), _ptr(err_flag),
+        _stream(stream)))
+
+
 def ls_status_string(status: int) -> str:
     return _lib.ls_status_string(int(status)).decode()
 
@@ -245,6 +261,12 @@ class DrafterState:
 
     def draft_attention(self, q, k_blk, v_blk, out, stream=None):
         ls_draft_attention(self.dims, self.c_state, q, k_blk, v_blk, out, stream)
+
+    def draft_argmax(self, logits, draft_tok, stream=None):
+        ls_draft_argmax(self.dims, logits, draft_tok, self.workspace, self.workspace.numel(), stream)
+
+    def gather_boundary(self, hidden, tau, out, stream=None):
+        ls_gather_boundary(self.dims, hidden, hidden.shape[-1], tau, out, self.err_flag, stream)
 
     def state_bytes(self) -> int:
         ts = (self.ring_k, self.ring_v, self.ring_pos, self.seq_len, self.sum_m, self.sum_l,

@@ -61,7 +61,7 @@ ls_status check_state(const ls_state* s, const ls_dims& d, int32_t L0) {
 
 extern "C" {
 
-int32_t ls_version(void) { return 100; }
+int32_t ls_version(void) { return 101; }
 
 const char* ls_status_string(ls_status status) {
   switch (status) {
@@ -105,6 +105,26 @@ ls_status ls_verify_greedy(const ls_dims* dims, const void* logits, const int32_
   if (workspace_bytes < size_t(ls::ws_layout(*dims, 1).total)) return LS_ERR_WORKSPACE;
   return ls::launch_verify(*dims, logits, draft, target_tok, tau, static_cast<char*>(workspace),
                            static_cast<hipStream_t>(stream));
+}
+
+ls_status ls_draft_argmax(const ls_dims* dims, const void* logits, int32_t* draft_tok,
+                          void* workspace, size_t workspace_bytes, ls_stream stream) {
+  ls_status st = check_dims(dims);
+  if (st != LS_OK) return st;
+  if (!logits || !draft_tok || !workspace) return LS_ERR_NULL;
+  if (!aligned16(workspace)) return LS_ERR_ALIGN;
+  if (workspace_bytes < size_t(ls::ws_layout(*dims, 1).total)) return LS_ERR_WORKSPACE;
+  return ls::launch_argmax(*dims, logits, draft_tok, static_cast<char*>(workspace),
+                           static_cast<hipStream_t>(stream));
+}
+
+ls_status ls_gather_boundary(const ls_dims* dims, const void* hidden, int32_t H,
+                             const int32_t* tau, void* out, int32_t* err_flag, ls_stream stream) {
+  ls_status st = check_dims(dims);
+  if (st != LS_OK) return st;
+  if (!hidden || !tau || !out) return LS_ERR_NULL;
+  if (H < 1) return LS_ERR_SHAPE;
+  return ls::launch_boundary(*dims, hidden, H, tau, out, err_flag, static_cast<hipStream_t>(stream));
 }
 
 ls_status ls_append_accepted(const ls_dims* dims, const ls_state* state, const void* k_new,

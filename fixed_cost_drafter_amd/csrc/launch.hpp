@@ -12,6 +12,14 @@ namespace ls {
 ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* draft,
                         int32_t* target_tok, int32_t* tau, char* ws, hipStream_t stream);
 
+// drafter proposal at T = 0: argmax over V of each of the C*B rows
+ls_status launch_argmax(const ls_dims& d, const void* logits, int32_t* draft_tok, char* ws,
+                        hipStream_t stream);
+
+// boundary state: row tau[c]-1 of each sequence's [B+1, H] states
+ls_status launch_boundary(const ls_dims& d, const void* hidden, int32_t H, const int32_t* tau,
+                          void* out, int32_t* err_flag, hipStream_t stream);
+
 ls_status launch_append(const ls_dims& d, const ls_state& st, const void* k_new,
                         const void* v_new, const int32_t* tau, hipStream_t stream);
 

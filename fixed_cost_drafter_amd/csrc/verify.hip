@@ -13,6 +13,10 @@
 // and tau.  The kernel boundary orders (1) before (2): no device-scope fence
 // is needed, which on a multi-XCD GPU would write back and invalidate L2.
 // The logits are streamed once (HBM-bound: 2 bytes per bf16 logit).
+//
+// The drafter's own proposal at T = 0 (Fig. 1 caption: drafting time counts
+// the proposal and sampling of the drafted tokens) is the same reduction over
+// its C*B rows of logits, finished by one thread per row (argmax_finalize).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -144,25 +148,55 @@ __global__ __launch_bounds__(kThreads) void verify_finalize(
   }
 }
 
+// one thread per row: the row's split keys -> its argmax token
+__global__ __launch_bounds__(kThreads) void argmax_finalize(const uint64_t* __restrict__ part,
+                                                            int32_t* __restrict__ tok, int rows,
+                                                            int nsplit) {
+  const int row = blockIdx.x * kThreads + threadIdx.x;
+  if (row >= rows) return;
+  const uint64_t* p = part + int64_t(row) * nsplit;
+  uint64_t k = 0;
+  for (int s = 0; s < nsplit; ++s) k = p[s] > k ? p[s] : k;
+  tok[row] = int32_t(~uint32_t(k));
+}
+
+template <typename Ty>
+ls_status launch_partials(const ls_dims& d, const void* logits, int rows, uint64_t* part,
+                          int nsplit, hipStream_t stream) {
+  const int esz = Ty::kBytes;
+  // 16-byte loads need every row start (and chunk start) 16-byte aligned
+  const int vec_ok = ((int64_t(d.V) * esz) % 16 == 0) && ((uintptr_t(logits) & 15) == 0);
+  hipLaunchKernelGGL(verify_partial<Ty>, dim3(nsplit, rows), dim3(kThreads), 0, stream,
+                     static_cast<const typename Ty::T*>(logits), part, d.V, nsplit, kVerifyChunk,
+                     vec_ok);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+}
+
 }  // namespace
+
+ls_status launch_argmax(const ls_dims& d, const void* logits, int32_t* draft_tok, char* ws,
+                        hipStream_t stream) {
+  const WsLayout lay = ws_layout(d, 1);
+  const int nsplit = lay.vsplit;
+  const int rows = d.C * d.B;  // the verify key area holds C*(B+1) rows
+  uint64_t* part = reinterpret_cast<uint64_t*>(ws + lay.verify_part);
+  const ls_status st = d.dtype == LS_BF16 ? launch_partials<BF16>(d, logits, rows, part, nsplit, stream)
+                                          : launch_partials<F32>(d, logits, rows, part, nsplit, stream);
+  if (st != LS_OK) return st;
+  hipLaunchKernelGGL(argmax_finalize, dim3(unsigned(cdiv(rows, kThreads))), dim3(kThreads), 0, stream,
+                     part, draft_tok, rows, nsplit);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+}
 
 ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* draft,
                         int32_t* target_tok, int32_t* tau, char* ws, hipStream_t stream) {
   const WsLayout lay = ws_layout(d, 1);
   const int nsplit = lay.vsplit;
-  const int chunk = kVerifyChunk;
-  const int esz = d.dtype == LS_BF16 ? 2 : 4;
-  // 16-byte loads need every row start (and chunk start) 16-byte aligned
-  const int vec_ok = ((int64_t(d.V) * esz) % 16 == 0) && ((uintptr_t(logits) & 15) == 0);
-  dim3 grid(nsplit, d.C * (d.B + 1));
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + lay.verify_part);
-  if (d.dtype == LS_BF16)
-    hipLaunchKernelGGL(verify_partial<BF16>, grid, dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(logits), part, d.V, nsplit, chunk, vec_ok);
-  else
-    hipLaunchKernelGGL(verify_partial<F32>, grid, dim3(kThreads), 0, stream,
-                       static_cast<const float*>(logits), part, d.V, nsplit, chunk, vec_ok);
-  if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
+  const int rows = d.C * (d.B + 1);
+  const ls_status st = d.dtype == LS_BF16 ? launch_partials<BF16>(d, logits, rows, part, nsplit, stream)
+                                          : launch_partials<F32>(d, logits, rows, part, nsplit, stream);
+  if (st != LS_OK) return st;
   const size_t shmem = sizeof(uint64_t) * size_t(d.B + 1) * nsplit;
   hipLaunchKernelGGL(verify_finalize, dim3(d.C), dim3(kThreads), shmem, stream, part, draft,
                      target_tok, tau, d.B, nsplit);

@@ -154,6 +154,30 @@ ls_status ls_append_accepted(const ls_dims* dims, const ls_state* state, const v
 ls_status ls_draft_attention(const ls_dims* dims, const ls_state* state, const void* q,
                              const void* k_blk, const void* v_blk, void* out, ls_stream stream);
 
+/* Drafter proposal at T = 0 (Fig. 1 caption: drafting time counts the
+ * proposal and sampling of the drafted tokens; Table 3: greedy decoding).
+ *   logits:    [C, B, V] dtype, the drafter's scores at the B block
+ *              positions; no NaN.
+ *   draft_tok: [C, B] int32 out, argmax over V of each row, lowest index on
+ *              ties (+0 and -0 compare equal).
+ *   workspace: as sized by ls_workspace_bytes (any max_L0).
+ * The same chunked reduction as ls_verify_greedy, over the C*B rows. */
+ls_status ls_draft_argmax(const ls_dims* dims, const void* logits, int32_t* draft_tok,
+                          void* workspace, size_t workspace_bytes, ls_stream stream);
+
+/* Boundary state view (Fig. 2 (b): a state taken from the target at the
+ * accepted boundary): the newest committed position of each sequence.
+ *   hidden:   [C, B+1, H] dtype, the target's states at the B+1 verified
+ *             positions (caller's buffer, read only).
+ *   H:        state width in elements, H >= 1.
+ *   tau:      [C] int32 in DEVICE memory (e.g. from ls_verify_greedy); a
+ *             value outside [1, B+1] is clamped and, if err_flag is not NULL,
+ *             sets bit 0 of *err_flag.
+ *   out:      [C, H] dtype out: row tau[c]-1 of sequence c, bit for bit.
+ *   err_flag: int32 in device memory, or NULL. */
+ls_status ls_gather_boundary(const ls_dims* dims, const void* hidden, int32_t H,
+                             const int32_t* tau, void* out, int32_t* err_flag, ls_stream stream);
+
 /* Static description of a status code. */
 const char* ls_status_string(ls_status status);
 

@@ -67,7 +67,7 @@ def test_header_compiles_as_plain_c(tmp_path):
 
 
 def test_version_and_status_strings(LB):
-    assert LB.ls_version() == 100
+    assert LB.ls_version() == 101
     assert LB.ls_status_string(0) == "ok"
     for s in range(1, 7):
         assert LB.ls_status_string(s) and LB.ls_status_string(s) != "unknown status"
@@ -163,3 +163,21 @@ def test_shape_workspace_and_alignment_errors(LB):
     assert L.ls_draft_attention(ctypes.byref(d), ctypes.byref(st), 16, 16, 16, 24, None) == 5
     # verify: workspace too small
     assert L.ls_verify_greedy(ctypes.byref(d), 16, 16, 16, 16, 256, 8, None) == 4
+
+
+@no_device
+def test_argmax_and_boundary_validation(LB):
+    d = _dims(LB)
+    L = LB.lib()
+    # the drafter argmax: null pointers, workspace too small, misaligned workspace
+    assert L.ls_draft_argmax(ctypes.byref(d), None, 16, 256, 1 << 30, None) == 1
+    assert L.ls_draft_argmax(ctypes.byref(d), 16, None, 256, 1 << 30, None) == 1
+    assert L.ls_draft_argmax(ctypes.byref(d), 16, 16, 256, 8, None) == 4
+    assert L.ls_draft_argmax(ctypes.byref(d), 16, 16, 264, 1 << 30, None) == 5
+    bad = LB.make_dims(1, 2, 1, 16, 16, 4, 4, 0, "f32")  # V = 0
+    assert L.ls_draft_argmax(ctypes.byref(bad), 16, 16, 256, 1 << 30, None) == 2
+    # the boundary gather: null pointers, H < 1
+    assert L.ls_gather_boundary(ctypes.byref(d), None, 8, 16, 16, None, None) == 1
+    assert L.ls_gather_boundary(ctypes.byref(d), 16, 8, None, 16, None, None) == 1
+    assert L.ls_gather_boundary(ctypes.byref(d), 16, 8, 16, None, None, None) == 1
+    assert L.ls_gather_boundary(ctypes.byref(d), 16, 0, 16, 16, None, None) == 2

@@ -49,10 +49,10 @@ SMALL = {
     "bf16_b40": WLM.Workload(
         "bf16_b40", "bf16", C=2, Hq=8, Hkv=8, d=128, L0=500, W=96, S=64, B=40, V=3000,
         rounds=6, p_match=0.9, seed=16),
-    # bf16, keys split over two workgroups per KV head + combine (W = 512),
-    # 64 query rows per KV head, prefix shorter than the window
+    # bf16, keys split over two workgroups per KV head + combine (W = 512,
+    # 32 query rows per KV head), prefix shorter than the window
     "bf16_halves": WLM.Workload(
-        "bf16_halves", "bf16", C=2, Hq=8, Hkv=2, d=128, L0=300, W=512, S=64, B=16, V=2000,
+        "bf16_halves", "bf16", C=2, Hq=8, Hkv=2, d=128, L0=300, W=512, S=64, B=8, V=2000,
         rounds=5, p_match=0.8, seed=17),
     # bf16, ring wraps inside the round loop, G=1, B=16 at C=5
     "bf16_wrap": WLM.Workload(
