@@ -21,11 +21,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 ls_status check_dims(const ls_dims* d) {
   if (d == nullptr) return LS_ERR_NULL;
   if (d->dtype != LS_F32 && d->dtype != LS_BF16) return LS_ERR_DTYPE;
-  if (d->C < 1 || d->Hq < 1 || d->Hkv < 1 || d->d < 1 || d->W < 1 || d->S < 1 || d->B < 1 ||
+  // W = 0 (no window view) and S = 0 (no summary view) are allowed: the
+  // ablations of one view (Table 5) on the cost side
+  if (d->C < 1 || d->Hq < 1 || d->Hkv < 1 || d->d < 1 || d->W < 0 || d->S < 0 || d->B < 1 ||
       d->V < 1)
     return LS_ERR_SHAPE;
   if (d->Hq % d->Hkv != 0) return LS_ERR_SHAPE;
-  if (d->B > kMaxB || d->B + 1 > d->W) return LS_ERR_SHAPE;
+  if (d->B > kMaxB || (d->W > 0 && d->B + 1 > d->W)) return LS_ERR_SHAPE;
   if (int64_t(d->C) * (d->B + 1) > 65535) return LS_ERR_SHAPE;
   if (d->V > (1 << 20)) return LS_ERR_SHAPE;  // verify keeps (B+1) x V/16384 keys in LDS
   if (int64_t(d->C) * d->Hkv * d->S > (int64_t(1) << 30)) return LS_ERR_SHAPE;
@@ -35,7 +37,7 @@ ls_status check_dims(const ls_dims* d) {
     if (d->S > 256) return LS_ERR_SHAPE;
   } else {
     if (d->d != 128) return LS_ERR_SHAPE;
-    if (d->S != 64 && d->S != 128) return LS_ERR_SHAPE;
+    if (d->S != 0 && d->S != 64 && d->S != 128) return LS_ERR_SHAPE;
     if (d->W % 32 != 0) return LS_ERR_SHAPE;  // 32-key chunks never straddle window | slots
     if (d->B * G > 64) return LS_ERR_SHAPE;
   }
@@ -44,9 +46,11 @@ ls_status check_dims(const ls_dims* d) {
 
 ls_status check_state(const ls_state* s, const ls_dims& d, int32_t L0) {
   if (s == nullptr) return LS_ERR_NULL;
-  if (!s->ring_k || !s->ring_v || !s->ring_pos || !s->seq_len || !s->sum_m || !s->sum_l ||
-      !s->sum_n || !s->slot_k || !s->slot_v || !s->u || !s->log_lambda || !s->err_flag ||
-      !s->workspace)
+  if (!s->seq_len || !s->err_flag || !s->workspace) return LS_ERR_NULL;
+  // the window arrays may be NULL when W = 0, the summary arrays when S = 0
+  if (d.W > 0 && (!s->ring_k || !s->ring_v || !s->ring_pos)) return LS_ERR_NULL;
+  if (d.S > 0 && (!s->sum_m || !s->sum_l || !s->sum_n || !s->slot_k || !s->slot_v || !s->u ||
+                  !s->log_lambda))
     return LS_ERR_NULL;
   if (!aligned16(s->ring_k) || !aligned16(s->ring_v) || !aligned16(s->sum_n) ||
       !aligned16(s->ring_pos) ||

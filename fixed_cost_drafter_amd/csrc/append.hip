@@ -213,6 +213,10 @@ __device__ __forceinline__ void append_window(
     Tn = Tn < 1 ? 1 : B1;
   }
   const int L = seq_len[c];
+  if (W == 0) {  // no window view: only the count advances
+    if (tid == 0) seq_len[c] = L + Tn;
+    return;
+  }
   const int slot0 = L % W;                  // window slot of row 0; row i -> slot0 + i (mod W)
   const bool tiled = value_tile(W) == 32;   // values in 32-key tiles (else one tile of W keys)
   // a group of HG heads at a time: stage the group's tau rows [head][row][k | v]

@@ -101,8 +101,8 @@ __device__ __forceinline__ void load_piece(Piece<PPT>& x, const Views& s, int ch
       x.d[j] = *reinterpret_cast<const u16x8*>(kt + (t + TPP * j) * 8);
       x.d[PPT + j] = *reinterpret_cast<const u16x8*>(vt + (t + TPP * j) * 8);
     }
-    const int p = s.rp[(ring ? key0 : 0) + (t & 31)];
-    x.bias = (ring && p < 0) ? -INFINITY : 0.f;
+    const int p = ring ? s.rp[key0 + (t & 31)] : 0;  // slots are always occupied
+    x.bias = p < 0 ? -INFINITY : 0.f;
   } else {  // block: K and V rows are the caller's token-major [b][Hkv][d]
     const int key0 = (ch - s.ngl) * 32;
 #pragma unroll

@@ -18,6 +18,8 @@
 // inputs).  The f32 kernel is a plain LDS-tiled loop for small shapes.
 // Phase 2 (init_finalize): merges the partials (associative max-rescale),
 // writes the state and the slots, fills the ring, sets seq_len and err_flag.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -485,7 +487,9 @@ ls_status finalize(const ls_dims& d, const ls_state& st, const float* part, int 
                    const void* kp, const void* vp, int L0, int64_t rows_stride,
                    hipStream_t stream) {
   using T = typename Ty::T;
-  const int NT = int(cdiv(d.S, 16));
+  // S/16 tiles of slots per unit; at least one workgroup per unit fills the
+  // window, seq_len and err_flag when there is no summary (S = 0)
+  const int NT = std::max(1, int(cdiv(d.S, 16)));
   const int units = d.C * d.Hkv;
   // merge weights [nsplit][16], then the value staging tile [32][d + 16 bytes]
   const size_t shmem = sizeof(float) * size_t(nsplit) * 16 + 32 * (D * sizeof(T) + 16);
@@ -502,6 +506,7 @@ template <int D>
 ls_status run_f32(const ls_dims& d, const ls_state& st, const void* kp, const void* vp, int L0,
                   int64_t rows_stride, float* part, int rows, int nsplit, hipStream_t stream) {
   const size_t shmem = sizeof(float) * (16 * (2 * D + 1) + size_t(d.S) * 16 + 3 * size_t(d.S));
+  if (d.S == 0) return finalize<F32, D>(d, st, part, nsplit, kp, vp, L0, rows_stride, stream);
   hipLaunchKernelGGL((init_generic_partial<F32, D>), dim3(d.C * d.Hkv * nsplit), dim3(kThreads),
                      shmem, stream, static_cast<const float*>(kp), static_cast<const float*>(vp),
                      rows_stride, L0, rows, nsplit, static_cast<const float*>(st.u),
@@ -526,9 +531,10 @@ ls_status launch_init(const ls_dims& d, const ls_state& st, const void* kp, cons
     if (d.S == 128)
       hipLaunchKernelGGL((init_mfma_partial<8, 64>), grid, dim3(512), 0, stream, k16, v16,
                          rows_stride, L0, rows, nsplit, u16, st.log_lambda, d.Hkv, part);
-    else
+    else if (d.S == 64)
       hipLaunchKernelGGL((init_mfma_partial<4, 64>), grid, dim3(256), 0, stream, k16, v16,
                          rows_stride, L0, rows, nsplit, u16, st.log_lambda, d.Hkv, part);
+    // S = 0: no summary to pool; the finalize fills the window only
     if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
     return finalize<BF16, 128>(d, st, part, nsplit, kp, vp, L0, rows_stride, stream);
   }

@@ -31,10 +31,15 @@
  *   - Calls that share one workspace or one state must not overlap (same
  *     stream, or ordered with events).
  *
- * Supported shapes: Hq % Hkv == 0; 1 <= B <= 47, B+1 <= W; 1 <= V <= 2^20;
- *   C*(B+1) <= 65535; S >= 1.
+ * Supported shapes: Hq % Hkv == 0; 1 <= B <= 47; 1 <= V <= 2^20;
+ *   C*(B+1) <= 65535; W >= 0 with B+1 <= W when W > 0; S >= 0.
  *   LS_F32 : d in {16, 32, 64, 128}, S <= 256, B*Hq/Hkv <= 64.
- *   LS_BF16: d == 128, S in {64, 128}, W % 32 == 0, B*Hq/Hkv <= 64.
+ *   LS_BF16: d == 128, S in {0, 64, 128}, W % 32 == 0, B*Hq/Hkv <= 64.
+ * W = 0 switches the window view off and S = 0 the summary view (the view
+ * ablations of Table 5, cost side): the drafter then attends to the other
+ * views and the block, and the switched-off view's state arrays may be NULL
+ * (ring_k, ring_v, ring_pos when W = 0; sum_m, sum_l, sum_n, slot_k, slot_v,
+ * u, log_lambda when S = 0).
  * Pointers to dtype arrays, ring_pos and sum_n must be 16-byte aligned.
  * The values of the window and of the slots are kept in key tiles of 32
  * (per tile: [d][32]) so that the drafter's P.V product reads contiguous

@@ -100,12 +100,12 @@ def test_workspace_bytes(LB):
 @no_device
 @pytest.mark.parametrize("bad,status", [
     (dict(dtype=7), 3),
-    (dict(C=0), 2), (dict(Hq=0), 2), (dict(V=0), 2), (dict(S=0), 2),
+    (dict(C=0), 2), (dict(Hq=0), 2), (dict(V=0), 2), (dict(S=-1), 2), (dict(W=-32), 2),
     (dict(Hq=30), 2),                 # Hq % Hkv != 0
     (dict(B=48), 2),                  # B > 47
     (dict(W=16, B=16), 2),            # B+1 > W
     (dict(d=64), 2),                  # bf16 needs d = 128
-    (dict(S=96), 2),                  # bf16 needs S in {64, 128}
+    (dict(S=96), 2),                  # bf16 needs S in {0, 64, 128}
     (dict(W=1000), 2),                # bf16 needs W % 32 == 0
     (dict(Hq=64, Hkv=8, B=16), 2),    # B*G = 128 > 64
     (dict(dtype="f32", d=48), 2),     # f32 d not supported
@@ -181,3 +181,21 @@ def test_argmax_and_boundary_validation(LB):
     assert L.ls_gather_boundary(ctypes.byref(d), 16, 8, None, 16, None, None) == 1
     assert L.ls_gather_boundary(ctypes.byref(d), 16, 8, 16, None, None, None) == 1
     assert L.ls_gather_boundary(ctypes.byref(d), 16, 0, 16, 16, None, None) == 2
+
+
+@no_device
+def test_view_ablations_accept_null_view_arrays(LB):
+    """W = 0 / S = 0: the switched-off view's arrays may be NULL; the others may not."""
+    L = LB.lib()
+    d = _dims(LB, W=0)
+    need = LB.ls_workspace_bytes(d, 1)
+    p = [0x10000 * (i + 1) for i in range(13)]
+    st = LB.LsState(*p, need)
+    st.ring_k = st.ring_v = st.ring_pos = None
+    st.u = None            # a summary array: still required with S > 0
+    assert L.ls_append_accepted(ctypes.byref(d), ctypes.byref(st), 16, 16, 16, None) == 1
+    d2 = _dims(LB, S=0)
+    st2 = LB.LsState(*p, LB.ls_workspace_bytes(d2, 1))
+    st2.sum_m = st2.sum_l = st2.sum_n = st2.slot_k = st2.slot_v = st2.u = st2.log_lambda = None
+    st2.ring_pos = None    # a window array: still required with W > 0
+    assert L.ls_append_accepted(ctypes.byref(d2), ctypes.byref(st2), 16, 16, 16, None) == 1

@@ -94,3 +94,23 @@ def test_gather_boundary_parity(dtype, H_):
     torch.cuda.synchronize()
     H.exact("boundary clamped", LB.to_host(out), O.boundary_row(hidden, [1, 7, 3, 2, 5]))
     assert int(LB.to_host(st.err_flag)[0]) & 1
+
+
+# one view switched off (Table 5's ablations, cost side): S = 0 or W = 0
+ABLATIONS = {
+    "bf16_no_summary": SMALL["bf16_s64_ragged"].with_(name="bf16_no_summary", S=0, rounds=5),
+    "bf16_no_window": SMALL["bf16_s64_ragged"].with_(name="bf16_no_window", W=0, rounds=5),
+    "bf16_block_only": SMALL["bf16_wrap"].with_(name="bf16_block_only", W=0, S=0, rounds=4),
+    "f32_no_summary": WLM.WORKLOADS["tiny_f32"].with_(name="f32_no_summary", S=0, lambdas=(),
+                                                      rounds=6),
+    "f32_no_window": WLM.WORKLOADS["tiny_f32"].with_(name="f32_no_window", W=0, rounds=6),
+}
+
+
+@pytest.mark.parametrize("name", list(ABLATIONS))
+def test_view_ablation_parity(name):
+    wl = ABLATIONS[name]
+    H.log(f"CASE ablation {name} dtype={wl.dtype} C={wl.C} W={wl.W} S={wl.S} B={wl.B} "
+          f"L0={wl.L0} seed={wl.seed}")
+    _, ost, stats = H.lockstep(wl, wl.rounds)
+    assert int(ost.seq_len.min()) > wl.L0
