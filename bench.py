@@ -29,6 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+HIDDEN = 4096                  # target hidden size of the Qwen3-8B-shaped layer (boundary state)
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 KERNEL_SOURCES = {
     "verify": "fixed_cost_drafter_amd/csrc/verify.hip",
@@ -208,17 +209,18 @@ def run_gpu(args, wl):
             ts.append(a.elapsed_time(b) * 1e-3)
         return statistics.median(ts)
 
-    def run_rounds(L0, per_call_events):
-        runner.init(L0)
+    def run_rounds(L0, per_call_events, rn=None):
+        runner_ = rn if rn is not None else runner
+        runner_.init(L0)
         for r in range(args.warmup):
-            runner.round(pool[r % len(pool)][0], rounds[r])
+            runner_.round(pool[r % len(pool)][0], rounds[r])
         torch.cuda.synchronize()
         ev = []
         t_start = time.perf_counter()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        s, b = runner.state, runner.buf
+        s, b = runner_.state, runner_.buf
         for r in range(args.warmup, n_rounds):
             logits = pool[r % len(pool)][0]
             inp = rounds[r]
@@ -233,7 +235,7 @@ def run_gpu(args, wl):
                 es[3].record(stream)
                 ev.append(es)
             else:
-                runner.round(logits, inp)
+                runner_.round(logits, inp)
         e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
@@ -290,6 +292,51 @@ def run_gpu(args, wl):
             log(f"sweep L0={L0}: init {it*1e3:.3f} ms, {args.steps / rr['wall_s']:.0f} rounds/s")
     out["sweep"] = sweep
     out["state_bytes_per_seq"] = runner.state.state_bytes() // wl.C
+
+    def per_call(fn, n):
+        """mean duration of fn(i) over n calls, events on the launch stream"""
+        for i in range(4):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record(stream)
+            fn(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return statistics.mean(a.elapsed_time(z) for a, z in ev) * 1e-3
+
+    if not args.next:
+        return out
+    # the drafter's proposal at T = 0 over [C, B, V] logits
+    drafter_logits = [t[:, :wl.B].contiguous() for t, _ in pool[:2]]
+    draft_tok = torch.empty((wl.C, wl.B), dtype=torch.int32, device=dev)
+    out["argmax_s"] = per_call(
+        lambda i: runner.state.draft_argmax(drafter_logits[i % 2], draft_tok), args.steps)
+    # the boundary state view: row tau-1 of [C, B+1, H] target states (H = 4096)
+    hidden = torch.randn((wl.C, wl.B + 1, HIDDEN), device=dev).to(LB.torch_dtype(wl.dtype))
+    hrow = torch.empty((wl.C, HIDDEN), dtype=hidden.dtype, device=dev)
+    out["boundary_s"] = per_call(
+        lambda i: runner.state.gather_boundary(hidden, runner.buf.tau, hrow), args.steps)
+    # one view switched off (cost side of the view ablations)
+    abl = {}
+    for name, kw in (("no_summary", dict(S=0, lambdas=())), ("no_window", dict(W=0))):
+        wl2 = wl.with_(name=f"{wl.name}_{name}", **kw)
+        rn2 = PathRunner(wl2, runner.k_prefix, runner.v_prefix, max_L0=rows, device=dev)
+        a = torch.cuda.Event(enable_timing=True)
+        z = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        rn2.init(wl.L0)
+        z.record(stream)
+        z.synchronize()
+        rr = run_rounds(wl.L0, per_call_events=False, rn=rn2)
+        abl[name] = dict(W=wl2.W, S=wl2.S, rounds_per_s=round(args.steps / rr["wall_s"], 1),
+                         init_ms=round(a.elapsed_time(z), 4),
+                         state_bytes_per_seq=rn2.state.state_bytes() // wl.C)
+        log(f"ablation {name}: {abl[name]}")
+        del rn2
+    out["ablations"] = abl
     out["last_tau"] = taus.tolist()
     return out
 
@@ -334,6 +381,22 @@ def cpu_baseline(wl, budget_s: float):
                 init_gb_per_s=round(init_bytes / t_init / 1e9, 4))
 
 
+def next_steps(wl, g) -> dict:
+    """The steps beside the headline round: proposal argmax, boundary gather, view ablations."""
+    e = 2 if wl.dtype == "bf16" else 4
+    arg_bytes = wl.C * wl.B * wl.V * e + wl.C * wl.B * 4
+    bnd_bytes = 2 * wl.C * HIDDEN * e + wl.C * 4
+    res = {}
+    for name, t, nbytes in (("draft_argmax", g["argmax_s"], arg_bytes),
+                            ("gather_boundary", g["boundary_s"], bnd_bytes)):
+        bw = nbytes / t / 1e9
+        res[name] = dict(avg_us=round(t * 1e6, 3), alg_bytes=int(nbytes), gb_per_s=round(bw, 1),
+                         hbm_frac=round(bw / HBM_PEAK_GBS, 4))
+    res["gather_boundary"]["hidden"] = HIDDEN
+    res["ablations"] = g["ablations"]
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -344,6 +407,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", dest="cpu", action="store_false")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--no-next", dest="next", action="store_false",
+                    help="skip the steps beside the round (argmax, boundary, view ablations)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the K rounds captured in one HIP graph")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -416,6 +481,7 @@ def main(argv=None):
         "sweep": g["sweep"],
         "graph_rounds_per_s": (round(args.steps / g["graph"]["wall_s"], 1) if "graph" in g else None),
         "state_bytes_per_seq": g["state_bytes_per_seq"],
+        "next": next_steps(wl, g) if args.next else None,
     }
     if args.cpu:
         log("timing the oracle on the host (cpu_baseline)")
