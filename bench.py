@@ -36,6 +36,7 @@ KERNEL_SOURCES = {
     "append": "fixed_cost_drafter_amd/csrc/append.hip",
     "draft": "fixed_cost_drafter_amd/csrc/draft.hip",
     "init": "fixed_cost_drafter_amd/csrc/init.hip",
+    "verify_attention": "fixed_cost_drafter_amd/csrc/verify_attn.hip",
 }
 
 
@@ -81,6 +82,7 @@ ENTRY_KERNELS = {
     "verify": ("verify_partial", "verify_finalize"),
     "append": ("append_kernel",),
     "draft": ("draft_mfma", "draft_combine", "draft_generic"),
+    "verify_attention": ("attn_mfma_partial", "attn_combine", "attn_generic"),
     "init": ("init_mfma_partial", "init_generic_partial", "init_finalize"),
 }
 CALIB_BYTES = 512 << 20        # the streaming copy used to scale the counters
@@ -273,6 +275,7 @@ def run_gpu(args, wl):
 
     out = {}
     # headline: the workload's own prefix
+    out["steps"] = args.steps
     out["init_s"] = time_init(wl.L0)
     main = run_rounds(wl.L0, per_call_events=False)
     taus = LB.to_host(runner.buf.tau)
@@ -319,6 +322,17 @@ def run_gpu(args, wl):
     hrow = torch.empty((wl.C, HIDDEN), dtype=hidden.dtype, device=dev)
     out["boundary_s"] = per_call(
         lambda i: runner.state.gather_boundary(hidden, runner.buf.tau, hrow), args.steps)
+    # the target's verification attention over the whole context (the O(L)
+    # cost per round that the drafter avoids): context L0 - B - 1 rows so that
+    # the verified block is the last B + 1 rows of the resident prefix
+    L_ctx = wl.L0 - wl.B - 1
+    Lt = torch.full((wl.C,), L_ctx, dtype=torch.int32, device=dev)
+    qv = LB.to_device(WLM.verify_queries(wl, 0), dev)
+    ov = torch.empty_like(qv)
+    out["vattn_L"] = L_ctx
+    out["vattn_s"] = per_call(
+        lambda i: runner.state.verify_attention(runner.k_prefix, runner.v_prefix, Lt, wl.L0, qv, ov),
+        8)
     # one view switched off (cost side of the view ablations)
     abl = {}
     for name, kw in (("no_summary", dict(S=0, lambdas=())), ("no_window", dict(W=0))):
@@ -393,6 +407,16 @@ def next_steps(wl, g) -> dict:
         res[name] = dict(avg_us=round(t * 1e6, 3), alg_bytes=int(nbytes), gb_per_s=round(bw, 1),
                          hbm_frac=round(bw / HBM_PEAK_GBS, 4))
     res["gather_boundary"]["hidden"] = HIDDEN
+    # verification attention: every context row's K and V, plus q and out
+    vat = g["vattn_s"]
+    vbytes = wl.C * (g["vattn_L"] + wl.B + 1) * wl.Hkv * wl.d * e * 2 + 2 * wl.C * (wl.B + 1) * wl.Hq * wl.d * e
+    vflop = 4 * wl.C * wl.Hq * (wl.B + 1) * (g["vattn_L"] + wl.B + 1) * wl.d
+    bw = vbytes / vat / 1e9
+    res["verify_attention"] = dict(avg_us=round(vat * 1e6, 2), context_rows=g["vattn_L"],
+                                   alg_bytes=int(vbytes), gb_per_s=round(bw, 1),
+                                   hbm_frac=round(bw / HBM_PEAK_GBS, 4),
+                                   tflop_per_s=round(vflop / vat / 1e12, 1),
+                                   vs_draft_round=round(vat / (g["main"]["wall_s"] / g["steps"]), 1))
     res["ablations"] = g["ablations"]
     return res
 

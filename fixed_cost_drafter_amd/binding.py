@@ -24,8 +24,8 @@ LS_F32, LS_BF16 = 0, 1
 STATUS = {0: "LS_OK", 1: "LS_ERR_NULL", 2: "LS_ERR_SHAPE", 3: "LS_ERR_DTYPE",
           4: "LS_ERR_WORKSPACE", 5: "LS_ERR_ALIGN", 6: "LS_ERR_HIP"}
 EXPORTS = ("ls_workspace_bytes", "ls_summary_init", "ls_verify_greedy", "ls_append_accepted",
-           "ls_draft_attention", "ls_draft_argmax", "ls_gather_boundary", "ls_status_string",
-           "ls_version")
+           "ls_draft_attention", "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention",
+           "ls_status_string", "ls_version")
 
 
 class LsDims(ctypes.Structure):
@@ -64,8 +64,9 @@ def _load() -> ctypes.CDLL:
     lib.ls_draft_attention.argtypes = [D, S, P, P, P, P, P]
     lib.ls_draft_argmax.argtypes = [D, P, P, P, SZ, P]
     lib.ls_gather_boundary.argtypes = [D, P, I32, P, P, P, P]
+    lib.ls_verify_attention.argtypes = [D, P, P, I64, P, I32, P, P, P, SZ, P, P]
     for f in ("ls_summary_init", "ls_verify_greedy", "ls_append_accepted", "ls_draft_attention",
-              "ls_draft_argmax", "ls_gather_boundary"):
+              "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ls_status_string.argtypes = [ctypes.c_int]
     lib.ls_status_string.restype = ctypes.c_char_p
@@ -190,6 +191,13 @@ def ls_gather_boundary(dims: LsDims, hidden, H: int, tau, out, err_flag=None, st
         _stream(stream)))
 
 
+def ls_verify_attention(dims: LsDims, k_cache, v_cache, rows_stride: int, L, max_rows: int, q, out,
+                        workspace, workspace_bytes, err_flag=None, stream=None):
+    _check("ls_verify_attention", _lib.ls_verify_attention(
+        ctypes.byref(dims), _ptr(k_cache), _ptr(v_cache), int(rows_stride), _ptr(L), int(max_rows),
+        _ptr(q), _ptr(out), _ptr(workspace), int(workspace_bytes), _ptr(err_flag), _stream(stream)))
+
+
 def ls_status_string(status: int) -> str:
     return _lib.ls_status_string(int(status)).decode()
 
@@ -267,6 +275,12 @@ class DrafterState:
 
     def gather_boundary(self, hidden, tau, out, stream=None):
         ls_gather_boundary(self.dims, hidden, hidden.shape[-1], tau, out, self.err_flag, stream)
+
+    def verify_attention(self, k_cache, v_cache, L, max_rows, q, out, stream=None):
+        """k_cache, v_cache [C, rows, Hkv, d]; L [C] int32 device; the workspace must have been
+        sized for max_L0 >= max_rows - B - 1."""
+        ls_verify_attention(self.dims, k_cache, v_cache, k_cache.shape[1], L, max_rows, q, out,
+                            self.workspace, self.workspace.numel(), self.err_flag, stream)
 
     def state_bytes(self) -> int:
         ts = (self.ring_k, self.ring_v, self.ring_pos, self.seq_len, self.sum_m, self.sum_l,

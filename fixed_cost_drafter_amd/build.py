@@ -19,7 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblongspark.so")
-SOURCES = ["abi.cpp", "verify.hip", "append.hip", "init.hip", "draft.hip", "boundary.hip"]
+SOURCES = ["abi.cpp", "verify.hip", "append.hip", "init.hip", "draft.hip", "boundary.hip",
+           "verify_attn.hip"]
 ARCH = "gfx950"
 
 

@@ -65,7 +65,7 @@ ls_status check_state(const ls_state* s, const ls_dims& d, int32_t L0) {
 
 extern "C" {
 
-int32_t ls_version(void) { return 101; }
+int32_t ls_version(void) { return 102; }
 
 const char* ls_status_string(ls_status status) {
   switch (status) {
@@ -129,6 +129,25 @@ ls_status ls_gather_boundary(const ls_dims* dims, const void* hidden, int32_t H,
   if (!hidden || !tau || !out) return LS_ERR_NULL;
   if (H < 1) return LS_ERR_SHAPE;
   return ls::launch_boundary(*dims, hidden, H, tau, out, err_flag, static_cast<hipStream_t>(stream));
+}
+
+ls_status ls_verify_attention(const ls_dims* dims, const void* k_cache, const void* v_cache,
+                              int64_t rows_stride, const int32_t* L, int32_t max_rows,
+                              const void* q, void* out, void* workspace, size_t workspace_bytes,
+                              int32_t* err_flag, ls_stream stream) {
+  ls_status st = check_dims(dims);
+  if (st != LS_OK) return st;
+  if (!k_cache || !v_cache || !L || !q || !out || !workspace) return LS_ERR_NULL;
+  if (max_rows < dims->B + 1 || rows_stride < max_rows) return LS_ERR_SHAPE;
+  if (dims->dtype == LS_BF16 && ls::attn_query_rows(*dims) > 128) return LS_ERR_SHAPE;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out) ||
+      !aligned16(workspace))
+    return LS_ERR_ALIGN;
+  if (workspace_bytes < size_t(ls::ws_layout(*dims, max_rows - dims->B - 1).total))
+    return LS_ERR_WORKSPACE;
+  return ls::launch_verify_attention(*dims, k_cache, v_cache, rows_stride, L, max_rows, q, out,
+                                     static_cast<char*>(workspace), err_flag,
+                                     static_cast<hipStream_t>(stream));
 }
 
 ls_status ls_append_accepted(const ls_dims* dims, const ls_state* state, const void* k_new,

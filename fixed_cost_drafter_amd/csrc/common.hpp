@@ -103,9 +103,26 @@ struct WsLayout {
   int64_t draft_part;                         // float [C*Hkv*halves * Mpad*(d+2)]
   int64_t verify_part;                        // uint64 keys [C*(B+1)*vsplit]
   int64_t init_part;                          // float [isplit*C*Hkv*S*(2d+2)]
+  int64_t attn_part;                          // float [C*Hkv*asplit * Mq*(d+2)]
   int64_t total;
-  int vsplit, isplit, init_rows;
+  int vsplit, isplit, init_rows, asplit;
 };
+
+// target verification attention: (B+1)*G query rows per KV head, padded to
+// row groups of 16, over up to max_rows context rows cut into `splits`
+// ranges of whole 64-row tiles (about kInitTargetBlocks workgroups in all)
+inline int attn_query_rows(const ls_dims& d) {
+  return int(cdiv(int64_t(d.B + 1) * (d.Hq / d.Hkv), 16) * 16);
+}
+inline int attn_splits(const ls_dims& d, int64_t max_rows) {
+  const int64_t want = cdiv(kInitTargetBlocks, int64_t(d.C) * d.Hkv);
+  const int64_t by_rows = cdiv(max_rows < 1 ? 1 : max_rows, kInitRowTile);
+  return int(want < by_rows ? want : by_rows);
+}
+inline int attn_rows_per_split(const ls_dims& d, int64_t max_rows) {
+  return int(cdiv(cdiv(max_rows < 1 ? 1 : max_rows, attn_splits(d, max_rows)), kInitRowTile) *
+             kInitRowTile);
+}
 
 inline int verify_splits(const ls_dims& d) { return int(cdiv(d.V, kVerifyChunk)); }
 
@@ -119,8 +136,6 @@ inline int init_rows_per_split(const ls_dims& d, int32_t L0) {
   return int(rows);
 }
 
-// key halves of the bf16 draft attention: two workgroups per KV head unit
-// when there are too few units to fill the GPU with one, and enough keys
 // bf16 draft attention with more than 32 query rows per KV head: the rows
 // are split over workgroups (each reads all keys, no partials)
 inline bool draft_row_split(const ls_dims& d) {
@@ -153,6 +168,10 @@ inline WsLayout ws_layout(const ls_dims& d, int32_t max_L0) {
   w.isplit = int(want < by_rows ? want : by_rows);
   w.init_part = off;
   off = align256(off + 4 * int64_t(w.isplit) * d.C * d.Hkv * d.S * (2 * d.d + 2));
+  // verification attention over up to max_L0 + B + 1 rows
+  w.asplit = attn_splits(d, L + d.B + 1);
+  w.attn_part = off;
+  off = align256(off + 4 * int64_t(w.asplit) * d.C * d.Hkv * attn_query_rows(d) * (d.d + 2));
   w.total = off;
   return w;
 }

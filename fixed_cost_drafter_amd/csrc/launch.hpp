@@ -20,6 +20,12 @@ ls_status launch_argmax(const ls_dims& d, const void* logits, int32_t* draft_tok
 ls_status launch_boundary(const ls_dims& d, const void* hidden, int32_t H, const int32_t* tau,
                           void* out, int32_t* err_flag, hipStream_t stream);
 
+// target verification attention of the B+1 verified positions over L + B + 1 rows
+ls_status launch_verify_attention(const ls_dims& d, const void* k_cache, const void* v_cache,
+                                  int64_t rows_stride, const int32_t* L, int32_t max_rows,
+                                  const void* q, void* out, char* ws, int32_t* err_flag,
+                                  hipStream_t stream);
+
 ls_status launch_append(const ls_dims& d, const ls_state& st, const void* k_new,
                         const void* v_new, const int32_t* tau, hipStream_t stream);
 

@@ -26,7 +26,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 # stream identifiers inside a workload's seed tree
-_U, _PREFIX, _ROUND, _LOGITS = 0, 1, 2, 3
+_U, _PREFIX, _ROUND, _LOGITS, _VQ = 0, 1, 2, 3, 4
 LOGIT_CLIP = 4.0        # ordinary logits are clipped to [-4, 4]
 LOGIT_TOP = 4.5         # the planted greedy token's logit (exact in bf16 and f32)
 TIE_PROB = 0.25         # share of rows with a second, higher-index copy of the top value
@@ -238,6 +238,12 @@ def round_inputs(wl: Workload, r: int, planted: np.ndarray):
     k_blk = normal(rng, (C, B, Hkv, d), wl.dtype)
     v_blk = normal(rng, (C, B, Hkv, d), wl.dtype)
     return dict(k_new=k_new, v_new=v_new, draft=draft, q=q, k_blk=k_blk, v_blk=v_blk)
+
+
+def verify_queries(wl: Workload, r: int) -> np.ndarray:
+    """q [C, B+1, Hq, d]: the target's queries at the B+1 verified positions of round r
+    (seeded N(0, 1); the matching K/V rows are prefix rows L..L+B)."""
+    return normal(_rng(wl.seed, _VQ, r), (wl.C, wl.B + 1, wl.Hq, wl.d), wl.dtype)
 
 
 def expected_tau(wl: Workload) -> float:

@@ -183,6 +183,28 @@ ls_status ls_draft_argmax(const ls_dims* dims, const void* logits, int32_t* draf
 ls_status ls_gather_boundary(const ls_dims* dims, const void* hidden, int32_t H,
                              const int32_t* tau, void* out, int32_t* err_flag, ls_stream stream);
 
+/* Target-side verification attention of one layer (Fig. 2 (a): the target
+ * verifies the proposed block, attending over its whole context) -- the
+ * per-round cost that grows with the prefix, which the drafter's fixed-size
+ * views avoid.
+ *   k_cache, v_cache: [C, rows_stride, Hkv, d] dtype, token-major; rows
+ *               0..L[c]-1 are the context and rows L[c]..L[c]+B hold the B+1
+ *               verified positions of sequence c (read only).
+ *   L:          [C] int32 in DEVICE memory, context rows per sequence; a value
+ *               outside [0, max_rows - B - 1] is clamped and, if err_flag is
+ *               not NULL, sets bit 0 of *err_flag.
+ *   max_rows:   host bound on L[c] + B + 1, with B + 1 <= max_rows <=
+ *               rows_stride (sizes the grid and the workspace).
+ *   q:          [C, B+1, Hq, d] dtype queries of the verified positions.
+ *   out:        [C, B+1, Hq, d] dtype: query i of head hq attends to rows
+ *               0..L[c]+i of KV head hq/(Hq/Hkv), scale 1/sqrt(d).
+ *   workspace:  at least ls_workspace_bytes(dims, max_rows - B - 1) bytes.
+ *   LS_BF16 needs (B+1)*Hq/Hkv <= 128.  Cost O(L): every context row is read. */
+ls_status ls_verify_attention(const ls_dims* dims, const void* k_cache, const void* v_cache,
+                              int64_t rows_stride, const int32_t* L, int32_t max_rows,
+                              const void* q, void* out, void* workspace, size_t workspace_bytes,
+                              int32_t* err_flag, ls_stream stream);
+
 /* Static description of a status code. */
 const char* ls_status_string(ls_status status);
 

@@ -67,7 +67,7 @@ def test_header_compiles_as_plain_c(tmp_path):
 
 
 def test_version_and_status_strings(LB):
-    assert LB.ls_version() == 101
+    assert LB.ls_version() == 102
     assert LB.ls_status_string(0) == "ok"
     for s in range(1, 7):
         assert LB.ls_status_string(s) and LB.ls_status_string(s) != "unknown status"
@@ -199,3 +199,21 @@ def test_view_ablations_accept_null_view_arrays(LB):
     st2.sum_m = st2.sum_l = st2.sum_n = st2.slot_k = st2.slot_v = st2.u = st2.log_lambda = None
     st2.ring_pos = None    # a window array: still required with W > 0
     assert L.ls_append_accepted(ctypes.byref(d2), ctypes.byref(st2), 16, 16, 16, None) == 1
+
+
+@no_device
+def test_verify_attention_validation(LB):
+    d = _dims(LB)
+    L = LB.lib()
+    ws = LB.ls_workspace_bytes(d, 1 << 17)
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("kc", 16), ("vc", 16), ("stride", 1 << 17), ("L", 16), ("max_rows", 1 << 17), ("q", 16),
+        ("out", 16), ("ws", 256), ("wsb", ws), ("err", None), ("stream", None))]
+    call = lambda **kw: L.ls_verify_attention(ctypes.byref(d), *args(**kw))
+    assert call(kc=None) == 1 and call(L=None) == 1 and call(out=None) == 1
+    assert call(max_rows=16) == 2                        # max_rows < B + 1
+    assert call(stride=1000, max_rows=2000) == 2         # rows_stride < max_rows
+    assert call(q=24) == 5                               # misaligned
+    assert call(wsb=ws - 1) == 4 or ws == 0              # workspace too small
+    wide = _dims(LB, Hq=64, Hkv=8, B=16)                 # (B+1)*G = 136 > 128 rows
+    assert L.ls_verify_attention(ctypes.byref(wide), *args()) == 2

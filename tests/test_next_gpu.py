@@ -114,3 +114,64 @@ def test_view_ablation_parity(name):
           f"L0={wl.L0} seed={wl.seed}")
     _, ost, stats = H.lockstep(wl, wl.rounds)
     assert int(ost.seq_len.min()) > wl.L0
+
+
+# target-side verification attention (the prefix-dependent cost the drafter avoids)
+ATTN_CASES = {
+    # M = (B+1)*G = 24 query rows (2 waves); ragged contexts incl. L = 0, tiles + tails
+    "bf16_m24": (SMALL["bf16_s64_ragged"].with_(name="vattn_m24", C=3, Hq=8, Hkv=2, B=5),
+                 [0, 37, 300]),
+    # M = 68 (5 waves, a 4-row tail group); contexts span several splits
+    "bf16_m68": (SMALL["bf16_s64_ragged"].with_(name="vattn_m68", C=2, Hq=16, Hkv=4, B=16),
+                 [5000, 777]),
+    # f32 generic path
+    "f32": (WLM.WORKLOADS["tiny_f32"].with_(name="vattn_f32", C=2, B=4), [60, 5]),
+}
+
+
+def _attn_run(wl, L, clamp_to=None):
+    import torch
+    from fixed_cost_drafter_amd import binding as LB
+    max_rows = max(L if clamp_to is None else clamp_to) + wl.B + 1
+    rows = max_rows + 7                                   # rows_stride > max_rows
+    Kc, Vc = WLM.prefix(wl, L0=rows, threads=4)
+    q = WLM.verify_queries(wl, 0)
+    st = LB.DrafterState.for_workload(wl, WLM.slot_queries(wl), WLM.log_lambda(wl),
+                                      max_L0=max_rows - wl.B - 1)
+    out = torch.empty((wl.C, wl.B + 1, wl.Hq, wl.d), dtype=LB.torch_dtype(wl.dtype), device="cuda")
+    st.verify_attention(LB.to_device(Kc), LB.to_device(Vc),
+                        LB.to_device(np.asarray(L, dtype=np.int32)), max_rows, LB.to_device(q), out)
+    torch.cuda.synchronize()
+    return Kc, Vc, q, LB.to_host(out), int(LB.to_host(st.err_flag)[0])
+
+
+@pytest.mark.parametrize("name", list(ATTN_CASES))
+def test_verify_attention_parity(name):
+    wl, L = ATTN_CASES[name]
+    H.log(f"CASE verify_attention {name} dtype={wl.dtype} C={wl.C} Hq={wl.Hq} Hkv={wl.Hkv} "
+          f"B={wl.B} L={L} seed={wl.seed}")
+    Kc, Vc, q, got, err = _attn_run(wl, L)
+    assert err == 0
+    H.close(f"verify_attention {name}", got, O.verify_attention(Kc, Vc, q, L), wl.dtype)
+
+
+def test_verify_attention_full_size_sampled():
+    """Qwen3-8B-shaped layer, 32K context, C = 16: sampled (sequence, head) pairs."""
+    wl = WLM.WORKLOADS["q3_8b_32k"]
+    L = [wl.L0 - 97 * c for c in range(wl.C)]             # ragged contexts near 32K
+    H.log(f"CASE verify_attention full C={wl.C} L={L[0]}..{L[-1]} B={wl.B} V={wl.V}")
+    Kc, Vc, q, got, err = _attn_run(wl, L)
+    assert err == 0
+    pairs = [(0, 0), (7, 13), (15, 31)]
+    ref = O.verify_attention(Kc, Vc, q, L, pairs=pairs)
+    for c, hq in pairs:
+        H.close(f"verify_attention ({c},{hq})", got[c, :, hq], ref[c, :, hq], wl.dtype)
+
+
+def test_verify_attention_clamps_and_flags_bad_context():
+    wl, _ = ATTN_CASES["bf16_m24"]
+    H.log("CASE verify_attention clamp L=[-4, 50, 10**6] max context 60")
+    L = [-4, 50, 10 ** 6]
+    Kc, Vc, q, got, err = _attn_run(wl, L, clamp_to=[0, 50, 60])
+    assert err & 1
+    H.close("verify_attention clamped", got, O.verify_attention(Kc, Vc, q, [0, 50, 60]), wl.dtype)
