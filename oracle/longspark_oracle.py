@@ -41,6 +41,9 @@ Parity status of each function (what pins it is in tests/test_oracle.py):
   draft_argmax, boundary_row, verify_attention, and the S = 0 / W = 0 views:
   pinned in tests/test_oracle_next.py (brute force, SDPA with an explicit
   mask, worked examples).
+  softmax_t, inverse_cdf, verify_sampling: pinned in tests/test_oracle_sampling.py
+  (worked example, brute force, the sampled token distributed as the target's,
+  p == q acceptance).
   Parity with the pages' own LongSpark numbers: unpinned -- the pages print
   no formula and no per-step output for this path.
 """
@@ -63,6 +66,9 @@ __all__ = [
     "draft_argmax",
     "boundary_row",
     "verify_attention",
+    "softmax_t",
+    "inverse_cdf",
+    "verify_sampling",
 ]
 
 
@@ -392,3 +398,62 @@ def verify_attention(k_cache, v_cache, q, L, pairs=None):
         p /= p.sum(axis=1, keepdims=True)
         out[c, :, hq, :] = p @ vals
     return out
+
+
+# --------------------------------------------------------------------------
+# sampled verification (Table 1 reports accepted lengths at temperature 1,
+# Table 3 separately for greedy decoding; the rule itself is not printed on
+# the pages: this is the textbook speculative-sampling rule)
+# --------------------------------------------------------------------------
+def softmax_t(logits, temperature):
+    """Row-wise softmax of decoded logits / temperature (float64), temperature > 0."""
+    x = decode(logits) / float(temperature)
+    x = x - x.max(axis=-1, keepdims=True)
+    e = np.exp(x)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def inverse_cdf(w, u):
+    """Draw from unnormalised weights w >= 0 with a uniform u in [0, 1): the
+    smallest index k whose running sum w_0 + ... + w_k exceeds u * sum(w)."""
+    c = np.cumsum(np.asarray(w, dtype=np.float64))
+    return int(np.searchsorted(c, u * c[-1], side="right"))
+
+
+def verify_sampling(target_logits, draft_logits, draft, temperature, u_accept, u_sample):
+    """Speculative-sampling verification of a drafted block.
+
+    target_logits [C, B+1, V]: the target's scores at the B+1 verified
+    positions; row j predicts the token after position j.  draft_logits
+    [C, B, V]: the drafter's scores for the same B predictions; draft [C, B]
+    its sampled tokens.  p_j = softmax(target row j / T), q_j = softmax(draft
+    row j / T).  Draft j is accepted when u_accept[c, j] * q_j(d) < p_j(d),
+    i.e. with probability min(1, p/q); at the first rejection the emitted
+    token is drawn from max(0, p_j - q_j) with u_sample[c] (inverse_cdf); if
+    all B drafts are accepted the extra token is drawn from p_B.
+
+    Returns tokens [C, B+1] int32 (the first tau[c] are emitted, the rest -1)
+    and tau [C] int32 in [1, B+1].
+    """
+    p = softmax_t(target_logits, temperature)
+    q = softmax_t(draft_logits, temperature)
+    draft = np.asarray(draft)
+    u_accept = np.asarray(u_accept, dtype=np.float64)
+    u_sample = np.asarray(u_sample, dtype=np.float64)
+    C, B1, _ = p.shape
+    B = B1 - 1
+    tokens = np.full((C, B1), -1, dtype=np.int32)
+    tau = np.zeros((C,), dtype=np.int32)
+    for c in range(C):
+        j = 0
+        while j < B:
+            d = int(draft[c, j])
+            if u_accept[c, j] * q[c, j, d] < p[c, j, d]:
+                tokens[c, j] = d
+                j += 1
+            else:
+                break
+        w = np.maximum(p[c, j] - q[c, j], 0.0) if j < B else p[c, B]
+        tokens[c, j] = inverse_cdf(w, u_sample[c])
+        tau[c] = j + 1
+    return tokens, tau
