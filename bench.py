@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "draft": "fixed_cost_drafter_amd/csrc/draft.hip",
     "init": "fixed_cost_drafter_amd/csrc/init.hip",
     "verify_attention": "fixed_cost_drafter_amd/csrc/verify_attn.hip",
+    "verify_sampling": "fixed_cost_drafter_amd/csrc/sampling.hip",
 }
 
 
@@ -80,6 +81,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 # kernels that make up one call of each entry point (substrings of their names)
 ENTRY_KERNELS = {
     "verify": ("verify_partial", "verify_finalize"),
+    "verify_sampling": ("samp_stats", "samp_decide", "samp_sums", "samp_draw"),
     "append": ("append_kernel",),
     "draft": ("draft_mfma", "draft_combine", "draft_generic"),
     "verify_attention": ("attn_mfma_partial", "attn_combine", "attn_generic"),
@@ -333,6 +335,18 @@ def run_gpu(args, wl):
     out["vattn_s"] = per_call(
         lambda i: runner.state.verify_attention(runner.k_prefix, runner.v_prefix, Lt, wl.L0, qv, ov),
         8)
+    # sampled verification at T = 1 (speculative sampling): both logit tensors once
+    tl_host, _ = WLM.logits_entry(wl, 0)
+    samp = WLM.sampling_inputs(wl, 0, tl_host, temperature=1.0)
+    dls = LB.to_device(samp["draft_logits"], dev)
+    sd = {k: LB.to_device(samp[k], dev) for k in ("draft", "u_accept", "u_sample")}
+    stoks = torch.empty((wl.C, wl.B + 1), dtype=torch.int32, device=dev)
+    staus = torch.empty((wl.C,), dtype=torch.int32, device=dev)
+    out["sampling_s"] = per_call(
+        lambda i: runner.state.verify_sampling(pool[0][0], dls, sd["draft"], 1.0, sd["u_accept"],
+                                               sd["u_sample"], stoks, staus), args.steps)
+    out["sampling_tau"] = float(LB.to_host(staus).mean())
+    del tl_host, samp, dls
     # one view switched off (cost side of the view ablations)
     abl = {}
     for name, kw in (("no_summary", dict(S=0, lambdas=())), ("no_window", dict(W=0))):
@@ -407,6 +421,11 @@ def next_steps(wl, g) -> dict:
         res[name] = dict(avg_us=round(t * 1e6, 3), alg_bytes=int(nbytes), gb_per_s=round(bw, 1),
                          hbm_frac=round(bw / HBM_PEAK_GBS, 4))
     res["gather_boundary"]["hidden"] = HIDDEN
+    sbytes = wl.C * (2 * wl.B + 1) * wl.V * e + 2 * wl.C * wl.V * e
+    bw = sbytes / g["sampling_s"] / 1e9
+    res["verify_sampling"] = dict(avg_us=round(g["sampling_s"] * 1e6, 3), alg_bytes=int(sbytes),
+                                  gb_per_s=round(bw, 1), hbm_frac=round(bw / HBM_PEAK_GBS, 4),
+                                  temperature=1.0, mean_tau=round(g["sampling_tau"], 3))
     # verification attention: every context row's K and V, plus q and out
     vat = g["vattn_s"]
     vbytes = wl.C * (g["vattn_L"] + wl.B + 1) * wl.Hkv * wl.d * e * 2 + 2 * wl.C * (wl.B + 1) * wl.Hq * wl.d * e

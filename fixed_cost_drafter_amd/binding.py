@@ -25,7 +25,7 @@ STATUS = {0: "LS_OK", 1: "LS_ERR_NULL", 2: "LS_ERR_SHAPE", 3: "LS_ERR_DTYPE",
           4: "LS_ERR_WORKSPACE", 5: "LS_ERR_ALIGN", 6: "LS_ERR_HIP"}
 EXPORTS = ("ls_workspace_bytes", "ls_summary_init", "ls_verify_greedy", "ls_append_accepted",
            "ls_draft_attention", "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention",
-           "ls_status_string", "ls_version")
+           "ls_verify_sampling", "ls_status_string", "ls_version")
 
 
 class LsDims(ctypes.Structure):
@@ -65,8 +65,9 @@ def _load() -> ctypes.CDLL:
     lib.ls_draft_argmax.argtypes = [D, P, P, P, SZ, P]
     lib.ls_gather_boundary.argtypes = [D, P, I32, P, P, P, P]
     lib.ls_verify_attention.argtypes = [D, P, P, I64, P, I32, P, P, P, SZ, P, P]
+    lib.ls_verify_sampling.argtypes = [D, P, P, P, ctypes.c_float, P, P, P, P, P, SZ, P]
     for f in ("ls_summary_init", "ls_verify_greedy", "ls_append_accepted", "ls_draft_attention",
-              "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention"):
+              "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention", "ls_verify_sampling"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ls_status_string.argtypes = [ctypes.c_int]
     lib.ls_status_string.restype = ctypes.c_char_p
@@ -198,6 +199,14 @@ def ls_verify_attention(dims: LsDims, k_cache, v_cache, rows_stride: int, L, max
         _ptr(q), _ptr(out), _ptr(workspace), int(workspace_bytes), _ptr(err_flag), _stream(stream)))
 
 
+def ls_verify_sampling(dims: LsDims, target_logits, draft_logits, draft, temperature: float,
+                       u_accept, u_sample, tokens, tau, workspace, workspace_bytes, stream=None):
+    _check("ls_verify_sampling", _lib.ls_verify_sampling(
+        ctypes.byref(dims), _ptr(target_logits), _ptr(draft_logits), _ptr(draft),
+        float(temperature), _ptr(u_accept), _ptr(u_sample), _ptr(tokens), _ptr(tau),
+        _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
 def ls_status_string(status: int) -> str:
     return _lib.ls_status_string(int(status)).decode()
 
@@ -281,6 +290,11 @@ class DrafterState:
         sized for max_L0 >= max_rows - B - 1."""
         ls_verify_attention(self.dims, k_cache, v_cache, k_cache.shape[1], L, max_rows, q, out,
                             self.workspace, self.workspace.numel(), self.err_flag, stream)
+
+    def verify_sampling(self, target_logits, draft_logits, draft, temperature, u_accept, u_sample,
+                        tokens, tau, stream=None):
+        ls_verify_sampling(self.dims, target_logits, draft_logits, draft, temperature, u_accept,
+                           u_sample, tokens, tau, self.workspace, self.workspace.numel(), stream)
 
     def state_bytes(self) -> int:
         ts = (self.ring_k, self.ring_v, self.ring_pos, self.seq_len, self.sum_m, self.sum_l,

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblongspark.so")
 SOURCES = ["abi.cpp", "verify.hip", "append.hip", "init.hip", "draft.hip", "boundary.hip",
-           "verify_attn.hip"]
+           "verify_attn.hip", "sampling.hip"]
 ARCH = "gfx950"
 
 

@@ -65,7 +65,7 @@ ls_status check_state(const ls_state* s, const ls_dims& d, int32_t L0) {
 
 extern "C" {
 
-int32_t ls_version(void) { return 102; }
+int32_t ls_version(void) { return 103; }
 
 const char* ls_status_string(ls_status status) {
   switch (status) {
@@ -148,6 +148,24 @@ ls_status ls_verify_attention(const ls_dims* dims, const void* k_cache, const vo
   return ls::launch_verify_attention(*dims, k_cache, v_cache, rows_stride, L, max_rows, q, out,
                                      static_cast<char*>(workspace), err_flag,
                                      static_cast<hipStream_t>(stream));
+}
+
+ls_status ls_verify_sampling(const ls_dims* dims, const void* target_logits,
+                             const void* draft_logits, const int32_t* draft, float temperature,
+                             const float* u_accept, const float* u_sample, int32_t* tokens,
+                             int32_t* tau, void* workspace, size_t workspace_bytes,
+                             ls_stream stream) {
+  ls_status st = check_dims(dims);
+  if (st != LS_OK) return st;
+  if (!target_logits || !draft_logits || !draft || !u_accept || !u_sample || !tokens || !tau ||
+      !workspace)
+    return LS_ERR_NULL;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return LS_ERR_SHAPE;
+  if (!aligned16(workspace)) return LS_ERR_ALIGN;
+  if (workspace_bytes < size_t(ls::ws_layout(*dims, 1).total)) return LS_ERR_WORKSPACE;
+  return ls::launch_sampling(*dims, target_logits, draft_logits, draft, temperature, u_accept,
+                             u_sample, tokens, tau, static_cast<char*>(workspace),
+                             static_cast<hipStream_t>(stream));
 }
 
 ls_status ls_append_accepted(const ls_dims* dims, const ls_state* state, const void* k_new,

@@ -104,6 +104,9 @@ struct WsLayout {
   int64_t verify_part;                        // uint64 keys [C*(B+1)*vsplit]
   int64_t init_part;                          // float [isplit*C*Hkv*S*(2d+2)]
   int64_t attn_part;                          // float [C*Hkv*asplit * Mq*(d+2)]
+  int64_t samp_stats;                         // float2 (max, sum) [C*(2B+1)*vsplit]
+  int64_t samp_seq;                           // per-sequence decision record [C*8] (4-byte words)
+  int64_t samp_sums;                          // float [C*vsplit] chunk sums of the drawn row
   int64_t total;
   int vsplit, isplit, init_rows, asplit;
 };
@@ -172,6 +175,11 @@ inline WsLayout ws_layout(const ls_dims& d, int32_t max_L0) {
   w.asplit = attn_splits(d, L + d.B + 1);
   w.attn_part = off;
   off = align256(off + 4 * int64_t(w.asplit) * d.C * d.Hkv * attn_query_rows(d) * (d.d + 2));
+  // sampled verification: softmax statistics of the C*(2B+1) rows, a record
+  // per sequence, and the chunk sums of the row its token is drawn from
+  w.samp_stats = off; off = align256(off + 8 * int64_t(d.C) * (2 * d.B + 1) * w.vsplit);
+  w.samp_seq = off; off = align256(off + 32 * int64_t(d.C));
+  w.samp_sums = off; off = align256(off + 4 * int64_t(d.C) * w.vsplit);
   w.total = off;
   return w;
 }

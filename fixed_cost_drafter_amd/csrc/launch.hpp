@@ -26,6 +26,12 @@ ls_status launch_verify_attention(const ls_dims& d, const void* k_cache, const v
                                   const void* q, void* out, char* ws, int32_t* err_flag,
                                   hipStream_t stream);
 
+// sampled (speculative) verification of a drafted block
+ls_status launch_sampling(const ls_dims& d, const void* target_logits, const void* draft_logits,
+                          const int32_t* draft, float temperature, const float* u_accept,
+                          const float* u_sample, int32_t* tokens, int32_t* tau, char* ws,
+                          hipStream_t stream);
+
 ls_status launch_append(const ls_dims& d, const ls_state& st, const void* k_new,
                         const void* v_new, const int32_t* tau, hipStream_t stream);
 

@@ -1,0 +1,316 @@
+// Sampled verification of a drafted block (LongSpark paper page, Table 1:
+// accepted lengths with sampling at temperature 1; Table 3 is the greedy
+// case).  The pages do not print the rule; this is the textbook
+// speculative-sampling rule:
+//   p_j = softmax(target row j / T), q_j = softmax(drafter row j / T);
+//   draft j is accepted when u_accept[j] * q_j(d_j) < p_j(d_j);
+//   at the first rejection j the emitted token is drawn from max(0, p_j - q_j),
+//   after B acceptances from p_B; the draw is the inverse CDF over the
+//   vocabulary in index order: the smallest k whose running sum exceeds
+//   u_sample times the total.
+//
+// Four launches, kernel boundaries between them (no device-scope fences):
+//  (1) samp_stats: (row, 16K-logit chunk) workgroups stream both logit
+//      tensors once and reduce each chunk to base-2 softmax statistics
+//      (max of x log2(e) / T, sum of 2^(y - max));
+//  (2) samp_decide: one workgroup per sequence merges its 2B+1 rows'
+//      statistics, gathers p_j(d_j), q_j(d_j) in parallel and runs the
+//      acceptance rule, then records the row to draw from;
+//  (3) samp_sums: chunk sums of that row's weights;
+//  (4) samp_draw: one workgroup per sequence locates the chunk, then the
+//      thread segment, then the element where the running sum crosses
+//      u_sample times the total.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ls {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// (m, s) += (m2, s2) for base-2 softmax statistics (s = sum of 2^(y - m))
+__device__ __forceinline__ void merge_stat(float& m, float& s, float m2, float s2) {
+  const float mx = fmaxf(m, m2);
+  if (mx == -INFINITY) return;
+  s = s * exp2_f(m - mx) + s2 * exp2_f(m2 - mx);
+  m = mx;
+}
+
+__device__ __forceinline__ void wave_merge_stat(float& m, float& s) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+    merge_stat(m, s, m2, s2);
+  }
+}
+
+template <typename Ty>
+struct Vec16;  // 16 bytes of logits
+template <>
+struct Vec16<F32> {
+  static constexpr int N = 4;
+  using V = float __attribute__((ext_vector_type(4)));
+  __device__ static inline float get(const V& v, int i) { return v[i]; }
+};
+template <>
+struct Vec16<BF16> {
+  static constexpr int N = 8;
+  using V = u16x8;
+  __device__ static inline float get(const V& v, int i) { return bf16_to_f32(v[i]); }
+};
+
+// per-sequence record written by samp_decide
+struct Record {
+  int32_t row;   // j: the verified row the emitted token is drawn from
+  int32_t bonus; // 1: drawn from p_B (all drafts accepted), 0: from max(0, p_j - q_j)
+  float mt, izt; // target row j: max and 1 / sum (base 2)
+  float md, izd; // drafter row j (residual draw only)
+  float pad[2];
+};
+static_assert(sizeof(Record) == 32, "one 32-byte record per sequence");
+
+template <typename Ty>
+__global__ __launch_bounds__(kThreads) void samp_stats(
+    const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
+    float2* __restrict__ stats, int C, int B, int V, int nsplit, float k2, int vec_ok) {
+  using VT = Vec16<Ty>;
+  const int split = blockIdx.x, r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int nt = C * (B + 1);
+  const typename Ty::T* x = r < nt ? tl + int64_t(r) * V : dl + int64_t(r - nt) * V;
+  const int begin = split * kVerifyChunk, end = min(V, begin + kVerifyChunk);
+  float m = -INFINITY, s = 0.f;
+  if (vec_ok) {
+    const typename VT::V* xv = reinterpret_cast<const typename VT::V*>(x + begin);
+    const int nvec = (end - begin) / VT::N;
+    constexpr int U = (kVerifyChunk / VT::N + kThreads - 1) / kThreads;
+    typename VT::V buf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = u * kThreads + tid;
+      if (v < nvec) buf[u] = __builtin_nontemporal_load(xv + v);
+    }
+    float bm = -INFINITY;  // batch max, then one rescale
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u * kThreads + tid < nvec)
+#pragma unroll
+        for (int e = 0; e < VT::N; ++e) bm = fmaxf(bm, VT::get(buf[u], e) * k2);
+    float bs = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u * kThreads + tid < nvec)
+#pragma unroll
+        for (int e = 0; e < VT::N; ++e) bs += exp2_f(VT::get(buf[u], e) * k2 - bm);
+    merge_stat(m, s, bm, bs);
+    for (int i = begin + nvec * VT::N + tid; i < end; i += kThreads)
+      merge_stat(m, s, Ty::load(x, i) * k2, 1.f);
+  } else {
+    for (int i = begin + tid; i < end; i += kThreads) merge_stat(m, s, Ty::load(x, i) * k2, 1.f);
+  }
+  wave_merge_stat(m, s);
+  __shared__ float wm[kThreads / 64], ws[kThreads / 64];
+  if ((tid & 63) == 0) { wm[tid >> 6] = m; ws[tid >> 6] = s; }
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < kThreads / 64; ++w) merge_stat(m, s, wm[w], ws[w]);
+    stats[int64_t(r) * nsplit + split] = make_float2(m, s);
+  }
+}
+
+template <typename Ty>
+__global__ __launch_bounds__(64) void samp_decide(
+    const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
+    const int32_t* __restrict__ draft, const float* __restrict__ u_accept,
+    const float2* __restrict__ stats, Record* __restrict__ rec, int32_t* __restrict__ tokens,
+    int32_t* __restrict__ tau, int C, int B, int V, int nsplit, float k2) {
+  __shared__ float pt[64], qd[64], mt[64], izt[64], md[64], izd[64];
+  __shared__ int js;
+  const int c = blockIdx.x, t = threadIdx.x;
+  const int nt = C * (B + 1);
+  if (t <= B) {  // target row t; drafter row t (t < B) and the two probabilities of draft t
+    float m = -INFINITY, s = 0.f;
+    const float2* st = stats + (int64_t(c) * (B + 1) + t) * nsplit;
+    for (int k = 0; k < nsplit; ++k) merge_stat(m, s, st[k].x, st[k].y);
+    mt[t] = m;
+    izt[t] = 1.0f / s;
+    if (t < B) {
+      float m2 = -INFINITY, s2 = 0.f;
+      const float2* sd = stats + (int64_t(nt) + int64_t(c) * B + t) * nsplit;
+      for (int k = 0; k < nsplit; ++k) merge_stat(m2, s2, sd[k].x, sd[k].y);
+      md[t] = m2;
+      izd[t] = 1.0f / s2;
+      const int d = min(max(draft[int64_t(c) * B + t], 0), V - 1);
+      pt[t] = exp2_f(Ty::load(tl, (int64_t(c) * (B + 1) + t) * V + d) * k2 - m) * izt[t];
+      qd[t] = exp2_f(Ty::load(dl, (int64_t(c) * B + t) * V + d) * k2 - m2) * izd[t];
+    }
+  }
+  __syncthreads();
+  if (t == 0) {
+    int j = 0;
+    while (j < B && u_accept[int64_t(c) * B + j] * qd[j] < pt[j]) ++j;
+    js = j;
+    tau[c] = j + 1;
+    Record r;
+    r.row = j;
+    r.bonus = j == B;
+    r.mt = mt[j];
+    r.izt = izt[j];
+    r.md = j < B ? md[j] : 0.f;
+    r.izd = j < B ? izd[j] : 0.f;
+    r.pad[0] = r.pad[1] = 0.f;
+    rec[c] = r;
+  }
+  __syncthreads();
+  for (int i = t; i <= B; i += 64)  // accepted drafts, then -1 (token js is drawn later)
+    if (i != js) tokens[int64_t(c) * (B + 1) + i] = i < js ? draft[int64_t(c) * B + i] : -1;
+}
+
+// weight of vocabulary entry k in the draw of a record's row
+template <typename Ty>
+__device__ __forceinline__ float draw_weight(const typename Ty::T* rt, const typename Ty::T* rd,
+                                             const Record& r, float k2, int k) {
+  const float p = exp2_f(Ty::load(rt, k) * k2 - r.mt) * r.izt;
+  if (r.bonus) return p;
+  const float q = exp2_f(Ty::load(rd, k) * k2 - r.md) * r.izd;
+  return fmaxf(p - q, 0.f);
+}
+
+template <typename Ty>
+__global__ __launch_bounds__(kThreads) void samp_sums(
+    const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
+    const Record* __restrict__ rec, float* __restrict__ sums, int B, int V, int nsplit, float k2) {
+  const int split = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const Record r = rec[c];
+  const typename Ty::T* rt = tl + (int64_t(c) * (B + 1) + r.row) * V;
+  const typename Ty::T* rd = dl + (int64_t(c) * B + min(r.row, B - 1)) * V;
+  const int begin = split * kVerifyChunk, end = min(V, begin + kVerifyChunk);
+  float a = 0.f;
+  for (int k = begin + tid; k < end; k += kThreads) a += draw_weight<Ty>(rt, rd, r, k2, k);
+  a = wave_sum(a);
+  __shared__ float wsum[kThreads / 64];
+  if ((tid & 63) == 0) wsum[tid >> 6] = a;
+  __syncthreads();
+  if (tid == 0) sums[int64_t(c) * nsplit + split] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+template <typename Ty>
+__global__ __launch_bounds__(kThreads) void samp_draw(
+    const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
+    const Record* __restrict__ rec, const float* __restrict__ sums,
+    const float* __restrict__ u_sample, int32_t* __restrict__ tokens, int B, int V, int nsplit,
+    float k2) {
+  constexpr int SEG = kVerifyChunk / kThreads;  // elements per thread segment
+  __shared__ float seg[kThreads];
+  __shared__ int s_split, s_seg, s_tok;
+  __shared__ float s_base, s_thr;
+  const int c = blockIdx.x, tid = threadIdx.x;
+  const Record r = rec[c];
+  const typename Ty::T* rt = tl + (int64_t(c) * (B + 1) + r.row) * V;
+  const typename Ty::T* rd = dl + (int64_t(c) * B + min(r.row, B - 1)) * V;
+  if (tid == 0) {
+    const float* sm = sums + int64_t(c) * nsplit;
+    float total = 0.f;
+    for (int k = 0; k < nsplit; ++k) total += sm[k];
+    const float thr = u_sample[c] * total;
+    float run = 0.f;
+    int sp = -1, last = 0;
+    for (int k = 0; k < nsplit; ++k) {
+      if (sm[k] > 0.f) last = k;
+      if (sp < 0 && run + sm[k] > thr) sp = k;
+      if (sp < 0) run += sm[k];
+    }
+    if (sp < 0) {  // rounding left the threshold at the very end: the last non-empty chunk
+      sp = last;
+      run = 0.f;
+      for (int k = 0; k < last; ++k) run += sm[k];
+    }
+    s_split = sp;
+    s_base = run;
+    s_thr = thr;
+    s_tok = -1;
+  }
+  __syncthreads();
+  const int begin = s_split * kVerifyChunk, end = min(V, begin + kVerifyChunk);
+  const int k0 = begin + tid * SEG, k1 = min(end, k0 + SEG);
+  float a = 0.f;
+  for (int k = k0; k < k1; ++k) a += draw_weight<Ty>(rt, rd, r, k2, k);
+  seg[tid] = a;
+  __syncthreads();
+  if (tid == 0) {  // the segment where the running sum crosses the threshold
+    float run = s_base;
+    int sg = -1, last = -1;
+    for (int t2 = 0; t2 < kThreads; ++t2) {
+      if (seg[t2] > 0.f) last = t2;
+      if (sg < 0 && run + seg[t2] > s_thr) sg = t2;
+      if (sg < 0) run += seg[t2];
+    }
+    if (sg < 0) {  // rounding: the last segment with weight
+      sg = last < 0 ? 0 : last;
+      run = s_base;
+      for (int t2 = 0; t2 < sg; ++t2) run += seg[t2];
+    }
+    s_seg = sg;
+    s_base = run;
+  }
+  __syncthreads();
+  if (tid == s_seg) {
+    float run = s_base;
+    int tok = -1, last = k0;
+    for (int k = k0; k < k1; ++k) {
+      const float w = draw_weight<Ty>(rt, rd, r, k2, k);
+      if (w > 0.f) last = k;
+      run += w;
+      if (run > s_thr) { tok = k; break; }
+    }
+    s_tok = tok < 0 ? last : tok;
+  }
+  __syncthreads();
+  if (tid == 0) tokens[int64_t(c) * (B + 1) + r.row] = s_tok;
+}
+
+template <typename Ty>
+ls_status run(const ls_dims& d, const void* tl, const void* dl, const int32_t* draft, float T,
+              const float* u_accept, const float* u_sample, int32_t* tokens, int32_t* tau,
+              char* ws, hipStream_t stream) {
+  using E = typename Ty::T;
+  const WsLayout lay = ws_layout(d, 1);
+  const int nsplit = lay.vsplit;
+  const float k2 = kLog2e / T;
+  auto* stats = reinterpret_cast<float2*>(ws + lay.samp_stats);
+  auto* rec = reinterpret_cast<Record*>(ws + lay.samp_seq);
+  auto* sums = reinterpret_cast<float*>(ws + lay.samp_sums);
+  const E* t = static_cast<const E*>(tl);
+  const E* dd = static_cast<const E*>(dl);
+  const int vec_ok = ((int64_t(d.V) * Ty::kBytes) % 16 == 0) && ((uintptr_t(tl) & 15) == 0) &&
+                     ((uintptr_t(dl) & 15) == 0);
+  hipLaunchKernelGGL(samp_stats<Ty>, dim3(nsplit, d.C * (2 * d.B + 1)), dim3(kThreads), 0, stream,
+                     t, dd, stats, d.C, d.B, d.V, nsplit, k2, vec_ok);
+  if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
+  hipLaunchKernelGGL(samp_decide<Ty>, dim3(d.C), dim3(64), 0, stream, t, dd, draft, u_accept, stats,
+                     rec, tokens, tau, d.C, d.B, d.V, nsplit, k2);
+  if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
+  hipLaunchKernelGGL(samp_sums<Ty>, dim3(nsplit, d.C), dim3(kThreads), 0, stream, t, dd, rec, sums,
+                     d.B, d.V, nsplit, k2);
+  if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
+  hipLaunchKernelGGL(samp_draw<Ty>, dim3(d.C), dim3(kThreads), 0, stream, t, dd, rec, sums, u_sample,
+                     tokens, d.B, d.V, nsplit, k2);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+}
+
+}  // namespace
+
+ls_status launch_sampling(const ls_dims& d, const void* target_logits, const void* draft_logits,
+                          const int32_t* draft, float temperature, const float* u_accept,
+                          const float* u_sample, int32_t* tokens, int32_t* tau, char* ws,
+                          hipStream_t stream) {
+  if (d.dtype == LS_BF16)
+    return run<BF16>(d, target_logits, draft_logits, draft, temperature, u_accept, u_sample,
+                     tokens, tau, ws, stream);
+  return run<F32>(d, target_logits, draft_logits, draft, temperature, u_accept, u_sample, tokens,
+                  tau, ws, stream);
+}
+
+}  // namespace ls

@@ -26,7 +26,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 # stream identifiers inside a workload's seed tree
-_U, _PREFIX, _ROUND, _LOGITS, _VQ = 0, 1, 2, 3, 4
+_U, _PREFIX, _ROUND, _LOGITS, _VQ, _SAMP = 0, 1, 2, 3, 4, 5
 LOGIT_CLIP = 4.0        # ordinary logits are clipped to [-4, 4]
 LOGIT_TOP = 4.5         # the planted greedy token's logit (exact in bf16 and f32)
 TIE_PROB = 0.25         # share of rows with a second, higher-index copy of the top value
@@ -244,6 +244,36 @@ def verify_queries(wl: Workload, r: int) -> np.ndarray:
     """q [C, B+1, Hq, d]: the target's queries at the B+1 verified positions of round r
     (seeded N(0, 1); the matching K/V rows are prefix rows L..L+B)."""
     return normal(_rng(wl.seed, _VQ, r), (wl.C, wl.B + 1, wl.Hq, wl.d), wl.dtype)
+
+
+def sampling_inputs(wl: Workload, r: int, target_logits: np.ndarray, temperature: float = 1.0,
+                    noise: float = 0.5) -> dict:
+    """Inputs of sampled verification for round r, beside the target's logits [C, B+1, V].
+
+    draft_logits [C, B, V]: target rows 0..B-1 plus N(0, noise), rounded to the
+    storage dtype (a drafter close to the target); draft [C, B]: tokens drawn
+    from softmax(draft_logits / T) row by row on the host (float64 inverse
+    CDF); u_accept [C, B] and u_sample [C]: float32 uniforms in [0, 1).
+    """
+    rng = _rng(wl.seed, _SAMP, r)
+    C, B = wl.C, wl.B
+    base = bf16_bits_to_f32(target_logits) if wl.dtype == "bf16" else np.asarray(target_logits, np.float32)
+    dl32 = base[:, :B].astype(np.float32) + (noise * rng.standard_normal((C, B, wl.V))).astype(np.float32)
+    draft_logits = f32_to_bf16_bits(dl32) if wl.dtype == "bf16" else dl32
+    dq = (bf16_bits_to_f32(draft_logits) if wl.dtype == "bf16" else draft_logits).astype(np.float64)
+    dq = dq / temperature
+    dq -= dq.max(axis=-1, keepdims=True)
+    w = np.exp(dq)
+    cdf = np.cumsum(w, axis=-1)
+    u = rng.random((C, B))
+    draft = np.empty((C, B), dtype=np.int32)
+    for c in range(C):
+        for j in range(B):
+            draft[c, j] = min(int(np.searchsorted(cdf[c, j], u[c, j] * cdf[c, j, -1], side="right")),
+                              wl.V - 1)
+    u_accept = rng.random((C, B)).astype(np.float32)
+    u_sample = rng.random((C,)).astype(np.float32)
+    return dict(draft_logits=draft_logits, draft=draft, u_accept=u_accept, u_sample=u_sample)
 
 
 def expected_tau(wl: Workload) -> float:

@@ -205,6 +205,29 @@ ls_status ls_verify_attention(const ls_dims* dims, const void* k_cache, const vo
                               const void* q, void* out, void* workspace, size_t workspace_bytes,
                               int32_t* err_flag, ls_stream stream);
 
+/* Sampled verification of a drafted block (Table 1: accepted lengths with
+ * sampling at temperature 1; Table 3 is the greedy case, ls_verify_greedy).
+ * The pages do not print the rule; this is the textbook speculative-sampling
+ * rule.  p_j = softmax(target row j / T), q_j = softmax(drafter row j / T);
+ * draft j is accepted when u_accept[c, j] * q_j(d) < p_j(d); at the first
+ * rejection the token is drawn from max(0, p_j - q_j), after B acceptances
+ * from p_B, as the smallest k whose running sum exceeds u_sample[c] times
+ * the total (inverse CDF over the vocabulary in index order).
+ *   target_logits: [C, B+1, V] dtype; draft_logits: [C, B, V] dtype; no NaN.
+ *   draft:         [C, B] int32 drafted tokens (each in [0, V)).
+ *   temperature:   T > 0 (host value).
+ *   u_accept:      [C, B] float32 uniforms in [0, 1) (device).
+ *   u_sample:      [C] float32 uniforms in [0, 1) (device).
+ *   tokens:        [C, B+1] int32 out: the tau[c] emitted tokens, then -1.
+ *   tau:           [C] int32 out, in [1, B+1].
+ *   workspace:     as sized by ls_workspace_bytes (any max_L0).
+ * Probabilities are formed in fp32 (base-2 exponentials of x log2(e) / T). */
+ls_status ls_verify_sampling(const ls_dims* dims, const void* target_logits,
+                             const void* draft_logits, const int32_t* draft, float temperature,
+                             const float* u_accept, const float* u_sample, int32_t* tokens,
+                             int32_t* tau, void* workspace, size_t workspace_bytes,
+                             ls_stream stream);
+
 /* Static description of a status code. */
 const char* ls_status_string(ls_status status);
 

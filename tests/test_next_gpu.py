@@ -175,3 +175,96 @@ def test_verify_attention_clamps_and_flags_bad_context():
     Kc, Vc, q, got, err = _attn_run(wl, L, clamp_to=[0, 50, 60])
     assert err & 1
     H.close("verify_attention clamped", got, O.verify_attention(Kc, Vc, q, [0, 50, 60]), wl.dtype)
+
+
+# sampled verification (textbook speculative sampling), fp32 decisions on the GPU.
+# The GPU forms p and q in fp32 and sums the drawn row in fp32 (64-element
+# segments, 256 segments, <= 64 chunks): relative error below 5e-5 for the
+# acceptance test and below 2e-5 of the total for the running sums.  A decision
+# inside that band may go either way: an acceptance inside it makes the rest of
+# the sequence ambiguous (skipped, and counted); a draw accepts every token whose
+# fp64 CDF interval comes within the band of the threshold (and has weight).
+ACCEPT_EPS, DRAW_EPS = 5e-5, 2e-5
+
+
+def _sampling_expectation(tl, dl, draft, T, ua, us, c):
+    """(tau, accepted drafts, allowed drawn tokens) from the fp64 rule, or None when an
+    acceptance decision of sequence c lies within ACCEPT_EPS of its threshold."""
+    p = O.softmax_t(tl[c:c + 1], T)[0]
+    q = O.softmax_t(dl[c:c + 1], T)[0]
+    B = q.shape[0]
+    j = 0
+    while j < B:
+        d = int(draft[c, j])
+        a, b = float(ua[c, j]) * q[j, d], p[j, d]
+        if abs(a - b) <= ACCEPT_EPS * max(a, b, 1e-300):
+            return None
+        if not a < b:
+            break
+        j += 1
+    w = np.maximum(p[j] - q[j], 0.0) if j < B else p[B]
+    cs = np.cumsum(w)
+    thr = float(us[c]) * cs[-1]
+    band = DRAW_EPS * cs[-1]
+    lo = np.concatenate([[0.0], cs[:-1]])
+    allowed = np.nonzero((w > 0) & (lo <= thr + band) & (cs >= thr - band))[0]
+    return j + 1, [int(x) for x in draft[c, :j]], set(int(x) for x in allowed)
+
+
+SAMPLING_CASES = {
+    "bf16_small_T1": (SMALL["bf16_s64_ragged"].with_(name="samp_bf16", C=6, B=5, V=3000), 1.0),
+    "bf16_small_T07": (SMALL["bf16_s64_ragged"].with_(name="samp_bf16_t07", C=6, B=5, V=20001), 0.7),
+    "f32_tiny": (WLM.WORKLOADS["tiny_f32"].with_(name="samp_f32", C=4, B=4), 1.0),
+    "q3_8b_full": (WLM.WORKLOADS["q3_8b_128k"], 1.0),
+}
+
+
+@pytest.mark.parametrize("name", list(SAMPLING_CASES))
+def test_verify_sampling_parity(name):
+    import torch
+    from fixed_cost_drafter_amd import binding as LB
+    wl, T = SAMPLING_CASES[name]
+    H.log(f"CASE verify_sampling {name} dtype={wl.dtype} C={wl.C} B={wl.B} V={wl.V} T={T}")
+    st = _state(wl)
+    tokens = torch.empty((wl.C, wl.B + 1), dtype=torch.int32, device="cuda")
+    tau = torch.empty((wl.C,), dtype=torch.int32, device="cuda")
+    checked = skipped = 0
+    for r in range(2):
+        tl, _ = WLM.logits_entry(wl, r)
+        inp = WLM.sampling_inputs(wl, r, tl, temperature=T)
+        dl = inp["draft_logits"]
+        st.verify_sampling(LB.to_device(tl), LB.to_device(dl), LB.to_device(inp["draft"]), T,
+                           LB.to_device(inp["u_accept"]), LB.to_device(inp["u_sample"]), tokens, tau)
+        torch.cuda.synchronize()
+        got_tok, got_tau = LB.to_host(tokens), LB.to_host(tau)
+        for c in range(wl.C):
+            exp = _sampling_expectation(tl, dl, inp["draft"], T, inp["u_accept"], inp["u_sample"], c)
+            if exp is None:
+                skipped += 1
+                continue
+            checked += 1
+            t_ref, acc, allowed = exp
+            assert got_tau[c] == t_ref, (name, r, c, got_tau[c], t_ref)
+            assert got_tok[c, :t_ref - 1].tolist() == acc, (name, r, c)
+            assert int(got_tok[c, t_ref - 1]) in allowed, (name, r, c, got_tok[c, t_ref - 1], sorted(allowed)[:8])
+            assert (got_tok[c, t_ref:] == -1).all()
+    H.log(f"{name}: {checked} sequences compared, {skipped} with an acceptance within {ACCEPT_EPS}")
+    assert skipped <= max(1, (checked + skipped) // 10)
+
+
+def test_verify_sampling_equal_distributions_accept_all():
+    """Drafter == target: every draft is accepted and the bonus comes from p_B."""
+    import torch
+    from fixed_cost_drafter_amd import binding as LB
+    wl = SMALL["bf16_s64_ragged"].with_(name="samp_equal", C=4, B=6, V=5000)
+    H.log(f"CASE verify_sampling equal distributions C={wl.C} B={wl.B} V={wl.V}")
+    tl, _ = WLM.logits_entry(wl, 0)
+    inp = WLM.sampling_inputs(wl, 0, tl, noise=0.0)
+    st = _state(wl)
+    tokens = torch.empty((wl.C, wl.B + 1), dtype=torch.int32, device="cuda")
+    tau = torch.empty((wl.C,), dtype=torch.int32, device="cuda")
+    st.verify_sampling(LB.to_device(tl), LB.to_device(inp["draft_logits"]), LB.to_device(inp["draft"]),
+                       1.0, LB.to_device(inp["u_accept"]), LB.to_device(inp["u_sample"]), tokens, tau)
+    torch.cuda.synchronize()
+    assert LB.to_host(tau).tolist() == [wl.B + 1] * wl.C
+    assert np.array_equal(LB.to_host(tokens)[:, :wl.B], inp["draft"])
