@@ -213,43 +213,22 @@ def run_gpu(args, wl):
             ts.append(a.elapsed_time(b) * 1e-3)
         return statistics.median(ts)
 
-    def run_rounds(L0, per_call_events, rn=None):
+    def run_rounds(L0, rn=None):
+        """the timed region: args.steps rounds after args.warmup untimed ones"""
         runner_ = rn if rn is not None else runner
         runner_.init(L0)
         for r in range(args.warmup):
             runner_.round(pool[r % len(pool)][0], rounds[r])
         torch.cuda.synchronize()
-        ev = []
         t_start = time.perf_counter()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        s, b = runner_.state, runner_.buf
         for r in range(args.warmup, n_rounds):
-            logits = pool[r % len(pool)][0]
-            inp = rounds[r]
-            if per_call_events:
-                es = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-                es[0].record(stream)
-                s.verify_greedy(logits, inp["draft"], b.target_tok, b.tau)
-                es[1].record(stream)
-                s.append_accepted(inp["k_new"], inp["v_new"], b.tau)
-                es[2].record(stream)
-                s.draft_attention(inp["q"], inp["k_blk"], inp["v_blk"], b.out)
-                es[3].record(stream)
-                ev.append(es)
-            else:
-                runner_.round(logits, inp)
+            runner_.round(pool[r % len(pool)][0], rounds[r])
         e1.record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t_start
-        gpu = e0.elapsed_time(e1) * 1e-3
-        res = dict(wall_s=wall, gpu_s=gpu)
-        if per_call_events:
-            res["verify_s"] = statistics.mean(x[0].elapsed_time(x[1]) for x in ev) * 1e-3
-            res["append_s"] = statistics.mean(x[1].elapsed_time(x[2]) for x in ev) * 1e-3
-            res["draft_s"] = statistics.mean(x[2].elapsed_time(x[3]) for x in ev) * 1e-3
-        return res
+        return dict(wall_s=time.perf_counter() - t_start, gpu_s=e0.elapsed_time(e1) * 1e-3)
 
     def run_graph(L0):
         """K rounds captured once in a HIP graph, replayed; the same inputs as run_rounds."""
@@ -279,9 +258,35 @@ def run_gpu(args, wl):
     # headline: the workload's own prefix
     out["steps"] = args.steps
     out["init_s"] = time_init(wl.L0)
-    main = run_rounds(wl.L0, per_call_events=False)
+    main = run_rounds(wl.L0)
     taus = LB.to_host(runner.buf.tau)
-    kern = run_rounds(wl.L0, per_call_events=True)
+
+    def back_to_back(fn, n):
+        """average launch duration: n consecutive launches between two events"""
+        for i in range(4):
+            fn(i)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        z = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        z.record(stream)
+        z.synchronize()
+        return a.elapsed_time(z) * 1e-3 / n
+
+    # each entry point of the round timed over its own region of back-to-back
+    # launches on the round's inputs (the state after the timed rounds)
+    s_, b_ = runner.state, runner.buf
+    P = len(pool)
+    kern = dict(
+        verify_s=back_to_back(lambda i: s_.verify_greedy(pool[i % P][0], rounds[i % n_rounds]["draft"],
+                                                         b_.target_tok, b_.tau), args.steps),
+        draft_s=back_to_back(lambda i: s_.draft_attention(rounds[i % n_rounds]["q"], rounds[i % n_rounds]["k_blk"],
+                                                          rounds[i % n_rounds]["v_blk"], b_.out), args.steps),
+        append_s=back_to_back(lambda i: s_.append_accepted(rounds[i % n_rounds]["k_new"],
+                                                           rounds[i % n_rounds]["v_new"], b_.tau), args.steps),
+    )
     out.update(main=main, kern=kern)
     if args.graph:
         out["graph"] = run_graph(wl.L0)
@@ -290,7 +295,7 @@ def run_gpu(args, wl):
     if args.sweep:
         for L0 in WLM.SWEEP_L0:
             it = time_init(L0)
-            rr = run_rounds(L0, per_call_events=False)
+            rr = run_rounds(L0)
             sweep[str(L0)] = dict(init_ms=round(it * 1e3, 4),
                                   rounds_per_s=round(args.steps / rr["wall_s"], 1),
                                   ms_per_round=round(rr["wall_s"] / args.steps * 1e3, 5))
@@ -358,7 +363,7 @@ def run_gpu(args, wl):
         rn2.init(wl.L0)
         z.record(stream)
         z.synchronize()
-        rr = run_rounds(wl.L0, per_call_events=False, rn=rn2)
+        rr = run_rounds(wl.L0, rn=rn2)
         abl[name] = dict(W=wl2.W, S=wl2.S, rounds_per_s=round(args.steps / rr["wall_s"], 1),
                          init_ms=round(a.elapsed_time(z), 4),
                          state_bytes_per_seq=rn2.state.state_bytes() // wl.C)

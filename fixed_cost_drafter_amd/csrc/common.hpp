@@ -90,7 +90,7 @@ __host__ __device__ inline int64_t value_index(int64_t unit, int rows, int d, in
 // workspace layout (bytes), shared by the host code and the kernels
 // ---------------------------------------------------------------------------
 #ifndef LS_VERIFY_CHUNK
-#define LS_VERIFY_CHUNK 16384
+#define LS_VERIFY_CHUNK 8192
 #endif
 constexpr int kVerifyChunk = LS_VERIFY_CHUNK;  // logits per verify workgroup
 constexpr int kInitTargetBlocks = 512; // aim of the init grid size
