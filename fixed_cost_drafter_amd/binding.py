@@ -127,6 +127,32 @@ def values_to_rows(a: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(np.swapaxes(a, -1, -2).reshape(*lead, nt * tw, d))
 
 
+def key_tiled(rows: int, d: int) -> bool:
+    """Window / slot keys are stored in 32-key tiles in MFMA operand order when d = 128."""
+    return d == 128 and rows % 32 == 0
+
+
+def key_tile_order() -> np.ndarray:
+    """[32, 128]: element offset of (key, dimension) inside one stored key tile.
+
+    Key k = 8a + 4b + r, dimension e = 32s + 8g + i go to element
+    ((((b*4 + s)*4 + g)*16 + 4a + r)*8 + i.
+    """
+    k = np.arange(32)[:, None]
+    e = np.arange(128)[None, :]
+    piece = ((((k >> 2) & 1) * 4 + (e >> 5)) * 4 + ((e >> 3) & 3)) * 16 + 4 * (k >> 3) + (k & 3)
+    return piece * 8 + (e & 7)
+
+
+def keys_to_rows(a: np.ndarray) -> np.ndarray:
+    """Host copy of stored window / slot keys [..., rows, d] -> row-major keys."""
+    *lead, rows, d = a.shape
+    if not key_tiled(rows, d):
+        return a
+    t = a.reshape(*lead, rows // 32, 32 * d)
+    return np.ascontiguousarray(t[..., key_tile_order()].reshape(*lead, rows, d))
+
+
 def torch_dtype(dtype: str) -> torch.dtype:
     return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
 

@@ -24,8 +24,9 @@
 // load waits for tau.  The tau new rows are merged two at a time: the key
 // lanes form partial dot products with the slot query, a DPP butterfly over
 // the slot's lanes completes the scores, and one rescale per batch folds them
-// into (m, l, n).  The slots n / l leave as pooled keys (row-major, one slot
-// row per lane group) and pooled values; the values of the workgroup's 32
+// into (m, l, n).  The slots n / l leave as pooled keys (each lane's 8
+// dimensions as one 16-byte piece at its place in the key layout) and
+// pooled values; the values of the workgroup's 32
 // slots are one key tile ([d][32]) of the value layout the drafter reads,
 // assembled in LDS and stored contiguously.
 #include <algorithm>
@@ -192,7 +193,7 @@ __device__ __forceinline__ float group_sum(float x) {
 // and seq_len advances by tau.  One workgroup per sequence does all of it, so
 // it is the only reader of seq_len in the launch and may update it in place.
 // Keys and values are staged in LDS (a group of heads at a time, 16-byte
-// loads), keys leave as 16-byte pieces and values go into the key-tiled
+// loads), keys leave as 16-byte pieces (key layout) and values go into the key-tiled
 // layout with lanes over rows, so neighbouring lanes store neighbouring
 // window slots.
 template <typename Ty, int D>
@@ -240,7 +241,7 @@ __device__ __forceinline__ void append_window(
       const int e = p % V16, pr = p / V16;
       const int hl = pr / Tn, i = pr - hl * Tn;
       const int slot = slot0 + i >= W ? slot0 + i - W : slot0 + i;
-      reinterpret_cast<uint4*>(ring_k + ((int64_t(c) * Hkv + h0 + hl) * W + slot) * D)[e] =
+      *reinterpret_cast<uint4*>(ring_k + key_index(int64_t(c) * Hkv + h0 + hl, W, D, slot, e * E16)) =
           reinterpret_cast<const uint4*>(stage + pr * 2 * D)[e];
     }
     // values: D lanes per (head, row) pair, one dimension each
@@ -374,7 +375,10 @@ __global__ __launch_bounds__(block_threads<D>()) void append_kernel(
       sum_m[sidx] = m_run;
       sum_l[sidx] = l_run;
     }
-    if (key_lane) store_elems<Ty, EPL>(slot_k + sidx * D + col, n, il);
+    // a lane's EPL key entries stay inside one group of 8 dimensions, which
+    // the key layout keeps contiguous
+    static_assert(D != 128 || EPL <= 8, "one key group of 8 dimensions per lane");
+    if (key_lane) store_elems<Ty, EPL>(slot_k + key_index(unit, S, D, jc, col), n, il);
   }
   // pooled values -> the tile [d][32] in LDS -> slot_v
   if (!key_lane) {

@@ -87,6 +87,24 @@ __host__ __device__ inline int64_t value_index(int64_t unit, int rows, int d, in
 }
 
 // ---------------------------------------------------------------------------
+// key layout of the window and of the slots.  With d = 128 and rows a
+// multiple of 32, each tile of 32 keys is stored in the order in which the
+// drafter's MFMA reads its A operand (S^T = K Q^T with 16x16x32 products),
+// so that every 64-lane operand load is 1 KB contiguous:
+//   key k = 8a + 4b + r (a < 4, b < 2, r < 4), dimension e = 32s + 8g + i
+//   -> element ((((b*4 + s)*4 + g)*16 + 4a + r)*8 + i of the tile.
+// The 8 dimensions 8g' .. 8g'+7 of one key stay contiguous (16 bytes in
+// bf16).  Other shapes keep keys row-major, [unit][rows][d].
+// ---------------------------------------------------------------------------
+__host__ __device__ inline bool key_tiled(int rows, int d) { return d == 128 && rows % 32 == 0; }
+__host__ __device__ inline int64_t key_index(int64_t unit, int rows, int d, int key, int dim) {
+  if (!key_tiled(rows, d)) return (unit * rows + key) * d + dim;
+  const int k = key & 31;
+  const int piece = ((((k >> 2) & 1) * 4 + (dim >> 5)) * 4 + ((dim >> 3) & 3)) * 16 + 4 * (k >> 3) + (k & 3);
+  return (unit * rows + (key & ~31)) * d + piece * 8 + (dim & 7);
+}
+
+// ---------------------------------------------------------------------------
 // workspace layout (bytes), shared by the host code and the kernels
 // ---------------------------------------------------------------------------
 #ifndef LS_VERIFY_CHUNK
@@ -139,17 +157,18 @@ inline int init_rows_per_split(const ls_dims& d, int32_t L0) {
   return int(rows);
 }
 
-// bf16 draft attention with more than 32 query rows per KV head: the rows
-// are split over workgroups (each reads all keys, no partials)
-inline bool draft_row_split(const ls_dims& d) {
-  return d.dtype == LS_BF16 && int64_t(d.B) * (d.Hq / d.Hkv) > 32;
-}
-// otherwise the keys may be split over two workgroups (partials + combine)
-// when the units alone do not fill the chip
+// bf16 draft attention: one workgroup per (KV head, 32 query rows, key
+// range).  The key range is the whole key list unless the (KV head, rows)
+// pairs alone leave the chip idle; then the keys are cut into up to 4
+// ranges whose (m, l, O) partials a second launch merges.
+inline int draft_row_splits(const ls_dims& d) { return int(cdiv(int64_t(d.B) * (d.Hq / d.Hkv), 32)); }
 inline int draft_halves(const ls_dims& d) {
-  if (d.dtype != LS_BF16 || draft_row_split(d)) return 1;
+  if (d.dtype != LS_BF16) return 1;
   const int64_t chunks = (int64_t(d.W) + d.S) / 32 + cdiv(d.B, 32);
-  return (int64_t(d.C) * d.Hkv < 256 && chunks >= 16) ? 2 : 1;
+  const int64_t blocks = int64_t(d.C) * d.Hkv * draft_row_splits(d);
+  int k = 1;
+  while (k < 4 && blocks * k * 2 <= 256 && chunks >= 8 * k * 2) k *= 2;
+  return k;
 }
 
 inline WsLayout ws_layout(const ls_dims& d, int32_t max_L0) {

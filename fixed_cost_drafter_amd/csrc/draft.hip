@@ -8,25 +8,28 @@
 // bidirectional (no mask inside the block).  The B*G query rows of one KV
 // head (G = Hq/Hkv) share its keys, so they form one query tile.
 //
-// bf16, d = 128 (draft_mfma).  One workgroup per (KV head unit, 32 query
-// rows), so a Qwen3-8B-shaped layer at C = 16 (128 units x 64 rows) fills the
-// 256 CUs.  Its 4 waves are 4 key parts, each for all 32 rows (2 row groups
-// of 16, one wave per SIMD with the full register file).  The keys are cut
-// in 32-key chunks that never straddle two views (W and S are multiples of
-// 32; the block gets its own chunks); each wave streams its part's chunks
-// with every MFMA operand loaded straight from memory into registers in
-// operand layout, two chunks in flight, with no LDS staging and no barrier
-// in the loop:
-//   S^T = K Q^T : A = key rows (row-major [key][d]: 16 contiguous bytes per
-//                 lane), B = the wave's 16 query rows (registers);
-//   O^T += V^T P^T : A = values, which the state keeps in key tiles of 32
-//                 ([rows/32][d][32]) so a lane's keys of one dimension are
-//                 16 contiguous bytes and a chunk is one 8 KB block; B = the
-//                 softmax weights from the S^T output layout, rounded to bf16.
-// Each loaded operand serves both row groups of the wave.  The block's
-// values arrive token-major from the caller and are transposed through LDS
-// once per workgroup.  The online softmax lives in registers (per query row,
-// per lane); the key parts merge (m, l, O) in LDS at the end.
+// bf16, d = 128 (draft_direct).  A workgroup takes one KV head unit, 32 of
+// its query rows (two row groups of 16) and one key range; its KPW waves are
+// KPW key parts.  The keys are cut in 32-key chunks that never straddle two
+// views (W and S are multiples of 32; the block gets its own chunks), and the
+// chunks of a range are dealt to its waves in turn.  Each wave loads every
+// MFMA operand of its chunks straight from memory into registers, IF chunks
+// ahead (KPW = 8 waves, two per SIMD, with IF = 1: about 64 registers per
+// lane hold the chunk in flight), with no LDS and no barrier in the loop:
+//   S^T = K Q^T : A = 16 keys x 32 dimensions; the window and slot keys are
+//                 stored in this operand order (tiles of 32 keys), so each
+//                 64-lane load is 1 KB contiguous; B = the query rows
+//                 (registers, loaded once);
+//   O^T += V^T P^T : A = 16 dimensions x 32 keys from the value tiles
+//                 [d][32] (1 KB contiguous per load); B = the softmax
+//                 weights from the S^T output layout, rounded to bf16.
+// Every loaded operand serves both row groups.  The verified block arrives
+// token-major from the caller; its (at most two) chunks are staged in LDS
+// once per workgroup and computed by the wave whose turn they fall on.  The
+// online softmax lives in registers (per query row, per lane) in base 2; the
+// key parts merge (m, l, O) in LDS at the end, and key ranges, when there is
+// more than one, through the workspace and draft_combine (a kernel boundary,
+// no device-scope fence).
 // f32 (draft_generic): one workgroup per query row, plain loop (small shapes).
 #include "common.hpp"
 #include "launch.hpp"
@@ -35,10 +38,14 @@ namespace ls {
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef LS_DRAFT_INFLIGHT
-#define LS_DRAFT_INFLIGHT 2
+#ifndef LS_DRAFT_KPW
+#define LS_DRAFT_KPW 8
 #endif
-constexpr int kInFlight = LS_DRAFT_INFLIGHT;  // chunks loading into registers per thread
+#ifndef LS_DRAFT_INFLIGHT
+#define LS_DRAFT_INFLIGHT 1
+#endif
+constexpr int kKPW = LS_DRAFT_KPW;             // key parts (waves) per workgroup
+constexpr int kInFlight = LS_DRAFT_INFLIGHT;   // chunks loading per wave
 // Scores are kept in base-2 units (log2(e) folded into the 1/sqrt(d) scale),
 // so every softmax weight is one v_exp_f32 (2^x).
 constexpr float kScale2 = 0.08838834764831845f * 1.4426950408889634f;  // log2(e)/sqrt(128)
@@ -51,86 +58,35 @@ __device__ inline uint16_t bf16_bits(float f) {
 
 // Keys are permuted inside a 32-key chunk so that the S^T output puts keys
 // 8kg..8kg+7 in lane group kg: A-row m of score block mb holds key
-// 8*(m/4) + 4*mb + m%4.  Then the P^T operand, the V^T operand (one 16-byte
-// read per dimension block) and the positions all see the lane's 8 keys in
-// natural order.
+// 8*(m/4) + 4*mb + m%4.  Then the P^T operand and the V^T operand (one
+// 16-byte load per dimension block) see the lane's 8 keys in natural order.
+// The stored key tiles (key_index) follow the same permutation.
 __device__ __forceinline__ int chunk_key(int m, int mb) { return 8 * (m >> 2) + 4 * mb + (m & 3); }
 
-// LDS image of one staged 32-key chunk: keys row-major (padded rows), values
-// [d][32] (padded), and a score bias per key (0, or -inf for an empty window
-// slot or a block row past B).
+// LDS image of one staged block chunk: keys row-major (padded rows), values
+// [d][32] (padded)
 constexpr int kKS = 128 + 8;   // key row stride (bf16)
 constexpr int kVS = 32 + 8;    // value row stride (bf16)
-constexpr int kStageElems = 32 * kKS + 128 * kVS + 64;  // bf16 elements (+ 32 int positions)
+constexpr int kBlkElems = 32 * kKS + 128 * kVS;
 
-struct Stage {  // pointers into one stage buffer
-  uint16_t* k;
-  uint16_t* v;
-  float* bias;
-  __device__ explicit Stage(uint16_t* base)
-      : k(base), v(base + 32 * kKS), bias(reinterpret_cast<float*>(base + 32 * kKS + 128 * kVS)) {}
+// the MFMA operands of one 32-key chunk for one wave
+struct Operands {
+  u16x8 k[8];  // A operands of S^T = K Q^T, [mb*4 + ks]
+  u16x8 v[8];  // A operands of O^T += V^T P^T, [dimension block of 16]
+  int pos;     // ring_pos of key (lane & 31); 0 for the slots
 };
 
-// One thread's share of a chunk: PPT pieces of 16 bytes of keys and PPT of
-// values out of the chunk's 512 + 512 (TPP = 512 / PPT staging threads per
-// key part), plus one key's score bias for t < 32.
-template <int PPT>
-struct Piece {
-  u16x8 d[2 * PPT];
-  float bias;
-};
-
-// Source of chunk ch of one unit: [window W/32 | slots S/32 | block].
-struct Views {
-  const uint16_t *rk, *rv, *sk, *sv, *kb, *vb;
-  const int32_t* rp;
-  int W, S, B, Hkv, c, h, nring, ngl;
-};
-
-// loads for staging chunk ch (thread t of the part's 512 / PPT staging threads)
-template <int PPT>
-__device__ __forceinline__ void load_piece(Piece<PPT>& x, const Views& s, int ch, int t) {
-  constexpr int D = 128, TPP = 512 / PPT;
-  if (ch < s.ngl) {  // window or slots: K rows [key][d], V tile [d][32], contiguous
-    const bool ring = ch < s.nring;
-    const int key0 = (ring ? ch : ch - s.nring) * 32;
-    const uint16_t* kt = (ring ? s.rk : s.sk) + int64_t(key0) * D;
-    const uint16_t* vt = (ring ? s.rv : s.sv) + int64_t(ring ? ch : ch - s.nring) * D * 32;
+// kt: the chunk's key tile (operand order), vt: its value tile [d][32],
+// rp: its 32 ring positions (nullptr for the slots: always occupied)
+__device__ __forceinline__ void load_operands(Operands& x, const uint16_t* kt, const uint16_t* vt,
+                                              const int32_t* rp, int lane) {
+  const int ln = lane & 15, kg = lane >> 4;
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      x.d[j] = *reinterpret_cast<const u16x8*>(kt + (t + TPP * j) * 8);
-      x.d[PPT + j] = *reinterpret_cast<const u16x8*>(vt + (t + TPP * j) * 8);
-    }
-    const int p = ring ? s.rp[key0 + (t & 31)] : 0;  // slots are always occupied
-    x.bias = p < 0 ? -INFINITY : 0.f;
-  } else {  // block: K and V rows are the caller's token-major [b][Hkv][d]
-    const int key0 = (ch - s.ngl) * 32;
+  for (int i = 0; i < 8; ++i) x.k[i] = *reinterpret_cast<const u16x8*>(kt + (i * 64 + lane) * 8);
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int piece = t + TPP * j, row = piece >> 4, col = (piece & 15) * 8;
-      const int64_t off = ((int64_t(s.c) * s.B + min(key0 + row, s.B - 1)) * s.Hkv + s.h) * D + col;
-      x.d[j] = *reinterpret_cast<const u16x8*>(s.kb + off);
-      x.d[PPT + j] = *reinterpret_cast<const u16x8*>(s.vb + off);
-    }
-    x.bias = key0 + (t & 31) < s.B ? 0.f : -INFINITY;
-  }
-}
-
-template <int PPT>
-__device__ __forceinline__ void store_piece(const Piece<PPT>& x, Stage st, bool block_chunk, int t) {
-  constexpr int TPP = 512 / PPT;
-#pragma unroll
-  for (int j = 0; j < PPT; ++j) {
-    const int piece = t + TPP * j, row = piece >> 4, col = (piece & 15) * 8;
-    *reinterpret_cast<u16x8*>(st.k + row * kKS + col) = x.d[j];
-    if (!block_chunk) {  // value tile piece: dim = piece / 4, keys (piece % 4) * 8 ..
-      *reinterpret_cast<u16x8*>(st.v + (piece >> 2) * kVS + (piece & 3) * 8) = x.d[PPT + j];
-    } else {  // token-major value row -> [d][32]
-#pragma unroll
-      for (int e = 0; e < 8; ++e) st.v[(col + e) * kVS + row] = x.d[PPT + j][e];
-    }
-  }
-  if (t < 32) st.bias[t] = x.bias;
+  for (int db = 0; db < 8; ++db)
+    x.v[db] = *reinterpret_cast<const u16x8*>(vt + (db * 16 + ln) * 32 + kg * 8);
+  x.pos = rp ? rp[lane & 31] : 0;
 }
 
 // Online softmax state of one row group of 16 query rows.
@@ -139,31 +95,19 @@ struct Softmax {
   f32x4 o[8];
 };
 
-// one staged chunk for the wave's row group: scores (base 2, biased), lazy
-// online softmax update, P.V
-__device__ __forceinline__ void compute_chunk(Softmax& st, Stage sg, const bf16x8 (&qb)[4], int ln,
-                                              int kg) {
+// scores of one row group for the chunk (s[mb][r] is key 8kg + 4mb + r) ->
+// lazy online softmax update; returns the bf16 weights as the P^T operand
+__device__ __forceinline__ bf16x8 softmax_chunk(Softmax& st, f32x4 (&s)[2], uint32_t valid8) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
-  f32x4 s[2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const uint16_t* krow = sg.k + chunk_key(ln, mb) * kKS + kg * 8;
-    s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      s[mb] = mfma16x16x32(as_bf16x8(*reinterpret_cast<const u16x8*>(krow + ks * 32)), qb[ks], s[mb]);
-  }
-  // s[mb][r] is key 8kg + 4mb + r of the chunk: score = s * log2(e)/sqrt(d) + bias
-  const f32x4 b0 = *reinterpret_cast<const f32x4*>(sg.bias + 8 * kg);
-  const f32x4 b1 = *reinterpret_cast<const f32x4*>(sg.bias + 8 * kg + 4);
   float tmax = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    s[0][r] = fmaf(s[0][r], kScale2, b0[r]);
-    s[1][r] = fmaf(s[1][r], kScale2, b1[r]);
-    tmax = fmaxf(tmax, fmaxf(s[0][r], s[1][r]));
-  }
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      s[mb][r] = ((valid8 >> (4 * mb + r)) & 1u) ? s[mb][r] * kScale2 : -INFINITY;
+      tmax = fmaxf(tmax, s[mb][r]);
+    }
   // the row's max over the 4 lane groups (lanes ln, ln+16, ln+32, ln+48):
   // swapping a register with itself across row pairs / halves leaves the
   // partner's value in one of the two results
@@ -197,159 +141,224 @@ __device__ __forceinline__ void compute_chunk(Softmax& st, Stage sg, const bf16x
   const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
   float lsum = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[w]), ones, lsum, false);
+  for (int w = 0; w < 4; ++w)
+    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[w]), ones, lsum, false);
   st.l += lsum;
-  const u16x8 pv = __builtin_bit_cast(u16x8, uint4{pw[0], pw[1], pw[2], pw[3]});
-  const bf16x8 pk = as_bf16x8(pv);
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) {
-    const u16x8 v = *reinterpret_cast<const u16x8*>(sg.v + (mb * 16 + ln) * kVS + kg * 8);
-    st.o[mb] = mfma16x16x32(as_bf16x8(v), pk, st.o[mb]);
-  }
+  return as_bf16x8(__builtin_bit_cast(u16x8, uint4{pw[0], pw[1], pw[2], pw[3]}));
 }
 
-// Workgroup = (KV head unit, split); 64*RG*KPW threads = RG row groups of 16
-// query rows x KPW key parts.  A split is either one of `ksplit` key ranges
-// (all rows; the ranges' (m, l, O) go to the workspace for draft_combine, a
-// kernel boundary, no fence) or, with ksplit = 1, one range of 16*RG query
-// rows over all keys (the output is written here).  The splits of a unit are
-// blockIdx = unit + k * units, on one XCD when units is a multiple of 8, so
-// the keys they share are fetched from HBM once.  Each key part stages its
-// chunks into its own double-buffered LDS stages (kInFlight chunks loading
-// in registers) and its RG row-group waves read them; the parts merge in LDS.
-template <int RG, int KPW>
-__global__ __launch_bounds__(64 * RG * KPW, 1) void draft_mfma(
+// one chunk for both row groups: S^T = K Q^T, softmax, O^T += V^T P^T.
+// valid8 bit e: key 8kg + e of the chunk is present.
+__device__ __forceinline__ void compute_chunk(Softmax (&st)[2], const Operands& x,
+                                              const bf16x8 (&qb)[2][4], uint32_t valid8) {
+  f32x4 s[2][2];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) s[rg][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+        s[rg][mb] = mfma16x16x32(as_bf16x8(x.k[mb * 4 + ks]), qb[rg][ks], s[rg][mb]);
+  bf16x8 pk[2];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) pk[rg] = softmax_chunk(st[rg], s[rg], valid8);
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) st[rg].o[db] = mfma16x16x32(as_bf16x8(x.v[db]), pk[rg], st[rg].o[db]);
+}
+
+// Workgroup = (unit, 32 query rows ridx, key range kidx): blockIdx =
+// unit + units * (kidx + ksplit * ridx), so the workgroups of one unit sit
+// on one XCD when units is a multiple of 8 and the keys they share are
+// fetched from HBM once.  Key range kidx's chunks are those with
+// chunk % (ksplit*KPW) in [kidx*KPW, kidx*KPW + KPW); wave kq takes residue
+// kidx*KPW + kq.  With ksplit = 1 the output is written here, else the
+// range's (m, l, O) go to the workspace: [unit][kidx][m[64] | l[64] | O[64][d]].
+template <int KPW, int IF>
+__global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, const uint16_t* __restrict__ ring_k,
     const uint16_t* __restrict__ ring_v, const int32_t* __restrict__ ring_pos,
     const uint16_t* __restrict__ slot_k, const uint16_t* __restrict__ slot_v,
-    uint16_t* __restrict__ out, float* __restrict__ part_out, int Hq, int Hkv, int W, int S,
-    int B, int units, int ksplit) {
-  constexpr int D = 128, TPP = 64 * RG, PPT = 512 / TPP;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[KPW * 2 * kStageElems];
+    uint16_t* __restrict__ out, float* __restrict__ part_out, int Hq, int Hkv, int W, int S, int B,
+    int units, int ksplit) {
+  constexpr int D = 128, NT = 64 * KPW;
+  constexpr int kRedBytes = (KPW - 1) * 2 * 64 * 34 * 4;
+  constexpr int kLdsBytes = (2 * kBlkElems * 2 > kRedBytes) ? 2 * kBlkElems * 2 : kRedBytes;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsBytes / 2];
 
-  const int split = blockIdx.x / units;
-  const int unit = blockIdx.x % units;
+  const int unit = blockIdx.x % units, split = blockIdx.x / units;
   const int kidx = split % ksplit, ridx = split / ksplit;
   const int c = unit / Hkv, h = unit % Hkv;
   const int G = Hq / Hkv, M = B * G;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, kq = tid >> 6, lane = tid & 63;
   const int ln = lane & 15, kg = lane >> 4;
-  const int g = wave % RG, kq = wave / RG;   // row group, key part
-  const int t = tid % TPP;                   // staging thread within the part
 
-  // query operand: lane (row ln of group g, kg) holds q[row][ks*32+kg*8..+7]
-  const int row = ridx * 16 * RG + g * 16 + ln;
-  const bool row_ok = row < M;
-  bf16x8 qb[4];
-  {
-    const int bq = row_ok ? row / G : 0, hq = h * G + (row_ok ? row % G : 0);
+  // query operands: lane (row ln of group rg, kg) holds q[row][ks*32+kg*8..+7]
+  bf16x8 qb[2][4];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    const int row = ridx * 32 + rg * 16 + ln;
+    const bool ok = row < M;
+    const int bq = ok ? row / G : 0, hq = h * G + (ok ? row % G : 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (row_ok)
-        v = *reinterpret_cast<const u16x8*>(q + ((int64_t(c) * B + bq) * Hq + hq) * D + ks * 32 + kg * 8);
-      qb[ks] = as_bf16x8(v);
+      if (ok) v = *reinterpret_cast<const u16x8*>(q + ((int64_t(c) * B + bq) * Hq + hq) * D + ks * 32 + kg * 8);
+      qb[rg][ks] = as_bf16x8(v);
     }
   }
 
-  const int nring = W / 32, ngl = nring + S / 32, nch = ngl + (B + 31) / 32;
-  const Views views{ring_k + int64_t(unit) * W * D, ring_v + int64_t(unit) * D * W,
-                    slot_k + int64_t(unit) * S * D, slot_v + int64_t(unit) * D * S, kb, vb,
-                    ring_pos + int64_t(c) * W, W, S, B, Hkv, c, h, nring, ngl};
+  const int nring = W / 32, ngl = nring + S / 32, nblk = (B + 31) / 32;
   const int nparts = ksplit * KPW, pidx = kidx * KPW + kq;
-  const int per = (nch + nparts - 1) / nparts;
-  const int ch0 = pidx * per, ch1 = min(nch, ch0 + per);
-  const int steps = per;  // same count in every part (empty chunks are skipped)
-  uint16_t* mine = lds + kq * 2 * kStageElems;
-  const bool active = ridx * 16 * RG + g * 16 < M;
+  const uint16_t* rk = ring_k + int64_t(unit) * W * D;
+  const uint16_t* rv = ring_v + int64_t(unit) * D * W;
+  const uint16_t* sk = slot_k + int64_t(unit) * S * D;
+  const uint16_t* sv = slot_v + int64_t(unit) * D * S;
+  const int32_t* rp = ring_pos + int64_t(c) * W;
 
-  Softmax st;
-  st.m = -INFINITY;
-  st.l = 0.f;
+  // this wave's window / slot chunks: pidx, pidx + nparts, ...
+  const int nmine = ngl > pidx ? (ngl - pidx + nparts - 1) / nparts : 0;
+  auto issue = [&](Operands& x, int j) {
+    const int ch = pidx + j * nparts;
+    if (ch < nring)
+      load_operands(x, rk + int64_t(ch) * 32 * D, rv + int64_t(ch) * D * 32, rp + ch * 32, lane);
+    else
+      load_operands(x, sk + int64_t(ch - nring) * 32 * D, sv + int64_t(ch - nring) * D * 32, nullptr, lane);
+  };
+  // the verified block's chunks, token-major rows -> LDS (keys row-major,
+  // values [d][32]); rows past B repeat row B-1 and are masked.  Staged
+  // before the first operand loads are issued, so that waiting for these
+  // loads does not wait for the chunk loads behind them.
+  for (int p = tid; p < nblk * 512; p += NT) {
+    const int bc = p >> 9, piece = p & 511, row = piece >> 4, col = (piece & 15) * 8;
+    const int key = min(bc * 32 + row, B - 1);
+    const int64_t off = ((int64_t(c) * B + key) * Hkv + h) * D + col;
+    const u16x8 kv = *reinterpret_cast<const u16x8*>(kb + off);
+    const u16x8 vv = *reinterpret_cast<const u16x8*>(vb + off);
+    uint16_t* bk = lds + bc * kBlkElems;
+    uint16_t* bv = bk + 32 * kKS;
+    *reinterpret_cast<u16x8*>(bk + row * kKS + col) = kv;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) st.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 8; ++e) bv[(col + e) * kVS + row] = vv[e];
+  }
 
-  // kInFlight chunks are loading into registers while one is computed; the
-  // LDS holds two stages (written at step k, read at step k, rewritten at
-  // step k + 2 after the barrier of step k + 1)
-  Piece<PPT> pc[kInFlight];
+  Operands buf[IF];
 #pragma unroll
-  for (int u = 0; u < kInFlight; ++u)
-    if (ch0 + u < ch1) load_piece(pc[u], views, ch0 + u, t);
-  for (int i = 0; i < steps; i += kInFlight) {
+  for (int u = 0; u < IF; ++u)
+    if (u < nmine) issue(buf[u], u);
+  Softmax st[2];
 #pragma unroll
-    for (int u = 0; u < kInFlight; ++u) {  // step i + u uses registers pc[u]
-      const int stp = i + u, ch = ch0 + stp;
-      Stage sg(mine + (stp & 1) * kStageElems);
-      if (stp < steps) {
-        if (ch < ch1) store_piece(pc[u], sg, ch >= ngl, t);
-        __syncthreads();  // stage ready; the stage written two steps ago was read before
-        if (ch + kInFlight < ch1) load_piece(pc[u], views, ch + kInFlight, t);
-        if (active && ch < ch1) compute_chunk(st, sg, qb, ln, kg);
+  for (int rg = 0; rg < 2; ++rg) {
+    st[rg].m = -INFINITY;
+    st[rg].l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st[rg].o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();  // block chunks staged
+
+  for (int j = 0; j < nmine; j += IF) {
+#pragma unroll
+    for (int u = 0; u < IF; ++u) {
+      if (j + u < nmine) {
+        const uint64_t mask = __ballot(buf[u].pos >= 0);  // bit k: key k of the chunk present
+        compute_chunk(st, buf[u], qb, uint32_t(mask >> (8 * kg)) & 0xFFu);
+        if (j + u + IF < nmine) issue(buf[u], j + u + IF);
       }
     }
   }
+  // block chunk b is chunk ngl + b of the list: its wave continues the turns
+  for (int b = 0; b < nblk; ++b) {
+    if ((ngl + b) % nparts != pidx) continue;
+    const uint16_t* bk = lds + b * kBlkElems;
+    const uint16_t* bv = bk + 32 * kKS;
+    Operands x;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        x.k[mb * 4 + ks] = *reinterpret_cast<const u16x8*>(bk + chunk_key(ln, mb) * kKS + ks * 32 + kg * 8);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) x.v[db] = *reinterpret_cast<const u16x8*>(bv + (db * 16 + ln) * kVS + kg * 8);
+    const int nvalid = B - b * 32 - 8 * kg;  // block keys among the lane group's 8
+    const uint32_t valid8 = nvalid >= 8 ? 0xFFu : nvalid <= 0 ? 0u : ((1u << nvalid) - 1u);
+    compute_chunk(st, x, qb, valid8);
+  }
 
-  // merge the KPW key parts in LDS (reusing the stages), then write
-  float lt = st.l;
-  lt += __shfl_xor(lt, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  // merge the key parts in LDS (reusing the block stages), then write
+  float lt[2];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    lt[rg] = st[rg].l;
+    lt[rg] += __shfl_xor(lt[rg], 16, 64);
+    lt[rg] += __shfl_xor(lt[rg], 32, 64);
+  }
   __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);  // [KPW-1][RG][64 lanes][34]
-  static_assert((KPW - 1) * RG * 64 * 34 * 4 <= KPW * 2 * kStageElems * 2, "merge buffer fits the stages");
+  float* red = reinterpret_cast<float*>(lds);  // [KPW-1][2 row groups][64 lanes][34]
   if (kq > 0) {
-    float* dst = red + (((kq - 1) * RG + g) * 64 + lane) * 34;
-    dst[0] = st.m;
-    dst[1] = lt;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int rg = 0; rg < 2; ++rg) {
+      float* dst = red + (((kq - 1) * 2 + rg) * 64 + lane) * 34;
+      dst[0] = st[rg].m;
+      dst[1] = lt[rg];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[2 + mb * 4 + r] = st.o[mb][r];
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[2 + mb * 4 + r] = st[rg].o[mb][r];
+    }
   }
   __syncthreads();
   if (kq != 0) return;
-  float mx = st.m;
 #pragma unroll
-  for (int k = 1; k < KPW; ++k) mx = fmaxf(mx, red[(((k - 1) * RG + g) * 64 + lane) * 34]);
-  const float w0 = st.m == -INFINITY ? 0.f : exp2_f(st.m - mx);
-  float l = lt * w0;
-  f32x4 o[8];
+  for (int rg = 0; rg < 2; ++rg) {
+    const int row = ridx * 32 + rg * 16 + ln;
+    float mx = st[rg].m;
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb) o[mb] = st.o[mb] * w0;
+    for (int k = 1; k < KPW; ++k) mx = fmaxf(mx, red[(((k - 1) * 2 + rg) * 64 + lane) * 34]);
+    const float w0 = st[rg].m == -INFINITY ? 0.f : exp2_f(st[rg].m - mx);
+    float l = lt[rg] * w0;
+    f32x4 o[8];
 #pragma unroll
-  for (int k = 1; k < KPW; ++k) {
-    const float* src = red + (((k - 1) * RG + g) * 64 + lane) * 34;
-    const float wk = src[0] == -INFINITY ? 0.f : exp2_f(src[0] - mx);
-    l = fmaf(src[1], wk, l);
+    for (int mb = 0; mb < 8; ++mb) o[mb] = st[rg].o[mb] * w0;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int k = 1; k < KPW; ++k) {
+      const float* src = red + (((k - 1) * 2 + rg) * 64 + lane) * 34;
+      const float wk = src[0] == -INFINITY ? 0.f : exp2_f(src[0] - mx);
+      l = fmaf(src[1], wk, l);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[mb][r] = fmaf(src[2 + mb * 4 + r], wk, o[mb][r]);
-  }
-  if (ksplit == 1) {  // the whole key range: write the output
-    if (!row_ok) return;
-    const float il = 1.0f / l;
-    uint16_t* orow = out + ((int64_t(c) * B + row / G) * Hq + h * G + row % G) * D;
+      for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-      *reinterpret_cast<u16x4*>(orow + mb * 16 + kg * 4) =
-          u16x4{bf16_bits(o[mb][0] * il), bf16_bits(o[mb][1] * il), bf16_bits(o[mb][2] * il),
-                bf16_bits(o[mb][3] * il)};
-  } else {  // partial of this key range: m[64] | l[64] | O[64][D] (m in base 2)
-    constexpr int Mpad = 64;
-    float* pbuf = part_out + (int64_t(unit) * ksplit + kidx) * int64_t(Mpad) * (D + 2);
-    if (kg == 0) {
-      pbuf[row] = mx;
-      pbuf[Mpad + row] = l;
+        for (int r = 0; r < 4; ++r) o[mb][r] = fmaf(src[2 + mb * 4 + r], wk, o[mb][r]);
     }
-    float* po = pbuf + 2 * Mpad + int64_t(row) * D;
+    if (row >= M) continue;
+    if (ksplit == 1) {  // the whole key list: write the output
+      const float il = 1.0f / l;
+      uint16_t* orow = out + ((int64_t(c) * B + row / G) * Hq + h * G + row % G) * D;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f32x4*>(po + mb * 16 + kg * 4) = o[mb];
+      for (int mb = 0; mb < 8; ++mb)
+        *reinterpret_cast<u16x4*>(orow + mb * 16 + kg * 4) =
+            u16x4{bf16_bits(o[mb][0] * il), bf16_bits(o[mb][1] * il), bf16_bits(o[mb][2] * il),
+                  bf16_bits(o[mb][3] * il)};
+    } else {  // partial of this key range (m in base 2)
+      constexpr int Mpad = 64;
+      float* pbuf = part_out + (int64_t(unit) * ksplit + kidx) * int64_t(Mpad) * (D + 2);
+      if (kg == 0) {
+        pbuf[row] = mx;
+        pbuf[Mpad + row] = l;
+      }
+      float* po = pbuf + 2 * Mpad + int64_t(row) * D;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f32x4*>(po + mb * 16 + kg * 4) = o[mb];
+    }
   }
 }
 
-// merge the key halves: one thread per (unit, query row, 4 dimensions)
+// merge the key ranges: one thread per (unit, query row, 4 dimensions)
 __global__ __launch_bounds__(kThreads) void draft_combine(
     const float* __restrict__ part, uint16_t* __restrict__ out, int Hq, int Hkv, int B,
     int halves, int Mpad, int units) {
@@ -416,11 +425,10 @@ __global__ __launch_bounds__(kThreads) void draft_generic(
     if (key < N && (key >= W || ring_pos[int64_t(c) * W + key] >= 0)) {
       float dot = 0.f;
       if (key < W) {
-        for (int e = 0; e < D; ++e)
-          dot = fmaf(qs[e], Ty::load(ring_k, (int64_t(unit) * W + key) * D + e), dot);
+        for (int e = 0; e < D; ++e) dot = fmaf(qs[e], Ty::load(ring_k, key_index(unit, W, D, key, e)), dot);
       } else if (key < W + S) {
         for (int e = 0; e < D; ++e)
-          dot = fmaf(qs[e], Ty::load(slot_k, (int64_t(unit) * S + key - W) * D + e), dot);
+          dot = fmaf(qs[e], Ty::load(slot_k, key_index(unit, S, D, key - W, e)), dot);
       } else {
         for (int e = 0; e < D; ++e)
           dot = fmaf(qs[e], Ty::load(kb, ((int64_t(c) * B + key - W - S) * Hkv + h) * D + e), dot);
@@ -483,29 +491,20 @@ ls_status launch_draft(const ls_dims& d, const ls_state& st, const void* q, cons
                        const void* vb, void* out, hipStream_t stream) {
   if (d.dtype == LS_BF16) {
     const int units = d.C * d.Hkv;
-    const int M = d.B * (d.Hq / d.Hkv);
-    const int ksplit = draft_halves(d);  // 1 under the row split
+    const int rsplit = draft_row_splits(d), ksplit = draft_halves(d);
     float* part = reinterpret_cast<float*>(static_cast<char*>(st.workspace) + ws_layout(d, 1).draft_part);
-    const uint16_t *q16 = static_cast<const uint16_t*>(q), *kb16 = static_cast<const uint16_t*>(kb),
-                   *vb16 = static_cast<const uint16_t*>(vb);
-    const uint16_t *rk = static_cast<const uint16_t*>(st.ring_k), *rv = static_cast<const uint16_t*>(st.ring_v),
-                   *sk = static_cast<const uint16_t*>(st.slot_k), *sv = static_cast<const uint16_t*>(st.slot_v);
-    uint16_t* o16 = static_cast<uint16_t*>(out);
-    if (draft_row_split(d)) {
-      // query rows in two halves of 32 (2 row groups x 4 key parts), all keys each
-      const int rsplit = int(cdiv(M, 32));
-      hipLaunchKernelGGL((draft_mfma<2, 4>), dim3(units * rsplit), dim3(512), 0, stream, q16, kb16, vb16,
-                         rk, rv, st.ring_pos, sk, sv, o16, part, d.Hq, d.Hkv, d.W, d.S, d.B, units, 1);
-      return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
-    }
-    hipLaunchKernelGGL((draft_mfma<4, 2>), dim3(units * ksplit), dim3(512), 0, stream, q16, kb16, vb16,
-                       rk, rv, st.ring_pos, sk, sv, o16, part, d.Hq, d.Hkv, d.W, d.S, d.B, units, ksplit);
+    hipLaunchKernelGGL((draft_direct<kKPW, kInFlight>), dim3(units * ksplit * rsplit), dim3(64 * kKPW), 0,
+                       stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kb),
+                       static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(st.ring_k),
+                       static_cast<const uint16_t*>(st.ring_v), st.ring_pos,
+                       static_cast<const uint16_t*>(st.slot_k), static_cast<const uint16_t*>(st.slot_v),
+                       static_cast<uint16_t*>(out), part, d.Hq, d.Hkv, d.W, d.S, d.B, units, ksplit);
     if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
     if (ksplit > 1) {
       const int Mpad = 64;
       const int64_t threads = int64_t(units) * Mpad * (128 / 4);
       hipLaunchKernelGGL(draft_combine, dim3(unsigned(cdiv(threads, kThreads))), dim3(kThreads), 0,
-                         stream, part, o16, d.Hq, d.Hkv, d.B, ksplit, Mpad, units);
+                         stream, part, static_cast<uint16_t*>(out), d.Hq, d.Hkv, d.B, ksplit, Mpad, units);
     }
     return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
   }

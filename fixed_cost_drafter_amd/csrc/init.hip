@@ -410,7 +410,7 @@ __global__ __launch_bounds__(kThreads) void init_finalize(
     sum_n[ni] = a;
     const int j = j0 + jj;
     if (e < D)
-      Ty::store(slot_k, (int64_t(unit) * S + j) * D + e, a * s_inv_l[jj]);
+      Ty::store(slot_k, key_index(unit, S, D, j, e), a * s_inv_l[jj]);
     else  // values in key tiles of 32 (one tile of S keys when S % 32 != 0)
       Ty::store(slot_v,
                 S % 32 == 0 ? ((int64_t(unit) * (S >> 5) + (j >> 5)) * D + (e - D)) * 32 + (j & 31)
@@ -422,8 +422,9 @@ __global__ __launch_bounds__(kThreads) void init_finalize(
   // p mod W == ws, if p >= max(0, L0 - W) (else it is empty: zeros, -1).
   // This workgroup fills the 32-slot key tiles kt = tile, tile + NT, ...:
   // every key and value piece of a tile is loaded first (several 16-byte
-  // loads in flight per thread), keys are stored as they are, values pass
-  // through LDS and leave as 16-byte pieces of the tile [d][32].
+  // loads in flight per thread), each key piece goes straight to its place
+  // in the key layout (key_index), values pass through LDS and leave as
+  // 16-byte pieces of the tile [d][32].
   auto newest_of = [&](int ws) -> int {  // -1: empty slot
     const int back = ((L0 - 1 - ws) % W + W) % W;
     return max(L0 - 1 - back, -1);
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void init_finalize(
       for (int q = 0; q < NPT; ++q) {
         const int pc = tid + q * kThreads, i = pc / P16, e = pc % P16;
         if (pc >= NP) break;
-        reinterpret_cast<uint4*>(ring_k + (int64_t(unit) * W + kt * 32 + i) * D)[e] = kr[q];
+        *reinterpret_cast<uint4*>(ring_k + key_index(unit, W, D, kt * 32 + i, e * E16)) = kr[q];
         reinterpret_cast<uint4*>(vls + i * VS)[e] = vr[q];
       }
       if (h == 0 && tid < 32) ring_pos[int64_t(c) * W + kt * 32 + tid] = newest_of(kt * 32 + tid);
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void init_finalize(
       const int p = newest_of(wsl);
       const int64_t src = ((int64_t(c) * rows_stride + max(p, 0)) * Hkv + h) * D;
       for (int e = tid; e < D; e += kThreads) {
-        ring_k[(int64_t(unit) * W + wsl) * D + e] = p >= 0 ? kp[src + e] : typename Ty::T(0);
+        ring_k[key_index(unit, W, D, wsl, e)] = p >= 0 ? kp[src + e] : typename Ty::T(0);
         ring_v[(int64_t(unit) * D + e) * W + wsl] = p >= 0 ? vp[src + e] : typename Ty::T(0);
       }
       if (h == 0 && tid == 0) ring_pos[int64_t(c) * W + wsl] = p;

@@ -44,6 +44,13 @@
  * The values of the window and of the slots are kept in key tiles of 32
  * (per tile: [d][32]) so that the drafter's P.V product reads contiguous
  * keys per dimension and each 32-key tile is one contiguous block.
+ * With d = 128 the keys of the window and of the slots are kept in tiles of
+ * 32 keys too, in the order in which the drafter's 16x16x32 MFMA reads its
+ * A operand: key k = 8a + 4b + r (a < 4, b < 2, r < 4) and dimension
+ * e = 32s + 8g + i (s < 4, g < 4, i < 8) of a tile sit at element
+ * ((((b*4 + s)*4 + g)*16 + 4a + r)*8 + i of the tile's 32*128 elements.
+ * Other d keep keys row-major.  The state is the library's own: callers
+ * allocate it, move it as a whole and never read it element by element.
  */
 #ifndef LONGSPARK_H
 #define LONGSPARK_H
@@ -86,7 +93,8 @@ typedef struct ls_dims {
 /* The drafter's fixed-size context state (Fig. 2 (b)) plus parameters.
  * Its size is independent of the prefix length. */
 typedef struct ls_state {
-  void* ring_k;             /* [C, Hkv, W, d] dtype: window keys            */
+  void* ring_k;             /* [C, Hkv, W, d] dtype: window keys (32-key
+                               tiles in MFMA operand order when d = 128)    */
   void* ring_v;             /* dtype window values in key tiles of 32:
                                [C, Hkv, W/32, d, 32] ([C, Hkv, d, W] when
                                W % 32 != 0)                                 */
@@ -95,7 +103,8 @@ typedef struct ls_state {
   float* sum_m;             /* [C, Hkv, S] running max m (natural log units) */
   float* sum_l;             /* [C, Hkv, S] denominator l                     */
   float* sum_n;             /* [C, Hkv, S, 2d] numerator n: keys | values    */
-  void* slot_k;             /* [C, Hkv, S, d] dtype: n[:d] / l               */
+  void* slot_k;             /* [C, Hkv, S, d] dtype: n[:d] / l (32-key
+                               tiles in MFMA operand order when d = 128)    */
   void* slot_v;             /* dtype n[d:] / l in key tiles of 32:
                                [C, Hkv, S/32, d, 32] ([C, Hkv, d, S] when
                                S % 32 != 0)                                 */

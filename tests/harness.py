@@ -62,9 +62,12 @@ def compare_state(runner, ost: O.OracleState, dtype, heads=None):
     """GPU state vs oracle state; ``heads`` restricts the float checks."""
     snap = runner.snapshot()
     # the library keeps window and slot values in key tiles [rows/tw][d][tw]
-    from fixed_cost_drafter_amd.binding import values_to_rows
+    # and, at d = 128, keys in 32-key tiles in MFMA operand order
+    from fixed_cost_drafter_amd.binding import keys_to_rows, values_to_rows
     snap["ring_v"] = values_to_rows(snap["ring_v"])
     snap["slot_v"] = values_to_rows(snap["slot_v"])
+    snap["ring_k"] = keys_to_rows(snap["ring_k"])
+    snap["slot_k"] = keys_to_rows(snap["slot_k"])
     exact("seq_len", snap["seq_len"].astype(np.int64), ost.seq_len)
     exact("ring_pos", snap["ring_pos"], ost.ring_pos)
     exact("ring_k", snap["ring_k"], ost.ring_k)

@@ -217,3 +217,30 @@ def test_verify_attention_validation(LB):
     assert call(wsb=ws - 1) == 4 or ws == 0              # workspace too small
     wide = _dims(LB, Hq=64, Hkv=8, B=16)                 # (B+1)*G = 136 > 128 rows
     assert L.ls_verify_attention(ctypes.byref(wide), *args()) == 2
+
+
+def test_key_tile_order(LB):
+    """The stored key tile is a permutation that keeps 8 dimensions of a key
+    together and puts each 16x16x32 A-operand load in 1 KB of consecutive
+    16-byte pieces (instruction mb*4 + ks, lane kg*16 + m reads key
+    8*(m//4) + 4*mb + m%4, dimensions 32*ks + 8*kg ..)."""
+    import numpy as np
+    o = LB.key_tile_order()
+    assert sorted(o.ravel().tolist()) == list(range(32 * 128))
+    assert np.all(np.diff(o.reshape(32, 16, 8), axis=-1) == 1)
+    for mb in range(2):
+        for ks in range(4):
+            for kg in range(4):
+                for m in range(16):
+                    key = 8 * (m // 4) + 4 * mb + m % 4
+                    assert o[key, 32 * ks + 8 * kg] == ((mb * 4 + ks) * 64 + kg * 16 + m) * 8
+    # host de-tiling inverts the layout; other shapes pass through
+    rng = np.random.default_rng(5)
+    rows = rng.integers(0, 1 << 16, size=(2, 3, 64, 128), dtype=np.uint16)
+    stored = np.empty_like(rows)
+    t = stored.reshape(2, 3, 2, 32 * 128)
+    t[..., o] = rows.reshape(2, 3, 2, 32, 128)
+    assert np.array_equal(LB.keys_to_rows(stored), rows)
+    small = rng.random((1, 2, 48, 128)).astype(np.float32)
+    assert LB.keys_to_rows(small) is small
+    assert not LB.key_tiled(64, 64) and LB.key_tiled(1024, 128)
