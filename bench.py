@@ -83,7 +83,7 @@ ENTRY_KERNELS = {
     "verify": ("verify_partial", "verify_finalize"),
     "verify_sampling": ("samp_stats", "samp_decide", "samp_sums", "samp_draw"),
     "append": ("append_kernel",),
-    "draft": ("draft_mfma", "draft_combine", "draft_generic"),
+    "draft": ("draft_direct", "draft_combine", "draft_generic"),
     "verify_attention": ("attn_mfma_partial", "attn_combine", "attn_generic"),
     "init": ("init_mfma_partial", "init_generic_partial", "init_finalize"),
 }
