@@ -50,6 +50,96 @@ struct Vec16<BF16> {
   __device__ static inline float get(const V& v, int i) { return bf16_to_f32(v[i]); }
 };
 
+#ifndef LS_VERIFY_PACKED
+#define LS_VERIFY_PACKED 1
+#endif
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// two bf16 (one 32-bit word) -> two 16-bit keys whose unsigned order is the
+// values' order: positive h -> h | 0x8000, negative h -> ~h.  -0 lands just
+// below +0 (0x7FFF vs 0x8000); the index search merges the two.
+__device__ __forceinline__ u16x2 order16x2(uint32_t x) {
+  const i16x2 h = __builtin_bit_cast(i16x2, x);
+  const u16x2 flip = __builtin_bit_cast(u16x2, i16x2(h >> 15)) | u16x2{0x8000, 0x8000};
+  return __builtin_bit_cast(u16x2, x) ^ flip;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, uint32_t(__shfl_xor(int(v), o, 64)));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, uint32_t(__shfl_xor(int(v), o, 64)));
+  return v;
+}
+
+// bf16 rows with 16-byte aligned chunks: the chunk's 8192 logits are one
+// 16-byte load per thread per 2048 logits (all in flight at once).  The
+// values are compared as packed 16-bit integer keys (two logits per
+// instruction), the workgroup agrees on the maximum key, and only the
+// threads that hold it search their registers for its lowest index.
+__device__ __forceinline__ uint64_t chunk_argmax_bf16(const uint16_t* __restrict__ x, int begin, int end,
+                                                      int tid) {
+  constexpr int U = kVerifyChunk / 8 / kThreads;
+  static_assert(U * 8 * kThreads == kVerifyChunk, "one load per thread per 2048 logits");
+  __shared__ uint32_t red[kThreads / 64];
+  const u32x4v* xv = reinterpret_cast<const u32x4v*>(x + begin);
+  const int nvec = (end - begin) / 8;
+  u32x4v buf[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int v = u * kThreads + tid;
+    buf[u] = v < nvec ? __builtin_nontemporal_load(xv + v) : u32x4v{0, 0, 0, 0};
+  }
+  u16x2 best = {0, 0};  // 0: below every key of a real value
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (u * kThreads + tid < nvec) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) best = __builtin_elementwise_max(best, order16x2(buf[u][w]));
+    }
+  const uint32_t tmax = max(uint32_t(best[0]), uint32_t(best[1]));
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t M = wave_max_u32(tmax);
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) M = max(M, red[w]);
+  __syncthreads();
+  // +0 and -0 are the same value: a maximum of either sign matches both
+  const bool zero = M == 0x8000u || M == 0x7FFFu;
+  const uint32_t lo = zero ? 0x7FFFu : M, hi = zero ? 0x8000u : M;
+  uint32_t idx = 0xFFFFFFFFu;
+  if (tmax >= lo && tmax <= hi && M != 0u) {
+    // this thread's logits in index order: vector u*kThreads + tid, then word, then half
+#pragma unroll
+    for (int u = U - 1; u >= 0; --u)
+      if (u * kThreads + tid < nvec) {
+#pragma unroll
+        for (int w = 3; w >= 0; --w) {
+          const u16x2 k = order16x2(buf[u][w]);
+          const int i0 = begin + (u * kThreads + tid) * 8 + 2 * w;
+          if (k[1] >= lo && k[1] <= hi) idx = uint32_t(i0 + 1);
+          if (k[0] >= lo && k[0] <= hi) idx = uint32_t(i0);
+        }
+      }
+  }
+  idx = wave_min_u32(idx);
+  if (lane == 0) red[wave] = idx;
+  __syncthreads();
+  idx = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) idx = min(idx, red[w]);
+  if (idx == 0xFFFFFFFFu) return 0ull;
+  const uint32_t h = M >= 0x8000u ? (M ^ 0x8000u) : (~M & 0xFFFFu);  // the bf16 bits back
+  return make_key(bf16_to_f32(uint16_t(h)), idx);
+}
+
 template <typename Ty>
 __global__ __launch_bounds__(kThreads) void verify_partial(
     const typename Ty::T* __restrict__ logits, uint64_t* __restrict__ part, int V, int nsplit,
@@ -62,6 +152,13 @@ __global__ __launch_bounds__(kThreads) void verify_partial(
   const int begin = split * chunk;
   const int end = min(V, begin + chunk);
 
+  if constexpr (Ty::kBytes == 2 && LS_VERIFY_PACKED) {
+    if (vec_ok) {
+      const uint64_t k = chunk_argmax_bf16(x, begin, end, tid);
+      if (tid == 0) part[int64_t(row) * nsplit + split] = k;
+      return;
+    }
+  }
   float best = -INFINITY;
   uint32_t best_i = 0xFFFFFFFFu;
   if (vec_ok) {
@@ -84,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void verify_partial(
 #pragma unroll
           for (int e = 0; e < VT::N; ++e) {
             float f = VT::get(buf[u], e);
-            if (f > best) {
+            if (f > best || best_i == 0xFFFFFFFFu) {  // the first element counts even at -inf
               best = f;
               best_i = uint32_t(begin + v * VT::N + e);
             }
@@ -95,12 +192,12 @@ __global__ __launch_bounds__(kThreads) void verify_partial(
     // tail that does not fill a vector (only in the last chunk)
     for (int i = begin + nvec * VT::N + tid; i < end; i += kThreads) {
       float f = Ty::load(x, i);
-      if (f > best) { best = f; best_i = uint32_t(i); }
+      if (f > best || best_i == 0xFFFFFFFFu) { best = f; best_i = uint32_t(i); }
     }
   } else {
     for (int i = begin + tid; i < end; i += kThreads) {
       float f = Ty::load(x, i);
-      if (f > best) { best = f; best_i = uint32_t(i); }
+      if (f > best || best_i == 0xFFFFFFFFu) { best = f; best_i = uint32_t(i); }
     }
   }
 

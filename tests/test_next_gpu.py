@@ -44,29 +44,44 @@ def test_draft_argmax_parity(name):
         H.exact(f"draft_tok {name} #{k}", LB.to_host(out), O.draft_argmax(drafter))
 
 
-def test_draft_argmax_edge_rows():
-    """All-equal rows, -0 against +0, the maximum at the last index or in the tail."""
+@pytest.mark.parametrize("V", [20001, 20000])
+def test_draft_argmax_edge_rows(V):
+    """All-equal rows, -0 against +0, negative rows, the maximum at the last
+    index or across a chunk boundary.  V = 20000 keeps rows 16-byte aligned
+    (the packed 16-bit key path); V = 20001 does not (the scalar path)."""
     import torch
     from fixed_cost_drafter_amd import binding as LB
-    wl = SMALL["bf16_s64_ragged"].with_(name="argmax_edges", C=1, B=6, V=20001)
+    wl = SMALL["bf16_s64_ragged"].with_(name="argmax_edges", C=1, B=12, V=V)
     H.log(f"CASE draft_argmax edges V={wl.V}")
-    x = np.zeros((1, 6, wl.V), dtype=np.float32)
+    x = np.zeros((1, 12, wl.V), dtype=np.float32)
     x[0, 1, :] = -0.0
     x[0, 1, 7] = 0.0                       # +0 after -0s: index 0 still wins
     x[0, 2, :] = -1.0
-    x[0, 2, wl.V - 1] = 2.0                # maximum in the ragged tail
-    x[0, 3, 16384] = 3.0                   # first element of the second chunk
-    x[0, 3, 16383] = 3.0                   # ... tied with the last of the first
+    x[0, 2, wl.V - 1] = 2.0                # maximum at the last index
+    x[0, 3, 16384] = 3.0                   # first element of a later chunk ...
+    x[0, 3, 16383] = 3.0                   # ... tied with the last of the one before
     x[0, 4, ::2] = 1.5                     # every even index ties
     x[0, 5, 12345] = 1e-30                 # a tiny positive against zeros
+    x[0, 6, :] = -1.0
+    x[0, 6, 100] = -0.0
+    x[0, 6, 50] = 0.0                      # +0 before -0, the rest negative: 50
+    x[0, 7, :] = -1.0
+    x[0, 7, 200] = 0.0
+    x[0, 7, 150] = -0.0                    # -0 before +0: 150
+    x[0, 8, :] = -2.0 - np.arange(wl.V) % 97   # all negative: the -2s tie, index 0
+    x[0, 9, :] = -np.inf
+    x[0, 9, wl.V - 2] = -3.0               # everything -inf but one
+    x[0, 10, :] = -np.inf                  # all -inf: index 0
+    x[0, 11, 8191] = 5.0
+    x[0, 11, 8192] = 5.0                   # tie across the 8192-logit chunk boundary
     bits = WLM.f32_to_bf16_bits(x)
     st = _state(wl)
-    out = torch.empty((1, 6), dtype=torch.int32, device="cuda")
+    out = torch.empty((1, 12), dtype=torch.int32, device="cuda")
     st.draft_argmax(LB.to_device(bits), out)
     torch.cuda.synchronize()
     got = LB.to_host(out)
     H.exact("edge rows", got, O.draft_argmax(bits))
-    assert got.tolist() == [[0, 0, wl.V - 1, 16383, 0, 12345]]
+    assert got.tolist() == [[0, 0, wl.V - 1, 16383, 0, 12345, 50, 150, 0, wl.V - 2, 0, 8191]]
 
 
 @pytest.mark.parametrize("dtype,H_", [("bf16", 4096), ("f32", 37), ("bf16", 7)])
