@@ -9,13 +9,13 @@
 // head (G = Hq/Hkv) share its keys, so they form one query tile.
 //
 // bf16, d = 128 (draft_direct).  A workgroup takes one KV head unit, 32 of
-// its query rows (two row groups of 16) and one key range; its KPW waves are
-// KPW key parts.  The keys are cut in 32-key chunks that never straddle two
-// views (W and S are multiples of 32; the block gets its own chunks), and the
-// chunks of a range are dealt to its waves in turn.  Each wave loads every
-// MFMA operand of its chunks straight from memory into registers, IF chunks
-// ahead (KPW = 8 waves, two per SIMD, with IF = 1: about 64 registers per
-// lane hold the chunk in flight), with no LDS and no barrier in the loop:
+// its query rows (two row groups of 16) and one key range; its KPW = 8
+// waves (two per SIMD) are 8 key parts.  The keys are cut in 32-key chunks
+// that never straddle two views (W and S are multiples of 32; the block
+// gets its own chunks), and the chunks of a range are dealt to its waves in
+// turn.  Each wave loads every MFMA operand of its window and slot chunks
+// straight from memory into registers, with no LDS and no barrier in the
+// loop:
 //   S^T = K Q^T : A = 16 keys x 32 dimensions; the window and slot keys are
 //                 stored in this operand order (tiles of 32 keys), so each
 //                 64-lane load is 1 KB contiguous; B = the query rows
@@ -23,13 +23,20 @@
 //   O^T += V^T P^T : A = 16 dimensions x 32 keys from the value tiles
 //                 [d][32] (1 KB contiguous per load); B = the softmax
 //                 weights from the S^T output layout, rounded to bf16.
-// Every loaded operand serves both row groups.  The verified block arrives
-// token-major from the caller; its (at most two) chunks are staged in LDS
-// once per workgroup and computed by the wave whose turn they fall on.  The
-// online softmax lives in registers (per query row, per lane) in base 2; the
-// key parts merge (m, l, O) in LDS at the end, and key ranges, when there is
-// more than one, through the workspace and draft_combine (a kernel boundary,
-// no device-scope fence).
+// A wave holds one chunk's key half and value half (8 loads each); the next
+// chunk's keys are requested as soon as the current scores are formed and
+// its values as soon as the current P.V is issued, so one chunk is always
+// in flight.  No load sits behind a branch, so the compiler waits only for
+// the loads a step uses.  Every loaded operand serves both row groups.  The
+// verified block arrives token-major from the caller; each of its (at most
+// two) chunks is loaded by the wave whose turn it falls on, at the start,
+// transposed through that wave's own LDS region and computed first, while
+// the wave's other loads are in flight.  The online softmax lives in
+// registers (per query row, per lane) in base 2; the key parts merge
+// (m, l, O) in LDS at the end, each wave combining 2 of the 16 (row group,
+// dimension block) pieces, and key ranges, when there is more than one,
+// through the workspace and draft_combine (a kernel boundary, no
+// device-scope fence).
 // f32 (draft_generic): one workgroup per query row, plain loop (small shapes).
 #include "common.hpp"
 #include "launch.hpp"
@@ -41,11 +48,7 @@ constexpr int kThreads = 256;
 #ifndef LS_DRAFT_KPW
 #define LS_DRAFT_KPW 8
 #endif
-#ifndef LS_DRAFT_INFLIGHT
-#define LS_DRAFT_INFLIGHT 1
-#endif
 constexpr int kKPW = LS_DRAFT_KPW;             // key parts (waves) per workgroup
-constexpr int kInFlight = LS_DRAFT_INFLIGHT;   // chunks loading per wave
 // Scores are kept in base-2 units (log2(e) folded into the 1/sqrt(d) scale),
 // so every softmax weight is one v_exp_f32 (2^x).
 constexpr float kScale2 = 0.08838834764831845f * 1.4426950408889634f;  // log2(e)/sqrt(128)
@@ -69,24 +72,33 @@ constexpr int kKS = 128 + 8;   // key row stride (bf16)
 constexpr int kVS = 32 + 8;    // value row stride (bf16)
 constexpr int kBlkElems = 32 * kKS + 128 * kVS;
 
-// the MFMA operands of one 32-key chunk for one wave
-struct Operands {
-  u16x8 k[8];  // A operands of S^T = K Q^T, [mb*4 + ks]
-  u16x8 v[8];  // A operands of O^T += V^T P^T, [dimension block of 16]
-  int pos;     // ring_pos of key (lane & 31); 0 for the slots
+// Half of one 32-key chunk's MFMA operands for one wave: the 8 key loads
+// (A operands of S^T = K Q^T, [mb*4 + ks]) or the 8 value loads (A operands
+// of O^T += V^T P^T, [dimension block of 16]).
+struct Half {
+  u16x8 r[8];
+  int pos;  // key halves: ring_pos of key (lane & 31); 0 for the slots
 };
 
-// kt: the chunk's key tile (operand order), vt: its value tile [d][32],
-// rp: its 32 ring positions (nullptr for the slots: always occupied)
-__device__ __forceinline__ void load_operands(Operands& x, const uint16_t* kt, const uint16_t* vt,
-                                              const int32_t* rp, int lane) {
+// kt: the chunk's key tile (operand order); pp: 32 ints to read the
+// positions from (the chunk's ring_pos, or any readable 128 bytes for the
+// slots, whose positions are then taken as 0 = occupied).  The position
+// loads first, so the occupancy mask never waits for the operands behind it.
+// No branch around any load: the compiler can then count the loads in
+// flight exactly and wait only for the ones a step needs.
+__device__ __forceinline__ void load_keys(Half& x, const uint16_t* kt, const int32_t* pp, bool ring,
+                                          int lane) {
+  const int p = pp[lane & 31];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x.r[i] = *reinterpret_cast<const u16x8*>(kt + (i * 64 + lane) * 8);
+  x.pos = ring ? p : 0;
+}
+// vt: the chunk's value tile [d][32]
+__device__ __forceinline__ void load_values(Half& x, const uint16_t* vt, int lane) {
   const int ln = lane & 15, kg = lane >> 4;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) x.k[i] = *reinterpret_cast<const u16x8*>(kt + (i * 64 + lane) * 8);
-#pragma unroll
   for (int db = 0; db < 8; ++db)
-    x.v[db] = *reinterpret_cast<const u16x8*>(vt + (db * 16 + ln) * 32 + kg * 8);
-  x.pos = rp ? rp[lane & 31] : 0;
+    x.r[db] = *reinterpret_cast<const u16x8*>(vt + (db * 16 + ln) * 32 + kg * 8);
 }
 
 // Online softmax state of one row group of 16 query rows.
@@ -95,19 +107,22 @@ struct Softmax {
   f32x4 o[8];
 };
 
-// scores of one row group for the chunk (s[mb][r] is key 8kg + 4mb + r) ->
-// lazy online softmax update; returns the bf16 weights as the P^T operand
-__device__ __forceinline__ bf16x8 softmax_chunk(Softmax& st, f32x4 (&s)[2], uint32_t valid8) {
+// raw scores of one row group for the chunk (s[mb][r] is key 8kg + 4mb + r)
+// -> lazy online softmax update in base 2; returns the bf16 weights as the
+// P^T operand.  valid8 bit e: key 8kg + e is present (all set for full
+// chunks, where masking is skipped).
+__device__ __forceinline__ bf16x8 softmax_chunk(Softmax& st, f32x4 (&s)[2], uint32_t valid8, bool full) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
-  float tmax = -INFINITY;
+  if (!full) {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s[mb][r] = ((valid8 >> (4 * mb + r)) & 1u) ? s[mb][r] * kScale2 : -INFINITY;
-      tmax = fmaxf(tmax, s[mb][r]);
-    }
+      for (int r = 0; r < 4; ++r)
+        if (!((valid8 >> (4 * mb + r)) & 1u)) s[mb][r] = -INFINITY;
+  }
+  float tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
   // the row's max over the 4 lane groups (lanes ln, ln+16, ln+32, ln+48):
   // swapping a register with itself across row pairs / halves leaves the
   // partner's value in one of the two results
@@ -117,6 +132,7 @@ __device__ __forceinline__ bf16x8 softmax_chunk(Softmax& st, f32x4 (&s)[2], uint
     const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
     tmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
   }
+  tmax *= kScale2;  // the scale is positive: max of the scaled scores
   // lazy rescale: the reference max moves only when some row's max grows by
   // more than kRescale, so weights stay <= e^8 and the O / l rescale is
   // skipped in the steady state
@@ -129,13 +145,14 @@ __device__ __forceinline__ bf16x8 softmax_chunk(Softmax& st, f32x4 (&s)[2], uint
     for (int mb = 0; mb < 8; ++mb) st.o[mb] *= scale;
   }
   const float m_use = st.m == -INFINITY ? 0.f : st.m;
-  // weights rounded to bf16 in pairs; l sums the same rounded weights
+  // weights 2^(s*scale - m) rounded to bf16 in pairs; l sums the same
+  // rounded weights
   uint32_t pw[4];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; r += 2) {
-      const f32x2 e2 = {exp2_f(s[mb][r] - m_use), exp2_f(s[mb][r + 1] - m_use)};
+      const f32x2 e2 = {exp2_f(fmaf(s[mb][r], kScale2, -m_use)), exp2_f(fmaf(s[mb][r + 1], kScale2, -m_use))};
       pw[mb * 2 + r / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(e2, bf16x2));
     }
   const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
@@ -147,11 +164,8 @@ __device__ __forceinline__ bf16x8 softmax_chunk(Softmax& st, f32x4 (&s)[2], uint
   return as_bf16x8(__builtin_bit_cast(u16x8, uint4{pw[0], pw[1], pw[2], pw[3]}));
 }
 
-// one chunk for both row groups: S^T = K Q^T, softmax, O^T += V^T P^T.
-// valid8 bit e: key 8kg + e of the chunk is present.
-__device__ __forceinline__ void compute_chunk(Softmax (&st)[2], const Operands& x,
-                                              const bf16x8 (&qb)[2][4], uint32_t valid8) {
-  f32x4 s[2][2];
+// S^T = K Q^T for both row groups (raw dot products)
+__device__ __forceinline__ void chunk_scores(f32x4 (&s)[2][2], const Half& k, const bf16x8 (&qb)[2][4]) {
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
@@ -162,24 +176,30 @@ __device__ __forceinline__ void compute_chunk(Softmax (&st)[2], const Operands& 
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg)
-        s[rg][mb] = mfma16x16x32(as_bf16x8(x.k[mb * 4 + ks]), qb[rg][ks], s[rg][mb]);
-  bf16x8 pk[2];
-#pragma unroll
-  for (int rg = 0; rg < 2; ++rg) pk[rg] = softmax_chunk(st[rg], s[rg], valid8);
+        s[rg][mb] = mfma16x16x32(as_bf16x8(k.r[mb * 4 + ks]), qb[rg][ks], s[rg][mb]);
+}
+
+// O^T += V^T P^T for both row groups
+__device__ __forceinline__ void chunk_pv(Softmax (&st)[2], const Half& v, const bf16x8 (&pk)[2]) {
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int rg = 0; rg < 2; ++rg) st[rg].o[db] = mfma16x16x32(as_bf16x8(x.v[db]), pk[rg], st[rg].o[db]);
+    for (int rg = 0; rg < 2; ++rg) st[rg].o[db] = mfma16x16x32(as_bf16x8(v.r[db]), pk[rg], st[rg].o[db]);
 }
 
 // Workgroup = (unit, 32 query rows ridx, key range kidx): blockIdx =
 // unit + units * (kidx + ksplit * ridx), so the workgroups of one unit sit
 // on one XCD when units is a multiple of 8 and the keys they share are
-// fetched from HBM once.  Key range kidx's chunks are those with
-// chunk % (ksplit*KPW) in [kidx*KPW, kidx*KPW + KPW); wave kq takes residue
-// kidx*KPW + kq.  With ksplit = 1 the output is written here, else the
-// range's (m, l, O) go to the workspace: [unit][kidx][m[64] | l[64] | O[64][d]].
-template <int KPW, int IF>
+// fetched from HBM once.  The window and slot chunks of key range kidx are
+// those with chunk % (ksplit*KPW) in [kidx*KPW, kidx*KPW + KPW); wave kq
+// takes residue kidx*KPW + kq.  Block chunk b (chunk ngl + b of the list)
+// belongs to the wave whose turn it falls on, which stages it in its own
+// LDS region and computes it before its other chunks, while their first
+// loads are in flight.  kEvery: every wave has at least one window or slot
+// chunk (checked by the host), so the first loads need no branch.  With
+// ksplit = 1 the output is written here, else the range's (m, l, O) go to
+// the workspace: [unit][kidx][m[64] | l[64] | O[64][d]].
+template <int KPW, bool kEvery>
 __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, const uint16_t* __restrict__ ring_k,
@@ -187,8 +207,9 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     const uint16_t* __restrict__ slot_k, const uint16_t* __restrict__ slot_v,
     uint16_t* __restrict__ out, float* __restrict__ part_out, int Hq, int Hkv, int W, int S, int B,
     int units, int ksplit) {
-  constexpr int D = 128, NT = 64 * KPW;
-  constexpr int kRedBytes = (KPW - 1) * 2 * 64 * 34 * 4;
+  constexpr int D = 128;
+  static_assert(16 % KPW == 0, "the merge deals 16 (row group, dimension block) pieces to the waves");
+  constexpr int kRedBytes = KPW * 2 * 64 * 34 * 4;
   constexpr int kLdsBytes = (2 * kBlkElems * 2 > kRedBytes) ? 2 * kBlkElems * 2 : kRedBytes;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsBytes / 2];
 
@@ -196,8 +217,51 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
   const int kidx = split % ksplit, ridx = split / ksplit;
   const int c = unit / Hkv, h = unit % Hkv;
   const int G = Hq / Hkv, M = B * G;
-  const int tid = threadIdx.x, kq = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int kq = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int ln = lane & 15, kg = lane >> 4;
+
+  const int nring = W / 32, ngl = nring + S / 32, nblk = (B + 31) / 32;
+  const int nparts = ksplit * KPW, pidx = kidx * KPW + kq;
+  const uint16_t* rk = ring_k + int64_t(unit) * W * D;
+  const uint16_t* rv = ring_v + int64_t(unit) * D * W;
+  const uint16_t* sk = slot_k + int64_t(unit) * S * D;
+  const uint16_t* sv = slot_v + int64_t(unit) * D * S;
+  const int32_t* rp = ring_pos + int64_t(c) * W;
+  const int32_t* any_ints = reinterpret_cast<const int32_t*>(q);  // >= 256 readable bytes
+
+  // this wave's window / slot chunks: pidx, pidx + nparts, ...
+  const int nmine = ngl > pidx ? (ngl - pidx + nparts - 1) / nparts : 0;
+  auto keys_of = [&](Half& x, int j) {
+    const int ch = pidx + j * nparts;
+    const bool ring = ch < nring;
+    load_keys(x, ring ? rk + int64_t(ch) * 32 * D : sk + int64_t(ch - nring) * 32 * D,
+              ring ? rp + ch * 32 : any_ints, ring, lane);
+  };
+  auto values_of = [&](Half& x, int j) {
+    const int ch = pidx + j * nparts;
+    const bool ring = ch < nring;
+    load_values(x, ring ? rv + int64_t(ch) * D * 32 : sv + int64_t(ch - nring) * D * 32, lane);
+  };
+
+  // the block chunk this wave owns, if any: B <= 47 gives at most 2 block
+  // chunks, which land on 2 different waves since there are at least 2
+  static_assert(KPW >= 2, "each block chunk gets a wave of its own");
+  int own = -1;
+  for (int b = 0; b < nblk; ++b)
+    if ((ngl + b) % nparts == pidx) own = b;
+  const bool owns = own >= 0;
+  u16x8 bk_r[8], bv_r[8];  // the owned block chunk's K / V rows, 16-byte pieces
+  if (owns) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int piece = lane + 64 * i, row = piece >> 4, col = (piece & 15) * 8;
+      const int key = min(own * 32 + row, B - 1);  // rows past B repeat row B-1 and are masked
+      const int64_t off = ((int64_t(c) * B + key) * Hkv + h) * D + col;
+      bk_r[i] = *reinterpret_cast<const u16x8*>(kb + off);
+      bv_r[i] = *reinterpret_cast<const u16x8*>(vb + off);
+    }
+  }
 
   // query operands: lane (row ln of group rg, kg) holds q[row][ks*32+kg*8..+7]
   bf16x8 qb[2][4];
@@ -208,50 +272,18 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     const int bq = ok ? row / G : 0, hq = h * G + (ok ? row % G : 0);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      u16x8 v = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (ok) v = *reinterpret_cast<const u16x8*>(q + ((int64_t(c) * B + bq) * Hq + hq) * D + ks * 32 + kg * 8);
-      qb[rg][ks] = as_bf16x8(v);
+      const u16x8 v = *reinterpret_cast<const u16x8*>(q + ((int64_t(c) * B + bq) * Hq + hq) * D + ks * 32 + kg * 8);
+      qb[rg][ks] = as_bf16x8(ok ? v : u16x8{0, 0, 0, 0, 0, 0, 0, 0});
     }
   }
 
-  const int nring = W / 32, ngl = nring + S / 32, nblk = (B + 31) / 32;
-  const int nparts = ksplit * KPW, pidx = kidx * KPW + kq;
-  const uint16_t* rk = ring_k + int64_t(unit) * W * D;
-  const uint16_t* rv = ring_v + int64_t(unit) * D * W;
-  const uint16_t* sk = slot_k + int64_t(unit) * S * D;
-  const uint16_t* sv = slot_v + int64_t(unit) * D * S;
-  const int32_t* rp = ring_pos + int64_t(c) * W;
-
-  // this wave's window / slot chunks: pidx, pidx + nparts, ...
-  const int nmine = ngl > pidx ? (ngl - pidx + nparts - 1) / nparts : 0;
-  auto issue = [&](Operands& x, int j) {
-    const int ch = pidx + j * nparts;
-    if (ch < nring)
-      load_operands(x, rk + int64_t(ch) * 32 * D, rv + int64_t(ch) * D * 32, rp + ch * 32, lane);
-    else
-      load_operands(x, sk + int64_t(ch - nring) * 32 * D, sv + int64_t(ch - nring) * D * 32, nullptr, lane);
-  };
-  // the verified block's chunks, token-major rows -> LDS (keys row-major,
-  // values [d][32]); rows past B repeat row B-1 and are masked.  Staged
-  // before the first operand loads are issued, so that waiting for these
-  // loads does not wait for the chunk loads behind them.
-  for (int p = tid; p < nblk * 512; p += NT) {
-    const int bc = p >> 9, piece = p & 511, row = piece >> 4, col = (piece & 15) * 8;
-    const int key = min(bc * 32 + row, B - 1);
-    const int64_t off = ((int64_t(c) * B + key) * Hkv + h) * D + col;
-    const u16x8 kv = *reinterpret_cast<const u16x8*>(kb + off);
-    const u16x8 vv = *reinterpret_cast<const u16x8*>(vb + off);
-    uint16_t* bk = lds + bc * kBlkElems;
-    uint16_t* bv = bk + 32 * kKS;
-    *reinterpret_cast<u16x8*>(bk + row * kKS + col) = kv;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bv[(col + e) * kVS + row] = vv[e];
+  // the first chunk's halves
+  Half hk, hv;
+  if (kEvery || nmine > 0) {
+    keys_of(hk, 0);
+    values_of(hv, 0);
   }
 
-  Operands buf[IF];
-#pragma unroll
-  for (int u = 0; u < IF; ++u)
-    if (u < nmine) issue(buf[u], u);
   Softmax st[2];
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
@@ -260,37 +292,61 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
 #pragma unroll
     for (int i = 0; i < 8; ++i) st[rg].o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  __syncthreads();  // block chunks staged
 
-  for (int j = 0; j < nmine; j += IF) {
+  // the owned block chunk first: its rows -> this wave's LDS region (keys
+  // row-major, values [d][32]) -> operands; only this wave touches the
+  // region, so a wave barrier orders the writes before the reads
+  auto block_chunk = [&](int b) {
+    uint16_t* bk = lds + b * kBlkElems;
+    uint16_t* bv = bk + 32 * kKS;
 #pragma unroll
-    for (int u = 0; u < IF; ++u) {
-      if (j + u < nmine) {
-        const uint64_t mask = __ballot(buf[u].pos >= 0);  // bit k: key k of the chunk present
-        compute_chunk(st, buf[u], qb, uint32_t(mask >> (8 * kg)) & 0xFFu);
-        if (j + u + IF < nmine) issue(buf[u], j + u + IF);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int piece = lane + 64 * i, row = piece >> 4, col = (piece & 15) * 8;
+      *reinterpret_cast<u16x8*>(bk + row * kKS + col) = bk_r[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bv[(col + e) * kVS + row] = bv_r[i][e];
     }
-  }
-  // block chunk b is chunk ngl + b of the list: its wave continues the turns
-  for (int b = 0; b < nblk; ++b) {
-    if ((ngl + b) % nparts != pidx) continue;
-    const uint16_t* bk = lds + b * kBlkElems;
-    const uint16_t* bv = bk + 32 * kKS;
-    Operands x;
+    __builtin_amdgcn_wave_barrier();
+    Half xk, xv;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        x.k[mb * 4 + ks] = *reinterpret_cast<const u16x8*>(bk + chunk_key(ln, mb) * kKS + ks * 32 + kg * 8);
+        xk.r[mb * 4 + ks] = *reinterpret_cast<const u16x8*>(bk + chunk_key(ln, mb) * kKS + ks * 32 + kg * 8);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) x.v[db] = *reinterpret_cast<const u16x8*>(bv + (db * 16 + ln) * kVS + kg * 8);
+    for (int db = 0; db < 8; ++db) xv.r[db] = *reinterpret_cast<const u16x8*>(bv + (db * 16 + ln) * kVS + kg * 8);
     const int nvalid = B - b * 32 - 8 * kg;  // block keys among the lane group's 8
     const uint32_t valid8 = nvalid >= 8 ? 0xFFu : nvalid <= 0 ? 0u : ((1u << nvalid) - 1u);
-    compute_chunk(st, x, qb, valid8);
-  }
+    f32x4 sc[2][2];
+    chunk_scores(sc, xk, qb);
+    bf16x8 pk[2];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) pk[rg] = softmax_chunk(st[rg], sc[rg], valid8, false);
+    chunk_pv(st, xv, pk);
+  };
+  if (owns) block_chunk(own);
 
-  // merge the key parts in LDS (reusing the block stages), then write
+  // window / slot chunks: chunk j+1's keys are requested as soon as chunk
+  // j's scores are formed, its values as soon as chunk j's P.V is issued,
+  // so a chunk is always in flight; the last step requests nothing.
+  auto step = [&](bool more, int j) {
+    const uint64_t mask = __ballot(hk.pos >= 0);  // bit k (and k+32): key k present
+    f32x4 s[2][2];
+    chunk_scores(s, hk, qb);
+    if (more) keys_of(hk, j + 1);
+    const bool full = mask == ~0ull;
+    const uint32_t valid8 = uint32_t(mask >> (8 * kg)) & 0xFFu;
+    bf16x8 pk[2];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg) pk[rg] = softmax_chunk(st[rg], s[rg], valid8, full);
+    chunk_pv(st, hv, pk);
+    if (more) values_of(hv, j + 1);
+  };
+  for (int j = 0; j < nmine - 1; ++j) step(true, j);
+  if (nmine > 0) step(false, nmine - 1);
+
+  // merge the key parts: every wave leaves (m, l, O) in LDS; then each wave
+  // combines 16 / KPW of the 16 (row group, dimension block) pieces
   float lt[2];
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
@@ -298,62 +354,51 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     lt[rg] += __shfl_xor(lt[rg], 16, 64);
     lt[rg] += __shfl_xor(lt[rg], 32, 64);
   }
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);  // [KPW-1][2 row groups][64 lanes][34]
-  if (kq > 0) {
-#pragma unroll
-    for (int rg = 0; rg < 2; ++rg) {
-      float* dst = red + (((kq - 1) * 2 + rg) * 64 + lane) * 34;
-      dst[0] = st[rg].m;
-      dst[1] = lt[rg];
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[2 + mb * 4 + r] = st[rg].o[mb][r];
-    }
-  }
-  __syncthreads();
-  if (kq != 0) return;
+  __syncthreads();  // every wave is done with the block regions
+  float* red = reinterpret_cast<float*>(lds);  // [KPW][2 row groups][64 lanes][34]
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
+    float* dst = red + ((kq * 2 + rg) * 64 + lane) * 34;
+    dst[0] = st[rg].m;
+    dst[1] = lt[rg];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[2 + mb * 4 + r] = st[rg].o[mb][r];
+  }
+  __syncthreads();
+  constexpr int kPer = 16 / KPW;  // pieces per wave
+#pragma unroll
+  for (int pc = 0; pc < kPer; ++pc) {
+    const int piece = kq * kPer + pc, rg = piece >> 3, mb = piece & 7;
     const int row = ridx * 32 + rg * 16 + ln;
-    float mx = st[rg].m;
+    float mx = -INFINITY;
 #pragma unroll
-    for (int k = 1; k < KPW; ++k) mx = fmaxf(mx, red[(((k - 1) * 2 + rg) * 64 + lane) * 34]);
-    const float w0 = st[rg].m == -INFINITY ? 0.f : exp2_f(st[rg].m - mx);
-    float l = lt[rg] * w0;
-    f32x4 o[8];
+    for (int k = 0; k < KPW; ++k) mx = fmaxf(mx, red[((k * 2 + rg) * 64 + lane) * 34]);
+    float l = 0.f;
+    f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) o[mb] = st[rg].o[mb] * w0;
-#pragma unroll
-    for (int k = 1; k < KPW; ++k) {
-      const float* src = red + (((k - 1) * 2 + rg) * 64 + lane) * 34;
+    for (int k = 0; k < KPW; ++k) {
+      const float* src = red + ((k * 2 + rg) * 64 + lane) * 34;
       const float wk = src[0] == -INFINITY ? 0.f : exp2_f(src[0] - mx);
       l = fmaf(src[1], wk, l);
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[mb][r] = fmaf(src[2 + mb * 4 + r], wk, o[mb][r]);
+      for (int r = 0; r < 4; ++r) o[r] = fmaf(src[2 + mb * 4 + r], wk, o[r]);
     }
     if (row >= M) continue;
     if (ksplit == 1) {  // the whole key list: write the output
       const float il = 1.0f / l;
       uint16_t* orow = out + ((int64_t(c) * B + row / G) * Hq + h * G + row % G) * D;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-        *reinterpret_cast<u16x4*>(orow + mb * 16 + kg * 4) =
-            u16x4{bf16_bits(o[mb][0] * il), bf16_bits(o[mb][1] * il), bf16_bits(o[mb][2] * il),
-                  bf16_bits(o[mb][3] * il)};
+      *reinterpret_cast<u16x4*>(orow + mb * 16 + kg * 4) =
+          u16x4{bf16_bits(o[0] * il), bf16_bits(o[1] * il), bf16_bits(o[2] * il), bf16_bits(o[3] * il)};
     } else {  // partial of this key range (m in base 2)
       constexpr int Mpad = 64;
       float* pbuf = part_out + (int64_t(unit) * ksplit + kidx) * int64_t(Mpad) * (D + 2);
-      if (kg == 0) {
+      if (kg == 0 && mb == 0) {
         pbuf[row] = mx;
         pbuf[Mpad + row] = l;
       }
-      float* po = pbuf + 2 * Mpad + int64_t(row) * D;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<f32x4*>(po + mb * 16 + kg * 4) = o[mb];
+      *reinterpret_cast<f32x4*>(pbuf + 2 * Mpad + int64_t(row) * D + mb * 16 + kg * 4) = o;
     }
   }
 }
@@ -493,7 +538,9 @@ ls_status launch_draft(const ls_dims& d, const ls_state& st, const void* q, cons
     const int units = d.C * d.Hkv;
     const int rsplit = draft_row_splits(d), ksplit = draft_halves(d);
     float* part = reinterpret_cast<float*>(static_cast<char*>(st.workspace) + ws_layout(d, 1).draft_part);
-    hipLaunchKernelGGL((draft_direct<kKPW, kInFlight>), dim3(units * ksplit * rsplit), dim3(64 * kKPW), 0,
+    const int ngl = d.W / 32 + d.S / 32;  // window and slot chunks
+    auto kernel = ngl >= ksplit * kKPW ? draft_direct<kKPW, true> : draft_direct<kKPW, false>;
+    hipLaunchKernelGGL(kernel, dim3(units * ksplit * rsplit), dim3(64 * kKPW), 0,
                        stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kb),
                        static_cast<const uint16_t*>(vb), static_cast<const uint16_t*>(st.ring_k),
                        static_cast<const uint16_t*>(st.ring_v), st.ring_pos,
