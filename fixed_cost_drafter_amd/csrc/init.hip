@@ -12,10 +12,12 @@
 // contiguous ranges; one workgroup streams its range once (token-major
 // [C, rows, Hkv, d] input, 256-byte row segments) and writes an (m, l, n)
 // partial.  The bf16 d=128 kernel runs both contractions on MFMA
-// (v_mfma_f32_16x16x32_bf16): S^T = K U^T per 64-row tile, then the online
+// (v_mfma_f32_32x32x16_bf16): S^T = K U^T per 64-row tile, then the online
 // softmax in registers, then n^T += [K|V]^T P^T with P rounded to bf16 (l
 // sums the same rounded weights, so n/l stays an exact weighted mean of the
-// inputs).  The f32 kernel is a plain LDS-tiled loop for small shapes.
+// inputs).  Tiles run newest first, so each slot's maximum (the distance
+// bias favours new rows) is met early and the lazy rescale rarely fires.
+// The f32 kernel is a plain LDS-tiled loop for small shapes.
 // Phase 2 (init_finalize): merges the partials (associative max-rescale),
 // writes the state and the slots, fills the ring, sets seq_len and err_flag.
 #include <algorithm>
@@ -29,7 +31,7 @@ namespace {
 constexpr int kThreads = 256;
 __device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
 #ifndef LS_INIT_PREFETCH
-#define LS_INIT_PREFETCH 2
+#define LS_INIT_PREFETCH 1
 #endif
 
 // partial block of (split, unit): m[S] | l[S] | n[S][2d]
@@ -38,60 +40,80 @@ __device__ __host__ inline int64_t part_off(int split, int units, int unit, int 
 }
 
 // ---------------------------------------------------------------------------
-// MFMA partial kernel: bf16, d = 128, S = 16 * NW; wave w owns slots 16w..16w+15
-// and every wave reads the whole LDS tile of TR rows
+// MFMA partial kernel, bf16, d = 128, S = 32 * NG slots.  2 * NG waves:
+// wave w owns slots 32 (w % NG) .. +31 and row half w / NG (rows 0-31 or
+// 32-63) of every 64-row tile, so each wave reads half the tile from LDS
+// once for 32 slots, two waves share a SIMD, and both products run on
+// v_mfma_f32_32x32x16_bf16:
+//   S^T[row][slot] = K U^T over the wave's 32 rows: A = 32 rows x 16 dims
+//     from the row-major K tile, B = U^T (registers, 8 k-steps).
+//     A-row m = 8j + 4h + r (j < 4, h < 2, r < 4) reads row 16(j/2) + 8h +
+//     4(j%2) + r of the half, so that the output lane (slot, half h) holds
+//     rows 8h..8h+7 and 16+8h..16+8h+7 in order: exactly the 8-row
+//     k-slices of the P^T operand of the second product.
+//   n^T[dim][slot] += [K|V]^T P^T per 16-row k-step: A = 32 dims x 16 rows
+//     from the transposed tile, B = P^T packed from the scores.
+// The two row halves of a slot group keep separate (m, l, n) and merge
+// through LDS at the end.
 // ---------------------------------------------------------------------------
-template <int NW, int TR>
-__global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
+template <int NG>
+__global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, int64_t rows_stride,
     int L0, int rows_per_split, int nsplit, const uint16_t* __restrict__ u,
     const float* __restrict__ log_lambda, int Hkv, float* __restrict__ part) {
-  constexpr int D = 128, S = 16 * NW, NT = 64 * NW;
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  constexpr int D = 128, S = 32 * NG, NT = 128 * NG, TR = 64;
   constexpr int KLS = D + 8;   // row-major K tile stride (bf16 elements)
-  constexpr int VTS = TR + 4;  // transposed [dim][row] stride (bf16 elements)
-  constexpr int MB = TR / 16;  // 16-row blocks per tile
-  constexpr int KS2 = TR / 32; // 32-row k-steps of the PV product
-  constexpr int PAIRS = TR / (8 * NW);  // row pairs staged per thread
-  static_assert(PAIRS >= 1 && TR % (8 * NW) == 0, "tile rows must cover the threads");
-  // prefix tiles loading in registers per thread (deeper when a thread's
-  // share of a tile is one row pair, so the registers still fit two waves)
+  // transposed [dim][row] tile: 144-byte rows (16-byte aligned), and the
+  // 8-row groups of dimension dim stored in the order g ^ ((dim >> 4) & 7),
+  // which spreads both the staging stores (8 dimensions apart across lanes)
+  // and the operand loads (consecutive dimensions) over all 64 banks
+  constexpr int VTS = TR + 8;
+  auto kvt_row = [](int dim, int row) { return (((row >> 3) ^ ((dim >> 4) & 7)) << 3) | (row & 7); };
+  constexpr int PAIRS = TR * 8 / NT;  // row pairs staged per thread
+  static_assert(PAIRS >= 1 && TR * 8 % NT == 0, "tile rows must cover the threads");
   constexpr int kInitPrefetch = PAIRS == 1 ? LS_INIT_PREFETCH : 1;
-  __shared__ __attribute__((aligned(16))) uint16_t KL[TR * KLS];
-  __shared__ __attribute__((aligned(16))) uint16_t KVT[2 * D * VTS];
+  constexpr int kTileElems = TR * KLS + 2 * D * VTS + S * KLS;
+  constexpr int kMergeFloats = NG * 64 * 131;  // per slot group and lane: m_true, m_run, l, 128 n
+  constexpr int kLdsBytes = kTileElems * 2 > kMergeFloats * 4 ? kTileElems * 2 : kMergeFloats * 4;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kLdsBytes / 2];
+  uint16_t* KL = smem;                         // [TR][KLS]
+  uint16_t* KVT = smem + TR * KLS;             // [2D][VTS]
+  uint16_t* UL = KVT + 2 * D * VTS;            // [S][KLS]: the slot queries
 
   const int split = blockIdx.x % nsplit;
   const int unit = blockIdx.x / nsplit;  // c * Hkv + h
   const int h = unit % Hkv;
   const int c = unit / Hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int ln = lane & 15, kg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sg = wave % NG, half = wave / NG;  // slot group, row half
+  const int m32 = lane & 31, hh = lane >> 5;
   const int r_begin = split * rows_per_split;
   const int r_end = min(L0, r_begin + rows_per_split);
   const int t_newest = L0 - 1;
-  // scores in base 2 (one v_exp_f32 per weight): a2 = a * log2(e)
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
   const float k2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
 
-  // slot queries as the B operand of S^T = K U^T: lane (slot ln, kg) holds
-  // u[slot][ks*32 + kg*8 .. +7]
-  const int slot = wave * 16 + ln;
+  // slot queries, read per tile as the B operand (lane (slot m32, hh) takes
+  // u[slot][16ks + 8hh .. +7]) from LDS: registers go to the accumulators
+  const int slot = sg * 32 + m32;
   const float lnl2 = log_lambda[slot] * kLog2e;  // -inf stays -inf (lambda = 0)
-  bf16x8 ub[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    ub[ks] = as_bf16x8(
-        *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + slot) * D + ks * 32 + kg * 8));
+  for (int p = tid; p < S * 16; p += NT)
+    *reinterpret_cast<u16x8*>(&UL[(p >> 4) * KLS + (p & 15) * 8]) =
+        *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + (p >> 4)) * D + (p & 15) * 8);
+  // the tile row read by this lane as A-row m32 of its half
+  const int prow = half * 32 + 16 * (m32 >> 4) + 8 * ((m32 >> 2) & 1) + 4 * ((m32 >> 3) & 1) + (m32 & 3);
 
   float m_run = -INFINITY, l_run = 0.f;  // reference max (may lag) and weight sum
   float m_true = -INFINITY;               // exact running max
-  f32x4 acc[16];  // n^T: lane (slot ln, kg) holds dims mb*16 + kg*4 + r
+  f32x16 acc[8];  // n^T block db: lane (slot m32, hh) holds dims 32db + 8j + 4hh + r at [4j + r]
 #pragma unroll
-  for (int mb = 0; mb < 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < 8; ++db) acc[db] = f32x16{};
 
   // global -> register staging: thread (dg = tid%16, rp = tid/16) loads row
   // pairs rp + k*(NT/16); 16 lanes cover one 256-byte row segment
   const int dg = tid & 15, rp = tid >> 4;
-  // kInitPrefetch tiles are loading into registers while one is computed
   u16x8 kr[kInitPrefetch][2 * PAIRS], vr[kInitPrefetch][2 * PAIRS];
   auto load_tile = [&](int t0, u16x8 (&kd)[2 * PAIRS], u16x8 (&vd)[2 * PAIRS])
                        __attribute__((always_inline)) {
@@ -110,93 +132,90 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
     }
   };
 
+  // Tiles run from the newest to the oldest: the distance bias makes newer
+  // rows score higher, so each slot's maximum is met in the first tiles and
+  // the lazy rescale below almost never fires (oldest first, it would fire
+  // every few tiles as the bias grows by |ln lambda| per row).
+  const int ntiles = (r_end - r_begin + TR - 1) / TR;
+  auto tile_t0 = [&](int idx) { return r_begin + (ntiles - 1 - idx) * TR; };
 #pragma unroll
-  for (int u = 0; u < kInitPrefetch; ++u)
-    if (r_begin + u * TR < r_end) load_tile(r_begin + u * TR, kr[u], vr[u]);
-  for (int tb = r_begin; tb < r_end; tb += kInitPrefetch * TR) {
+  for (int uu = 0; uu < kInitPrefetch; ++uu)
+    if (uu < ntiles) load_tile(tile_t0(uu), kr[uu], vr[uu]);
+  for (int ib = 0; ib < ntiles; ib += kInitPrefetch) {
 #pragma unroll
-  for (int u = 0; u < kInitPrefetch; ++u) {  // tile t0 uses registers kr[u], vr[u]
-    const int t0 = tb + u * TR;
-    if (t0 >= r_end) break;
+  for (int uu = 0; uu < kInitPrefetch; ++uu) {  // tile idx uses registers kr[uu], vr[uu]
+    const int idx = ib + uu;
+    if (idx >= ntiles) break;
+    const int t0 = tile_t0(idx);
     const int nrows = min(TR, r_end - t0);
     __syncthreads();  // the previous tile's LDS reads are done
 #pragma unroll
     for (int pp = 0; pp < PAIRS; ++pp) {
       const int row0 = 2 * (rp + pp * (NT / 16));  // even row of the pair
-      *reinterpret_cast<u16x8*>(&KL[row0 * KLS + dg * 8]) = kr[u][2 * pp];
-      *reinterpret_cast<u16x8*>(&KL[(row0 + 1) * KLS + dg * 8]) = kr[u][2 * pp + 1];
+      *reinterpret_cast<u16x8*>(&KL[row0 * KLS + dg * 8]) = kr[uu][2 * pp];
+      *reinterpret_cast<u16x8*>(&KL[(row0 + 1) * KLS + dg * 8]) = kr[uu][2 * pp + 1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // (row0, row0 + 1) of one dimension as one dword: v_perm of the two rows
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint4 k0 = __builtin_bit_cast(uint4, kr[u][2 * pp]), k1 = __builtin_bit_cast(uint4, kr[u][2 * pp + 1]);
-        const uint4 v0 = __builtin_bit_cast(uint4, vr[u][2 * pp]), v1 = __builtin_bit_cast(uint4, vr[u][2 * pp + 1]);
+        const uint4 k0 = __builtin_bit_cast(uint4, kr[uu][2 * pp]), k1 = __builtin_bit_cast(uint4, kr[uu][2 * pp + 1]);
+        const uint4 v0 = __builtin_bit_cast(uint4, vr[uu][2 * pp]), v1 = __builtin_bit_cast(uint4, vr[uu][2 * pp + 1]);
         const uint32_t k0w[4] = {k0.x, k0.y, k0.z, k0.w}, k1w[4] = {k1.x, k1.y, k1.z, k1.w};
         const uint32_t v0w[4] = {v0.x, v0.y, v0.z, v0.w}, v1w[4] = {v1.x, v1.y, v1.z, v1.w};
         const uint32_t kk = __builtin_amdgcn_perm(k1w[e >> 1], k0w[e >> 1], sel);
         const uint32_t vv = __builtin_amdgcn_perm(v1w[e >> 1], v0w[e >> 1], sel);
-        *reinterpret_cast<uint32_t*>(&KVT[(dg * 8 + e) * VTS + row0]) = kk;
-        *reinterpret_cast<uint32_t*>(&KVT[(D + dg * 8 + e) * VTS + row0]) = vv;
+        *reinterpret_cast<uint32_t*>(&KVT[(dg * 8 + e) * VTS + kvt_row(dg * 8 + e, row0)]) = kk;
+        *reinterpret_cast<uint32_t*>(&KVT[(D + dg * 8 + e) * VTS + kvt_row(D + dg * 8 + e, row0)]) = vv;
       }
     }
     __syncthreads();
-    if (t0 + kInitPrefetch * TR < r_end)  // refill: that tile loads during the next computes
-      load_tile(t0 + kInitPrefetch * TR, kr[u], vr[u]);
+    if (idx + kInitPrefetch < ntiles)  // refill: that tile loads during the next computes
+      load_tile(tile_t0(idx + kInitPrefetch), kr[uu], vr[uu]);
 
-    // S^T[row][slot]: lane (slot ln, kg) holds rows mb*16 + kg*4 + r
-    f32x4 s[MB];
+    // S^T for the wave's 32 rows
+    f32x16 s = f32x16{};
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) s[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a =
-            as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[(mb * 16 + ln) * KLS + ks * 32 + kg * 8]));
-        s[mb] = mfma16x16x32(a, ub[ks], s[mb]);
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[prow * KLS + ks * 16 + hh * 8]));
+      const bf16x8 b = as_bf16x8(*reinterpret_cast<const u16x8*>(&UL[slot * KLS + ks * 16 + hh * 8]));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
     }
 
-    // online softmax per slot over this tile (base 2).  Row r of the tile
-    // sits at distance t_newest - t0 - r >= 1 from the newest row except in
-    // the tile holding the newest row or the ragged tail, which take the
-    // exact per-row path (distance 0 has no bias; rows past the end are out).
+    // online softmax per slot over the half (base 2).  Element 4j + r is
+    // tile row 32 half + 16(j/2) + 8hh + 4(j%2) + r, at distance
+    // t_newest - t0 - row >= 1 except in the tile holding the newest row or
+    // the ragged tail, which take the exact per-row path.
     float tmax = -INFINITY;
     if (t0 + TR <= t_newest && nrows == TR) {
-      const float dk = float(t_newest - t0 - kg * 4);
+      const float dk = float(t_newest - t0 - 32 * half - 8 * hh);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float bias = (dk - float(mb * 16 + r)) * lnl2;
-          const float a = fmaf(s[mb][r], k2, bias);
-          s[mb][r] = a;
-          tmax = fmaxf(tmax, a);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int j = i >> 2, r = i & 3;
+        const float bias = (dk - float(16 * (j >> 1) + 4 * (j & 1) + r)) * lnl2;
+        const float a = fmaf(s[i], k2, bias);
+        s[i] = a;
+        tmax = fmaxf(tmax, a);
+      }
     } else {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = mb * 16 + kg * 4 + r;
-          const int dist = t_newest - (t0 + row);
-          const float bias = dist == 0 ? 0.f : float(dist) * lnl2;
-          float a = fmaf(s[mb][r], k2, bias);
-          if (row >= nrows) a = -INFINITY;
-          s[mb][r] = a;
-          tmax = fmaxf(tmax, a);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int j = i >> 2, r = i & 3;
+        const int row = 32 * half + 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + r;
+        const int dist = t_newest - (t0 + row);
+        const float bias = dist == 0 ? 0.f : float(dist) * lnl2;
+        float a = fmaf(s[i], k2, bias);
+        if (row >= nrows) a = -INFINITY;
+        s[i] = a;
+        tmax = fmaxf(tmax, a);
+      }
     }
-    // the slot's max over the 4 lane groups (rows): swapping a register with
-    // itself across row pairs / halves leaves the partner's value in one result
+    // the slot's max over the two lane halves (the other rows)
     {
-      const auto x16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-      tmax = fmaxf(__uint_as_float(x16[0]), __uint_as_float(x16[1]));
       const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
       tmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
     }
     // lazy rescale: the reference max moves only when some slot's max grows
-    // by more than 8 e-folds (weights stay <= e^8), so the 64-register
+    // by more than 8 e-folds (weights stay <= e^8), so the 128-register
     // accumulator rescale is skipped in the steady state
     m_true = fmaxf(m_true, tmax);
     if (__any(tmax > m_run + 8.f * kLog2e)) {
@@ -205,68 +224,88 @@ __global__ __launch_bounds__(64 * NW, 1) void init_mfma_partial(
       m_run = m_new;
       l_run *= scale;
 #pragma unroll
-      for (int mb = 0; mb < 16; ++mb) acc[mb] *= scale;
+      for (int db = 0; db < 8; ++db) acc[db] *= scale;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    // weights rounded to bf16 in pairs; l sums the same rounded weights
+    // weights rounded to bf16 in pairs; l sums the same rounded weights;
+    // elements 8t..8t+7 are the P^T operand of k-step t
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
-    uint32_t pw[MB * 2];
+    bf16x8 pk[2];
     float lsum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int t = 0; t < 2; ++t) {
+      uint32_t pw[4];
 #pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const f32x2 e2 = {exp2_f(s[mb][r] - m_use), exp2_f(s[mb][r + 1] - m_use)};
+      for (int q = 0; q < 4; ++q) {
+        const f32x2 e2 = {exp2_f(s[8 * t + 2 * q] - m_use), exp2_f(s[8 * t + 2 * q + 1] - m_use)};
         const bf16x2 b2 = __builtin_convertvector(e2, bf16x2);
-        pw[mb * 2 + r / 2] = __builtin_bit_cast(uint32_t, b2);
+        pw[q] = __builtin_bit_cast(uint32_t, b2);
         lsum = __builtin_amdgcn_fdot2_f32_bf16(b2, ones, lsum, false);
       }
-    l_run += lsum;
-    u16x8 pv[KS2];
-#pragma unroll
-    for (int ks = 0; ks < KS2; ++ks)  // rows of 16-row blocks 2ks and 2ks+1
-      pv[ks] = __builtin_bit_cast(u16x8, uint4{pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]});
-
-    // n^T[dim][slot] += [K|V]^T[dim][row] P^T[row][slot]; the k order of the
-    // A operand (rows 32ks+4kg..+3, 32ks+16+4kg..+3) matches pv's element order
-#pragma unroll
-    for (int ks = 0; ks < KS2; ++ks) {
-      const bf16x8 pk = as_bf16x8(pv[ks]);
-#pragma unroll
-      for (int mb = 0; mb < 16; ++mb) {
-        const uint16_t* base = &KVT[(mb * 16 + ln) * VTS + ks * 32 + kg * 4];
-        const u16x4 lo = *reinterpret_cast<const u16x4*>(base);
-        const u16x4 hi = *reinterpret_cast<const u16x4*>(base + 16);
-        const bf16x8 a = as_bf16x8(u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        acc[mb] = mfma16x16x32(a, pk, acc[mb]);
-      }
+      pk[t] = as_bf16x8(__builtin_bit_cast(u16x8, uint4{pw[0], pw[1], pw[2], pw[3]}));
     }
-  }
-  }
+    l_run += lsum;
 
-  // the state's m is the exact max: move the reference there once
-  if (m_true > m_run) {
-    const float scale = exp2_f(m_run - m_true);
-    m_run = m_true;
-    l_run *= scale;
+    // n^T[dim][slot] += [K|V]^T[dim][row] P^T[row][slot], 16 rows per k-step:
+    // A = dims 32db + m32, rows 32 half + 16t + 8hh .. +7 of the transposed tile
 #pragma unroll
-    for (int mb = 0; mb < 16; ++mb) acc[mb] *= scale;
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int dim = db * 32 + m32;
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(
+            &KVT[dim * VTS + kvt_row(dim, half * 32 + t * 16 + hh * 8)]));
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[t], acc[db], 0, 0, 0);
+      }
+  }
   }
 
-  // write the partial: lane (slot ln, kg) holds n[slot][mb*16 + kg*4 + r]
-  float* pb = part + part_off(split, gridDim.x / nsplit, unit, S, D);
+  // merge the two row halves of each slot group: half 1 leaves (m_true,
+  // m_run, l, n) in LDS, half 0 takes the exact max of both and rescales
   float lt = l_run;
-  lt += __shfl_xor(lt, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
-  if (kg == 0) {
-    pb[slot] = m_run * kLn2;  // natural units, as the state keeps m
+  {
+    const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
+    lt = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
+  }
+  __syncthreads();  // the last tile's LDS reads are done
+  float* mg = reinterpret_cast<float*>(smem) + sg * 64 * 131;  // [64 lanes][m_true, m_run, l, 128 n]
+  if (half == 1) {
+    float* dst = mg + lane * 131;
+    dst[0] = m_true;
+    dst[1] = m_run;
+    dst[2] = lt;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dst[3 + db * 16 + i] = acc[db][i];
+  }
+  __syncthreads();
+  if (half == 1) return;
+  const float* src = mg + lane * 131;
+  const float mt = fmaxf(m_true, src[0]);  // the state's m: the exact max of all rows
+  const float w0 = m_run == -INFINITY ? 0.f : exp2_f(m_run - mt);
+  const float w1 = src[1] == -INFINITY ? 0.f : exp2_f(src[1] - mt);
+  lt = fmaf(lt, w0, src[2] * w1);
+
+  // write the partial: lane (slot, hh) holds n[slot][32db + 8j + 4hh + r];
+  // each block is combined and stored in turn
+  float* pb = part + part_off(split, gridDim.x / nsplit, unit, S, D);
+  if (hh == 0) {
+    pb[slot] = mt * kLn2;  // natural units, as the state keeps m
     pb[S + slot] = lt;
   }
   float* nrow = pb + 2 * S + int64_t(slot) * 2 * D;
 #pragma unroll
-  for (int mb = 0; mb < 16; ++mb) *reinterpret_cast<f32x4*>(nrow + mb * 16 + kg * 4) = acc[mb];
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = fmaf(acc[db][4 * j + r], w0, src[3 + db * 16 + 4 * j + r] * w1);
+      *reinterpret_cast<f32x4*>(nrow + db * 32 + 8 * j + 4 * hh) = o;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -530,10 +569,10 @@ ls_status launch_init(const ls_dims& d, const ls_state& st, const void* kp, cons
     const uint16_t* v16 = static_cast<const uint16_t*>(vp);
     const uint16_t* u16 = static_cast<const uint16_t*>(st.u);
     if (d.S == 128)
-      hipLaunchKernelGGL((init_mfma_partial<8, 64>), grid, dim3(512), 0, stream, k16, v16,
+      hipLaunchKernelGGL((init_mfma32_partial<4>), grid, dim3(512), 0, stream, k16, v16,
                          rows_stride, L0, rows, nsplit, u16, st.log_lambda, d.Hkv, part);
     else if (d.S == 64)
-      hipLaunchKernelGGL((init_mfma_partial<4, 64>), grid, dim3(256), 0, stream, k16, v16,
+      hipLaunchKernelGGL((init_mfma32_partial<2>), grid, dim3(256), 0, stream, k16, v16,
                          rows_stride, L0, rows, nsplit, u16, st.log_lambda, d.Hkv, part);
     // S = 0: no summary to pool; the finalize fills the window only
     if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
