@@ -85,7 +85,7 @@ ENTRY_KERNELS = {
     "append": ("append_kernel",),
     "draft": ("draft_direct", "draft_combine", "draft_generic"),
     "verify_attention": ("attn_mfma_partial", "attn_combine", "attn_generic"),
-    "init": ("init_mfma_partial", "init_generic_partial", "init_finalize"),
+    "init": ("init_mfma32_partial", "init_generic_partial", "init_finalize"),
 }
 CALIB_BYTES = 512 << 20        # the streaming copy used to scale the counters
 CALIB_KERNEL = "neg_kernel"
