@@ -10,16 +10,18 @@
 //   u_sample times the total.
 //
 // Four launches, kernel boundaries between them (no device-scope fences):
-//  (1) samp_stats: (row, 16K-logit chunk) workgroups stream both logit
+//  (1) samp_stats: (row, 8192-logit chunk) workgroups stream both logit
 //      tensors once and reduce each chunk to base-2 softmax statistics
 //      (max of x log2(e) / T, sum of 2^(y - max));
 //  (2) samp_decide: one workgroup per sequence merges its 2B+1 rows'
-//      statistics, gathers p_j(d_j), q_j(d_j) in parallel and runs the
-//      acceptance rule, then records the row to draw from;
+//      statistics (a wave per row, a lane per chunk), gathers p_j(d_j),
+//      q_j(d_j) and runs the acceptance rule, then records the row to draw
+//      from;
 //  (3) samp_sums: chunk sums of that row's weights;
-//  (4) samp_draw: one workgroup per sequence locates the chunk, then the
-//      thread segment, then the element where the running sum crosses
-//      u_sample times the total.
+//  (4) samp_draw: one workgroup per sequence locates the chunk, then (a
+//      workgroup scan over per-thread sums of 32 entries held in registers)
+//      the thread, then the entry where the running sum crosses u_sample
+//      times the total.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -93,17 +95,43 @@ __global__ __launch_bounds__(kThreads) void samp_stats(
       if (v < nvec) buf[u] = __builtin_nontemporal_load(xv + v);
     }
     float bm = -INFINITY;  // batch max, then one rescale
+    if constexpr (Ty::kBytes == 2) {
+      // bf16: the max over packed 16-bit order keys (two logits per
+      // instruction), converted back to a value once
+      typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+      typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+      u16x2 best = {0, 0};  // 0: below every key of a real value
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (u * kThreads + tid < nvec)
+      for (int u = 0; u < U; ++u)
+        if (u * kThreads + tid < nvec) {
+          const uint4 w4 = __builtin_bit_cast(uint4, buf[u]);
+          const uint32_t ws4[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
-        for (int e = 0; e < VT::N; ++e) bm = fmaxf(bm, VT::get(buf[u], e) * k2);
+          for (int q = 0; q < 4; ++q) {
+            const i16x2 h = __builtin_bit_cast(i16x2, ws4[q]);
+            const u16x2 flip = __builtin_bit_cast(u16x2, i16x2(h >> 15)) | u16x2{0x8000, 0x8000};
+            best = __builtin_elementwise_max(best, __builtin_bit_cast(u16x2, ws4[q]) ^ flip);
+          }
+        }
+      const uint32_t key = max(uint32_t(best[0]), uint32_t(best[1]));
+      if (key != 0u) {
+        const uint32_t hb = key >= 0x8000u ? (key ^ 0x8000u) : (~key & 0xFFFFu);
+        bm = bf16_to_f32(uint16_t(hb)) * k2;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u * kThreads + tid < nvec)
+#pragma unroll
+          for (int e = 0; e < VT::N; ++e) bm = fmaxf(bm, VT::get(buf[u], e) * k2);
+    }
     float bs = 0.f;
+    const float nbm = bm == -INFINITY ? 0.f : -bm;
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (u * kThreads + tid < nvec)
 #pragma unroll
-        for (int e = 0; e < VT::N; ++e) bs += exp2_f(VT::get(buf[u], e) * k2 - bm);
+        for (int e = 0; e < VT::N; ++e) bs += exp2_f(fmaf(VT::get(buf[u], e), k2, nbm));
     merge_stat(m, s, bm, bs);
     for (int i = begin + nvec * VT::N + tid; i < end; i += kThreads)
       merge_stat(m, s, Ty::load(x, i) * k2, 1.f);
@@ -120,31 +148,44 @@ __global__ __launch_bounds__(kThreads) void samp_stats(
   }
 }
 
+// merged base-2 statistics of one row from its nsplit chunk statistics: one
+// lane per chunk, then a wave merge (every lane returns the result)
+__device__ __forceinline__ float2 row_stat(const float2* __restrict__ st, int nsplit, int lane) {
+  float m = -INFINITY, s = 0.f;
+  for (int k = lane; k < nsplit; k += 64) merge_stat(m, s, st[k].x, st[k].y);
+  wave_merge_stat(m, s);
+  return make_float2(m, s);
+}
+
+// One workgroup of kDecideWaves waves per sequence: wave w merges the
+// statistics of target rows w, w + kDecideWaves, ... and of the drafter rows
+// of the same index, and gathers p_j(d_j) and q_j(d_j); thread 0 then runs
+// the acceptance rule.
+constexpr int kDecideWaves = 8;
 template <typename Ty>
-__global__ __launch_bounds__(64) void samp_decide(
+__global__ __launch_bounds__(64 * kDecideWaves) void samp_decide(
     const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
     const int32_t* __restrict__ draft, const float* __restrict__ u_accept,
     const float2* __restrict__ stats, Record* __restrict__ rec, int32_t* __restrict__ tokens,
     int32_t* __restrict__ tau, int C, int B, int V, int nsplit, float k2) {
   __shared__ float pt[64], qd[64], mt[64], izt[64], md[64], izd[64];
   __shared__ int js;
-  const int c = blockIdx.x, t = threadIdx.x;
+  const int c = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int nt = C * (B + 1);
-  if (t <= B) {  // target row t; drafter row t (t < B) and the two probabilities of draft t
-    float m = -INFINITY, s = 0.f;
-    const float2* st = stats + (int64_t(c) * (B + 1) + t) * nsplit;
-    for (int k = 0; k < nsplit; ++k) merge_stat(m, s, st[k].x, st[k].y);
-    mt[t] = m;
-    izt[t] = 1.0f / s;
-    if (t < B) {
-      float m2 = -INFINITY, s2 = 0.f;
-      const float2* sd = stats + (int64_t(nt) + int64_t(c) * B + t) * nsplit;
-      for (int k = 0; k < nsplit; ++k) merge_stat(m2, s2, sd[k].x, sd[k].y);
-      md[t] = m2;
-      izd[t] = 1.0f / s2;
-      const int d = min(max(draft[int64_t(c) * B + t], 0), V - 1);
-      pt[t] = exp2_f(Ty::load(tl, (int64_t(c) * (B + 1) + t) * V + d) * k2 - m) * izt[t];
-      qd[t] = exp2_f(Ty::load(dl, (int64_t(c) * B + t) * V + d) * k2 - m2) * izd[t];
+  for (int j = wave; j <= B; j += kDecideWaves) {  // target row j; drafter row j (j < B)
+    const float2 ts = row_stat(stats + (int64_t(c) * (B + 1) + j) * nsplit, nsplit, lane);
+    float2 ds = make_float2(0.f, 1.f);
+    if (j < B) ds = row_stat(stats + (int64_t(nt) + int64_t(c) * B + j) * nsplit, nsplit, lane);
+    if (lane == 0) {
+      mt[j] = ts.x;
+      izt[j] = 1.0f / ts.y;
+      if (j < B) {
+        md[j] = ds.x;
+        izd[j] = 1.0f / ds.y;
+        const int d = min(max(draft[int64_t(c) * B + j], 0), V - 1);
+        pt[j] = exp2_f(Ty::load(tl, (int64_t(c) * (B + 1) + j) * V + d) * k2 - ts.x) * izt[j];
+        qd[j] = exp2_f(Ty::load(dl, (int64_t(c) * B + j) * V + d) * k2 - ds.x) * izd[j];
+      }
     }
   }
   __syncthreads();
@@ -164,7 +205,7 @@ __global__ __launch_bounds__(64) void samp_decide(
     rec[c] = r;
   }
   __syncthreads();
-  for (int i = t; i <= B; i += 64)  // accepted drafts, then -1 (token js is drawn later)
+  for (int i = t; i <= B; i += 64 * kDecideWaves)  // accepted drafts, then -1 (token js is drawn later)
     if (i != js) tokens[int64_t(c) * (B + 1) + i] = i < js ? draft[int64_t(c) * B + i] : -1;
 }
 
@@ -178,17 +219,56 @@ __device__ __forceinline__ float draw_weight(const typename Ty::T* rt, const typ
   return fmaxf(p - q, 0.f);
 }
 
+// weights of the N logits of one 16-byte vector of the drawn row (vt: target
+// logits, vd: drafter logits, unused for a bonus draw)
+template <typename Ty>
+__device__ __forceinline__ void draw_weights16(const typename Vec16<Ty>::V& vt, const typename Vec16<Ty>::V& vd,
+                                               const Record& r, float k2, float* w) {
+  using VT = Vec16<Ty>;
+#pragma unroll
+  for (int e = 0; e < VT::N; ++e) {
+    const float p = exp2_f(VT::get(vt, e) * k2 - r.mt) * r.izt;
+    w[e] = r.bonus ? p : fmaxf(p - exp2_f(VT::get(vd, e) * k2 - r.md) * r.izd, 0.f);
+  }
+}
+
+// chunk sums of the drawn row's weights: (chunk, sequence) workgroups, all
+// 16-byte loads of a thread in flight at once
 template <typename Ty>
 __global__ __launch_bounds__(kThreads) void samp_sums(
     const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
-    const Record* __restrict__ rec, float* __restrict__ sums, int B, int V, int nsplit, float k2) {
+    const Record* __restrict__ rec, float* __restrict__ sums, int B, int V, int nsplit, float k2,
+    int vec_ok) {
+  using VT = Vec16<Ty>;
+  constexpr int U = kVerifyChunk / VT::N / kThreads;  // vectors per thread
   const int split = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const Record r = rec[c];
   const typename Ty::T* rt = tl + (int64_t(c) * (B + 1) + r.row) * V;
   const typename Ty::T* rd = dl + (int64_t(c) * B + min(r.row, B - 1)) * V;
   const int begin = split * kVerifyChunk, end = min(V, begin + kVerifyChunk);
   float a = 0.f;
-  for (int k = begin + tid; k < end; k += kThreads) a += draw_weight<Ty>(rt, rd, r, k2, k);
+  if (vec_ok) {
+    const typename VT::V* xt = reinterpret_cast<const typename VT::V*>(rt + begin);
+    const typename VT::V* xd = reinterpret_cast<const typename VT::V*>(rd + begin);
+    const int nvec = (end - begin) / VT::N;  // whole: V is a multiple of N here
+    typename VT::V bt[U], bd[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = min(u * kThreads + tid, nvec - 1);
+      bt[u] = xt[v];
+      bd[u] = r.bonus ? bt[u] : xd[v];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u * kThreads + tid < nvec) {
+        float w[VT::N];
+        draw_weights16<Ty>(bt[u], bd[u], r, k2, w);
+#pragma unroll
+        for (int e = 0; e < VT::N; ++e) a += w[e];
+      }
+  } else {
+    for (int k = begin + tid; k < end; k += kThreads) a += draw_weight<Ty>(rt, rd, r, k2, k);
+  }
   a = wave_sum(a);
   __shared__ float wsum[kThreads / 64];
   if ((tid & 63) == 0) wsum[tid >> 6] = a;
@@ -196,17 +276,28 @@ __global__ __launch_bounds__(kThreads) void samp_sums(
   if (tid == 0) sums[int64_t(c) * nsplit + split] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
 
+// The draw: one workgroup per sequence.  Thread 0 finds the chunk where the
+// running sum of the chunk sums crosses u_sample * total.  Each thread then
+// forms the weights of its SEG consecutive entries of that chunk in
+// registers; a workgroup scan of the thread totals finds the thread whose
+// entries hold the crossing, and that thread walks its registers.  When
+// rounding leaves the threshold past the end, the last entry with weight
+// is drawn (last non-empty chunk, thread, entry).
 template <typename Ty>
 __global__ __launch_bounds__(kThreads) void samp_draw(
     const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
     const Record* __restrict__ rec, const float* __restrict__ sums,
     const float* __restrict__ u_sample, int32_t* __restrict__ tokens, int B, int V, int nsplit,
-    float k2) {
-  constexpr int SEG = kVerifyChunk / kThreads;  // elements per thread segment
-  __shared__ float seg[kThreads];
-  __shared__ int s_split, s_seg, s_tok;
+    float k2, int vec_ok) {
+  using VT = Vec16<Ty>;
+  constexpr int SEG = kVerifyChunk / kThreads;  // entries per thread
+  constexpr int NV = SEG / VT::N;               // 16-byte vectors per thread
+  static_assert(SEG % VT::N == 0, "whole vectors per thread");
+  __shared__ int s_split;
   __shared__ float s_base, s_thr;
-  const int c = blockIdx.x, tid = threadIdx.x;
+  __shared__ float wtot[kThreads / 64];
+  __shared__ int s_first[kThreads / 64], s_last[kThreads / 64];
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const Record r = rec[c];
   const typename Ty::T* rt = tl + (int64_t(c) * (B + 1) + r.row) * V;
   const typename Ty::T* rd = dl + (int64_t(c) * B + min(r.row, B - 1)) * V;
@@ -230,45 +321,67 @@ __global__ __launch_bounds__(kThreads) void samp_draw(
     s_split = sp;
     s_base = run;
     s_thr = thr;
-    s_tok = -1;
   }
   __syncthreads();
   const int begin = s_split * kVerifyChunk, end = min(V, begin + kVerifyChunk);
-  const int k0 = begin + tid * SEG, k1 = min(end, k0 + SEG);
+  const int k0 = begin + tid * SEG;
+  float w[SEG];
+  if (vec_ok && k0 + SEG <= end) {
+    typename VT::V bt[NV], bd[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      bt[i] = *reinterpret_cast<const typename VT::V*>(rt + k0 + i * VT::N);
+      bd[i] = r.bonus ? bt[i] : *reinterpret_cast<const typename VT::V*>(rd + k0 + i * VT::N);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) draw_weights16<Ty>(bt[i], bd[i], r, k2, w + i * VT::N);
+  } else {
+#pragma unroll
+    for (int e = 0; e < SEG; ++e) w[e] = k0 + e < end ? draw_weight<Ty>(rt, rd, r, k2, k0 + e) : 0.f;
+  }
   float a = 0.f;
-  for (int k = k0; k < k1; ++k) a += draw_weight<Ty>(rt, rd, r, k2, k);
-  seg[tid] = a;
+#pragma unroll
+  for (int e = 0; e < SEG; ++e) a += w[e];
+  // inclusive scan of the thread totals over the workgroup
+  float incl = a;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wtot[wave] = incl;
   __syncthreads();
-  if (tid == 0) {  // the segment where the running sum crosses the threshold
-    float run = s_base;
-    int sg = -1, last = -1;
-    for (int t2 = 0; t2 < kThreads; ++t2) {
-      if (seg[t2] > 0.f) last = t2;
-      if (sg < 0 && run + seg[t2] > s_thr) sg = t2;
-      if (sg < 0) run += seg[t2];
-    }
-    if (sg < 0) {  // rounding: the last segment with weight
-      sg = last < 0 ? 0 : last;
-      run = s_base;
-      for (int t2 = 0; t2 < sg; ++t2) run += seg[t2];
-    }
-    s_seg = sg;
-    s_base = run;
+  float before = s_base;
+  for (int w2 = 0; w2 < wave; ++w2) before += wtot[w2];
+  incl += before;                       // running sum up to this thread's last entry
+  const float excl = incl - a;          // ... up to its first entry
+  const float thr = s_thr;
+  const uint64_t cross = __ballot(incl > thr && a > 0.f);
+  const uint64_t some = __ballot(a > 0.f);
+  if (lane == 0) {
+    s_first[wave] = cross ? wave * 64 + __builtin_ctzll(cross) : kThreads;
+    s_last[wave] = some ? wave * 64 + 63 - __builtin_clzll(some) : -1;
   }
   __syncthreads();
-  if (tid == s_seg) {
-    float run = s_base;
-    int tok = -1, last = k0;
-    for (int k = k0; k < k1; ++k) {
-      const float w = draw_weight<Ty>(rt, rd, r, k2, k);
-      if (w > 0.f) last = k;
-      run += w;
-      if (run > s_thr) { tok = k; break; }
-    }
-    s_tok = tok < 0 ? last : tok;
+  int first = kThreads, lastt = -1;
+#pragma unroll
+  for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+    first = min(first, s_first[w2]);
+    lastt = max(lastt, s_last[w2]);
   }
-  __syncthreads();
-  if (tid == 0) tokens[int64_t(c) * (B + 1) + r.row] = s_tok;
+  const int pick = first < kThreads ? first : (lastt >= 0 ? lastt : 0);
+  if (tid == pick) {
+    float run = excl;
+    int tok = -1, lst = -1;
+#pragma unroll
+    for (int e = 0; e < SEG; ++e) {
+      if (w[e] > 0.f) lst = e;
+      run += w[e];
+      if (tok < 0 && run > thr) tok = e;
+    }
+    const int e = tok >= 0 ? tok : (lst >= 0 ? lst : 0);
+    tokens[int64_t(c) * (B + 1) + r.row] = k0 + e;
+  }
 }
 
 template <typename Ty>
@@ -289,14 +402,14 @@ ls_status run(const ls_dims& d, const void* tl, const void* dl, const int32_t* d
   hipLaunchKernelGGL(samp_stats<Ty>, dim3(nsplit, d.C * (2 * d.B + 1)), dim3(kThreads), 0, stream,
                      t, dd, stats, d.C, d.B, d.V, nsplit, k2, vec_ok);
   if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
-  hipLaunchKernelGGL(samp_decide<Ty>, dim3(d.C), dim3(64), 0, stream, t, dd, draft, u_accept, stats,
+  hipLaunchKernelGGL(samp_decide<Ty>, dim3(d.C), dim3(64 * kDecideWaves), 0, stream, t, dd, draft, u_accept, stats,
                      rec, tokens, tau, d.C, d.B, d.V, nsplit, k2);
   if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
   hipLaunchKernelGGL(samp_sums<Ty>, dim3(nsplit, d.C), dim3(kThreads), 0, stream, t, dd, rec, sums,
-                     d.B, d.V, nsplit, k2);
+                     d.B, d.V, nsplit, k2, vec_ok);
   if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
   hipLaunchKernelGGL(samp_draw<Ty>, dim3(d.C), dim3(kThreads), 0, stream, t, dd, rec, sums, u_sample,
-                     tokens, d.B, d.V, nsplit, k2);
+                     tokens, d.B, d.V, nsplit, k2, vec_ok);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
 
