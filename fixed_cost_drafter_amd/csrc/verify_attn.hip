@@ -52,7 +52,19 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_partial(
     int32_t* __restrict__ err_flag) {
   constexpr int D = 128, TR = 64, NT = 64 * NW, Mq = 16 * NW;
   constexpr int KLS = D + 8;   // row-major K tile stride (bf16 elements)
-  constexpr int VTS = TR + 4;  // transposed V [dim][row] stride (bf16 elements)
+  // transposed V tile [dim][row]: 144-byte rows (16-byte aligned).  Inside
+  // each 32-key group key 16hb + 4g + i sits at 8g + 4hb + i, the order in
+  // which a lane (key group g) reads its 8 keys of the P.V operand, so each
+  // operand load is one 16-byte read; and the 8-row groups of dimension dim
+  // are stored in the order group ^ ((dim >> 4) & 7), which spreads the
+  // staging stores (8 dimensions apart across lanes) and the operand loads
+  // (consecutive dimensions) over all 64 banks.
+  constexpr int VTS = TR + 8;
+  auto vt_row = [](int dim, int row) {
+    const int r32 = row & 31;
+    const int ph = (row & ~31) | (8 * ((r32 >> 2) & 3) + 4 * (r32 >> 4) + (r32 & 3));
+    return (((ph >> 3) ^ ((dim >> 4) & 7)) << 3) | (ph & 7);
+  };
   constexpr int MB = TR / 16;  // 16-row key blocks per tile
   constexpr int KS2 = TR / 32; // 32-row k-steps of the PV product
   constexpr int NITEM = (TR / 2) * 16;          // (row pair, 8-dim group) staging items
@@ -129,7 +141,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_partial(
       const uint32_t v0w[4] = {v0.x, v0.y, v0.z, v0.w}, v1w[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e)  // (row0, row0 + 1) of one dimension as one dword
-        *reinterpret_cast<uint32_t*>(&VT[(dg * 8 + e) * VTS + row0]) =
+        *reinterpret_cast<uint32_t*>(&VT[(dg * 8 + e) * VTS + vt_row(dg * 8 + e, row0)]) =
             __builtin_amdgcn_perm(v1w[e >> 1], v0w[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
     }
     __syncthreads();
@@ -200,11 +212,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_partial(
           u16x8, uint4{pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]}));
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-        const uint16_t* base = &VT[(mb * 16 + ln) * VTS + ks * 32 + kg * 4];
-        const u16x4 lo = *reinterpret_cast<const u16x4*>(base);
-        const u16x4 hi = *reinterpret_cast<const u16x4*>(base + 16);
-        acc[mb] = mfma16x16x32(as_bf16x8(u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}),
-                               pk, acc[mb]);
+        const int dim = mb * 16 + ln;
+        const u16x8 v = *reinterpret_cast<const u16x8*>(&VT[dim * VTS + vt_row(dim, ks * 32 + kg * 4)]);
+        acc[mb] = mfma16x16x32(as_bf16x8(v), pk, acc[mb]);
       }
     }
   }
