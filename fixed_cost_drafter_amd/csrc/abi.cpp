@@ -14,8 +14,6 @@
 
 namespace {
 
-constexpr int kMaxB = 47;  // keeps the per-round row staging within 64 KB of LDS
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 ls_status check_dims(const ls_dims* d) {
@@ -27,9 +25,9 @@ ls_status check_dims(const ls_dims* d) {
       d->V < 1)
     return LS_ERR_SHAPE;
   if (d->Hq % d->Hkv != 0) return LS_ERR_SHAPE;
-  if (d->B > kMaxB || (d->W > 0 && d->B + 1 > d->W)) return LS_ERR_SHAPE;
+  if (d->B > ls::kMaxBlock || (d->W > 0 && d->B + 1 > d->W)) return LS_ERR_SHAPE;
   if (int64_t(d->C) * (d->B + 1) > 65535) return LS_ERR_SHAPE;
-  if (d->V > (1 << 20)) return LS_ERR_SHAPE;  // verify keeps (B+1) x V/16384 keys in LDS
+  if (d->V > (1 << 20)) return LS_ERR_SHAPE;  // at most 128 logit chunks per row
   if (int64_t(d->C) * d->Hkv * d->S > (int64_t(1) << 30)) return LS_ERR_SHAPE;
   const int G = d->Hq / d->Hkv;
   if (d->dtype == LS_F32) {

@@ -111,6 +111,11 @@ __host__ __device__ inline int64_t key_index(int64_t unit, int rows, int d, int 
 #define LS_VERIFY_CHUNK 8192
 #endif
 constexpr int kVerifyChunk = LS_VERIFY_CHUNK;  // logits per verify workgroup
+// Largest drafted block: B + 1 verified rows fit one 64-lane ballot, the
+// block's keys fill at most two 32-key chunks of the draft attention, and the
+// append's staging of B + 1 fp32 rows of [k | v] (d = 128) stays under 64 KB
+// of LDS.
+constexpr int kMaxBlock = 47;
 constexpr int kInitTargetBlocks = 512; // aim of the init grid size
 constexpr int kInitRowTile = 64;       // rows per init tile (MFMA path)
 

@@ -9,14 +9,15 @@
 // unsigned order is "larger value first, then lower index": the high word is
 // the value's bits mapped to an order-preserving unsigned integer (+0 and -0
 // merged), the low word is ~index.  (2) One workgroup per sequence reduces
-// its (B+1) x splits keys, counts the accepted prefix and writes target_tok
-// and tau.  The kernel boundary orders (1) before (2): no device-scope fence
-// is needed, which on a multi-XCD GPU would write back and invalidate L2.
-// The logits are streamed once (HBM-bound: 2 bytes per bf16 logit).
+// its (B+1) x splits keys, 16 lanes per row, counts the accepted prefix with
+// one ballot and writes target_tok and tau.  The kernel boundary orders (1)
+// before (2): no device-scope fence is needed, which on a multi-XCD GPU would
+// write back and invalidate L2.  The logits are streamed once (HBM-bound:
+// 2 bytes per bf16 logit).
 //
 // The drafter's own proposal at T = 0 (Fig. 1 caption: drafting time counts
 // the proposal and sampling of the drafted tokens) is the same reduction over
-// its C*B rows of logits, finished by one thread per row (argmax_finalize).
+// its C*B rows of logits, finished by 16 lanes per row (argmax_finalize).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -50,94 +51,104 @@ struct Vec16<BF16> {
   __device__ static inline float get(const V& v, int i) { return bf16_to_f32(v[i]); }
 };
 
-#ifndef LS_VERIFY_PACKED
-#define LS_VERIFY_PACKED 1
-#endif
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 // two bf16 (one 32-bit word) -> two 16-bit keys whose unsigned order is the
-// values' order: positive h -> h | 0x8000, negative h -> ~h.  -0 lands just
-// below +0 (0x7FFF vs 0x8000); the index search merges the two.
-__device__ __forceinline__ u16x2 order16x2(uint32_t x) {
-  const i16x2 h = __builtin_bit_cast(i16x2, x);
-  const u16x2 flip = __builtin_bit_cast(u16x2, i16x2(h >> 15)) | u16x2{0x8000, 0x8000};
-  return __builtin_bit_cast(u16x2, x) ^ flip;
+// values' order, with -0 and +0 equal: positive h -> h ^ 0x8000, negative
+// h -> -h (mod 2^16).  Every key of a real value is at least 1.
+__device__ __forceinline__ uint32_t key16x2(uint32_t x) {
+  const u16x2 s = __builtin_bit_cast(u16x2, i16x2(__builtin_bit_cast(i16x2, x) >> 15));  // 0xFFFF: negative
+  return __builtin_bit_cast(uint32_t, (__builtin_bit_cast(u16x2, x) ^ (s | u16x2{0x8000, 0x8000})) - s);
+}
+// the bf16 bits of a 16-bit key
+__device__ __forceinline__ uint16_t key16_bits(uint32_t k) {
+  return uint16_t(k >= 0x8000u ? k ^ 0x8000u : 0x10000u - k);
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, uint32_t(__shfl_xor(int(v), o, 64)));
-  return v;
+// wave max in registers (every lane gets it): quad swaps and rotations by 4
+// and 8 inside each 16-lane row (DPP), then the rows swap in pairs and the
+// wave's halves swap (v_permlane16_swap / v_permlane32_swap)
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(x), int(x), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, uint32_t(__shfl_xor(int(v), o, 64)));
-  return v;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x124>(v));  // row_ror:4
+  v = max(v, dpp_u32<0x128>(v));  // row_ror:8
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(uint32_t(a[0]), uint32_t(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(uint32_t(b[0]), uint32_t(b[1]));
 }
 
 // bf16 rows with 16-byte aligned chunks: the chunk's 8192 logits are one
-// 16-byte load per thread per 2048 logits (all in flight at once).  The
-// values are compared as packed 16-bit integer keys (two logits per
-// instruction), the workgroup agrees on the maximum key, and only the
-// threads that hold it search their registers for its lowest index.
+// 16-byte load per thread per 2048 logits (all in flight at once; the tail
+// chunk's missing vectors repeat its last one and are masked afterwards).
+// Each logit becomes one 32-bit key, value key in the high half and
+// 0xFFFF - (index in the chunk) in the low half, so a single max finds the
+// largest value and its lowest index.  Fast path: while the maximum is
+// positive, the raw bits ordered as signed 16-bit integers already order the
+// values that matter (the positive ones; every negative one and -0 rank below
+// them), so a key is one shift-or of the raw word.  A wave whose maximum is
+// not positive redoes its keys with key16x2, which orders every value and
+// merges -0 with +0.  One barrier merges the 4 waves.
 __device__ __forceinline__ uint64_t chunk_argmax_bf16(const uint16_t* __restrict__ x, int begin, int end,
                                                       int tid) {
   constexpr int U = kVerifyChunk / 8 / kThreads;
   static_assert(U * 8 * kThreads == kVerifyChunk, "one load per thread per 2048 logits");
+  static_assert(kVerifyChunk <= 8192, "indices in the chunk fit the low key half with room to spare");
   __shared__ uint32_t red[kThreads / 64];
   const u32x4v* xv = reinterpret_cast<const u32x4v*>(x + begin);
   const int nvec = (end - begin) / 8;
   u32x4v buf[U];
 #pragma unroll
+  for (int u = 0; u < U; ++u) buf[u] = __builtin_nontemporal_load(xv + min(u * kThreads + tid, nvec - 1));
+  // low key halves of the thread's elements in vector u = c0[e] - 8 * kThreads * u
+  // (c0 >= 0xFFFF - 8 * kThreads + 1 > 8 * kThreads * (U - 1): no borrow)
+  uint32_t c0[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c0[e] = 0xFFFFu - 8u * tid - e;
+
+  int32_t fast = INT32_MIN;
+#pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int v = u * kThreads + tid;
-    buf[u] = v < nvec ? __builtin_nontemporal_load(xv + v) : u32x4v{0, 0, 0, 0};
-  }
-  u16x2 best = {0, 0};  // 0: below every key of a real value
+    int32_t acc = INT32_MIN;
 #pragma unroll
-  for (int u = 0; u < U; ++u)
-    if (u * kThreads + tid < nvec) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) best = __builtin_elementwise_max(best, order16x2(buf[u][w]));
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t ww = buf[u][w];
+      acc = max(acc, max(int32_t((ww << 16) | c0[2 * w]), int32_t((ww & 0xFFFF0000u) | c0[2 * w + 1])));
     }
-  const uint32_t tmax = max(uint32_t(best[0]), uint32_t(best[1]));
-  const int lane = tid & 63, wave = tid >> 6;
-  uint32_t M = wave_max_u32(tmax);
-  if (lane == 0) red[wave] = M;
-  __syncthreads();
-  M = red[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) M = max(M, red[w]);
-  __syncthreads();
-  // +0 and -0 are the same value: a maximum of either sign matches both
-  const bool zero = M == 0x8000u || M == 0x7FFFu;
-  const uint32_t lo = zero ? 0x7FFFu : M, hi = zero ? 0x8000u : M;
-  uint32_t idx = 0xFFFFFFFFu;
-  if (tmax >= lo && tmax <= hi && M != 0u) {
-    // this thread's logits in index order: vector u*kThreads + tid, then word, then half
-#pragma unroll
-    for (int u = U - 1; u >= 0; --u)
-      if (u * kThreads + tid < nvec) {
-#pragma unroll
-        for (int w = 3; w >= 0; --w) {
-          const u16x2 k = order16x2(buf[u][w]);
-          const int i0 = begin + (u * kThreads + tid) * 8 + 2 * w;
-          if (k[1] >= lo && k[1] <= hi) idx = uint32_t(i0 + 1);
-          if (k[0] >= lo && k[0] <= hi) idx = uint32_t(i0);
-        }
-      }
+    fast = max(fast, u * kThreads + tid < nvec ? acc - 8 * kThreads * u : INT32_MIN);
   }
-  idx = wave_min_u32(idx);
-  if (lane == 0) red[wave] = idx;
-  __syncthreads();
-  idx = red[0];
+  // signed -> unsigned order: the value key becomes h ^ 0x8000, as key16x2 has it
+  uint32_t W = __builtin_amdgcn_readfirstlane(wave_max_u32(uint32_t(fast) ^ 0x80000000u));
+  if ((W >> 16) <= 0x8000u) {  // the wave's maximum is <= +0: exact keys for every value
+    uint32_t slow = 0;
 #pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) idx = min(idx, red[w]);
-  if (idx == 0xFFFFFFFFu) return 0ull;
-  const uint32_t h = M >= 0x8000u ? (M ^ 0x8000u) : (~M & 0xFFFFu);  // the bf16 bits back
-  return make_key(bf16_to_f32(uint16_t(h)), idx);
+    for (int u = 0; u < U; ++u) {
+      uint32_t acc = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t k = key16x2(buf[u][w]);
+        acc = max(acc, max((k << 16) | c0[2 * w], (k & 0xFFFF0000u) | c0[2 * w + 1]));
+      }
+      slow = max(slow, u * kThreads + tid < nvec ? acc - 8u * kThreads * u : 0u);
+    }
+    W = __builtin_amdgcn_readfirstlane(wave_max_u32(slow));
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane == 0) red[wave] = W;
+  __syncthreads();
+  uint32_t K = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) K = max(K, red[w]);
+  // every chunk holds at least one logit, so K >= 1 << 16
+  const uint32_t idx = uint32_t(begin) + (0xFFFFu - (K & 0xFFFFu));
+  return make_key(bf16_to_f32(key16_bits(K >> 16)), idx);
 }
 
 template <typename Ty>
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void verify_partial(
   const int begin = split * chunk;
   const int end = min(V, begin + chunk);
 
-  if constexpr (Ty::kBytes == 2 && LS_VERIFY_PACKED) {
+  if constexpr (Ty::kBytes == 2) {
     if (vec_ok) {
       const uint64_t k = chunk_argmax_bf16(x, begin, end, tid);
       if (tid == 0) part[int64_t(row) * nsplit + split] = k;
@@ -218,43 +229,58 @@ __global__ __launch_bounds__(kThreads) void verify_partial(
   }
 }
 
-// one workgroup per sequence: keys -> g_i -> accepted prefix -> tau
-__global__ __launch_bounds__(kThreads) void verify_finalize(
+// The nkeys partial keys of a row are reduced by kLanesPerRow lanes of one
+// wave: lane s takes keys s, s + kLanesPerRow, ..., then a max across the lanes.
+constexpr int kLanesPerRow = 16;
+__device__ __forceinline__ uint64_t row_key(const uint64_t* __restrict__ p, int nkeys, int sub) {
+  uint64_t k = 0;
+  for (int s = sub; s < nkeys; s += kLanesPerRow) k = p[s] > k ? p[s] : k;
+#pragma unroll
+  for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) {
+    const uint64_t other = shfl_xor_u64(k, o);
+    k = other > k ? other : k;
+  }
+  return k;
+}
+
+// one workgroup per sequence: keys -> g_i -> accepted prefix -> tau.  Rows
+// are spread kLanesPerRow lanes each over the workgroup (B + 1 <= 64 rows in
+// one pass); the draft tokens are requested first, so their latency hides
+// behind the key loads; the accepted prefix is one ballot of mismatches.
+constexpr int kFinalizeThreads = 64 * kLanesPerRow;
+__global__ __launch_bounds__(kFinalizeThreads) void verify_finalize(
     const uint64_t* __restrict__ part, const int32_t* __restrict__ draft,
-    int32_t* __restrict__ target_tok, int32_t* __restrict__ tau, int B, int nsplit) {
-  extern __shared__ uint64_t keys[];  // [(B+1) * nsplit]
+    int32_t* __restrict__ target_tok, int32_t* __restrict__ tau, int B, int nkeys) {
   __shared__ int32_t g[64];
   const int c = blockIdx.x;
   const int tid = threadIdx.x;
-  const int n = (B + 1) * nsplit;
-  const uint64_t* p = part + int64_t(c) * n;
-  for (int i = tid; i < n; i += kThreads) keys[i] = p[i];
-  __syncthreads();
-  for (int i = tid; i <= B; i += kThreads) {
-    uint64_t k = 0;
-    for (int s = 0; s < nsplit; ++s) k = keys[i * nsplit + s] > k ? keys[i * nsplit + s] : k;
-    const int32_t gi = int32_t(~uint32_t(k));
-    g[i] = gi;
-    target_tok[int64_t(c) * (B + 1) + i] = gi;
+  const int32_t dj = tid < B ? draft[int64_t(c) * B + tid] : 0;
+  const int row = tid / kLanesPerRow, sub = tid % kLanesPerRow;
+  if (row <= B) {
+    const uint64_t k = row_key(part + (int64_t(c) * (B + 1) + row) * nkeys, nkeys, sub);
+    if (sub == 0) {
+      const int32_t gi = int32_t(~uint32_t(k));
+      g[row] = gi;
+      target_tok[int64_t(c) * (B + 1) + row] = gi;
+    }
   }
   __syncthreads();
-  if (tid == 0) {
-    int M = 0;
-    while (M < B && draft[int64_t(c) * B + M] == g[M]) ++M;
-    tau[c] = M + 1;
+  if (tid < 64) {
+    // bit B stands for "all B drafts accepted"
+    const uint64_t miss = __ballot(tid < B && dj != g[tid]) | (uint64_t(1) << B);
+    if (tid == 0) tau[c] = int32_t(__builtin_ctzll(miss)) + 1;
   }
 }
 
-// one thread per row: the row's split keys -> its argmax token
+// kLanesPerRow lanes per row: the row's partial keys -> its argmax token
 __global__ __launch_bounds__(kThreads) void argmax_finalize(const uint64_t* __restrict__ part,
                                                             int32_t* __restrict__ tok, int rows,
-                                                            int nsplit) {
-  const int row = blockIdx.x * kThreads + threadIdx.x;
-  if (row >= rows) return;
-  const uint64_t* p = part + int64_t(row) * nsplit;
-  uint64_t k = 0;
-  for (int s = 0; s < nsplit; ++s) k = p[s] > k ? p[s] : k;
-  tok[row] = int32_t(~uint32_t(k));
+                                                            int nkeys) {
+  const int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+  const int row = int(t / kLanesPerRow), sub = int(t % kLanesPerRow);
+  if (row >= rows) return;  // whole 16-lane groups leave together (kThreads % 16 == 0)
+  const uint64_t k = row_key(part + int64_t(row) * nkeys, nkeys, sub);
+  if (sub == 0) tok[row] = int32_t(~uint32_t(k));
 }
 
 template <typename Ty>
@@ -280,7 +306,8 @@ ls_status launch_argmax(const ls_dims& d, const void* logits, int32_t* draft_tok
   const ls_status st = d.dtype == LS_BF16 ? launch_partials<BF16>(d, logits, rows, part, nsplit, stream)
                                           : launch_partials<F32>(d, logits, rows, part, nsplit, stream);
   if (st != LS_OK) return st;
-  hipLaunchKernelGGL(argmax_finalize, dim3(unsigned(cdiv(rows, kThreads))), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL(argmax_finalize, dim3(unsigned(cdiv(int64_t(rows) * kLanesPerRow, kThreads))),
+                     dim3(kThreads), 0, stream,
                      part, draft_tok, rows, nsplit);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
@@ -294,8 +321,8 @@ ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* dra
   const ls_status st = d.dtype == LS_BF16 ? launch_partials<BF16>(d, logits, rows, part, nsplit, stream)
                                           : launch_partials<F32>(d, logits, rows, part, nsplit, stream);
   if (st != LS_OK) return st;
-  const size_t shmem = sizeof(uint64_t) * size_t(d.B + 1) * nsplit;
-  hipLaunchKernelGGL(verify_finalize, dim3(d.C), dim3(kThreads), shmem, stream, part, draft,
+  static_assert(kMaxBlock + 1 <= 64, "one ballot covers the drafts, one pass covers the rows");
+  hipLaunchKernelGGL(verify_finalize, dim3(d.C), dim3(kFinalizeThreads), 0, stream, part, draft,
                      target_tok, tau, d.B, nsplit);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
