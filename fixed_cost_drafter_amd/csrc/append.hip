@@ -192,17 +192,21 @@ __device__ __forceinline__ float group_sum(float x) {
 // window slots (L + i) mod W of every KV head, their positions to ring_pos,
 // and seq_len advances by tau.  One workgroup per sequence does all of it, so
 // it is the only reader of seq_len in the launch and may update it in place.
-// Keys and values are staged in LDS (a group of heads at a time, 16-byte
-// loads), keys leave as 16-byte pieces (key layout) and values go into the key-tiled
-// layout with lanes over rows, so neighbouring lanes store neighbouring
-// window slots.
+// Work item p = (head, 16-byte piece, row), rows fastest: a thread copies the
+// key piece to its place in the key layout and scatters the value piece's
+// elements into the value layout, where neighbouring lanes (neighbouring rows)
+// land in neighbouring window slots of one dimension's tile row.  Every load
+// of a thread's items is in flight before its first store, and nothing waits
+// on another thread, so the latency is tau's load, one load and the stores,
+// whatever tau is.
+constexpr int kWindowUnroll = 4;  // items per thread per pass
 template <typename Ty, int D>
 __device__ __forceinline__ void append_window(
     const typename Ty::T* __restrict__ k_new, const typename Ty::T* __restrict__ v_new,
     const int32_t* __restrict__ tau_in, typename Ty::T* __restrict__ ring_k,
     typename Ty::T* __restrict__ ring_v, int32_t* __restrict__ ring_pos,
-    int32_t* __restrict__ seq_len, int32_t* __restrict__ err_flag, typename Ty::T* stage,
-    int stage_elems, int c, int Hkv, int W, int B) {
+    int32_t* __restrict__ seq_len, int32_t* __restrict__ err_flag, int c, int Hkv, int W, int B) {
+  using T = typename Ty::T;
   constexpr int kThreads = block_threads<D>();
   constexpr int E16 = 16 / Ty::kBytes;      // elements per 16-byte piece
   constexpr int V16 = D / E16;              // 16-byte pieces per key row
@@ -220,42 +224,35 @@ __device__ __forceinline__ void append_window(
   }
   const int slot0 = L % W;                  // window slot of row 0; row i -> slot0 + i (mod W)
   const bool tiled = value_tile(W) == 32;   // values in 32-key tiles (else one tile of W keys)
-  // a group of HG heads at a time: stage the group's tau rows [head][row][k | v]
-  // in LDS (every 16-byte load in flight at once: LDS stores never alias the
-  // global loads), then store keys as 16-byte pieces and values into the
-  // key tiles.  Index arithmetic stays 32-bit with divisions by constants:
-  // this workgroup's work grows with tau and must not be ALU-bound.
-  const int HG = max(1, min(Hkv, stage_elems / (B1 * 2 * D)));
-  for (int h0 = 0; h0 < Hkv; h0 += HG) {
-    const int hg = min(HG, Hkv - h0);
-    const int rows = hg * Tn;                 // (head, row) pairs, row fastest
-    for (int p = tid; p < rows * 2 * V16; p += kThreads) {
-      const int e = p % V16, half = (p / V16) & 1, pr = p / (2 * V16);
-      const int hl = pr / Tn, i = pr - hl * Tn;
-      reinterpret_cast<uint4*>(stage + (pr * 2 + half) * D)[e] =
-          reinterpret_cast<const uint4*>((half ? v_new : k_new) +
-                                         ((int64_t(c) * B1 + i) * Hkv + h0 + hl) * D)[e];
+  const int items = Hkv * V16 * Tn;
+  for (int p0 = 0; p0 < items; p0 += kThreads * kWindowUnroll) {
+    uint4 kv[kWindowUnroll], vv[kWindowUnroll];
+#pragma unroll
+    for (int u = 0; u < kWindowUnroll; ++u) {
+      const int p = min(p0 + u * kThreads + tid, items - 1);  // past the end: repeat the last item
+      const int i = p % Tn, hp = p / Tn, e = hp % V16, hl = hp / V16;
+      const int64_t src = ((int64_t(c) * B1 + i) * Hkv + hl) * D + e * E16;
+      kv[u] = *reinterpret_cast<const uint4*>(k_new + src);
+      vv[u] = *reinterpret_cast<const uint4*>(v_new + src);
     }
-    __syncthreads();
-    for (int p = tid; p < rows * V16; p += kThreads) {
-      const int e = p % V16, pr = p / V16;
-      const int hl = pr / Tn, i = pr - hl * Tn;
-      const int slot = slot0 + i >= W ? slot0 + i - W : slot0 + i;
-      *reinterpret_cast<uint4*>(ring_k + key_index(int64_t(c) * Hkv + h0 + hl, W, D, slot, e * E16)) =
-          reinterpret_cast<const uint4*>(stage + pr * 2 * D)[e];
+#pragma unroll
+    for (int u = 0; u < kWindowUnroll; ++u) {
+      const int p = p0 + u * kThreads + tid;
+      if (p < items) {
+        const int i = p % Tn, hp = p / Tn, e = hp % V16, hl = hp / V16;
+        const int slot = slot0 + i >= W ? slot0 + i - W : slot0 + i;
+        const int64_t unit = int64_t(c) * Hkv + hl;
+        *reinterpret_cast<uint4*>(ring_k + key_index(unit, W, D, slot, e * E16)) = kv[u];
+        const T* ve = reinterpret_cast<const T*>(&vv[u]);
+#pragma unroll
+        for (int q = 0; q < E16; ++q) {
+          const int dim = e * E16 + q;
+          const int64_t idx = tiled ? ((unit * (W >> 5) + (slot >> 5)) * D + dim) * 32 + (slot & 31)
+                                    : (unit * D + dim) * W + slot;
+          ring_v[idx] = ve[q];
+        }
+      }
     }
-    // values: D lanes per (head, row) pair, one dimension each
-    constexpr int PAIRS = kThreads / D;       // pairs per pass
-    for (int pr = tid / D; pr < rows; pr += PAIRS) {
-      const int dim = tid % D;
-      const int hl = pr / Tn, i = pr - hl * Tn;
-      const int slot = slot0 + i >= W ? slot0 + i - W : slot0 + i;
-      const int64_t unit = int64_t(c) * Hkv + h0 + hl;
-      const int64_t idx = tiled ? ((unit * (W >> 5) + (slot >> 5)) * D + dim) * 32 + (slot & 31)
-                                : (unit * D + dim) * W + slot;
-      ring_v[idx] = stage[(pr * 2 + 1) * D + dim];
-    }
-    __syncthreads();
   }
   for (int i = tid; i < Tn; i += kThreads) {
     const int slot = slot0 + i >= W ? slot0 + i - W : slot0 + i;
@@ -273,13 +270,13 @@ __global__ __launch_bounds__(block_threads<D>()) void append_kernel(
     float* __restrict__ sum_n, typename Ty::T* __restrict__ slot_k,
     typename Ty::T* __restrict__ slot_v, const typename Ty::T* __restrict__ u,
     const float* __restrict__ log_lambda, int32_t* __restrict__ err_flag, int C, int Hkv, int W,
-    int S, int B, int stage_elems) {
+    int S, int B) {
   using T = typename Ty::T;
   extern __shared__ float4 smem4[];
   T* lds = reinterpret_cast<T*>(smem4);
   if (int(blockIdx.x) < C) {
-    append_window<Ty, D>(k_new, v_new, tau_in, ring_k, ring_v, ring_pos, seq_len, err_flag, lds,
-                         stage_elems, int(blockIdx.x), Hkv, W, B);
+    append_window<Ty, D>(k_new, v_new, tau_in, ring_k, ring_v, ring_pos, seq_len, err_flag,
+                         int(blockIdx.x), Hkv, W, B);
     return;
   }
   constexpr int LPS = lanes_per_slot<D>();
@@ -411,20 +408,15 @@ ls_status run(const ls_dims& d, const ls_state& st, const void* k_new, const voi
               const int32_t* tau, hipStream_t stream) {
   using T = typename Ty::T;
   const int ntile = int(cdiv(d.S, kSlotsPerBlock));
-  // LDS: the summary value tile [d][32] and the B+1 staged rows [B+1][2d]
-  // (fp32), or the window's staging (up to all heads' B+1 rows of k and v,
-  // capped at 40 KB; the window loops over head groups)
-  const size_t tile_bytes = size_t(D) * kSlotsPerBlock * sizeof(T) + size_t(d.B + 1) * 2 * D * sizeof(float);
-  const size_t head_bytes = size_t(d.B + 1) * 2 * D * sizeof(T);
-  const size_t heads = std::max<size_t>(1, std::min<size_t>(size_t(d.Hkv), (size_t(40) << 10) / head_bytes));
-  const size_t shmem = std::max(tile_bytes, heads * head_bytes);
-  const int stage_elems = int(shmem / sizeof(T));
+  // LDS of a summary workgroup: the value tile [d][32] and the B+1 staged
+  // rows [B+1][2d] (fp32); the window workgroups use none
+  const size_t shmem = size_t(D) * kSlotsPerBlock * sizeof(T) + size_t(d.B + 1) * 2 * D * sizeof(float);
   hipLaunchKernelGGL((append_kernel<Ty, D>), dim3(d.C + d.C * d.Hkv * ntile), dim3(block_threads<D>()), shmem,
                      stream, static_cast<const T*>(k_new), static_cast<const T*>(v_new), tau,
                      static_cast<T*>(st.ring_k), static_cast<T*>(st.ring_v), st.ring_pos,
                      st.seq_len, st.sum_m, st.sum_l, st.sum_n, static_cast<T*>(st.slot_k),
                      static_cast<T*>(st.slot_v), static_cast<const T*>(st.u), st.log_lambda,
-                     st.err_flag, d.C, d.Hkv, d.W, d.S, d.B, stage_elems);
+                     st.err_flag, d.C, d.Hkv, d.W, d.S, d.B);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
 
