@@ -153,6 +153,31 @@ def keys_to_rows(a: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(t[..., key_tile_order()].reshape(*lead, rows, d))
 
 
+def n_tiled(dtype: str, d: int, S: int) -> bool:
+    """bf16 states at d = 128 keep the summary numerators n in MFMA accumulator tiles."""
+    return dtype == "bf16" and d == 128 and S % 32 == 0
+
+
+def n_tile_order() -> np.ndarray:
+    """[32, 256]: float offset of (slot, entry) inside one stored 32-slot tile of n.
+
+    Entry e = 32t + 8g + 4b + r of slot s goes to float ((t*4 + g)*64 + 32b + s)*4 + r.
+    """
+    s = np.arange(32)[:, None]
+    e = np.arange(256)[None, :]
+    lane = s + 32 * ((e >> 2) & 1)
+    return (((e >> 5) * 4 + ((e >> 3) & 3)) * 64 + lane) * 4 + (e & 3)
+
+
+def n_to_rows(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Host copy of stored numerators [..., S, 2d] -> [slot][entry] order."""
+    *lead, S, e2 = a.shape
+    if not n_tiled(dtype, e2 // 2, S):
+        return a
+    t = a.reshape(*lead, S // 32, 32 * e2)
+    return np.ascontiguousarray(t[..., n_tile_order()].reshape(*lead, S, e2))
+
+
 def torch_dtype(dtype: str) -> torch.dtype:
     return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
 

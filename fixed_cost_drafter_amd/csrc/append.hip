@@ -13,22 +13,25 @@
 //
 // Grid: C window workgroups (one per sequence: the only reader and writer of
 // seq_len in the launch, so the update needs no second kernel and no
-// device-scope fence), then one workgroup per (sequence, KV head, 32 slots).
+// device-scope fence), then the summary workgroups.
 //
-// Summary workgroups: 32 slots, LPS lanes per slot (32; at most d for f32).
-// Lane g of a slot owns 2d/LPS consecutive entries of the slot's [k | v]
-// numerator n (the first half of the lanes the key half, the rest the value
-// half) and keeps them in registers from the first load to the last store,
-// so the fp32 state crosses HBM once each way.  All B+1 verified rows of the
-// (sequence, KV head) are staged once in LDS as fp32, whatever tau is, so no
-// load waits for tau.  The tau new rows are merged two at a time: the key
-// lanes form partial dot products with the slot query, a DPP butterfly over
-// the slot's lanes completes the scores, and one rescale per batch folds them
-// into (m, l, n).  The slots n / l leave as pooled keys (each lane's 8
-// dimensions as one 16-byte piece at its place in the key layout) and
-// pooled values; the values of the workgroup's 32
-// slots are one key tile ([d][32]) of the value layout the drafter reads,
-// assembled in LDS and stored contiguously.
+// bf16 (d = 128, S = 64 or 128): append_tiles below, the summary merge on
+// MFMA, 32-slot tiles two per workgroup.
+//
+// f32 (append_kernel): one workgroup per (sequence, KV head, 32 slots), LPS
+// lanes per slot (32; at most d).  Lane g of a slot owns 2d/LPS consecutive
+// entries of the slot's [k | v] numerator n (the first half of the lanes the
+// key half, the rest the value half) and keeps them in registers from the
+// first load to the last store, so the fp32 state crosses HBM once each way.
+// All B+1 verified rows of the (sequence, KV head) are staged once in LDS as
+// fp32, whatever tau is, so no load waits for tau.  The tau new rows are
+// merged two at a time: the key lanes form partial dot products with the
+// slot query, a DPP butterfly over the slot's lanes completes the scores,
+// and one rescale per batch folds them into (m, l, n).  The slots n / l
+// leave as pooled keys (each lane's entries at their place in the key
+// layout) and pooled values; the values of the workgroup's 32 slots are one
+// key tile ([d][32]) of the value layout the drafter reads, assembled in LDS
+// and stored contiguously.
 #include <algorithm>
 
 #include "common.hpp"
@@ -192,72 +195,75 @@ __device__ __forceinline__ float group_sum(float x) {
 // window slots (L + i) mod W of every KV head, their positions to ring_pos,
 // and seq_len advances by tau.  One workgroup per sequence does all of it, so
 // it is the only reader of seq_len in the launch and may update it in place.
-// Work item p = (head, 16-byte piece, row), rows fastest: a thread copies the
-// key piece to its place in the key layout and scatters the value piece's
-// elements into the value layout, where neighbouring lanes (neighbouring rows)
-// land in neighbouring window slots of one dimension's tile row.  Every load
-// of a thread's items is in flight before its first store, and nothing waits
-// on another thread, so the latency is tau's load, one load and the stores,
-// whatever tau is.
-constexpr int kWindowUnroll = 4;  // items per thread per pass
-template <typename Ty, int D>
+// Thread t takes row i = t mod (B+1) and the (head, 16-byte piece) pairs
+// t / (B+1), + G, + 2G, ... (G = threads / (B+1)): it copies the key piece to
+// its place in the key layout and scatters the value piece's elements into
+// the value layout, where lanes of neighbouring rows land in neighbouring
+// window slots of one dimension's tile row.  Every row of the block is
+// loaded, so the loads wait neither for tau nor for seq_len; only rows
+// i < tau are stored.  kWindowUnroll pieces' loads are in flight before their
+// stores, and nothing waits on another thread.
+template <typename Ty, int D, int kThreads, int kWindowUnroll>
 __device__ __forceinline__ void append_window(
     const typename Ty::T* __restrict__ k_new, const typename Ty::T* __restrict__ v_new,
     const int32_t* __restrict__ tau_in, typename Ty::T* __restrict__ ring_k,
     typename Ty::T* __restrict__ ring_v, int32_t* __restrict__ ring_pos,
     int32_t* __restrict__ seq_len, int32_t* __restrict__ err_flag, int c, int Hkv, int W, int B) {
   using T = typename Ty::T;
-  constexpr int kThreads = block_threads<D>();
   constexpr int E16 = 16 / Ty::kBytes;      // elements per 16-byte piece
   constexpr int V16 = D / E16;              // 16-byte pieces per key row
+  static_assert(kThreads > 48, "every row of the block gets a thread");
   const int tid = threadIdx.x;
   const int B1 = B + 1;
   int Tn = tau_in[c];
+  const int L = seq_len[c];
   if (Tn < 1 || Tn > B1) {
     if (tid == 0) atomicOr(err_flag, 1);
     Tn = Tn < 1 ? 1 : B1;
   }
-  const int L = seq_len[c];
   if (W == 0) {  // no window view: only the count advances
     if (tid == 0) seq_len[c] = L + Tn;
     return;
   }
-  const int slot0 = L % W;                  // window slot of row 0; row i -> slot0 + i (mod W)
-  const bool tiled = value_tile(W) == 32;   // values in 32-key tiles (else one tile of W keys)
-  const int items = Hkv * V16 * Tn;
-  for (int p0 = 0; p0 < items; p0 += kThreads * kWindowUnroll) {
-    uint4 kv[kWindowUnroll], vv[kWindowUnroll];
+  const int G = kThreads / B1, i = tid % B1, g = tid / B1;
+  const int pairs = Hkv * V16;
+  const int64_t src0 = (int64_t(c) * B1 + i) * Hkv * D;
+  const int64_t hstride = int64_t(W) * D;
+  const int kstep = key_tiled(W, D) ? 16 * 8 : E16;  // tiled keys: 16 pieces apart
+  const int tw = value_tile(W);
+  if (g < G) {
+    for (int hp0 = g; hp0 < pairs; hp0 += G * kWindowUnroll) {
+      uint4 kv[kWindowUnroll], vv[kWindowUnroll];
 #pragma unroll
-    for (int u = 0; u < kWindowUnroll; ++u) {
-      const int p = min(p0 + u * kThreads + tid, items - 1);  // past the end: repeat the last item
-      const int i = p % Tn, hp = p / Tn, e = hp % V16, hl = hp / V16;
-      const int64_t src = ((int64_t(c) * B1 + i) * Hkv + hl) * D + e * E16;
-      kv[u] = *reinterpret_cast<const uint4*>(k_new + src);
-      vv[u] = *reinterpret_cast<const uint4*>(v_new + src);
-    }
+      for (int u = 0; u < kWindowUnroll; ++u) {
+        const int hp = min(hp0 + u * G, pairs - 1);  // past the end: repeat the last pair
+        const int64_t src = src0 + (hp / V16) * D + (hp % V16) * E16;
+        kv[u] = *reinterpret_cast<const uint4*>(k_new + src);
+        vv[u] = *reinterpret_cast<const uint4*>(v_new + src);
+      }
+      if (i < Tn) {
+        // offsets of this thread's row: head hl and piece e add hl W d and
+        // e kstep (keys) or (e E16 + q) tw (value element q)
+        const int slot = (L + i) % W;
+        const int64_t kb0 = key_index(int64_t(c) * Hkv, W, D, slot, 0);
+        const int64_t vb0 = value_index(int64_t(c) * Hkv, W, D, slot, 0);
 #pragma unroll
-    for (int u = 0; u < kWindowUnroll; ++u) {
-      const int p = p0 + u * kThreads + tid;
-      if (p < items) {
-        const int i = p % Tn, hp = p / Tn, e = hp % V16, hl = hp / V16;
-        const int slot = slot0 + i >= W ? slot0 + i - W : slot0 + i;
-        const int64_t unit = int64_t(c) * Hkv + hl;
-        *reinterpret_cast<uint4*>(ring_k + key_index(unit, W, D, slot, e * E16)) = kv[u];
-        const T* ve = reinterpret_cast<const T*>(&vv[u]);
+        for (int u = 0; u < kWindowUnroll; ++u) {
+          const int hp = hp0 + u * G;
+          if (hp < pairs) {
+            const int e = hp % V16;
+            const int64_t ho = (hp / V16) * hstride;
+            *reinterpret_cast<uint4*>(ring_k + kb0 + ho + e * kstep) = kv[u];
+            const T* ve = reinterpret_cast<const T*>(&vv[u]);
+            T* vd = ring_v + vb0 + ho + int64_t(e * E16) * tw;
 #pragma unroll
-        for (int q = 0; q < E16; ++q) {
-          const int dim = e * E16 + q;
-          const int64_t idx = tiled ? ((unit * (W >> 5) + (slot >> 5)) * D + dim) * 32 + (slot & 31)
-                                    : (unit * D + dim) * W + slot;
-          ring_v[idx] = ve[q];
+            for (int q = 0; q < E16; ++q) vd[q * tw] = ve[q];
+          }
         }
       }
     }
   }
-  for (int i = tid; i < Tn; i += kThreads) {
-    const int slot = slot0 + i >= W ? slot0 + i - W : slot0 + i;
-    ring_pos[int64_t(c) * W + slot] = L + i;
-  }
+  if (tid < Tn) ring_pos[int64_t(c) * W + (L + tid) % W] = L + tid;
   if (tid == 0) seq_len[c] = L + Tn;
 }
 
@@ -275,8 +281,8 @@ __global__ __launch_bounds__(block_threads<D>()) void append_kernel(
   extern __shared__ float4 smem4[];
   T* lds = reinterpret_cast<T*>(smem4);
   if (int(blockIdx.x) < C) {
-    append_window<Ty, D>(k_new, v_new, tau_in, ring_k, ring_v, ring_pos, seq_len, err_flag,
-                         int(blockIdx.x), Hkv, W, B);
+    append_window<Ty, D, block_threads<D>(), 4>(k_new, v_new, tau_in, ring_k, ring_v, ring_pos,
+                                                 seq_len, err_flag, int(blockIdx.x), Hkv, W, B);
     return;
   }
   constexpr int LPS = lanes_per_slot<D>();
@@ -403,6 +409,290 @@ __global__ __launch_bounds__(block_threads<D>()) void append_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16, d = 128, S a multiple of 32: the summary merge on MFMA.
+//
+// Workgroup = (unit, kTPW tiles of 32 slots), 4 waves per tile.  For the 32
+// slots j of a tile and the tau new rows i of the unit, with
+// a_ji = u_j.k_i/sqrt(d) + (tau-1-i) ln(lambda_j):
+//   S^T = K U^T        rows x slots, 32x32x16 MFMA, each wave for itself;
+//   per slot (one lane column): m' = max(m + tau ln(lambda), max_i a_ji),
+//   s = e^(m + tau ln(lambda) - m'), w_ji = e^(a_ji - m'), l' = l s + sum_i w_ji;
+//   N^T = s N^T + R^T W^T    entries x slots, R = [k | v] of the new rows;
+//   wave q of a tile owns the entries 64q..64q+63 (two 32x32 accumulators).
+// The weights enter the MFMA as bf16 hi + lo (w - hi), so the products keep
+// about 16 bits of the fp32 weight; l sums the fp32 weights.  The state n is
+// read once into the accumulators and written once; its tiled layout makes
+// each 16-byte load or store of a wave 1 KB contiguous.  The workgroup
+// stages, once for its tiles, all
+// B+1 verified rows of the unit whatever tau is (keys row-major for S^T,
+// [entry][row] for R^T, rows past B+1 zero) and the slot queries, so no load
+// waits for tau; K-steps past tau are skipped and the weights of rows past
+// tau are 0.  The pooled slots leave through LDS as one key tile (operand
+// order) and one value tile ([d][32]) per tile, in 16-byte stores.  The
+// window workgroups of the same launch have the same 512 threads.
+// ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// A-row m of a 32-row score block holds verified row tile_row(m) (bits 2 and
+// 3 of m swapped): the S^T output then gives lanes 0-31 rows 0-7 and 16-23 of
+// the block, lanes 32-63 rows 8-15 and 24-31, which are the 8 consecutive
+// rows each lane feeds the N^T product as its B operand.
+__device__ __forceinline__ int tile_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+constexpr int kTPW = 2;  // 32-slot tiles per workgroup (S = 64: one workgroup per unit, S = 128: two)
+template <int kRB>  // 32-row score blocks: B + 1 <= 32 kRB
+__global__ __launch_bounds__(256 * kTPW) void append_tiles(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    const int32_t* __restrict__ tau_in, uint16_t* __restrict__ ring_k,
+    uint16_t* __restrict__ ring_v, int32_t* __restrict__ ring_pos, int32_t* __restrict__ seq_len,
+    float* __restrict__ sum_m, float* __restrict__ sum_l, float* __restrict__ sum_n,
+    uint16_t* __restrict__ slot_k, uint16_t* __restrict__ slot_v, const uint16_t* __restrict__ u,
+    const float* __restrict__ log_lambda, int32_t* __restrict__ err_flag, int C, int Hkv, int W,
+    int S, int B) {
+  constexpr int D = 128, E = 2 * D;
+  constexpr int kThreads = 256 * kTPW;
+  constexpr int RP = 32 * kRB;              // staged rows
+  constexpr int KLS = D + 8;                // key / query row stride (bf16)
+  constexpr int RTS = RP + 8;               // [entry][row] stride (bf16), 16-byte multiple
+  constexpr int kStage = RP * KLS + E * RTS + 32 * kTPW * KLS;
+  constexpr int kOut = kTPW * 2 * 32 * D;   // pooled key and value tiles
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kStage > kOut ? kStage : kOut];
+  uint16_t* KL = lds;                       // [RP][KLS]   verified keys
+  uint16_t* RT = KL + RP * KLS;             // [E][RTS]    verified [k | v], transposed
+  uint16_t* UL = RT + E * RTS;              // [32 kTPW][KLS] slot queries
+  if (int(blockIdx.x) < C) {
+    append_window<BF16, D, kThreads, 8>(k_new, v_new, tau_in, ring_k, ring_v, ring_pos, seq_len,
+                                         err_flag, int(blockIdx.x), Hkv, W, B);
+    return;
+  }
+  const int ngroup = S / (32 * kTPW);       // S is 64 or 128
+  const int bid = int(blockIdx.x) - C;
+  const int grp = bid % ngroup, unit = bid / ngroup;
+  const int c = unit / Hkv, h = unit % Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tl = wave >> 2, q4 = wave & 3;  // tile of the group, entry quarter
+  const int tile = grp * kTPW + tl;
+  const int ln = lane & 31, hi = lane >> 5;
+  const int B1 = B + 1;
+  const int j = tile * 32 + ln;             // this lane's slot
+  const int64_t sidx = int64_t(unit) * S + j;
+  // the wave's part of the tile's state (tiled numerator layout):
+  // acc[t][4k + r] = n[j][32 (2 q4 + t) + 8k + 4 hi + r]
+  float* nt = sum_n + (int64_t(unit) * S + tile * 32) * E + q4 * 2 * 4 * 64 * 4 + lane * 4;
+  f32x16 acc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(nt + (t * 4 + k) * 64 * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t][4 * k + r] = v[r];
+    }
+  const float m_old = sum_m[sidx], l_old = sum_l[sidx], lnl = log_lambda[j];
+
+  // staging loads: item (16-byte piece of [k | v], row), rows fastest, so the
+  // [entry][row] writes of a wave fall on consecutive banks; then the group's
+  // slot queries, 16 pieces per slot
+  constexpr int kItems = RP * (E / 8) / kThreads;
+  static_assert(kItems >= 1 && kItems * kThreads == RP * (E / 8), "whole passes");
+  constexpr int kUItems = 32 * kTPW * (D / 8) / kThreads;
+  static_assert(kUItems * kThreads == 32 * kTPW * (D / 8), "whole passes");
+  u16x8 x[kItems], xu[kUItems];
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) {
+    const int p = q * kThreads + tid, row = p % RP, pc = p / RP;
+    const int half = pc >> 4, e = pc & 15;
+    const int rc = min(row, B1 - 1);  // rows past B+1 load a real row and are zeroed
+    x[q] = *reinterpret_cast<const u16x8*>((half ? v_new : k_new) + ((int64_t(c) * B1 + rc) * Hkv + h) * D + 8 * e);
+  }
+#pragma unroll
+  for (int q = 0; q < kUItems; ++q) {
+    const int p = q * kThreads + tid, sl = p >> 4, pc = p & 15;
+    const int slot = grp * 32 * kTPW + sl;
+    xu[q] = *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + slot) * D + 8 * pc);
+  }
+  int Tn = tau_in[c];
+  Tn = Tn < 1 ? 1 : (Tn > B1 ? B1 : Tn);
+#pragma unroll
+  for (int q = 0; q < kItems; ++q) {
+    const int p = q * kThreads + tid, row = p % RP, pc = p / RP;
+    const int half = pc >> 4, e = pc & 15;
+    const u16x8 v = row < B1 ? x[q] : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (!half) *reinterpret_cast<u16x8*>(&KL[row * KLS + 8 * e]) = v;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) RT[(half * D + 8 * e + r) * RTS + row] = v[r];
+  }
+#pragma unroll
+  for (int q = 0; q < kUItems; ++q) {
+    const int p = q * kThreads + tid, sl = p >> 4, pc = p & 15;
+    *reinterpret_cast<u16x8*>(&UL[sl * KLS + 8 * pc]) = xu[q];
+  }
+  __syncthreads();
+
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  float l_new;
+  {
+    // S^T = K U^T; element 8 (s % 2) + e of block s / 2 is verified row 16 s + 8 hi + e
+    f32x16 sc[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      sc[rb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[(32 * rb + tile_row(ln)) * KLS + 16 * ks + 8 * hi]));
+        const bf16x8 b = as_bf16x8(*reinterpret_cast<const u16x8*>(&UL[(32 * tl + ln) * KLS + 16 * ks + 8 * hi]));
+        sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, sc[rb], 0, 0, 0);
+      }
+    }
+
+    // softmax of slot j over the new rows in base 2, K-step by K-step (rows
+    // 16 s .. 16 s + 15; steps past tau are skipped); the partner lane
+    // (lane ^ 32) holds the other 8 rows of each step.  x_ji = a_ji log2(e);
+    // a zero decay (ln(lambda) = -inf) enters the bias as -1e30, so every
+    // older row's exponent is hugely negative and 0 * bias never occurs.
+    constexpr float kLog2e = 1.4426950408889634f;
+    const int nks = (Tn + 15) >> 4;
+    const float sc2 = kLog2e / sqrtf(float(D));
+    const float lb2 = fmaxf(lnl, -1e30f) * kLog2e;
+    const float base2 = lnl == -INFINITY ? -INFINITY : fmaf(float(Tn), lnl, m_old) * kLog2e;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < 2 * kRB; ++s)
+      if (s < nks) {
+        const int rem = Tn - 16 * s - 8 * hi;         // rows e < rem are new rows
+        const float d0 = float(rem - 1);              // distance of e = 0 to row tau-1
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // the distance enters as an exact small integer: row tau-1 gets bias 0 exactly
+          const float x = fmaf(d0 - float(e), lb2, sc[s >> 1][8 * (s & 1) + e] * sc2);
+          sc[s >> 1][8 * (s & 1) + e] = e < rem ? x : -INFINITY;
+          mx = fmaxf(mx, sc[s >> 1][8 * (s & 1) + e]);
+        }
+      }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // row tau-1 always counts and has a finite exponent, so m2 is finite and
+    // 2^(-inf - m2) = 0 needs no test
+    const float m2 = fmaxf(base2, mx);
+    const float s_old = __builtin_amdgcn_exp2f(base2 - m2);
+    float lsum = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2 * kRB; ++s)
+      if (s < nks) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float w = __builtin_amdgcn_exp2f(sc[s >> 1][8 * (s & 1) + e] - m2);
+          sc[s >> 1][8 * (s & 1) + e] = w;
+          lsum += w;
+        }
+      }
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+      lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    l_new = fmaf(l_old, s_old, lsum);
+    const float m_new = m2 * 0.6931471805599453f;  // back to natural-log units
+
+    // N^T = s N^T + R^T W^T over the K-steps that hold new rows; the weights
+    // as bf16 pairs hi = rne(w), lo = rne(w - hi)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[t] *= s_old;
+#pragma unroll
+    for (int s = 0; s < 2 * kRB; ++s) {
+      if (s < nks) {
+        uint32_t whi[4], wlo[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const f32x2 w2 = {sc[s >> 1][8 * (s & 1) + e], sc[s >> 1][8 * (s & 1) + e + 1]};
+          const bf16x2 h2 = __builtin_convertvector(w2, bf16x2);
+          const f32x2 r2 = w2 - __builtin_convertvector(h2, f32x2);
+          whi[e / 2] = __builtin_bit_cast(uint32_t, h2);
+          wlo[e / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2));
+        }
+        const bf16x8 bhi = __builtin_bit_cast(bf16x8, uint4{whi[0], whi[1], whi[2], whi[3]});
+        const bf16x8 blo = __builtin_bit_cast(bf16x8, uint4{wlo[0], wlo[1], wlo[2], wlo[3]});
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(&RT[((2 * q4 + t) * 32 + ln) * RTS + 16 * s + 8 * hi]));
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bhi, acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, blo, acc[t], 0, 0, 0);
+        }
+      }
+    }
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<f32x4*>(nt + (t * 4 + k) * 64 * 4) =
+            f32x4{acc[t][4 * k], acc[t][4 * k + 1], acc[t][4 * k + 2], acc[t][4 * k + 3]};
+    if (q4 == 0 && hi == 0) {
+      sum_m[sidx] = m_new;
+      sum_l[sidx] = l_new;
+    }
+  }
+
+  // pooled slots n / l -> the tile's key tile (operand order) and value tile
+  // [d][32] in LDS, then 16-byte stores of the group's tiles.  A lane's 4
+  // consecutive entries are 4 consecutive dimensions of its slot: one 8-byte
+  // write in the key tile, 4 rows of the value tile.
+  const float il = 1.0f / l_new;
+  __syncthreads();  // every wave is done with the staged rows
+  {
+    uint16_t* kt = lds + tl * 2 * 32 * D;
+    uint16_t* vt = kt + 32 * D;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int ent = (2 * q4 + t) * 32 + 8 * k + 4 * hi;  // first of the 4 entries
+        const bf16x2 p0 = __builtin_convertvector((f32x2{acc[t][4 * k], acc[t][4 * k + 1]} * il), bf16x2);
+        const bf16x2 p1 = __builtin_convertvector((f32x2{acc[t][4 * k + 2], acc[t][4 * k + 3]} * il), bf16x2);
+        if (q4 < 2) {  // key entries (uniform in the wave)
+          *reinterpret_cast<uint2*>(&kt[key_index(0, 32, D, ln, ent)]) =
+              uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
+        } else {
+          const uint32_t w0 = __builtin_bit_cast(uint32_t, p0), w1 = __builtin_bit_cast(uint32_t, p1);
+          uint16_t* v = vt + (ent - D) * 32 + ln;
+          v[0] = uint16_t(w0);
+          v[32] = uint16_t(w0 >> 16);
+          v[64] = uint16_t(w1);
+          v[96] = uint16_t(w1 >> 16);
+        }
+      }
+  }
+  __syncthreads();
+  constexpr int P16 = 32 * D * 2 / 16;  // 16-byte pieces per key (or value) tile
+  const uint4* src = reinterpret_cast<const uint4*>(lds);
+#pragma unroll
+  for (int q = 0; q < 2 * P16 * kTPW / kThreads; ++q) {
+    const int p = q * kThreads + tid, t2 = p / (2 * P16), r = p % (2 * P16);
+    const int tt = grp * kTPW + t2;
+    if (r < P16)
+      reinterpret_cast<uint4*>(slot_k + key_index(unit, S, D, tt * 32, 0))[r] = src[p];
+    else
+      reinterpret_cast<uint4*>(slot_v + value_index(unit, S, D, tt * 32, 0))[r - P16] = src[p];
+  }
+}
+
+template <int kRB>
+void launch_tiles(const ls_dims& d, const ls_state& st, const void* k_new, const void* v_new,
+                  const int32_t* tau, hipStream_t stream) {
+  const int ngroup = d.S / (32 * kTPW);
+  hipLaunchKernelGGL((append_tiles<kRB>), dim3(unsigned(d.C + d.C * d.Hkv * ngroup)),
+                     dim3(256 * kTPW), 0, stream, static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), tau, static_cast<uint16_t*>(st.ring_k),
+                     static_cast<uint16_t*>(st.ring_v), st.ring_pos, st.seq_len, st.sum_m, st.sum_l,
+                     st.sum_n, static_cast<uint16_t*>(st.slot_k), static_cast<uint16_t*>(st.slot_v),
+                     static_cast<const uint16_t*>(st.u), st.log_lambda, st.err_flag, d.C, d.Hkv, d.W,
+                     d.S, d.B);
+}
+
 template <typename Ty, int D>
 ls_status run(const ls_dims& d, const ls_state& st, const void* k_new, const void* v_new,
               const int32_t* tau, hipStream_t stream) {
@@ -424,7 +714,11 @@ ls_status run(const ls_dims& d, const ls_state& st, const void* k_new, const voi
 
 ls_status launch_append(const ls_dims& d, const ls_state& st, const void* k_new,
                         const void* v_new, const int32_t* tau, hipStream_t stream) {
-  if (d.dtype == LS_BF16) return run<BF16, 128>(d, st, k_new, v_new, tau, stream);
+  if (d.dtype == LS_BF16) {  // d = 128, S in {0, 64, 128}
+    if (d.B + 1 <= 32) launch_tiles<1>(d, st, k_new, v_new, tau, stream);
+    else launch_tiles<2>(d, st, k_new, v_new, tau, stream);
+    return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+  }
   switch (d.d) {
     case 16: return run<F32, 16>(d, st, k_new, v_new, tau, stream);
     case 32: return run<F32, 32>(d, st, k_new, v_new, tau, stream);

@@ -105,6 +105,24 @@ __host__ __device__ inline int64_t key_index(int64_t unit, int rows, int d, int 
 }
 
 // ---------------------------------------------------------------------------
+// layout of the fp32 summary numerators n ([unit][S][2d] entries: keys |
+// values).  bf16 states at d = 128 (S a multiple of 32) keep each 32-slot
+// tile in the order of the summary update's MFMA accumulators, so that each
+// 64-lane 16-byte load or store of the state is 1 KB contiguous: entry
+// e = 32 t + 8 g + 4 b + r (t < 8, g < 4, b < 2, r < 4) of slot 32 T + s goes
+// to float ((t*4 + g)*64 + 32b + s)*4 + r of tile T.  Other states keep
+// [unit][S][2d].
+// ---------------------------------------------------------------------------
+__host__ __device__ inline bool n_tiled(int dtype_bytes, int d, int S) {
+  return dtype_bytes == 2 && d == 128 && S % 32 == 0;
+}
+__host__ __device__ inline int64_t n_index(bool tiled, int64_t unit, int S, int d, int slot, int e) {
+  if (!tiled) return (unit * S + slot) * 2 * d + e;
+  const int lane = (slot & 31) + 32 * ((e >> 2) & 1);
+  return (unit * S + (slot & ~31)) * 2 * d + ((((e >> 5) * 4 + ((e >> 3) & 3)) * 64 + lane) << 2) + (e & 3);
+}
+
+// ---------------------------------------------------------------------------
 // workspace layout (bytes), shared by the host code and the kernels
 // ---------------------------------------------------------------------------
 #ifndef LS_VERIFY_CHUNK

@@ -445,8 +445,7 @@ __global__ __launch_bounds__(kThreads) void init_finalize(
       const float* pn = part + part_off(s, units, unit, S, D) + 2 * S;
       a = fmaf(pn[int64_t(j0 + jj) * 2 * D + e], wsm[s * SPB + jj], a);
     }
-    const int64_t ni = (int64_t(unit) * S + j0 + jj) * 2 * D + e;
-    sum_n[ni] = a;
+    sum_n[n_index(n_tiled(Ty::kBytes, D, S), unit, S, D, j0 + jj, e)] = a;
     const int j = j0 + jj;
     if (e < D)
       Ty::store(slot_k, key_index(unit, S, D, j, e), a * s_inv_l[jj]);

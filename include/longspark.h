@@ -102,7 +102,10 @@ typedef struct ls_state {
   int32_t* seq_len;         /* [C] retained rows per sequence                */
   float* sum_m;             /* [C, Hkv, S] running max m (natural log units) */
   float* sum_l;             /* [C, Hkv, S] denominator l                     */
-  float* sum_n;             /* [C, Hkv, S, 2d] numerator n: keys | values    */
+  float* sum_n;             /* [C, Hkv, S, 2d] numerator n: keys | values;
+                               bf16 states keep each 32-slot tile in MFMA
+                               accumulator order: entry e = 32t + 8g + 4b + r
+                               of slot s at float ((t*4+g)*64 + 32b + s)*4 + r */
   void* slot_k;             /* [C, Hkv, S, d] dtype: n[:d] / l (32-key
                                tiles in MFMA operand order when d = 128)    */
   void* slot_v;             /* dtype n[d:] / l in key tiles of 32:

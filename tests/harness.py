@@ -61,9 +61,11 @@ def exact(name, got, ref):
 def compare_state(runner, ost: O.OracleState, dtype, heads=None):
     """GPU state vs oracle state; ``heads`` restricts the float checks."""
     snap = runner.snapshot()
-    # the library keeps window and slot values in key tiles [rows/tw][d][tw]
-    # and, at d = 128, keys in 32-key tiles in MFMA operand order
-    from fixed_cost_drafter_amd.binding import keys_to_rows, values_to_rows
+    # the library keeps window and slot values in key tiles [rows/tw][d][tw],
+    # at d = 128 keys in 32-key tiles in MFMA operand order, and bf16
+    # numerators in 32-slot accumulator tiles
+    from fixed_cost_drafter_amd.binding import keys_to_rows, n_to_rows, values_to_rows
+    snap["sum_n"] = n_to_rows(snap["sum_n"], dtype)
     snap["ring_v"] = values_to_rows(snap["ring_v"])
     snap["slot_v"] = values_to_rows(snap["slot_v"])
     snap["ring_k"] = keys_to_rows(snap["ring_k"])

@@ -244,3 +244,25 @@ def test_key_tile_order(LB):
     small = rng.random((1, 2, 48, 128)).astype(np.float32)
     assert LB.keys_to_rows(small) is small
     assert not LB.key_tiled(64, 64) and LB.key_tiled(1024, 128)
+
+
+def test_n_tile_order(LB):
+    """The stored numerator tile is a permutation in which the summary update's
+    accumulator load (entry block t, group g, lanes 32b + s: slot s, entries
+    32t + 8g + 4b .. + 3) is 1 KB of consecutive 16-byte pieces."""
+    import numpy as np
+    o = LB.n_tile_order()
+    assert sorted(o.ravel().tolist()) == list(range(32 * 256))
+    assert np.all(np.diff(o.reshape(32, 64, 4), axis=-1) == 1)
+    for t in range(8):
+        for g in range(4):
+            for lane in range(64):
+                s, b = lane % 32, lane // 32
+                assert o[s, 32 * t + 8 * g + 4 * b] == ((t * 4 + g) * 64 + lane) * 4
+    rng = np.random.default_rng(6)
+    rows = rng.random((2, 3, 64, 256)).astype(np.float32)
+    stored = np.empty_like(rows)
+    stored.reshape(2, 3, 2, 32 * 256)[..., o] = rows.reshape(2, 3, 2, 32, 256)
+    assert np.array_equal(LB.n_to_rows(stored, "bf16"), rows)
+    assert LB.n_to_rows(rows, "f32") is rows
+

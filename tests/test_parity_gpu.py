@@ -58,6 +58,10 @@ SMALL = {
     "bf16_wrap": WLM.Workload(
         "bf16_wrap", "bf16", C=5, Hq=4, Hkv=4, d=128, L0=130, W=32, S=64, B=16, V=9000,
         rounds=14, p_match=0.75, seed=15),
+    # the summary merge with two 32-row score blocks (B + 1 > 32) over 128 slots
+    "bf16_s128_b40": WLM.Workload(
+        "bf16_s128_b40", "bf16", C=2, Hq=2, Hkv=2, d=128, L0=90, W=128, S=128, B=40, V=1504,
+        rounds=5, p_match=0.92, seed=20),
 }
 
 
