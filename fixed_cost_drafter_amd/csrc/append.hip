@@ -412,9 +412,9 @@ __global__ __launch_bounds__(block_threads<D>()) void append_kernel(
 // ---------------------------------------------------------------------------
 // bf16, d = 128, S a multiple of 32: the summary merge on MFMA.
 //
-// Workgroup = (unit, kTPW tiles of 32 slots), 4 waves per tile.  For the 32
-// slots j of a tile and the tau new rows i of the unit, with
-// a_ji = u_j.k_i/sqrt(d) + (tau-1-i) ln(lambda_j):
+// Workgroup = one unit (sequence, KV head) with its S / 32 tiles of 32 slots,
+// 4 waves per tile.  For the 32 slots j of a tile and the tau new rows i of
+// the unit, with a_ji = u_j.k_i/sqrt(d) + (tau-1-i) ln(lambda_j):
 //   S^T = K U^T        rows x slots, 32x32x16 MFMA, each wave for itself;
 //   per slot (one lane column): m' = max(m + tau ln(lambda), max_i a_ji),
 //   s = e^(m + tau ln(lambda) - m'), w_ji = e^(a_ji - m'), l' = l s + sum_i w_ji;
@@ -424,13 +424,13 @@ __global__ __launch_bounds__(block_threads<D>()) void append_kernel(
 // about 16 bits of the fp32 weight; l sums the fp32 weights.  The state n is
 // read once into the accumulators and written once; its tiled layout makes
 // each 16-byte load or store of a wave 1 KB contiguous.  The workgroup
-// stages, once for its tiles, all
-// B+1 verified rows of the unit whatever tau is (keys row-major for S^T,
-// [entry][row] for R^T, rows past B+1 zero) and the slot queries, so no load
-// waits for tau; K-steps past tau are skipped and the weights of rows past
-// tau are 0.  The pooled slots leave through LDS as one key tile (operand
-// order) and one value tile ([d][32]) per tile, in 16-byte stores.  The
-// window workgroups of the same launch have the same 512 threads.
+// stages, once for its tiles, all B+1 verified rows of the unit whatever tau
+// is (keys row-major for S^T, [entry][row] for R^T, rows past B+1 zero) and
+// the slot queries, so no load waits for tau; K-steps past tau are skipped
+// and the weights of rows past tau are 0.  The pooled slots leave through LDS
+// as one key tile (operand order) and one value tile ([d][32]) per tile, in
+// 16-byte stores.  The window workgroups of the same launch have the same
+// 256 S / 32 threads (1024 at S = 128), which keeps their stores short.
 // ---------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -440,8 +440,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // rows each lane feeds the N^T product as its B operand.
 __device__ __forceinline__ int tile_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-constexpr int kTPW = 2;  // 32-slot tiles per workgroup (S = 64: one workgroup per unit, S = 128: two)
-template <int kRB>  // 32-row score blocks: B + 1 <= 32 kRB
+// kRB: 32-row score blocks (B + 1 <= 32 kRB); kTPW = S / 32 tiles: one
+// workgroup per unit
+template <int kRB, int kTPW>
 __global__ __launch_bounds__(256 * kTPW) void append_tiles(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ tau_in, uint16_t* __restrict__ ring_k,
@@ -466,14 +467,12 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
                                          err_flag, int(blockIdx.x), Hkv, W, B);
     return;
   }
-  const int ngroup = S / (32 * kTPW);       // S is 64 or 128
-  const int bid = int(blockIdx.x) - C;
-  const int grp = bid % ngroup, unit = bid / ngroup;
+  const int unit = int(blockIdx.x) - C;
   const int c = unit / Hkv, h = unit % Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tl = wave >> 2, q4 = wave & 3;  // tile of the group, entry quarter
-  const int tile = grp * kTPW + tl;
+  const int tile = tl;
   const int ln = lane & 31, hi = lane >> 5;
   const int B1 = B + 1;
   const int j = tile * 32 + ln;             // this lane's slot
@@ -510,7 +509,7 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
 #pragma unroll
   for (int q = 0; q < kUItems; ++q) {
     const int p = q * kThreads + tid, sl = p >> 4, pc = p & 15;
-    const int slot = grp * 32 * kTPW + sl;
+    const int slot = sl;
     xu[q] = *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + slot) * D + 8 * pc);
   }
   int Tn = tau_in[c];
@@ -672,23 +671,22 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
 #pragma unroll
   for (int q = 0; q < 2 * P16 * kTPW / kThreads; ++q) {
     const int p = q * kThreads + tid, t2 = p / (2 * P16), r = p % (2 * P16);
-    const int tt = grp * kTPW + t2;
     if (r < P16)
-      reinterpret_cast<uint4*>(slot_k + key_index(unit, S, D, tt * 32, 0))[r] = src[p];
+      reinterpret_cast<uint4*>(slot_k + key_index(unit, S, D, t2 * 32, 0))[r] = src[p];
     else
-      reinterpret_cast<uint4*>(slot_v + value_index(unit, S, D, tt * 32, 0))[r - P16] = src[p];
+      reinterpret_cast<uint4*>(slot_v + value_index(unit, S, D, t2 * 32, 0))[r - P16] = src[p];
   }
 }
 
-template <int kRB>
+template <int kRB, int kTPW>
 void launch_tiles(const ls_dims& d, const ls_state& st, const void* k_new, const void* v_new,
                   const int32_t* tau, hipStream_t stream) {
-  const int ngroup = d.S / (32 * kTPW);
-  hipLaunchKernelGGL((append_tiles<kRB>), dim3(unsigned(d.C + d.C * d.Hkv * ngroup)),
-                     dim3(256 * kTPW), 0, stream, static_cast<const uint16_t*>(k_new),
-                     static_cast<const uint16_t*>(v_new), tau, static_cast<uint16_t*>(st.ring_k),
-                     static_cast<uint16_t*>(st.ring_v), st.ring_pos, st.seq_len, st.sum_m, st.sum_l,
-                     st.sum_n, static_cast<uint16_t*>(st.slot_k), static_cast<uint16_t*>(st.slot_v),
+  const int units = d.S > 0 ? d.C * d.Hkv : 0;
+  hipLaunchKernelGGL((append_tiles<kRB, kTPW>), dim3(unsigned(d.C + units)), dim3(256 * kTPW), 0,
+                     stream, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                     tau, static_cast<uint16_t*>(st.ring_k), static_cast<uint16_t*>(st.ring_v),
+                     st.ring_pos, st.seq_len, st.sum_m, st.sum_l, st.sum_n,
+                     static_cast<uint16_t*>(st.slot_k), static_cast<uint16_t*>(st.slot_v),
                      static_cast<const uint16_t*>(st.u), st.log_lambda, st.err_flag, d.C, d.Hkv, d.W,
                      d.S, d.B);
 }
@@ -714,9 +712,15 @@ ls_status run(const ls_dims& d, const ls_state& st, const void* k_new, const voi
 
 ls_status launch_append(const ls_dims& d, const ls_state& st, const void* k_new,
                         const void* v_new, const int32_t* tau, hipStream_t stream) {
-  if (d.dtype == LS_BF16) {  // d = 128, S in {0, 64, 128}
-    if (d.B + 1 <= 32) launch_tiles<1>(d, st, k_new, v_new, tau, stream);
-    else launch_tiles<2>(d, st, k_new, v_new, tau, stream);
+  if (d.dtype == LS_BF16) {  // d = 128, S in {0, 64, 128}; S = 0 runs the window part only
+    const bool four = d.S != 64;
+    if (d.B + 1 <= 32) {
+      if (four) launch_tiles<1, 4>(d, st, k_new, v_new, tau, stream);
+      else launch_tiles<1, 2>(d, st, k_new, v_new, tau, stream);
+    } else {
+      if (four) launch_tiles<2, 4>(d, st, k_new, v_new, tau, stream);
+      else launch_tiles<2, 2>(d, st, k_new, v_new, tau, stream);
+    }
     return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
   }
   switch (d.d) {
