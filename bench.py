@@ -82,7 +82,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 ENTRY_KERNELS = {
     "verify": ("verify_partial", "verify_finalize"),
     "verify_sampling": ("samp_stats", "samp_decide", "samp_sums", "samp_draw"),
-    "append": ("append_kernel",),
+    "append": ("append_tiles", "append_kernel"),
     "draft": ("draft_direct", "draft_combine", "draft_generic"),
     "verify_attention": ("attn_mfma_partial", "attn_combine", "attn_generic"),
     "init": ("init_mfma32_partial", "init_generic_partial", "init_finalize"),
