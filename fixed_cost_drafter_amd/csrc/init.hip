@@ -438,22 +438,38 @@ __global__ __launch_bounds__(kThreads) void init_finalize(
     s_inv_l[tid] = 1.0f / l;
   }
   __syncthreads();
-  for (int p = tid; p < nj * 2 * D; p += kThreads) {
-    const int jj = p / (2 * D), e = p % (2 * D);
-    float a = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float* pn = part + part_off(s, units, unit, S, D) + 2 * S;
-      a = fmaf(pn[int64_t(j0 + jj) * 2 * D + e], wsm[s * SPB + jj], a);
-    }
-    sum_n[n_index(n_tiled(Ty::kBytes, D, S), unit, S, D, j0 + jj, e)] = a;
+  // 4 consecutive entries of one slot per thread, one 16-byte piece of the
+  // stored numerators (both layouts keep entries 4q .. 4q+3 of a slot
+  // together).  Tiled numerators: neighbouring threads take neighbouring
+  // slots of one piece position, so the pieces they store are contiguous;
+  // otherwise neighbouring threads take a slot's neighbouring pieces.
+  const bool ntiled = n_tiled(Ty::kBytes, D, S);
+  auto entries4 = [&](int jj, int e) {
     const int j = j0 + jj;
-    if (e < D)
-      Ty::store(slot_k, key_index(unit, S, D, j, e), a * s_inv_l[jj]);
-    else  // values in key tiles of 32 (one tile of S keys when S % 32 != 0)
-      Ty::store(slot_v,
-                S % 32 == 0 ? ((int64_t(unit) * (S >> 5) + (j >> 5)) * D + (e - D)) * 32 + (j & 31)
-                            : (int64_t(unit) * D + (e - D)) * S + j,
-                a * s_inv_l[jj]);
+    f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nsplit; ++s) {
+      const float* pn = part + part_off(s, units, unit, S, D) + 2 * S + int64_t(j) * 2 * D + e;
+      const float w = wsm[s * SPB + jj];  // (partials are only 4-byte aligned for odd S)
+      a += f32x4{pn[0], pn[1], pn[2], pn[3]} * w;
+    }
+    *reinterpret_cast<f32x4*>(sum_n + n_index(ntiled, unit, S, D, j, e)) = a;
+    const float il = s_inv_l[jj];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (e < D)
+        Ty::store(slot_k, key_index(unit, S, D, j, e + r), a[r] * il);
+      else  // values in key tiles of 32 (one tile of S keys when S % 32 != 0)
+        Ty::store(slot_v,
+                  S % 32 == 0 ? ((int64_t(unit) * (S >> 5) + (j >> 5)) * D + (e + r - D)) * 32 + (j & 31)
+                              : (int64_t(unit) * D + (e + r - D)) * S + j,
+                  a[r] * il);
+    }
+  };
+  for (int p = tid; p < nj * (2 * D / 4); p += kThreads) {
+    if (ntiled)  // p = ((t*4 + g)*2 + b)*nj + slot: entry 32t + 8g + 4b
+      entries4(p % nj, (p / nj) * 4);
+    else
+      entries4(p / (2 * D / 4), (p % (2 * D / 4)) * 4);
   }
 
   // ring window: window slot ws holds the newest prefix position p with
