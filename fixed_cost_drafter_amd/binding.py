@@ -25,7 +25,7 @@ STATUS = {0: "LS_OK", 1: "LS_ERR_NULL", 2: "LS_ERR_SHAPE", 3: "LS_ERR_DTYPE",
           4: "LS_ERR_WORKSPACE", 5: "LS_ERR_ALIGN", 6: "LS_ERR_HIP"}
 EXPORTS = ("ls_workspace_bytes", "ls_summary_init", "ls_verify_greedy", "ls_append_accepted",
            "ls_draft_attention", "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention",
-           "ls_verify_sampling", "ls_status_string", "ls_version")
+           "ls_verify_sampling", "ls_verify_append", "ls_status_string", "ls_version")
 
 
 class LsDims(ctypes.Structure):
@@ -66,8 +66,10 @@ def _load() -> ctypes.CDLL:
     lib.ls_gather_boundary.argtypes = [D, P, I32, P, P, P, P]
     lib.ls_verify_attention.argtypes = [D, P, P, I64, P, I32, P, P, P, SZ, P, P]
     lib.ls_verify_sampling.argtypes = [D, P, P, P, ctypes.c_float, P, P, P, P, P, SZ, P]
+    lib.ls_verify_append.argtypes = [D, S, P, P, P, P, P, P, P]
     for f in ("ls_summary_init", "ls_verify_greedy", "ls_append_accepted", "ls_draft_attention",
-              "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention", "ls_verify_sampling"):
+              "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention", "ls_verify_sampling",
+              "ls_verify_append"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ls_status_string.argtypes = [ctypes.c_int]
     lib.ls_status_string.restype = ctypes.c_char_p
@@ -225,6 +227,13 @@ def ls_append_accepted(dims: LsDims, state: LsState, k_new, v_new, tau, stream=N
         _stream(stream)))
 
 
+def ls_verify_append(dims: LsDims, state: LsState, logits, draft, target_tok, tau, k_new, v_new,
+                     stream=None):
+    _check("ls_verify_append", _lib.ls_verify_append(
+        ctypes.byref(dims), ctypes.byref(state), _ptr(logits), _ptr(draft), _ptr(target_tok),
+        _ptr(tau), _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+
 def ls_draft_attention(dims: LsDims, state: LsState, q, k_blk, v_blk, out, stream=None):
     _check("ls_draft_attention", _lib.ls_draft_attention(
         ctypes.byref(dims), ctypes.byref(state), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(out),
@@ -326,6 +335,10 @@ class DrafterState:
 
     def append_accepted(self, k_new, v_new, tau, stream=None):
         ls_append_accepted(self.dims, self.c_state, k_new, v_new, tau, stream)
+
+    def verify_append(self, logits, draft, target_tok, tau, k_new, v_new, stream=None):
+        ls_verify_append(self.dims, self.c_state, logits, draft, target_tok, tau, k_new, v_new,
+                         stream)
 
     def draft_attention(self, q, k_blk, v_blk, out, stream=None):
         ls_draft_attention(self.dims, self.c_state, q, k_blk, v_blk, out, stream)

@@ -177,6 +177,19 @@ ls_status ls_append_accepted(const ls_dims* dims, const ls_state* state, const v
   return ls::launch_append(*dims, *state, k_new, v_new, tau, static_cast<hipStream_t>(stream));
 }
 
+ls_status ls_verify_append(const ls_dims* dims, const ls_state* state, const void* logits,
+                           const int32_t* draft, int32_t* target_tok, int32_t* tau,
+                           const void* k_new, const void* v_new, ls_stream stream) {
+  ls_status st = check_dims(dims);
+  if (st != LS_OK) return st;
+  st = check_state(state, *dims, 1);
+  if (st != LS_OK) return st;
+  if (!logits || !draft || !target_tok || !tau || !k_new || !v_new) return LS_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return LS_ERR_ALIGN;
+  return ls::launch_verify_append(*dims, *state, logits, draft, target_tok, tau, k_new, v_new,
+                                  static_cast<hipStream_t>(stream));
+}
+
 ls_status ls_draft_attention(const ls_dims* dims, const ls_state* state, const void* q,
                              const void* k_blk, const void* v_blk, void* out, ls_stream stream) {
   ls_status st = check_dims(dims);

@@ -34,6 +34,7 @@
 // and stored contiguously.
 #include <algorithm>
 
+#include "accept.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -202,25 +203,20 @@ __device__ __forceinline__ float group_sum(float x) {
 // window slots of one dimension's tile row.  Every row of the block is
 // loaded, so the loads wait neither for tau nor for seq_len; only rows
 // i < tau are stored.  kWindowUnroll pieces' loads are in flight before their
-// stores, and nothing waits on another thread.
+// stores.  Tn: tau, already clamped into [1, B+1] (its value is needed only
+// by the stores).
 template <typename Ty, int D, int kThreads, int kWindowUnroll>
 __device__ __forceinline__ void append_window(
-    const typename Ty::T* __restrict__ k_new, const typename Ty::T* __restrict__ v_new,
-    const int32_t* __restrict__ tau_in, typename Ty::T* __restrict__ ring_k,
-    typename Ty::T* __restrict__ ring_v, int32_t* __restrict__ ring_pos,
-    int32_t* __restrict__ seq_len, int32_t* __restrict__ err_flag, int c, int Hkv, int W, int B) {
+    const typename Ty::T* __restrict__ k_new, const typename Ty::T* __restrict__ v_new, int Tn,
+    typename Ty::T* __restrict__ ring_k, typename Ty::T* __restrict__ ring_v,
+    int32_t* __restrict__ ring_pos, int32_t* __restrict__ seq_len, int c, int Hkv, int W, int B) {
   using T = typename Ty::T;
   constexpr int E16 = 16 / Ty::kBytes;      // elements per 16-byte piece
   constexpr int V16 = D / E16;              // 16-byte pieces per key row
   static_assert(kThreads > 48, "every row of the block gets a thread");
   const int tid = threadIdx.x;
   const int B1 = B + 1;
-  int Tn = tau_in[c];
   const int L = seq_len[c];
-  if (Tn < 1 || Tn > B1) {
-    if (tid == 0) atomicOr(err_flag, 1);
-    Tn = Tn < 1 ? 1 : B1;
-  }
   if (W == 0) {  // no window view: only the count advances
     if (tid == 0) seq_len[c] = L + Tn;
     return;
@@ -231,40 +227,64 @@ __device__ __forceinline__ void append_window(
   const int64_t hstride = int64_t(W) * D;
   const int kstep = key_tiled(W, D) ? 16 * 8 : E16;  // tiled keys: 16 pieces apart
   const int tw = value_tile(W);
-  if (g < G) {
-    for (int hp0 = g; hp0 < pairs; hp0 += G * kWindowUnroll) {
-      uint4 kv[kWindowUnroll], vv[kWindowUnroll];
+  // pass hp0: pairs hp0, hp0 + G, ... (kWindowUnroll of them) of this row
+  auto load_pass = [&](int hp0, uint4 (&kv)[kWindowUnroll], uint4 (&vv)[kWindowUnroll]) {
 #pragma unroll
-      for (int u = 0; u < kWindowUnroll; ++u) {
-        const int hp = min(hp0 + u * G, pairs - 1);  // past the end: repeat the last pair
-        const int64_t src = src0 + (hp / V16) * D + (hp % V16) * E16;
-        kv[u] = *reinterpret_cast<const uint4*>(k_new + src);
-        vv[u] = *reinterpret_cast<const uint4*>(v_new + src);
-      }
-      if (i < Tn) {
-        // offsets of this thread's row: head hl and piece e add hl W d and
-        // e kstep (keys) or (e E16 + q) tw (value element q)
-        const int slot = (L + i) % W;
-        const int64_t kb0 = key_index(int64_t(c) * Hkv, W, D, slot, 0);
-        const int64_t vb0 = value_index(int64_t(c) * Hkv, W, D, slot, 0);
+    for (int u = 0; u < kWindowUnroll; ++u) {
+      const int hp = min(hp0 + u * G, pairs - 1);  // past the end: repeat the last pair
+      const int64_t src = src0 + (hp / V16) * D + (hp % V16) * E16;
+      kv[u] = *reinterpret_cast<const uint4*>(k_new + src);
+      vv[u] = *reinterpret_cast<const uint4*>(v_new + src);
+    }
+  };
+  auto store_pass = [&](int hp0, const uint4 (&kv)[kWindowUnroll], const uint4 (&vv)[kWindowUnroll],
+                        int64_t kb0, int64_t vb0) {
 #pragma unroll
-        for (int u = 0; u < kWindowUnroll; ++u) {
-          const int hp = hp0 + u * G;
-          if (hp < pairs) {
-            const int e = hp % V16;
-            const int64_t ho = (hp / V16) * hstride;
-            *reinterpret_cast<uint4*>(ring_k + kb0 + ho + e * kstep) = kv[u];
-            const T* ve = reinterpret_cast<const T*>(&vv[u]);
-            T* vd = ring_v + vb0 + ho + int64_t(e * E16) * tw;
+    for (int u = 0; u < kWindowUnroll; ++u) {
+      const int hp = hp0 + u * G;
+      if (hp < pairs) {
+        const int e = hp % V16;
+        const int64_t ho = (hp / V16) * hstride;
+        *reinterpret_cast<uint4*>(ring_k + kb0 + ho + e * kstep) = kv[u];
+        T* vd = ring_v + vb0 + ho + int64_t(e * E16) * tw;
+        const uint32_t w[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
 #pragma unroll
-            for (int q = 0; q < E16; ++q) vd[q * tw] = ve[q];
-          }
+        for (int q = 0; q < E16; ++q) {
+          if constexpr (Ty::kBytes == 2)
+            vd[q * tw] = T(w[q >> 1] >> (16 * (q & 1)));
+          else
+            vd[q * tw] = __uint_as_float(w[q]);
         }
       }
+    }
+  };
+  if (g < G) {
+    // offsets of this thread's row: head hl and piece e add hl W d and e
+    // kstep (keys) or (e E16 + q) tw (value element q)
+    const int slot = (L + i) % W;
+    const int64_t kb0 = key_index(int64_t(c) * Hkv, W, D, slot, 0);
+    const int64_t vb0 = value_index(int64_t(c) * Hkv, W, D, slot, 0);
+    for (int hp0 = g; hp0 < pairs; hp0 += G * kWindowUnroll) {
+      uint4 kv[kWindowUnroll], vv[kWindowUnroll];
+      load_pass(hp0, kv, vv);
+      if (i < Tn) store_pass(hp0, kv, vv, kb0, vb0);
     }
   }
   if (tid < Tn) ring_pos[int64_t(c) * W + (L + tid) % W] = L + tid;
   if (tid == 0) seq_len[c] = L + Tn;
+}
+
+// tau of sequence c read from device memory, clamped into [1, B+1]; a value
+// outside sets bit 0 of *err_flag (when flag is set: the window workgroup)
+__device__ __forceinline__ int read_tau(const int32_t* __restrict__ tau_in, int c, int B,
+                                        int32_t* __restrict__ err_flag, bool flag) {
+  const int B1 = B + 1;
+  int Tn = tau_in[c];
+  if (Tn < 1 || Tn > B1) {
+    if (flag && threadIdx.x == 0) atomicOr(err_flag, 1);
+    Tn = Tn < 1 ? 1 : B1;
+  }
+  return Tn;
 }
 
 template <typename Ty, int D>
@@ -281,8 +301,9 @@ __global__ __launch_bounds__(block_threads<D>()) void append_kernel(
   extern __shared__ float4 smem4[];
   T* lds = reinterpret_cast<T*>(smem4);
   if (int(blockIdx.x) < C) {
-    append_window<Ty, D, block_threads<D>(), 4>(k_new, v_new, tau_in, ring_k, ring_v, ring_pos,
-                                                 seq_len, err_flag, int(blockIdx.x), Hkv, W, B);
+    const int c = int(blockIdx.x);
+    append_window<Ty, D, block_threads<D>(), 4>(k_new, v_new, read_tau(tau_in, c, B, err_flag, true),
+                                                 ring_k, ring_v, ring_pos, seq_len, c, Hkv, W, B);
     return;
   }
   constexpr int LPS = lanes_per_slot<D>();
@@ -442,10 +463,22 @@ __device__ __forceinline__ int tile_row(int m) { return (m & ~12) | ((m & 4) << 
 
 // kRB: 32-row score blocks (B + 1 <= 32 kRB); kTPW = S / 32 tiles: one
 // workgroup per unit
-template <int kRB, int kTPW>
+// kVerify: tau is not an input but the accepted prefix of the greedy
+// verification whose partial argmax keys are vkeys (nkeys per row): every
+// workgroup derives it for its sequence, and the window workgroup also writes
+// target_tok and tau_out.
+struct VerifyKeys {
+  const uint64_t* keys;
+  int nkeys;
+  const int32_t* draft;
+  int32_t* target_tok;
+  int32_t* tau_out;
+};
+
+template <int kRB, int kTPW, bool kVerify>
 __global__ __launch_bounds__(256 * kTPW) void append_tiles(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ tau_in, uint16_t* __restrict__ ring_k,
+    const int32_t* __restrict__ tau_in, VerifyKeys vk, uint16_t* __restrict__ ring_k,
     uint16_t* __restrict__ ring_v, int32_t* __restrict__ ring_pos, int32_t* __restrict__ seq_len,
     float* __restrict__ sum_m, float* __restrict__ sum_l, float* __restrict__ sum_n,
     uint16_t* __restrict__ slot_k, uint16_t* __restrict__ slot_v, const uint16_t* __restrict__ u,
@@ -462,14 +495,26 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
   uint16_t* KL = lds;                       // [RP][KLS]   verified keys
   uint16_t* RT = KL + RP * KLS;             // [E][RTS]    verified [k | v], transposed
   uint16_t* UL = RT + E * RTS;              // [32 kTPW][KLS] slot queries
+  __shared__ int32_t g_tok[64];              // kVerify: the rows' argmax tokens
+  const int tid = threadIdx.x, lane = tid & 63;
   if (int(blockIdx.x) < C) {
-    append_window<BF16, D, kThreads, 8>(k_new, v_new, tau_in, ring_k, ring_v, ring_pos, seq_len,
-                                         err_flag, int(blockIdx.x), Hkv, W, B);
+    const int c = int(blockIdx.x);
+    int Tn;
+    if constexpr (kVerify) {  // tau first: its barrier must not hold the window's loads
+      const int32_t dj = lane < B ? vk.draft[int64_t(c) * B + lane] : 0;
+      accept_rows<kThreads>(vk.keys, vk.nkeys, c, B, g_tok, vk.target_tok);
+      __syncthreads();
+      Tn = accept_tau(g_tok, dj, B);
+      if (tid == 0) vk.tau_out[c] = Tn;
+    } else {
+      Tn = read_tau(tau_in, c, B, err_flag, true);
+    }
+    append_window<BF16, D, kThreads, 8>(k_new, v_new, Tn, ring_k, ring_v, ring_pos, seq_len, c,
+                                         Hkv, W, B);
     return;
   }
   const int unit = int(blockIdx.x) - C;
   const int c = unit / Hkv, h = unit % Hkv;
-  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tl = wave >> 2, q4 = wave & 3;  // tile of the group, entry quarter
   const int tile = tl;
@@ -512,8 +557,14 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
     const int slot = sl;
     xu[q] = *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + slot) * D + 8 * pc);
   }
-  int Tn = tau_in[c];
-  Tn = Tn < 1 ? 1 : (Tn > B1 ? B1 : Tn);
+  int Tn = 1;
+  int32_t dj = 0;
+  if constexpr (kVerify) {
+    dj = lane < B ? vk.draft[int64_t(c) * B + lane] : 0;
+    accept_rows<kThreads>(vk.keys, vk.nkeys, c, B, g_tok, nullptr);
+  } else {
+    Tn = read_tau(tau_in, c, B, err_flag, false);
+  }
 #pragma unroll
   for (int q = 0; q < kItems; ++q) {
     const int p = q * kThreads + tid, row = p % RP, pc = p / RP;
@@ -529,6 +580,7 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
     *reinterpret_cast<u16x8*>(&UL[sl * KLS + 8 * pc]) = xu[q];
   }
   __syncthreads();
+  if constexpr (kVerify) Tn = accept_tau(g_tok, dj, B);  // every wave, from the LDS tokens
 
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -678,17 +730,32 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
   }
 }
 
-template <int kRB, int kTPW>
+template <int kRB, int kTPW, bool kVerify>
 void launch_tiles(const ls_dims& d, const ls_state& st, const void* k_new, const void* v_new,
-                  const int32_t* tau, hipStream_t stream) {
+                  const int32_t* tau, const VerifyKeys& vk, hipStream_t stream) {
   const int units = d.S > 0 ? d.C * d.Hkv : 0;
-  hipLaunchKernelGGL((append_tiles<kRB, kTPW>), dim3(unsigned(d.C + units)), dim3(256 * kTPW), 0,
-                     stream, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-                     tau, static_cast<uint16_t*>(st.ring_k), static_cast<uint16_t*>(st.ring_v),
+  hipLaunchKernelGGL((append_tiles<kRB, kTPW, kVerify>), dim3(unsigned(d.C + units)),
+                     dim3(256 * kTPW), 0, stream, static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), tau, vk,
+                     static_cast<uint16_t*>(st.ring_k), static_cast<uint16_t*>(st.ring_v),
                      st.ring_pos, st.seq_len, st.sum_m, st.sum_l, st.sum_n,
                      static_cast<uint16_t*>(st.slot_k), static_cast<uint16_t*>(st.slot_v),
                      static_cast<const uint16_t*>(st.u), st.log_lambda, st.err_flag, d.C, d.Hkv, d.W,
                      d.S, d.B);
+}
+
+// bf16: the shape's instantiation (S = 0 runs the window part only)
+template <bool kVerify>
+void launch_tiles_for(const ls_dims& d, const ls_state& st, const void* k_new, const void* v_new,
+                      const int32_t* tau, const VerifyKeys& vk, hipStream_t stream) {
+  const bool four = d.S != 64;
+  if (d.B + 1 <= 32) {
+    if (four) launch_tiles<1, 4, kVerify>(d, st, k_new, v_new, tau, vk, stream);
+    else launch_tiles<1, 2, kVerify>(d, st, k_new, v_new, tau, vk, stream);
+  } else {
+    if (four) launch_tiles<2, 4, kVerify>(d, st, k_new, v_new, tau, vk, stream);
+    else launch_tiles<2, 2, kVerify>(d, st, k_new, v_new, tau, vk, stream);
+  }
 }
 
 template <typename Ty, int D>
@@ -712,15 +779,8 @@ ls_status run(const ls_dims& d, const ls_state& st, const void* k_new, const voi
 
 ls_status launch_append(const ls_dims& d, const ls_state& st, const void* k_new,
                         const void* v_new, const int32_t* tau, hipStream_t stream) {
-  if (d.dtype == LS_BF16) {  // d = 128, S in {0, 64, 128}; S = 0 runs the window part only
-    const bool four = d.S != 64;
-    if (d.B + 1 <= 32) {
-      if (four) launch_tiles<1, 4>(d, st, k_new, v_new, tau, stream);
-      else launch_tiles<1, 2>(d, st, k_new, v_new, tau, stream);
-    } else {
-      if (four) launch_tiles<2, 4>(d, st, k_new, v_new, tau, stream);
-      else launch_tiles<2, 2>(d, st, k_new, v_new, tau, stream);
-    }
+  if (d.dtype == LS_BF16) {  // d = 128, S in {0, 64, 128}
+    launch_tiles_for<false>(d, st, k_new, v_new, tau, VerifyKeys{}, stream);
     return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
   }
   switch (d.d) {
@@ -730,6 +790,23 @@ ls_status launch_append(const ls_dims& d, const ls_state& st, const void* k_new,
     case 128: return run<F32, 128>(d, st, k_new, v_new, tau, stream);
   }
   return LS_ERR_SHAPE;
+}
+
+ls_status launch_verify_append(const ls_dims& d, const ls_state& st, const void* logits,
+                               const int32_t* draft, int32_t* target_tok, int32_t* tau,
+                               const void* k_new, const void* v_new, hipStream_t stream) {
+  char* ws = static_cast<char*>(st.workspace);
+  if (d.dtype != LS_BF16) {  // f32: the two entry points' launches
+    const ls_status s1 = launch_verify(d, logits, draft, target_tok, tau, ws, stream);
+    return s1 != LS_OK ? s1 : launch_append(d, st, k_new, v_new, tau, stream);
+  }
+  const ls_status s1 = launch_verify_keys(d, logits, ws, stream);
+  if (s1 != LS_OK) return s1;
+  const WsLayout lay = ws_layout(d, 1);
+  const VerifyKeys vk{reinterpret_cast<const uint64_t*>(ws + lay.verify_part), lay.vsplit, draft,
+                      target_tok, tau};
+  launch_tiles_for<true>(d, st, k_new, v_new, nullptr, vk, stream);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
 
 }  // namespace ls

@@ -12,6 +12,15 @@ namespace ls {
 ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* draft,
                         int32_t* target_tok, int32_t* tau, char* ws, hipStream_t stream);
 
+// the verification's partial argmax keys only (into the workspace's key area)
+ls_status launch_verify_keys(const ls_dims& d, const void* logits, char* ws, hipStream_t stream);
+
+// greedy verification, then the append of the accepted rows (tau derived by
+// the append from the partial keys in st.workspace)
+ls_status launch_verify_append(const ls_dims& d, const ls_state& st, const void* logits,
+                               const int32_t* draft, int32_t* target_tok, int32_t* tau,
+                               const void* k_new, const void* v_new, hipStream_t stream);
+
 // drafter proposal at T = 0: argmax over V of each of the C*B rows
 ls_status launch_argmax(const ls_dims& d, const void* logits, int32_t* draft_tok, char* ws,
                         hipStream_t stream);

@@ -18,6 +18,7 @@
 // The drafter's own proposal at T = 0 (Fig. 1 caption: drafting time counts
 // the proposal and sampling of the drafted tokens) is the same reduction over
 // its C*B rows of logits, finished by 16 lanes per row (argmax_finalize).
+#include "accept.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -229,20 +230,6 @@ __global__ __launch_bounds__(kThreads) void verify_partial(
   }
 }
 
-// The nkeys partial keys of a row are reduced by kLanesPerRow lanes of one
-// wave: lane s takes keys s, s + kLanesPerRow, ..., then a max across the lanes.
-constexpr int kLanesPerRow = 16;
-__device__ __forceinline__ uint64_t row_key(const uint64_t* __restrict__ p, int nkeys, int sub) {
-  uint64_t k = 0;
-  for (int s = sub; s < nkeys; s += kLanesPerRow) k = p[s] > k ? p[s] : k;
-#pragma unroll
-  for (int o = kLanesPerRow / 2; o >= 1; o >>= 1) {
-    const uint64_t other = shfl_xor_u64(k, o);
-    k = other > k ? other : k;
-  }
-  return k;
-}
-
 // one workgroup per sequence: keys -> g_i -> accepted prefix -> tau.  Rows
 // are spread kLanesPerRow lanes each over the workgroup (B + 1 <= 64 rows in
 // one pass); the draft tokens are requested first, so their latency hides
@@ -255,20 +242,11 @@ __global__ __launch_bounds__(kFinalizeThreads) void verify_finalize(
   const int c = blockIdx.x;
   const int tid = threadIdx.x;
   const int32_t dj = tid < B ? draft[int64_t(c) * B + tid] : 0;
-  const int row = tid / kLanesPerRow, sub = tid % kLanesPerRow;
-  if (row <= B) {
-    const uint64_t k = row_key(part + (int64_t(c) * (B + 1) + row) * nkeys, nkeys, sub);
-    if (sub == 0) {
-      const int32_t gi = int32_t(~uint32_t(k));
-      g[row] = gi;
-      target_tok[int64_t(c) * (B + 1) + row] = gi;
-    }
-  }
+  accept_rows<kFinalizeThreads>(part, nkeys, c, B, g, target_tok);
   __syncthreads();
   if (tid < 64) {
-    // bit B stands for "all B drafts accepted"
-    const uint64_t miss = __ballot(tid < B && dj != g[tid]) | (uint64_t(1) << B);
-    if (tid == 0) tau[c] = int32_t(__builtin_ctzll(miss)) + 1;
+    const int t = accept_tau(g, dj, B);
+    if (tid == 0) tau[c] = t;
   }
 }
 
@@ -310,6 +288,14 @@ ls_status launch_argmax(const ls_dims& d, const void* logits, int32_t* draft_tok
                      dim3(kThreads), 0, stream,
                      part, draft_tok, rows, nsplit);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+}
+
+ls_status launch_verify_keys(const ls_dims& d, const void* logits, char* ws, hipStream_t stream) {
+  const WsLayout lay = ws_layout(d, 1);
+  uint64_t* part = reinterpret_cast<uint64_t*>(ws + lay.verify_part);
+  const int rows = d.C * (d.B + 1);
+  return d.dtype == LS_BF16 ? launch_partials<BF16>(d, logits, rows, part, lay.vsplit, stream)
+                            : launch_partials<F32>(d, logits, rows, part, lay.vsplit, stream);
 }
 
 ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* draft,

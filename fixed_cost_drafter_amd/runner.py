@@ -51,6 +51,14 @@ class PathRunner:
         self.state.summary_init(self.k_prefix, self.v_prefix, L0 or rows, rows, stream)
 
     def round(self, logits: torch.Tensor, dev: dict, stream=None):
+        """One drafting round: verification and update in one call (the update
+        derives tau from the verification's keys), then the draft attention."""
+        s, b = self.state, self.buf
+        s.verify_append(logits, dev["draft"], b.target_tok, b.tau, dev["k_new"], dev["v_new"], stream)
+        s.draft_attention(dev["q"], dev["k_blk"], dev["v_blk"], b.out, stream)
+
+    def round_separate(self, logits: torch.Tensor, dev: dict, stream=None):
+        """The same round through the three separate entry points."""
         s, b = self.state, self.buf
         s.verify_greedy(logits, dev["draft"], b.target_tok, b.tau, stream)
         s.append_accepted(dev["k_new"], dev["v_new"], b.tau, stream)

@@ -161,6 +161,20 @@ ls_status ls_verify_greedy(const ls_dims* dims, const void* logits, const int32_
 ls_status ls_append_accepted(const ls_dims* dims, const ls_state* state, const void* k_new,
                              const void* v_new, const int32_t* tau, ls_stream stream);
 
+/* Greedy verification followed by the per-round update (Fig. 2 (a) then
+ * (b): the target verifies the drafted block, the accepted rows extend the
+ * views).  The same results, bit for bit, as ls_verify_greedy (into
+ * target_tok and tau) then ls_append_accepted with that tau, in one launch
+ * fewer: the update derives tau itself from the verification's partial
+ * argmax keys, so the verification's finishing launch is not needed.
+ *   logits, draft, target_tok, tau: as in ls_verify_greedy (tau is written,
+ *        in [1, B+1]); the keys go to state->workspace.
+ *   k_new, v_new: as in ls_append_accepted.
+ * f32 shapes run the two entry points' launches. */
+ls_status ls_verify_append(const ls_dims* dims, const ls_state* state, const void* logits,
+                           const int32_t* draft, int32_t* target_tok, int32_t* tau,
+                           const void* k_new, const void* v_new, ls_stream stream);
+
 /* Drafter block attention (Fig. 2 (c)).
  *   q:            [C, B, Hq, d] dtype, block queries.
  *   k_blk, v_blk: [C, B, Hkv, d] dtype, block keys/values.

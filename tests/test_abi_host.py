@@ -119,6 +119,8 @@ def test_bad_dims_are_rejected_before_any_launch(LB, bad, status):
     st = LB.LsState()
     rc = LB.lib().ls_draft_attention(ctypes.byref(d), ctypes.byref(st), 16, 16, 16, 16, None)
     assert rc == status
+    rc = LB.lib().ls_verify_append(ctypes.byref(d), ctypes.byref(st), 16, 16, 16, 16, 16, 16, None)
+    assert rc == status
 
 
 @no_device
@@ -130,6 +132,7 @@ def test_null_state_and_pointers(LB):
     st = LB.LsState()  # all NULL
     assert L.ls_append_accepted(ctypes.byref(d), ctypes.byref(st), 16, 16, 16, None) == 1
     assert L.ls_verify_greedy(ctypes.byref(d), None, 16, 16, 16, 256, 1 << 30, None) == 1
+    assert L.ls_verify_append(ctypes.byref(d), ctypes.byref(st), 16, 16, 16, 16, 16, 16, None) == 1
 
 
 def _fake_state(LB, d, ws_bytes, align=16):
@@ -265,4 +268,23 @@ def test_n_tile_order(LB):
     stored.reshape(2, 3, 2, 32 * 256)[..., o] = rows.reshape(2, 3, 2, 32, 256)
     assert np.array_equal(LB.n_to_rows(stored, "bf16"), rows)
     assert LB.n_to_rows(rows, "f32") is rows
+
+
+@no_device
+def test_verify_append_validation(LB):
+    """The fused verification + update checks the state like ls_append_accepted and
+    every per-round pointer like both calls, before any launch."""
+    d = _dims(LB)
+    L = LB.lib()
+    st = _fake_state(LB, d, LB.ls_workspace_bytes(d, 1))
+    call = lambda *a: L.ls_verify_append(ctypes.byref(d), ctypes.byref(st), *a, None)
+    assert call(None, 16, 16, 16, 16, 16) == 1       # logits
+    assert call(16, None, 16, 16, 16, 16) == 1       # draft
+    assert call(16, 16, None, 16, 16, 16) == 1       # target_tok
+    assert call(16, 16, 16, None, 16, 16) == 1       # tau
+    assert call(16, 16, 16, 16, None, 16) == 1       # k_new
+    assert call(16, 16, 16, 16, 16, 24) == 5         # v_new not 16-byte aligned
+    small = _fake_state(LB, d, 256)
+    assert L.ls_verify_append(ctypes.byref(d), ctypes.byref(small), 16, 16, 16, 16, 16, 16,
+                              None) == 4             # workspace too small
 
