@@ -38,6 +38,7 @@ KERNEL_SOURCES = {
     "init": "fixed_cost_drafter_amd/csrc/init.hip",
     "verify_attention": "fixed_cost_drafter_amd/csrc/verify_attn.hip",
     "verify_sampling": "fixed_cost_drafter_amd/csrc/sampling.hip",
+    "verify_append": ("fixed_cost_drafter_amd/csrc/verify.hip", "fixed_cost_drafter_amd/csrc/append.hip"),
 }
 
 
@@ -45,9 +46,10 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_hash(rel: str) -> str:
+def source_hash(rel) -> str:
     h = hashlib.sha256()
-    for p in (rel, "fixed_cost_drafter_amd/csrc/common.hpp"):
+    rels = rel if isinstance(rel, tuple) else (rel,)
+    for p in (*rels, "fixed_cost_drafter_amd/csrc/common.hpp", "fixed_cost_drafter_amd/csrc/accept.hpp"):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -78,11 +80,13 @@ def algorithmic(wl, mean_tau: float, L0: int) -> dict:
 
 
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-# kernels that make up one call of each entry point (substrings of their names)
+# kernels that make up one call of each entry point: substrings of their
+# names (a tuple: all of its substrings)
 ENTRY_KERNELS = {
     "verify": ("verify_partial", "verify_finalize"),
+    "verify_append": ("verify_partial", ("append_tiles", "true>")),
     "verify_sampling": ("samp_stats", "samp_decide", "samp_sums", "samp_draw"),
-    "append": ("append_tiles", "append_kernel"),
+    "append": (("append_tiles", "false>"), "append_kernel"),
     "draft": ("draft_direct", "draft_combine", "draft_generic"),
     "verify_attention": ("attn_mfma_partial", "attn_combine", "attn_generic"),
     "init": ("init_mfma32_partial", "init_generic_partial", "init_finalize"),
@@ -161,7 +165,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> dict:
         f = w = 0.0
         seen = []
         for short, ent in out["kernels"].items():
-            if any(p in short for p in parts):
+            if any(all(q in short for q in (p if isinstance(p, tuple) else (p,))) for p in parts):
                 f += ent.get("fetch_bytes", 0.0)
                 w += ent.get("write_bytes", 0.0)
                 seen.append(short)
@@ -287,6 +291,12 @@ def run_gpu(args, wl):
         append_s=back_to_back(lambda i: s_.append_accepted(rounds[i % n_rounds]["k_new"],
                                                            rounds[i % n_rounds]["v_new"], b_.tau), args.steps),
     )
+    # the fused call the rounds use (verification keys + update deriving tau);
+    # the state keeps advancing, which the per-call cost does not depend on
+    kern["verify_append_s"] = back_to_back(
+        lambda i: s_.verify_append(pool[i % P][0], rounds[i % n_rounds]["draft"], b_.target_tok, b_.tau,
+                                   rounds[i % n_rounds]["k_new"], rounds[i % n_rounds]["v_new"]),
+        args.steps)
     out.update(main=main, kern=kern)
     if args.graph:
         out["graph"] = run_graph(wl.L0)
@@ -496,6 +506,10 @@ def main(argv=None):
             ent.update(alg_flop=int(alg["draft_flop"]), tflop_per_s=round(tf, 2),
                        mfma_frac=round(tf / MFMA_BF16_PEAK_TFS, 4))
         kernels[name] = ent
+    t_va = k["verify_append_s"]
+    bw_va = (alg["verify"] + alg["append"]) / t_va / 1e9
+    kernels["verify_append"] = dict(avg_us=round(t_va * 1e6, 3), alg_bytes=int(alg["verify"] + alg["append"]),
+                                    gb_per_s=round(bw_va, 1), hbm_frac=round(bw_va / HBM_PEAK_GBS, 4))
     init_s = g["init_s"]
     init_bw = alg["init"] / init_s / 1e9
     kernels["init"] = dict(avg_us=round(init_s * 1e6, 2), alg_bytes=int(alg["init"]),
