@@ -42,20 +42,27 @@ __device__ __host__ inline int64_t part_off(int split, int units, int unit, int 
 // ---------------------------------------------------------------------------
 // MFMA partial kernel, bf16, d = 128, S = 32 * NG slots.  2 * NG waves:
 // wave w owns slots 32 (w % NG) .. +31 and row half w / NG (rows 0-31 or
-// 32-63) of every 64-row tile, so each wave reads half the tile from LDS
-// once for 32 slots, two waves share a SIMD, and both products run on
-// v_mfma_f32_32x32x16_bf16:
+// 32-63) of every 64-row tile, two waves share a SIMD, and both products run
+// on v_mfma_f32_32x32x16_bf16:
 //   S^T[row][slot] = K U^T over the wave's 32 rows: A = 32 rows x 16 dims
-//     from the row-major K tile, B = U^T (registers, 8 k-steps).
+//     from the row-major K tile, B = U^T (8 k-steps, read from LDS).
 //     A-row m = 8j + 4h + r (j < 4, h < 2, r < 4) reads row 16(j/2) + 8h +
 //     4(j%2) + r of the half, so that the output lane (slot, half h) holds
 //     rows 8h..8h+7 and 16+8h..16+8h+7 in order: exactly the 8-row
 //     k-slices of the P^T operand of the second product.
-//   n^T[dim][slot] += [K|V]^T P^T per 16-row k-step: A = 32 dims x 16 rows
-//     from the transposed tile, B = P^T packed from the scores.
+//   n^T[dim][slot] += [K|V]^T P^T per 16-row k-step: A = 32 dims x 16 rows,
+//     read from the same row-major K and V tiles with ds_read_b64_tr_b16
+//     (two 4-row transposed reads per operand), B = P^T packed from the
+//     scores.
+// The tiles hold K and V rows as they arrive (256 bytes per row, no
+// transposition while staging); 16-byte chunk c of row r sits at chunk
+// c ^ tile_swz(r), which keeps the score reads (16 rows, one chunk) and the
+// transposed reads (4 rows x 4 chunks per 16 lanes) on distinct banks.
 // The two row halves of a slot group keep separate (m, l, n) and merge
 // through LDS at the end.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
 template <int NG>
 __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, int64_t rows_stride,
@@ -63,23 +70,20 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
     const float* __restrict__ log_lambda, int Hkv, float* __restrict__ part) {
   typedef float f32x16 __attribute__((ext_vector_type(16)));
   constexpr int D = 128, S = 32 * NG, NT = 128 * NG, TR = 64;
-  constexpr int KLS = D + 8;   // row-major K tile stride (bf16 elements)
-  // transposed [dim][row] tile: 144-byte rows (16-byte aligned), and the
-  // 8-row groups of dimension dim stored in the order g ^ ((dim >> 4) & 7),
-  // which spreads both the staging stores (8 dimensions apart across lanes)
-  // and the operand loads (consecutive dimensions) over all 64 banks
-  constexpr int VTS = TR + 8;
-  auto kvt_row = [](int dim, int row) { return (((row >> 3) ^ ((dim >> 4) & 7)) << 3) | (row & 7); };
+  constexpr int KLS = D + 8;   // slot-query row stride (bf16 elements)
+  constexpr int RS = D;        // K / V tile row stride: 256 bytes, swizzled chunks
   constexpr int PAIRS = TR * 8 / NT;  // row pairs staged per thread
   static_assert(PAIRS >= 1 && TR * 8 % NT == 0, "tile rows must cover the threads");
   constexpr int kInitPrefetch = PAIRS == 1 ? LS_INIT_PREFETCH : 1;
-  constexpr int kTileElems = TR * KLS + 2 * D * VTS + S * KLS;
+  constexpr int kTileElems = 2 * TR * RS + S * KLS;
   constexpr int kMergeFloats = NG * 64 * 131;  // per slot group and lane: m_true, m_run, l, 128 n
   constexpr int kLdsBytes = kTileElems * 2 > kMergeFloats * 4 ? kTileElems * 2 : kMergeFloats * 4;
   __shared__ __attribute__((aligned(16))) uint16_t smem[kLdsBytes / 2];
-  uint16_t* KL = smem;                         // [TR][KLS]
-  uint16_t* KVT = smem + TR * KLS;             // [2D][VTS]
-  uint16_t* UL = KVT + 2 * D * VTS;            // [S][KLS]: the slot queries
+  uint16_t* KL = smem;                         // [TR][RS] K rows
+  uint16_t* VL = smem + TR * RS;               // [TR][RS] V rows
+  uint16_t* UL = VL + TR * RS;                 // [S][KLS]: the slot queries
+  // element offset of 16-byte chunk c of tile row r
+  auto chunk_at = [](int r, int c) { return r * RS + ((c ^ tile_swz(r)) << 3); };
 
   const int split = blockIdx.x % nsplit;
   const int unit = blockIdx.x / nsplit;  // c * Hkv + h
@@ -152,20 +156,10 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
 #pragma unroll
     for (int pp = 0; pp < PAIRS; ++pp) {
       const int row0 = 2 * (rp + pp * (NT / 16));  // even row of the pair
-      *reinterpret_cast<u16x8*>(&KL[row0 * KLS + dg * 8]) = kr[uu][2 * pp];
-      *reinterpret_cast<u16x8*>(&KL[(row0 + 1) * KLS + dg * 8]) = kr[uu][2 * pp + 1];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // (row0, row0 + 1) of one dimension as one dword: v_perm of the two rows
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const uint4 k0 = __builtin_bit_cast(uint4, kr[uu][2 * pp]), k1 = __builtin_bit_cast(uint4, kr[uu][2 * pp + 1]);
-        const uint4 v0 = __builtin_bit_cast(uint4, vr[uu][2 * pp]), v1 = __builtin_bit_cast(uint4, vr[uu][2 * pp + 1]);
-        const uint32_t k0w[4] = {k0.x, k0.y, k0.z, k0.w}, k1w[4] = {k1.x, k1.y, k1.z, k1.w};
-        const uint32_t v0w[4] = {v0.x, v0.y, v0.z, v0.w}, v1w[4] = {v1.x, v1.y, v1.z, v1.w};
-        const uint32_t kk = __builtin_amdgcn_perm(k1w[e >> 1], k0w[e >> 1], sel);
-        const uint32_t vv = __builtin_amdgcn_perm(v1w[e >> 1], v0w[e >> 1], sel);
-        *reinterpret_cast<uint32_t*>(&KVT[(dg * 8 + e) * VTS + kvt_row(dg * 8 + e, row0)]) = kk;
-        *reinterpret_cast<uint32_t*>(&KVT[(D + dg * 8 + e) * VTS + kvt_row(D + dg * 8 + e, row0)]) = vv;
+      for (int q = 0; q < 2; ++q) {
+        *reinterpret_cast<u16x8*>(&KL[chunk_at(row0 + q, dg)]) = kr[uu][2 * pp + q];
+        *reinterpret_cast<u16x8*>(&VL[chunk_at(row0 + q, dg)]) = vr[uu][2 * pp + q];
       }
     }
     __syncthreads();
@@ -176,7 +170,7 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
     f32x16 s = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[prow * KLS + ks * 16 + hh * 8]));
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[chunk_at(prow, 2 * ks + hh)]));
       const bf16x8 b = as_bf16x8(*reinterpret_cast<const u16x8*>(&UL[slot * KLS + ks * 16 + hh * 8]));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
     }
@@ -248,15 +242,35 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
     }
     l_run += lsum;
 
-    // n^T[dim][slot] += [K|V]^T[dim][row] P^T[row][slot], 16 rows per k-step:
-    // A = dims 32db + m32, rows 32 half + 16t + 8hh .. +7 of the transposed tile
+    // n^T[dim][slot] += [K|V]^T[dim][row] P^T[row][slot], 16 rows per k-step.
+    // A operand of dimension block db: lane l takes dimension 32db + l % 32
+    // and rows 8(l/32) .. +7 of the k-step as two transposed 4-row reads:
+    // in 16-lane group g = l/16 reader lane r reads 4 dimensions
+    // 32db + 16(g%2) + 4(r%4) .. +3 of row 8(g/2) + r/4 (+4), and lane 4a + b
+    // of the group receives element b of readers a, a+4, a+8, a+12.
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const int g4 = lane >> 4, r16 = lane & 15;
+    const int tr_row = half * 32 + 8 * (g4 >> 1) + (r16 >> 2);     // + 16t (+ 4)
+    const int tr_dim = 16 * (g4 & 1) + 4 * (r16 & 3);               // + 32 (db % 4)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const int dim = db * 32 + m32;
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(
-            &KVT[dim * VTS + kvt_row(dim, half * 32 + t * 16 + hh * 8)]));
+        const uint16_t* tile = db < 4 ? KL : VL;
+        const int dim = 32 * (db & 3) + tr_dim;
+        i16x4 lo, hi;
+        {
+          const int row = tr_row + 16 * t;
+          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(tile + chunk_at(row, dim >> 3) + (dim & 7)));
+        }
+        {
+          const int row = tr_row + 16 * t + 4;
+          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(tile + chunk_at(row, dim >> 3) + (dim & 7)));
+        }
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[t], acc[db], 0, 0, 0);
       }
   }
