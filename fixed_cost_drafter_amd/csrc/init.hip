@@ -108,6 +108,27 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
         *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + (p >> 4)) * D + (p & 15) * 8);
   // the tile row read by this lane as A-row m32 of its half
   const int prow = half * 32 + 16 * (m32 >> 4) + 8 * ((m32 >> 2) & 1) + 4 * ((m32 >> 3) & 1) + (m32 & 3);
+  // LDS element offsets, the same for every tile:
+  //  score operand k-step ks: chunk 2 ks + hh of row prow of the K tile;
+  //  P.V operands: in 16-lane group g = lane / 16 reader lane r reads
+  //  dimensions 32 (db % 4) + 16 (g % 2) + 4 (r % 4) .. +3 of row
+  //  tr_row + 16 t + 4 u (u = 0, 1: the two 4-row halves of the operand).
+  //  With tile_swz, chunk 4 (db % 4) + c0 of such a row lands at
+  //  ((db % 4) ^ (row % 4)) << 2 | (c0 ^ ((row / 4) % 4)), and row % 4 and
+  //  (row / 4) % 4 do not depend on t, so an operand's offset is
+  //  pv_base[u] + pv_blk[db % 4] + 16 t RS (+ the V tile's offset).
+  int sc_off[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) sc_off[ks] = chunk_at(prow, 2 * ks + hh);
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int tr_row = half * 32 + 8 * (g4 >> 1) + (r16 >> 2);
+  const int c0 = 2 * (g4 & 1) + ((r16 & 3) >> 1);
+  int pv_base[2], pv_blk[4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    pv_base[u] = (tr_row + 4 * u) * RS + ((c0 ^ (((tr_row >> 2) + u) & 3)) << 3) + 4 * (r16 & 1);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pv_blk[k] = (k ^ (tr_row & 3)) << 5;
 
   float m_run = -INFINITY, l_run = 0.f;  // reference max (may lag) and weight sum
   float m_true = -INFINITY;               // exact running max
@@ -170,7 +191,7 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
     f32x16 s = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[chunk_at(prow, 2 * ks + hh)]));
+      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[sc_off[ks]]));
       const bf16x8 b = as_bf16x8(*reinterpret_cast<const u16x8*>(&UL[slot * KLS + ks * 16 + hh * 8]));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
     }
@@ -244,32 +265,18 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
 
     // n^T[dim][slot] += [K|V]^T[dim][row] P^T[row][slot], 16 rows per k-step.
     // A operand of dimension block db: lane l takes dimension 32db + l % 32
-    // and rows 8(l/32) .. +7 of the k-step as two transposed 4-row reads:
-    // in 16-lane group g = l/16 reader lane r reads 4 dimensions
-    // 32db + 16(g%2) + 4(r%4) .. +3 of row 8(g/2) + r/4 (+4), and lane 4a + b
-    // of the group receives element b of readers a, a+4, a+8, a+12.
+    // and rows 8(l/32) .. +7 of the k-step as two transposed 4-row reads
+    // (offsets above): lane 4a + b of a 16-lane group receives element b of
+    // the reads of lanes a, a+4, a+8, a+12, which cover 4 consecutive rows.
     typedef short i16x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const int g4 = lane >> 4, r16 = lane & 15;
-    const int tr_row = half * 32 + 8 * (g4 >> 1) + (r16 >> 2);     // + 16t (+ 4)
-    const int tr_dim = 16 * (g4 & 1) + 4 * (r16 & 3);               // + 32 (db % 4)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const uint16_t* tile = db < 4 ? KL : VL;
-        const int dim = 32 * (db & 3) + tr_dim;
-        i16x4 lo, hi;
-        {
-          const int row = tr_row + 16 * t;
-          lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(tile + chunk_at(row, dim >> 3) + (dim & 7)));
-        }
-        {
-          const int row = tr_row + 16 * t + 4;
-          hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(tile + chunk_at(row, dim >> 3) + (dim & 7)));
-        }
+        const uint16_t* tile = (db < 4 ? KL : VL) + 16 * t * RS + pv_blk[db & 3];
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + pv_base[0]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + pv_base[1]));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[t], acc[db], 0, 0, 0);
       }
