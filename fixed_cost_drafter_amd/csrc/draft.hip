@@ -192,10 +192,12 @@ __device__ __forceinline__ void chunk_pv(Softmax (&st)[2], const Half& v, const 
 // on one XCD when units is a multiple of 8 and the keys they share are
 // fetched from HBM once.  The window and slot chunks of key range kidx are
 // those with chunk % (ksplit*KPW) in [kidx*KPW, kidx*KPW + KPW); wave kq
-// takes residue kidx*KPW + kq.  Block chunk b (chunk ngl + b of the list)
-// belongs to the wave whose turn it falls on, which stages it in its own
-// LDS region and computes it before its other chunks, while their first
-// loads are in flight.  kEvery: every wave has at least one window or slot
+// takes residue kidx*KPW + kq.  Block chunk b belongs to key part b (wave b
+// of the first key range): the first wave of each SIMD gets its loads into
+// the memory pipeline microseconds before the second, so the block chunk
+// goes where the chain starts early.  The owner stages it in its own LDS
+// slot and computes it before its other chunks, while their first loads are
+// in flight.  kEvery: every wave has at least one window or slot
 // chunk (checked by the host), so the first loads need no branch.  With
 // ksplit = 1 the output is written here, else the range's (m, l, O) go to
 // the workspace: [unit][kidx][m[64] | l[64] | O[64][d]].
@@ -209,9 +211,12 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     int units, int ksplit) {
   constexpr int D = 128;
   static_assert(16 % KPW == 0, "the merge deals 16 (row group, dimension block) pieces to the waves");
-  constexpr int kRedBytes = KPW * 2 * 64 * 34 * 4;
-  constexpr int kLdsBytes = (2 * kBlkElems * 2 > kRedBytes) ? 2 * kBlkElems * 2 : kRedBytes;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsBytes / 2];
+  // one LDS slot per wave, touched only by that wave until the merge: first
+  // its block chunk (if it owns one), then its (m, l, O) partial
+  constexpr int kRedFloats = 2 * 34 * 64;  // [row group][m, l, O[32]][lane]
+  constexpr int kSlotElems = (kBlkElems > 2 * kRedFloats) ? kBlkElems : 2 * kRedFloats;
+  static_assert(KPW * kSlotElems * 2 <= 160 * 1024, "the wave slots must fit the LDS");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[KPW * kSlotElems];
 
   const int unit = blockIdx.x % units, split = blockIdx.x / units;
   const int kidx = split % ksplit, ridx = split / ksplit;
@@ -247,9 +252,7 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
   // the block chunk this wave owns, if any: B <= 47 gives at most 2 block
   // chunks, which land on 2 different waves since there are at least 2
   static_assert(KPW >= 2, "each block chunk gets a wave of its own");
-  int own = -1;
-  for (int b = 0; b < nblk; ++b)
-    if ((ngl + b) % nparts == pidx) own = b;
+  const int own = pidx < nblk ? pidx : -1;
   const bool owns = own >= 0;
   u16x8 bk_r[8], bv_r[8];  // the owned block chunk's K / V rows, 16-byte pieces
   if (owns) {
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
   // row-major, values [d][32]) -> operands; only this wave touches the
   // region, so a wave barrier orders the writes before the reads
   auto block_chunk = [&](int b) {
-    uint16_t* bk = lds + b * kBlkElems;
+    uint16_t* bk = lds + kq * kSlotElems;
     uint16_t* bv = bk + 32 * kKS;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -345,8 +348,10 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
   for (int j = 0; j < nmine - 1; ++j) step(true, j);
   if (nmine > 0) step(false, nmine - 1);
 
-  // merge the key parts: every wave leaves (m, l, O) in LDS; then each wave
-  // combines 16 / KPW of the 16 (row group, dimension block) pieces
+  // merge the key parts: each wave leaves (m, l, O) in its own slot as soon
+  // as its chunks are done (element-major, lanes contiguous: every access is
+  // 64 consecutive floats); after one barrier each wave combines 16 / KPW of
+  // the 16 (row group, dimension block) pieces
   float lt[2];
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
@@ -354,17 +359,17 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     lt[rg] += __shfl_xor(lt[rg], 16, 64);
     lt[rg] += __shfl_xor(lt[rg], 32, 64);
   }
-  __syncthreads();  // every wave is done with the block regions
-  float* red = reinterpret_cast<float*>(lds);  // [KPW][2 row groups][64 lanes][34]
+  auto red_at = [&](int k, int rg, int e) {
+    return reinterpret_cast<float*>(lds + k * kSlotElems) + (rg * 34 + e) * 64 + lane;
+  };
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
-    float* dst = red + ((kq * 2 + rg) * 64 + lane) * 34;
-    dst[0] = st[rg].m;
-    dst[1] = lt[rg];
+    *red_at(kq, rg, 0) = st[rg].m;
+    *red_at(kq, rg, 1) = lt[rg];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[2 + mb * 4 + r] = st[rg].o[mb][r];
+      for (int r = 0; r < 4; ++r) *red_at(kq, rg, 2 + mb * 4 + r) = st[rg].o[mb][r];
   }
   __syncthreads();
   constexpr int kPer = 16 / KPW;  // pieces per wave
@@ -374,16 +379,16 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     const int row = ridx * 32 + rg * 16 + ln;
     float mx = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < KPW; ++k) mx = fmaxf(mx, red[((k * 2 + rg) * 64 + lane) * 34]);
+    for (int k = 0; k < KPW; ++k) mx = fmaxf(mx, *red_at(k, rg, 0));
     float l = 0.f;
     f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KPW; ++k) {
-      const float* src = red + ((k * 2 + rg) * 64 + lane) * 34;
-      const float wk = src[0] == -INFINITY ? 0.f : exp2_f(src[0] - mx);
-      l = fmaf(src[1], wk, l);
+      const float mk = *red_at(k, rg, 0);
+      const float wk = mk == -INFINITY ? 0.f : exp2_f(mk - mx);
+      l = fmaf(*red_at(k, rg, 1), wk, l);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = fmaf(src[2 + mb * 4 + r], wk, o[r]);
+      for (int r = 0; r < 4; ++r) o[r] = fmaf(*red_at(k, rg, 2 + mb * 4 + r), wk, o[r]);
     }
     if (row >= M) continue;
     if (ksplit == 1) {  // the whole key list: write the output
