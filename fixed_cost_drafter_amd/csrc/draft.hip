@@ -373,22 +373,35 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
   }
   __syncthreads();
   constexpr int kPer = 16 / KPW;  // pieces per wave
+  // every read of the wave's pieces is issued before the arithmetic, so the
+  // LDS round trips overlap instead of forming a chain per key part
+  float pm[kPer][KPW], pl[kPer][KPW], po[kPer][KPW][4];
+#pragma unroll
+  for (int pc = 0; pc < kPer; ++pc) {
+    const int piece = kq * kPer + pc, rg = piece >> 3, mb = piece & 7;
+#pragma unroll
+    for (int k = 0; k < KPW; ++k) {
+      pm[pc][k] = *red_at(k, rg, 0);
+      pl[pc][k] = *red_at(k, rg, 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) po[pc][k][r] = *red_at(k, rg, 2 + mb * 4 + r);
+    }
+  }
 #pragma unroll
   for (int pc = 0; pc < kPer; ++pc) {
     const int piece = kq * kPer + pc, rg = piece >> 3, mb = piece & 7;
     const int row = ridx * 32 + rg * 16 + ln;
     float mx = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < KPW; ++k) mx = fmaxf(mx, *red_at(k, rg, 0));
+    for (int k = 0; k < KPW; ++k) mx = fmaxf(mx, pm[pc][k]);
     float l = 0.f;
     f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KPW; ++k) {
-      const float mk = *red_at(k, rg, 0);
-      const float wk = mk == -INFINITY ? 0.f : exp2_f(mk - mx);
-      l = fmaf(*red_at(k, rg, 1), wk, l);
+      const float wk = pm[pc][k] == -INFINITY ? 0.f : exp2_f(pm[pc][k] - mx);
+      l = fmaf(pl[pc][k], wk, l);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = fmaf(*red_at(k, rg, 2 + mb * 4 + r), wk, o[r]);
+      for (int r = 0; r < 4; ++r) o[r] = fmaf(po[pc][k][r], wk, o[r]);
     }
     if (row >= M) continue;
     if (ksplit == 1) {  // the whole key list: write the output
