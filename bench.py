@@ -85,7 +85,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 ENTRY_KERNELS = {
     "verify": ("verify_partial", "verify_finalize"),
     "verify_append": ("verify_partial", ("append_tiles", "true>")),
-    "verify_sampling": ("samp_stats", "samp_decide", "samp_sums", "samp_draw"),
+    "verify_sampling": ("samp_stats", "samp_decide_sums", "samp_draw"),
     "append": (("append_tiles", "false>"), "append_kernel"),
     "draft": ("draft_direct", "draft_combine", "draft_generic"),
     "verify_attention": ("attn_mfma_partial", "attn_combine", "attn_generic"),

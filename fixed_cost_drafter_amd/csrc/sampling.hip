@@ -9,16 +9,15 @@
 //   vocabulary in index order: the smallest k whose running sum exceeds
 //   u_sample times the total.
 //
-// Four launches, kernel boundaries between them (no device-scope fences):
+// Three launches, kernel boundaries between them (no device-scope fences):
 //  (1) samp_stats: (row, 8192-logit chunk) workgroups stream both logit
 //      tensors once and reduce each chunk to base-2 softmax statistics
 //      (max of x log2(e) / T, sum of 2^(y - max));
-//  (2) samp_decide: one workgroup per sequence merges its 2B+1 rows'
-//      statistics (a wave per row, a lane per chunk), gathers p_j(d_j),
-//      q_j(d_j) and runs the acceptance rule, then records the row to draw
-//      from;
-//  (3) samp_sums: chunk sums of that row's weights;
-//  (4) samp_draw: one workgroup per sequence locates the chunk, then (a
+//  (2) samp_decide_sums: (chunk, sequence) workgroups; each merges its
+//      sequence's 2B+1 rows' statistics (a wave per row, a lane per chunk),
+//      gathers p_j(d_j), q_j(d_j) and runs the acceptance rule, then sums
+//      the weights of the row to draw from over its chunk;
+//  (3) samp_draw: one workgroup per sequence locates the chunk, then (a
 //      workgroup scan over per-thread sums of 32 entries held in registers)
 //      the thread, then the entry where the running sum crosses u_sample
 //      times the total.
@@ -63,7 +62,7 @@ struct Vec16<BF16> {
   __device__ static inline float get(const V& v, int i) { return bf16_to_f32(v[i]); }
 };
 
-// per-sequence record written by samp_decide
+// per-sequence record of the decision (written by the chunk-0 workgroup)
 struct Record {
   int32_t row;   // j: the verified row the emitted token is drawn from
   int32_t bonus; // 1: drawn from p_B (all drafts accepted), 0: from max(0, p_j - q_j)
@@ -148,67 +147,6 @@ __global__ __launch_bounds__(kThreads) void samp_stats(
   }
 }
 
-// merged base-2 statistics of one row from its nsplit chunk statistics: one
-// lane per chunk, then a wave merge (every lane returns the result)
-__device__ __forceinline__ float2 row_stat(const float2* __restrict__ st, int nsplit, int lane) {
-  float m = -INFINITY, s = 0.f;
-  for (int k = lane; k < nsplit; k += 64) merge_stat(m, s, st[k].x, st[k].y);
-  wave_merge_stat(m, s);
-  return make_float2(m, s);
-}
-
-// One workgroup of kDecideWaves waves per sequence: wave w merges the
-// statistics of target rows w, w + kDecideWaves, ... and of the drafter rows
-// of the same index, and gathers p_j(d_j) and q_j(d_j); thread 0 then runs
-// the acceptance rule.
-constexpr int kDecideWaves = 8;
-template <typename Ty>
-__global__ __launch_bounds__(64 * kDecideWaves) void samp_decide(
-    const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
-    const int32_t* __restrict__ draft, const float* __restrict__ u_accept,
-    const float2* __restrict__ stats, Record* __restrict__ rec, int32_t* __restrict__ tokens,
-    int32_t* __restrict__ tau, int C, int B, int V, int nsplit, float k2) {
-  __shared__ float pt[64], qd[64], mt[64], izt[64], md[64], izd[64];
-  __shared__ int js;
-  const int c = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int nt = C * (B + 1);
-  for (int j = wave; j <= B; j += kDecideWaves) {  // target row j; drafter row j (j < B)
-    const float2 ts = row_stat(stats + (int64_t(c) * (B + 1) + j) * nsplit, nsplit, lane);
-    float2 ds = make_float2(0.f, 1.f);
-    if (j < B) ds = row_stat(stats + (int64_t(nt) + int64_t(c) * B + j) * nsplit, nsplit, lane);
-    if (lane == 0) {
-      mt[j] = ts.x;
-      izt[j] = 1.0f / ts.y;
-      if (j < B) {
-        md[j] = ds.x;
-        izd[j] = 1.0f / ds.y;
-        const int d = min(max(draft[int64_t(c) * B + j], 0), V - 1);
-        pt[j] = exp2_f(Ty::load(tl, (int64_t(c) * (B + 1) + j) * V + d) * k2 - ts.x) * izt[j];
-        qd[j] = exp2_f(Ty::load(dl, (int64_t(c) * B + j) * V + d) * k2 - ds.x) * izd[j];
-      }
-    }
-  }
-  __syncthreads();
-  if (t == 0) {
-    int j = 0;
-    while (j < B && u_accept[int64_t(c) * B + j] * qd[j] < pt[j]) ++j;
-    js = j;
-    tau[c] = j + 1;
-    Record r;
-    r.row = j;
-    r.bonus = j == B;
-    r.mt = mt[j];
-    r.izt = izt[j];
-    r.md = j < B ? md[j] : 0.f;
-    r.izd = j < B ? izd[j] : 0.f;
-    r.pad[0] = r.pad[1] = 0.f;
-    rec[c] = r;
-  }
-  __syncthreads();
-  for (int i = t; i <= B; i += 64 * kDecideWaves)  // accepted drafts, then -1 (token js is drawn later)
-    if (i != js) tokens[int64_t(c) * (B + 1) + i] = i < js ? draft[int64_t(c) * B + i] : -1;
-}
-
 // weight of vocabulary entry k in the draw of a record's row
 template <typename Ty>
 __device__ __forceinline__ float draw_weight(const typename Ty::T* rt, const typename Ty::T* rd,
@@ -232,31 +170,124 @@ __device__ __forceinline__ void draw_weights16(const typename Vec16<Ty>::V& vt, 
   }
 }
 
-// chunk sums of the drawn row's weights: (chunk, sequence) workgroups, all
-// 16-byte loads of a thread in flight at once
+// (chunk, sequence) workgroups.  Every workgroup of sequence c first takes
+// the acceptance decision of c itself (the same loads and arithmetic in
+// each, so the same result): wave w merges the chunk statistics of target
+// rows w, w + 4, ... and of the drafter rows of the same index (a lane per
+// chunk, all loads issued before the first merge), with p_j(d_j) and
+// q_j(d_j) gathered by lane i for row w + 4i; thread 0 runs the rule.  The
+// chunk-0 workgroup writes tau, the accepted drafts and the record that the
+// draw reads.  Then each workgroup sums the drawn row's weights over its
+// chunk, all 16-byte loads of a thread in flight at once.
 template <typename Ty>
-__global__ __launch_bounds__(kThreads) void samp_sums(
+__global__ __launch_bounds__(kThreads) void samp_decide_sums(
     const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
-    const Record* __restrict__ rec, float* __restrict__ sums, int B, int V, int nsplit, float k2,
-    int vec_ok) {
+    const int32_t* __restrict__ draft, const float* __restrict__ u_accept,
+    const float2* __restrict__ stats, Record* __restrict__ rec, int32_t* __restrict__ tokens,
+    int32_t* __restrict__ tau, float* __restrict__ sums, int C, int B, int V, int nsplit,
+    float k2, int vec_ok) {
   using VT = Vec16<Ty>;
+  constexpr int kW = kThreads / 64;
+  constexpr int kRows = (kMaxBlock + 1 + kW - 1) / kW;  // rows per wave
+  static_assert(kRows <= 64, "a lane per row for the gathers");
+  __shared__ float pt[64], qd[64], mt[64], izt[64], md[64], izd[64];
+  __shared__ Record s_rec;
+  __shared__ int s_js;
+  const int split = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63,
+            wave = tid >> 6;
+  const int nt = C * (B + 1);
+
+  // the decision's loads: chunk statistics (lane = chunk) and, in lane i,
+  // the drafted token's logits of row wave + kW i
+  float2 ts[kRows], ds[kRows];
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int j = wave + kW * i;
+    ts[i] = make_float2(-INFINITY, 0.f);
+    ds[i] = make_float2(-INFINITY, 0.f);
+    if (j <= B && lane < nsplit) ts[i] = stats[(int64_t(c) * (B + 1) + j) * nsplit + lane];
+    if (j < B && lane < nsplit) ds[i] = stats[(int64_t(nt) + int64_t(c) * B + j) * nsplit + lane];
+  }
+  float xt = 0.f, xd = 0.f;
+  {
+    const int j = wave + kW * lane;
+    if (lane < kRows && j < B) {
+      const int d = min(max(draft[int64_t(c) * B + j], 0), V - 1);
+      xt = Ty::load(tl, (int64_t(c) * (B + 1) + j) * V + d);
+      xd = Ty::load(dl, (int64_t(c) * B + j) * V + d);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kRows; ++i) {
+    const int j = wave + kW * i;
+    if (j > B) break;  // uniform in the wave
+    float m = -INFINITY, sm = 0.f, m2 = -INFINITY, s2 = 0.f;
+    merge_stat(m, sm, ts[i].x, ts[i].y);
+    merge_stat(m2, s2, ds[i].x, ds[i].y);
+    for (int k = lane + 64; k < nsplit; k += 64) {  // more than 64 chunks: V > 512K
+      merge_stat(m, sm, stats[(int64_t(c) * (B + 1) + j) * nsplit + k].x,
+                 stats[(int64_t(c) * (B + 1) + j) * nsplit + k].y);
+      if (j < B)
+        merge_stat(m2, s2, stats[(int64_t(nt) + int64_t(c) * B + j) * nsplit + k].x,
+                   stats[(int64_t(nt) + int64_t(c) * B + j) * nsplit + k].y);
+    }
+    wave_merge_stat(m, sm);
+    if (j < B) wave_merge_stat(m2, s2);
+    const float yt = __shfl(xt, i), yd = __shfl(xd, i);
+    if (lane == 0) {
+      mt[j] = m;
+      izt[j] = 1.0f / sm;
+      if (j < B) {
+        md[j] = m2;
+        izd[j] = 1.0f / s2;
+        pt[j] = exp2_f(yt * k2 - m) * izt[j];
+        qd[j] = exp2_f(yd * k2 - m2) * izd[j];
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int j = 0;
+    while (j < B && u_accept[int64_t(c) * B + j] * qd[j] < pt[j]) ++j;
+    s_js = j;
+    Record r;
+    r.row = j;
+    r.bonus = j == B;
+    r.mt = mt[j];
+    r.izt = izt[j];
+    r.md = j < B ? md[j] : 0.f;
+    r.izd = j < B ? izd[j] : 0.f;
+    r.pad[0] = r.pad[1] = 0.f;
+    s_rec = r;
+    if (split == 0) {
+      tau[c] = j + 1;
+      rec[c] = r;
+    }
+  }
+  __syncthreads();
+  const Record r = s_rec;
+  if (split == 0) {
+    const int js = s_js;
+    for (int i = tid; i <= B; i += kThreads)  // accepted drafts, then -1 (token js is drawn later)
+      if (i != js) tokens[int64_t(c) * (B + 1) + i] = i < js ? draft[int64_t(c) * B + i] : -1;
+  }
+
+  // chunk sum of the drawn row's weights
   constexpr int U = kVerifyChunk / VT::N / kThreads;  // vectors per thread
-  const int split = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-  const Record r = rec[c];
   const typename Ty::T* rt = tl + (int64_t(c) * (B + 1) + r.row) * V;
   const typename Ty::T* rd = dl + (int64_t(c) * B + min(r.row, B - 1)) * V;
   const int begin = split * kVerifyChunk, end = min(V, begin + kVerifyChunk);
   float a = 0.f;
   if (vec_ok) {
-    const typename VT::V* xt = reinterpret_cast<const typename VT::V*>(rt + begin);
-    const typename VT::V* xd = reinterpret_cast<const typename VT::V*>(rd + begin);
+    const typename VT::V* vt = reinterpret_cast<const typename VT::V*>(rt + begin);
+    const typename VT::V* vd = reinterpret_cast<const typename VT::V*>(rd + begin);
     const int nvec = (end - begin) / VT::N;  // whole: V is a multiple of N here
     typename VT::V bt[U], bd[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int v = min(u * kThreads + tid, nvec - 1);
-      bt[u] = xt[v];
-      bd[u] = r.bonus ? bt[u] : xd[v];
+      bt[u] = vt[v];
+      bd[u] = r.bonus ? bt[u] : vd[v];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -270,8 +301,8 @@ __global__ __launch_bounds__(kThreads) void samp_sums(
     for (int k = begin + tid; k < end; k += kThreads) a += draw_weight<Ty>(rt, rd, r, k2, k);
   }
   a = wave_sum(a);
-  __shared__ float wsum[kThreads / 64];
-  if ((tid & 63) == 0) wsum[tid >> 6] = a;
+  __shared__ float wsum[kW];
+  if (lane == 0) wsum[wave] = a;
   __syncthreads();
   if (tid == 0) sums[int64_t(c) * nsplit + split] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
 }
@@ -402,11 +433,8 @@ ls_status run(const ls_dims& d, const void* tl, const void* dl, const int32_t* d
   hipLaunchKernelGGL(samp_stats<Ty>, dim3(nsplit, d.C * (2 * d.B + 1)), dim3(kThreads), 0, stream,
                      t, dd, stats, d.C, d.B, d.V, nsplit, k2, vec_ok);
   if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
-  hipLaunchKernelGGL(samp_decide<Ty>, dim3(d.C), dim3(64 * kDecideWaves), 0, stream, t, dd, draft, u_accept, stats,
-                     rec, tokens, tau, d.C, d.B, d.V, nsplit, k2);
-  if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
-  hipLaunchKernelGGL(samp_sums<Ty>, dim3(nsplit, d.C), dim3(kThreads), 0, stream, t, dd, rec, sums,
-                     d.B, d.V, nsplit, k2, vec_ok);
+  hipLaunchKernelGGL(samp_decide_sums<Ty>, dim3(nsplit, d.C), dim3(kThreads), 0, stream, t, dd, draft,
+                     u_accept, stats, rec, tokens, tau, sums, d.C, d.B, d.V, nsplit, k2, vec_ok);
   if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
   hipLaunchKernelGGL(samp_draw<Ty>, dim3(d.C), dim3(kThreads), 0, stream, t, dd, rec, sums, u_sample,
                      tokens, d.B, d.V, nsplit, k2, vec_ok);
