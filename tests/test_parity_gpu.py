@@ -82,7 +82,7 @@ def test_parity_q3_4b_8k_all_heads():
     H.log(f"mean tau {taus.mean():.2f} (expected {WLM.expected_tau(wl):.2f})")
 
 
-@pytest.mark.parametrize("name", ["q3_8b_32k"])
+@pytest.mark.parametrize("name", ["q3_8b_32k", "q3_8b_128k"])
 def test_parity_full_size_sampled(name):
     """Full shape, full prefix, bench launch configuration; sampled heads."""
     wl = WLM.WORKLOADS[name]
