@@ -30,9 +30,6 @@ namespace {
 
 constexpr int kThreads = 256;
 __device__ __forceinline__ float exp2_f(float x) { return __builtin_amdgcn_exp2f(x); }
-#ifndef LS_INIT_PREFETCH
-#define LS_INIT_PREFETCH 1
-#endif
 
 // partial block of (split, unit): m[S] | l[S] | n[S][2d]
 __device__ __host__ inline int64_t part_off(int split, int units, int unit, int S, int D) {
@@ -58,6 +55,11 @@ __device__ __host__ inline int64_t part_off(int split, int units, int unit, int 
 // transposition while staging); 16-byte chunk c of row r sits at chunk
 // c ^ tile_swz(r), which keeps the score reads (16 rows, one chunk) and the
 // transposed reads (4 rows x 4 chunks per 16 lanes) on distinct banks.
+// Tiles go from global memory straight into LDS (global_load_lds_dwordx4:
+// lane i of an instruction fills the i-th 16 bytes of a 1 KB LDS block, so
+// each lane fetches the chunk that the swizzle places there), double
+// buffered: the next tile streams in while the current one is computed, and
+// one barrier per tile separates the two.
 // The two row halves of a slot group keep separate (m, l, n) and merge
 // through LDS at the end.
 // ---------------------------------------------------------------------------
@@ -72,16 +74,21 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
   constexpr int D = 128, S = 32 * NG, NT = 128 * NG, TR = 64;
   constexpr int KLS = D + 8;   // slot-query row stride (bf16 elements)
   constexpr int RS = D;        // K / V tile row stride: 256 bytes, swizzled chunks
-  constexpr int PAIRS = TR * 8 / NT;  // row pairs staged per thread
-  static_assert(PAIRS >= 1 && TR * 8 % NT == 0, "tile rows must cover the threads");
-  constexpr int kInitPrefetch = PAIRS == 1 ? LS_INIT_PREFETCH : 1;
-  constexpr int kTileElems = 2 * TR * RS + S * KLS;
-  constexpr int kMergeFloats = NG * 64 * 131;  // per slot group and lane: m_true, m_run, l, 128 n
-  constexpr int kLdsBytes = kTileElems * 2 > kMergeFloats * 4 ? kTileElems * 2 : kMergeFloats * 4;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kLdsBytes / 2];
-  uint16_t* KL = smem;                         // [TR][RS] K rows
-  uint16_t* VL = smem + TR * RS;               // [TR][RS] V rows
-  uint16_t* UL = VL + TR * RS;                 // [S][KLS]: the slot queries
+  constexpr int KI = TR * RS / 512 / (NT / 64);  // 1 KB blocks of a K (or V) tile per wave
+  static_assert(KI >= 1 && KI * (NT / 64) * 512 == TR * RS, "tile blocks must cover the waves");
+  // four LDS arrays of at least one slot group's merge record (64 lanes x
+  // m_true, m_run, l, 128 n): tile buffers 0 and 1 ([K rows | V rows] each),
+  // the slot queries, and a spare; after the loop slot group g merges
+  // through array g.  Separate arrays let the compiler see that the tile
+  // streaming into one buffer does not alias the reads of the other.
+  constexpr int kMergeElems = 64 * 131 * 2;
+  constexpr int kBufElems = 2 * TR * RS > kMergeElems ? 2 * TR * RS : kMergeElems;
+  constexpr int kUElems = S * KLS > kMergeElems ? S * KLS : kMergeElems;
+  static_assert(NG <= 4, "one merge array per slot group");
+  __shared__ __attribute__((aligned(16))) uint16_t buf0[kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t buf1[kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t UL[kUElems];  // [S][KLS]: the slot queries
+  __shared__ __attribute__((aligned(16))) uint16_t spare[NG > 3 ? kMergeElems : 8];
   // element offset of 16-byte chunk c of tile row r
   auto chunk_at = [](int r, int c) { return r * RS + ((c ^ tile_swz(r)) << 3); };
 
@@ -136,24 +143,21 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
 #pragma unroll
   for (int db = 0; db < 8; ++db) acc[db] = f32x16{};
 
-  // global -> register staging: thread (dg = tid%16, rp = tid/16) loads row
-  // pairs rp + k*(NT/16); 16 lanes cover one 256-byte row segment
-  const int dg = tid & 15, rp = tid >> 4;
-  u16x8 kr[kInitPrefetch][2 * PAIRS], vr[kInitPrefetch][2 * PAIRS];
-  auto load_tile = [&](int t0, u16x8 (&kd)[2 * PAIRS], u16x8 (&vd)[2 * PAIRS])
-                       __attribute__((always_inline)) {
+  // tile t0 -> LDS buffer b: wave w's block j holds K (or V) rows
+  // 4(KI w + j) .. +3; lane i of it lands at 16-byte position p = 64 (KI w + j)
+  // + i of the tile, i.e. row p / 16, chunk slot p % 16, which holds chunk
+  // (p % 16) ^ tile_swz(row).  Rows past the tail repeat the last real row
+  // (their scores are masked and their weights are 0).
+  auto issue_tile = [&](int t0, uint16_t* buf) __attribute__((always_inline)) {
     const int nrows = min(TR, r_end - t0);
 #pragma unroll
-    for (int i = 0; i < 2 * PAIRS; ++i) {
-      const int row = 2 * (rp + (i >> 1) * (NT / 16)) + (i & 1);
-      if (row < nrows) {
-        const int64_t off = ((int64_t(c) * rows_stride + t0 + row) * Hkv + h) * D + dg * 8;
-        kd[i] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(kp + off));
-        vd[i] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(vp + off));
-      } else {
-        kd[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        vd[i] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      }
+    for (int j = 0; j < KI; ++j) {
+      const int blk = KI * wave + j, p = 64 * blk + lane;
+      const int row = p >> 4, ch = (p & 15) ^ tile_swz(p >> 4);
+      const int64_t off = ((int64_t(c) * rows_stride + t0 + min(row, nrows - 1)) * Hkv + h) * D + ch * 8;
+      uint16_t* kl = buf + blk * 512;
+      __builtin_amdgcn_global_load_lds(kp + off, (__attribute__((address_space(3))) void*)kl, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + off, (__attribute__((address_space(3))) void*)(kl + TR * RS), 16, 0, 0);
     }
   };
 
@@ -163,29 +167,15 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
   // every few tiles as the bias grows by |ln lambda| per row).
   const int ntiles = (r_end - r_begin + TR - 1) / TR;
   auto tile_t0 = [&](int idx) { return r_begin + (ntiles - 1 - idx) * TR; };
-#pragma unroll
-  for (int uu = 0; uu < kInitPrefetch; ++uu)
-    if (uu < ntiles) load_tile(tile_t0(uu), kr[uu], vr[uu]);
-  for (int ib = 0; ib < ntiles; ib += kInitPrefetch) {
-#pragma unroll
-  for (int uu = 0; uu < kInitPrefetch; ++uu) {  // tile idx uses registers kr[uu], vr[uu]
-    const int idx = ib + uu;
-    if (idx >= ntiles) break;
+  // one tile computed from buffer cur while the next streams into nxt
+  auto tile_step = [&](int idx, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
     const int t0 = tile_t0(idx);
     const int nrows = min(TR, r_end - t0);
-    __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-    for (int pp = 0; pp < PAIRS; ++pp) {
-      const int row0 = 2 * (rp + pp * (NT / 16));  // even row of the pair
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        *reinterpret_cast<u16x8*>(&KL[chunk_at(row0 + q, dg)]) = kr[uu][2 * pp + q];
-        *reinterpret_cast<u16x8*>(&VL[chunk_at(row0 + q, dg)]) = vr[uu][2 * pp + q];
-      }
-    }
-    __syncthreads();
-    if (idx + kInitPrefetch < ntiles)  // refill: that tile loads during the next computes
-      load_tile(tile_t0(idx + kInitPrefetch), kr[uu], vr[uu]);
+    const uint16_t* KL = cur;
+    const uint16_t* VL = cur + TR * RS;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's blocks of the tile are in LDS
+    __syncthreads();  // ... and every wave's; the other buffer's reads (tile idx-1) are done
+    if (idx + 1 < ntiles) issue_tile(tile_t0(idx + 1), nxt);  // streams in during this tile
 
     // S^T for the wave's 32 rows
     f32x16 s = f32x16{};
@@ -280,7 +270,11 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[t], acc[db], 0, 0, 0);
       }
-  }
+  };
+  if (ntiles > 0) issue_tile(tile_t0(0), buf0);
+  for (int idx = 0; idx < ntiles; idx += 2) {  // even tiles in buffer 0, odd in buffer 1
+    tile_step(idx, buf0, buf1);
+    if (idx + 1 < ntiles) tile_step(idx + 1, buf1, buf0);
   }
 
   // merge the two row halves of each slot group: half 1 leaves (m_true,
@@ -291,7 +285,7 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
     lt = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
   }
   __syncthreads();  // the last tile's LDS reads are done
-  float* mg = reinterpret_cast<float*>(smem) + sg * 64 * 131;  // [64 lanes][m_true, m_run, l, 128 n]
+  float* mg = reinterpret_cast<float*>(sg == 0 ? buf0 : sg == 1 ? buf1 : sg == 2 ? UL : spare);  // [64 lanes][m_true, m_run, l, 128 n]
   if (half == 1) {
     float* dst = mg + lane * 131;
     dst[0] = m_true;
