@@ -16,7 +16,7 @@ from tests.test_parity_gpu import SMALL, _announce
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["bf16_wrap", "bf16_b40", "bf16_s128_b40", "bf16_s128_short",
+@pytest.mark.parametrize("name", ["bf16_wrap", "bf16_b40", "bf16_b47", "bf16_s128_b40", "bf16_s128_short",
                                   "f32_d32_wrap"])
 def test_verify_append_matches_separate_calls(name):
     import torch

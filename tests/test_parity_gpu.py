@@ -58,6 +58,11 @@ SMALL = {
     "bf16_wrap": WLM.Workload(
         "bf16_wrap", "bf16", C=5, Hq=4, Hkv=4, d=128, L0=130, W=32, S=64, B=16, V=9000,
         rounds=14, p_match=0.75, seed=15),
+    # the largest block (B = 47): 48 verified rows, a ragged second block chunk
+    # (15 keys), B*G = 47 query rows (a full and a ragged 32-row slice)
+    "bf16_b47": WLM.Workload(
+        "bf16_b47", "bf16", C=2, Hq=4, Hkv=4, d=128, L0=333, W=64, S=128, B=47, V=5000,
+        rounds=5, p_match=0.95, seed=21),
     # the summary merge with two 32-row score blocks (B + 1 > 32) over 128 slots
     "bf16_s128_b40": WLM.Workload(
         "bf16_s128_b40", "bf16", C=2, Hq=2, Hkv=2, d=128, L0=90, W=128, S=128, B=40, V=1504,
