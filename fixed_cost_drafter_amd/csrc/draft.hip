@@ -66,11 +66,11 @@ __device__ inline uint16_t bf16_bits(float f) {
 // The stored key tiles (key_index) follow the same permutation.
 __device__ __forceinline__ int chunk_key(int m, int mb) { return 8 * (m >> 2) + 4 * mb + (m & 3); }
 
-// LDS image of one staged block chunk: keys row-major (padded rows), values
-// [d][32] (padded)
-constexpr int kKS = 128 + 8;   // key row stride (bf16)
-constexpr int kVS = 32 + 8;    // value row stride (bf16)
-constexpr int kBlkElems = 32 * kKS + 128 * kVS;
+// LDS image of one staged block chunk: its 32 value rows as they arrive
+// (row-major, rows padded to 288 bytes so that the 16 rows one transposed
+// read touches fall on 8 distinct 8-bank groups, twice)
+constexpr int kBVS = 128 + 16;  // value row stride (bf16)
+constexpr int kBlkElems = 32 * kBVS;
 
 // Half of one 32-key chunk's MFMA operands for one wave: the 8 key loads
 // (A operands of S^T = K Q^T, [mb*4 + ks]) or the 8 value loads (A operands
@@ -254,15 +254,25 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
   static_assert(KPW >= 2, "each block chunk gets a wave of its own");
   const int own = pidx < nblk ? pidx : -1;
   const bool owns = own >= 0;
-  u16x8 bk_r[8], bv_r[8];  // the owned block chunk's K / V rows, 16-byte pieces
+  // the owned block chunk: the key operands straight from the caller's rows
+  // (lane (kg, ln) of load mb * 4 + ks: key chunk_key(ln, mb), dimensions
+  // 32 ks + 8 kg .. +7), the value rows as 16-byte pieces for LDS; rows past
+  // B repeat row B-1 and are masked
+  Half bk;
+  u16x8 bv_r[8];
   if (owns) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int key = min(own * 32 + chunk_key(ln, mb), B - 1);
+        bk.r[mb * 4 + ks] = *reinterpret_cast<const u16x8*>(kb + ((int64_t(c) * B + key) * Hkv + h) * D + ks * 32 + kg * 8);
+      }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int piece = lane + 64 * i, row = piece >> 4, col = (piece & 15) * 8;
-      const int key = min(own * 32 + row, B - 1);  // rows past B repeat row B-1 and are masked
-      const int64_t off = ((int64_t(c) * B + key) * Hkv + h) * D + col;
-      bk_r[i] = *reinterpret_cast<const u16x8*>(kb + off);
-      bv_r[i] = *reinterpret_cast<const u16x8*>(vb + off);
+      const int key = min(own * 32 + row, B - 1);
+      bv_r[i] = *reinterpret_cast<const u16x8*>(vb + ((int64_t(c) * B + key) * Hkv + h) * D + col);
     }
   }
 
@@ -296,28 +306,33 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     for (int i = 0; i < 8; ++i) st[rg].o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // the owned block chunk first: its rows -> this wave's LDS region (keys
-  // row-major, values [d][32]) -> operands; only this wave touches the
-  // region, so a wave barrier orders the writes before the reads
+  // the owned block chunk first: its value rows -> this wave's LDS slot
+  // (row-major) -> the [dimension][8 keys] operands by transposed reads; only
+  // this wave touches the slot, so a wave barrier orders the writes before
+  // the reads.  ds_read_b64_tr_b16 gives lane 4a + b of a 16-lane group
+  // element b of the 8-byte reads of lanes a, a+4, a+8, a+12: reader lane ln
+  // of group kg reads row 8 kg + ln / 4 (+ 4 for keys 4..7) at dimensions
+  // 16 db + 4 (ln % 4) .. +3, so lane ln receives keys 8 kg .. 8 kg + 3 (+4)
+  // of dimension 16 db + ln, the layout of a value tile's operand.
   auto block_chunk = [&](int b) {
-    uint16_t* bk = lds + kq * kSlotElems;
-    uint16_t* bv = bk + 32 * kKS;
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    uint16_t* bv = lds + kq * kSlotElems;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int piece = lane + 64 * i, row = piece >> 4, col = (piece & 15) * 8;
-      *reinterpret_cast<u16x8*>(bk + row * kKS + col) = bk_r[i];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bv[(col + e) * kVS + row] = bv_r[i][e];
+      *reinterpret_cast<u16x8*>(bv + row * kBVS + col) = bv_r[i];
     }
     __builtin_amdgcn_wave_barrier();
-    Half xk, xv;
+    Half xv;
+    const uint16_t* rd = bv + (8 * kg + (ln >> 2)) * kBVS + 4 * (ln & 3);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        xk.r[mb * 4 + ks] = *reinterpret_cast<const u16x8*>(bk + chunk_key(ln, mb) * kKS + ks * 32 + kg * 8);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) xv.r[db] = *reinterpret_cast<const u16x8*>(bv + (db * 16 + ln) * kVS + kg * 8);
+    for (int db = 0; db < 8; ++db) {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(rd + 16 * db));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(rd + 4 * kBVS + 16 * db));
+      xv.r[db] = __builtin_bit_cast(u16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    const Half& xk = bk;
     const int nvalid = B - b * 32 - 8 * kg;  // block keys among the lane group's 8
     const uint32_t valid8 = nvalid >= 8 ? 0xFFu : nvalid <= 0 ? 0u : ((1u << nvalid) - 1u);
     f32x4 sc[2][2];
