@@ -51,26 +51,22 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_partial(
     int Hkv, int B, int rows_per_split, int nsplit, float* __restrict__ part,
     int32_t* __restrict__ err_flag) {
   constexpr int D = 128, TR = 64, NT = 64 * NW, Mq = 16 * NW;
-  constexpr int KLS = D + 8;   // row-major K tile stride (bf16 elements)
-  // transposed V tile [dim][row]: 144-byte rows (16-byte aligned).  Inside
-  // each 32-key group key 16hb + 4g + i sits at 8g + 4hb + i, the order in
-  // which a lane (key group g) reads its 8 keys of the P.V operand, so each
-  // operand load is one 16-byte read; and the 8-row groups of dimension dim
-  // are stored in the order group ^ ((dim >> 4) & 7), which spreads the
-  // staging stores (8 dimensions apart across lanes) and the operand loads
-  // (consecutive dimensions) over all 64 banks.
-  constexpr int VTS = TR + 8;
-  auto vt_row = [](int dim, int row) {
-    const int r32 = row & 31;
-    const int ph = (row & ~31) | (8 * ((r32 >> 2) & 3) + 4 * (r32 >> 4) + (r32 & 3));
-    return (((ph >> 3) ^ ((dim >> 4) & 7)) << 3) | (ph & 7);
-  };
+  // K and V tiles: 64 rows of 256 bytes as they arrive, 16-byte chunk c of
+  // row r at chunk c ^ (r % 16).  That puts the score operand reads (16 rows,
+  // one chunk per lane group) and the transposed P.V reads (16 rows x 32
+  // bytes) on the fewest bank cycles.  Tiles go from global memory straight
+  // into LDS (global_load_lds_dwordx4: lane i of an instruction fills the
+  // i-th 16 bytes of a 1 KB block, so each lane fetches the chunk the swizzle
+  // puts there), double buffered in separate arrays so that the compiler can
+  // tell the tile in flight from the one being read.
   constexpr int MB = TR / 16;  // 16-row key blocks per tile
   constexpr int KS2 = TR / 32; // 32-row k-steps of the PV product
-  constexpr int NITEM = (TR / 2) * 16;          // (row pair, 8-dim group) staging items
-  constexpr int NPT = (NITEM + NT - 1) / NT;    // items per thread
-  __shared__ __attribute__((aligned(16))) uint16_t KL[TR * KLS];
-  __shared__ __attribute__((aligned(16))) uint16_t VT[D * VTS];
+  constexpr int NBLK = TR * D * 2 / 1024;  // 1 KB blocks per K (or V) tile
+  __shared__ __attribute__((aligned(16))) uint16_t K0[TR * D];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[TR * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[TR * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[TR * D];
+  auto chunk_at = [](int r, int ch) { return r * D + ((ch ^ (r & 15)) << 3); };
 
   const int split = blockIdx.x % nsplit;
   const int unit = blockIdx.x / nsplit;  // c * Hkv + h
@@ -105,47 +101,28 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_partial(
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // staging: item p = (row pair p / 16, dim group p % 16), rows 2*pair, 2*pair+1
-  u16x8 kr[NPT][2], vr[NPT][2];
-  auto load_tile = [&](int t0) __attribute__((always_inline)) {
+  // tile rows t0 .. t0+63 -> (Kb, Vb): wave w fills blocks w, w + NW, ...;
+  // rows past the range repeat its last row (masked, weight 0)
+  auto issue_tile = [&](int t0, uint16_t* Kb, uint16_t* Vb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-      const int p = min(tid + k * NT, NITEM - 1);
-      const int pair = p >> 4, dg = p & 15;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int row = t0 + 2 * pair + e;
-        if (row < r_end) {
-          const int64_t off = ((int64_t(c) * rows_stride + row) * Hkv + h) * D + dg * 8;
-          kr[k][e] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(kc + off));
-          vr[k][e] = __builtin_nontemporal_load(reinterpret_cast<const u16x8*>(vc + off));
-        } else {
-          kr[k][e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-          vr[k][e] = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
+    for (int j = 0; j < (NBLK + NW - 1) / NW; ++j) {
+      const int blk = wave + NW * j;
+      if (blk < NBLK) {  // uniform in the wave
+        const int p = 64 * blk + lane, row = p >> 4, ch = (p & 15) ^ (row & 15);
+        const int64_t off = ((int64_t(c) * rows_stride + min(t0 + row, r_end - 1)) * Hkv + h) * D + ch * 8;
+        __builtin_amdgcn_global_load_lds(kc + off, (__attribute__((address_space(3))) void*)(Kb + blk * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vc + off, (__attribute__((address_space(3))) void*)(Vb + blk * 512), 16, 0, 0);
       }
     }
   };
 
-  if (r_begin < r_end) load_tile(r_begin);
-  for (int t0 = r_begin; t0 < r_end; t0 += TR) {
-    __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-    for (int k = 0; k < NPT; ++k) {
-      const int p = tid + k * NT;
-      if (p >= NITEM) break;
-      const int pair = p >> 4, dg = p & 15, row0 = 2 * pair;
-      *reinterpret_cast<u16x8*>(&KL[row0 * KLS + dg * 8]) = kr[k][0];
-      *reinterpret_cast<u16x8*>(&KL[(row0 + 1) * KLS + dg * 8]) = kr[k][1];
-      const uint4 v0 = __builtin_bit_cast(uint4, vr[k][0]), v1 = __builtin_bit_cast(uint4, vr[k][1]);
-      const uint32_t v0w[4] = {v0.x, v0.y, v0.z, v0.w}, v1w[4] = {v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)  // (row0, row0 + 1) of one dimension as one dword
-        *reinterpret_cast<uint32_t*>(&VT[(dg * 8 + e) * VTS + vt_row(dg * 8 + e, row0)]) =
-            __builtin_amdgcn_perm(v1w[e >> 1], v0w[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-    }
-    __syncthreads();
-    if (t0 + TR < r_end) load_tile(t0 + TR);  // next tile in flight during compute
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  auto tile_step = [&](int t0, const uint16_t* KL, const uint16_t* VL, uint16_t* Kn, uint16_t* Vn)
+                       __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's blocks of the tile are in LDS
+    __syncthreads();  // ... and every wave's; the other buffers' reads (previous tile) are done
+    if (t0 + TR < r_end) issue_tile(t0 + TR, Kn, Vn);  // streams in during this tile
 
     // S^T[key][query]: lane (query ln, kg) holds keys mb*16 + kg*4 + r
     f32x4 s[MB];
@@ -155,7 +132,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_partial(
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         s[mb] = mfma16x16x32(
-            as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[(mb * 16 + ln) * KLS + ks * 32 + kg * 8])),
+            as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[chunk_at(mb * 16 + ln, ks * 4 + kg)])),
             qb[ks], s[mb]);
     }
     // base-2 scores; keys past the query's own row (or past the range) only
@@ -205,18 +182,31 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_mfma_partial(
       }
     l_run += lsum;
     // O^T[dim][query] += V^T[dim][key] P^T[key][query]; the k order of the A
-    // operand (keys 32ks+4kg..+3, 32ks+16+4kg..+3) matches the weights' order
+    // operand (keys 32ks+4kg..+3, 32ks+16+4kg..+3) matches the weights'
+    // order.  ds_read_b64_tr_b16 gives lane 4a + b of a 16-lane group element
+    // b of the 8-byte reads of lanes a, a+4, a+8, a+12: reader lane ln of
+    // group kg reads row 32ks + 4kg + ln / 4 (+16 for the second half) at
+    // dimensions 16mb + 4(ln % 4) .. +3, so lane ln receives those 4 keys of
+    // dimension 16mb + ln.
 #pragma unroll
     for (int ks = 0; ks < KS2; ++ks) {
       const bf16x8 pk = as_bf16x8(__builtin_bit_cast(
           u16x8, uint4{pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]}));
+      const int vrow = 32 * ks + 4 * kg + (ln >> 2);
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) {
-        const int dim = mb * 16 + ln;
-        const u16x8 v = *reinterpret_cast<const u16x8*>(&VT[dim * VTS + vt_row(dim, ks * 32 + kg * 4)]);
-        acc[mb] = mfma16x16x32(as_bf16x8(v), pk, acc[mb]);
+        const int ch = 2 * mb + ((ln & 3) >> 1), sub = 4 * (ln & 1);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(VL + chunk_at(vrow, ch) + sub));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(VL + chunk_at(vrow + 16, ch) + sub));
+        acc[mb] = mfma16x16x32(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)),
+                               pk, acc[mb]);
       }
     }
+  };
+  if (r_begin < r_end) issue_tile(r_begin, K0, V0);
+  for (int t0 = r_begin; t0 < r_end; t0 += 2 * TR) {  // even tiles in buffers 0, odd in 1
+    tile_step(t0, K0, V0, K1, V1);
+    if (t0 + TR < r_end) tile_step(t0 + TR, K1, V1, K0, V0);
   }
 
   // partial of this range: m[Mq] | l[Mq] | O[Mq][D]  (m in base 2)
