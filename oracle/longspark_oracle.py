@@ -36,8 +36,9 @@ fusion or reordering beyond what the definitions state.
 
 Parity status of each function (what pins it is in tests/test_oracle.py):
   summary_reference, summary_init, append_accepted, full_recompute,
-  verify_greedy, draft_attention: pinned (closed forms, brute force, SDPA
-  special cases, worked examples under tests/golden/).
+  target_argmax, accepted_length, verify_greedy, draft_attention: pinned
+  (closed forms, brute force, SDPA special cases, worked examples under
+  tests/golden/).
   draft_argmax, boundary_row, verify_attention, and the S = 0 / W = 0 views:
   pinned in tests/test_oracle_next.py (brute force, SDPA with an explicit
   mask, worked examples).
@@ -59,6 +60,8 @@ __all__ = [
     "summary_reference",
     "OracleState",
     "summary_init",
+    "target_argmax",
+    "accepted_length",
     "verify_greedy",
     "append_accepted",
     "full_recompute",
@@ -207,6 +210,41 @@ def summary_init(u, log_lambda, k_prefix, v_prefix, W, heads=None):
 # --------------------------------------------------------------------------
 # greedy verification (Fig. 2 (a); Table 3, T = 0)
 # --------------------------------------------------------------------------
+def target_argmax(logits):
+    """The target's greedy token at each verified position.
+
+    logits [C, B+1, V] (any decodable dtype).  Returns int32 [C, B+1]:
+    g_i = argmax_v logits[c, i, v], the lowest index on ties (+0 and -0 are
+    equal as decoded float64 values).
+    """
+    x = decode(logits)
+    C, B1, _ = x.shape
+    target = np.zeros((C, B1), dtype=np.int32)
+    for c in range(C):
+        for i in range(B1):
+            target[c, i] = int(np.argmax(x[c, i]))   # first occurrence of the max
+    return target
+
+
+def accepted_length(target, draft):
+    """tau = M + 1, where M is the longest prefix with draft[c, i] == g_i.
+
+    target [C, B+1] (the g_i), draft [C, B].  Returns tau [C] int32: the M
+    accepted drafts plus the target's own token g_M are committed.
+    """
+    target = np.asarray(target)
+    draft = np.asarray(draft)
+    C, B1 = target.shape
+    B = B1 - 1
+    tau = np.zeros((C,), dtype=np.int32)
+    for c in range(C):
+        M = 0
+        while M < B and int(draft[c, M]) == int(target[c, M]):
+            M += 1
+        tau[c] = M + 1
+    return tau
+
+
 def verify_greedy(logits, draft):
     """Greedy acceptance of a drafted block.
 
@@ -218,20 +256,8 @@ def verify_greedy(logits, draft):
 
     Returns target_tok [C, B+1] int32 (all g_i) and tau [C] int32.
     """
-    x = decode(logits)
-    draft = np.asarray(draft)
-    C, B1, _ = x.shape
-    B = B1 - 1
-    target = np.zeros((C, B1), dtype=np.int32)
-    tau = np.zeros((C,), dtype=np.int32)
-    for c in range(C):
-        for i in range(B1):
-            target[c, i] = int(np.argmax(x[c, i]))   # first occurrence of the max
-        M = 0
-        while M < B and int(draft[c, M]) == int(target[c, M]):
-            M += 1
-        tau[c] = M + 1
-    return target, tau
+    target = target_argmax(logits)
+    return target, accepted_length(target, draft)
 
 
 # --------------------------------------------------------------------------
@@ -429,8 +455,10 @@ def verify_sampling(target_logits, draft_logits, draft, temperature, u_accept, u
     its sampled tokens.  p_j = softmax(target row j / T), q_j = softmax(draft
     row j / T).  Draft j is accepted when u_accept[c, j] * q_j(d) < p_j(d),
     i.e. with probability min(1, p/q); at the first rejection the emitted
-    token is drawn from max(0, p_j - q_j) with u_sample[c] (inverse_cdf); if
-    all B drafts are accepted the extra token is drawn from p_B.
+    token is drawn from max(0, p_j - q_j) with u_sample[c] (inverse_cdf), or
+    from p_j when that residual is zero everywhere (p_j == q_j, reachable only
+    when the drafted token has p = q = 0); if all B drafts are accepted the
+    extra token is drawn from p_B.
 
     Returns tokens [C, B+1] int32 (the first tau[c] are emitted, the rest -1)
     and tau [C] int32 in [1, B+1].
@@ -454,6 +482,10 @@ def verify_sampling(target_logits, draft_logits, draft, temperature, u_accept, u
             else:
                 break
         w = np.maximum(p[c, j] - q[c, j], 0.0) if j < B else p[c, B]
+        if not np.any(w > 0.0):
+            # a rejection with p_j == q_j (the drafted token has p = q = 0):
+            # the residual is empty, so the token is drawn from p_j itself
+            w = p[c, j]
         tokens[c, j] = inverse_cdf(w, u_sample[c])
         tau[c] = j + 1
     return tokens, tau

@@ -104,13 +104,33 @@ def test_equal_distributions_accept_every_draft():
         assert tokens[c, 3] == _brute_inverse_cdf(p_b.tolist(), u_s[c])
 
 
+def test_empty_residual_draws_from_the_target():
+    """p_j == q_j with p_j(d) = q_j(d) = 0 (a drafted token with logit -inf):
+    u * 0 < 0 fails, so d is rejected, max(0, p - q) is zero everywhere and the
+    token comes from p_j itself (an inverse-CDF draw over the target row)."""
+    rng = np.random.default_rng(45)
+    logits = rng.standard_normal((3, 4, 25)).astype(np.float32)
+    draft = rng.integers(0, 25, size=(3, 3))
+    for c in range(3):                      # row 1: its draft has p = q = 0
+        logits[c, 1, draft[c, 1]] = -np.inf
+    draft[:, 0] = np.argmax(logits[:, 0], axis=-1)   # accepted: p/q = 1 > u
+    u_s = np.array([0.05, 0.5, 0.95])
+    tokens, tau = O.verify_sampling(logits, logits[:, :3], draft, 1.0, rng.random((3, 3)) * 0.9, u_s)
+    assert tau.tolist() == [2, 2, 2]
+    for c in range(3):
+        p1 = O.softmax_t(logits[c, 1], 1.0)
+        assert tokens[c, 0] == draft[c, 0]
+        assert tokens[c, 1] == _brute_inverse_cdf(p1.tolist(), u_s[c])
+        assert 0 <= tokens[c, 1] < 25 and tokens[c, 1] != draft[c, 1]
+
+
 # --------------------------------------------------------------------------
 # the pins catch planted mistakes
 # --------------------------------------------------------------------------
 def _run_pins():
     pins = [test_sampling_worked_example, test_inverse_cdf_brute_force,
             lambda: test_first_token_is_distributed_as_the_target(1.0),
-            test_equal_distributions_accept_every_draft]
+            test_equal_distributions_accept_every_draft, test_empty_residual_draws_from_the_target]
     failed = 0
     for p in pins:
         try:
