@@ -26,7 +26,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 # stream identifiers inside a workload's seed tree
-_U, _PREFIX, _ROUND, _LOGITS, _VQ, _SAMP = 0, 1, 2, 3, 4, 5
+_U, _PREFIX, _ROUND, _LOGITS, _VQ, _SAMP, _EDGE = 0, 1, 2, 3, 4, 5, 6
 LOGIT_CLIP = 4.0        # ordinary logits are clipped to [-4, 4]
 LOGIT_TOP = 4.5         # the planted greedy token's logit (exact in bf16 and f32)
 TIE_PROB = 0.25         # share of rows with a second, higher-index copy of the top value
@@ -212,6 +212,67 @@ def logits_entry(wl: Workload, k: int):
             if tie[c, i] and room > 0:
                 x[c, i, g[c, i] + 1 + off[c, i] % room] = LOGIT_TOP
     return to_storage(x, wl.dtype), g.astype(np.int32)
+
+
+EDGE_KINDS = 8
+EDGE_CHUNK = 8192       # a boundary the rows put ties across (any reduction that splits rows)
+
+
+def edge_logits(wl: Workload, k: int) -> np.ndarray:
+    """Logits [C, B+1, V] made of the rows on which an argmax reduction slips most easily.
+
+    Row (c, i) is of kind (c (B+1) + i + k) mod 8:
+      0  every value negative; the maximum -0.125 sits at two positions on
+         either side of a multiple of 8192 (a tie across a chunk boundary);
+      1  +0 and -0 only, signs drawn at random (all equal: the first wins);
+      2  -inf everywhere;
+      3  -inf everywhere except a -0 and a +0 at two random positions;
+      4  N(0, 1) with 3.0 at 8192 m - 1, 8192 m and V - 1 (positive ties);
+      5  N(0, 1) with 3.0 at V - 1 only (the ragged last chunk);
+      6  N(0, 1) with 3.0 at 0 and at V - 1;
+      7  the smallest positive subnormal of the storage type at a random
+         position, +0 / -0 elsewhere in the first half and negative values
+         in the second.
+    No value is compared here: each kind is built from its description.
+    """
+    rng = _rng(wl.seed, _EDGE, k)
+    C, B1, V = wl.C, wl.B + 1, wl.V
+    x = rng.standard_normal(size=(C, B1, V), dtype=np.float32)
+    np.clip(x, -LOGIT_CLIP, LOGIT_CLIP, out=x)
+    tiny = np.float32(np.uint32(0x00010000).view(np.float32) if wl.dtype == "bf16"
+                      else np.uint32(1).view(np.float32))
+    nb = max(1, (V - 1) // EDGE_CHUNK)           # chunk boundaries inside the row
+    for c in range(C):
+        for i in range(B1):
+            kind = (c * B1 + i + k) % EDGE_KINDS
+            row = x[c, i]
+            m = 1 + int(rng.integers(0, nb))
+            lo, hi = min(EDGE_CHUNK * m - 1, V - 2), min(EDGE_CHUNK * m, V - 1)
+            if kind == 0:
+                np.negative(np.abs(row), out=row)
+                row -= np.float32(0.25)
+                row[lo] = row[hi] = np.float32(-0.125)
+            elif kind == 1:
+                row[:] = np.where(rng.random(V) < 0.5, np.float32(-0.0), np.float32(0.0))
+            elif kind == 2:
+                row[:] = -np.inf
+            elif kind == 3:
+                row[:] = -np.inf
+                a, b = rng.choice(V, size=2, replace=False)
+                row[a], row[b] = np.float32(-0.0), np.float32(0.0)
+            elif kind == 4:
+                row[lo] = row[hi] = row[V - 1] = np.float32(3.0)
+            elif kind == 5:
+                row[V - 1] = np.float32(3.0)
+            elif kind == 6:
+                row[0] = row[V - 1] = np.float32(3.0)
+            else:
+                half = V // 2
+                row[:half] = np.where(rng.random(half) < 0.5, np.float32(-0.0), np.float32(0.0))
+                np.negative(np.abs(row[half:]), out=row[half:])
+                row[half:] -= np.float32(0.25)
+                row[int(rng.integers(0, V))] = tiny
+    return to_storage(x, wl.dtype)
 
 
 def pool_size(wl: Workload) -> int:

@@ -98,19 +98,27 @@ def compare_state(runner, ost: O.OracleState, dtype, heads=None):
 
 
 def lockstep(wl: WLM.Workload, rounds: int, k_prefix=None, v_prefix=None, heads=None,
-             check_state_every=1, runner=None, tau_override=None, device="cuda"):
+             check_state_every=1, runner=None, tau_override=None, device="cuda", fused=False,
+             logits_fn=None, draft_fn=None):
     """Run ``rounds`` rounds on both sides and compare after each.
 
     ``heads`` samples (c, h) pairs for the float checks of large workloads
     (the oracle's summary and attention are computed only there).
     ``tau_override`` (round -> tau array) replaces the verified tau on both
     sides before the append (device-side clamping and the error flag).
+    ``fused`` runs each round as the bench does (runner.round:
+    ls_verify_append, then ls_draft_attention) instead of the three separate
+    entry points; target_tok and tau are then checked after the round.
+    ``logits_fn(r)`` -> (logits, planted or None) replaces the pooled logits;
+    ``draft_fn(r, target)`` -> draft [C, B] replaces the round's drafts, built
+    from the oracle's target tokens ``target`` (never from GPU output).
     Returns (runner, oracle_state, stats).
     """
     import torch
     from fixed_cost_drafter_amd import binding as LB
     from fixed_cost_drafter_amd.runner import PathRunner, upload_round
 
+    assert not (fused and tau_override), "the fused call derives tau itself"
     t0 = time.time()
     if k_prefix is None:
         k_prefix, v_prefix = WLM.prefix(wl, threads=16)
@@ -133,34 +141,52 @@ def lockstep(wl: WLM.Workload, rounds: int, k_prefix=None, v_prefix=None, heads=
     if heads is not None:
         pairs = [(c, h * G + g) for c, h in heads for g in range(G)]
     for r in range(rounds):
-        k = r % WLM.pool_size(wl)
-        if k not in pool:
-            logits, planted = WLM.logits_entry(wl, k)
-            pool[k] = (logits, planted, LB.to_device(logits, device))
-        logits, planted, logits_dev = pool[k]
-        inp = WLM.round_inputs(wl, r, planted)
+        if logits_fn is None:
+            # a pooled logits tensor: its oracle argmax is a pure function of
+            # it, computed once per pool entry
+            k = r % WLM.pool_size(wl)
+            if k not in pool:
+                logits, planted = WLM.logits_entry(wl, k)
+                pool[k] = (logits, planted, LB.to_device(logits, device), O.target_argmax(logits))
+            logits, planted, logits_dev, tgt_ref = pool[k]
+        else:
+            logits, planted = logits_fn(r)
+            logits_dev = LB.to_device(logits, device)
+            tgt_ref = O.target_argmax(logits)
+        inp = WLM.round_inputs(wl, r, planted if planted is not None else tgt_ref)
+        if draft_fn is not None:
+            inp["draft"] = np.ascontiguousarray(draft_fn(r, tgt_ref), dtype=np.int32)
+        tau_ref = O.accepted_length(tgt_ref, inp["draft"])
+        if planted is not None:
+            exact("target_tok==planted", tgt_ref, planted)
         dev = upload_round(inp, device)
         b = runner.buf
         s = runner.state
-        s.verify_greedy(logits_dev, dev["draft"], b.target_tok, b.tau)
-        tgt_ref, tau_ref = O.verify_greedy(logits, inp["draft"])
-        torch.cuda.synchronize()
-        exact("target_tok", LB.to_host(b.target_tok), tgt_ref)
-        exact("tau", LB.to_host(b.tau), tau_ref)
-        exact("target_tok==planted", tgt_ref, planted)
         tau_use = tau_ref
-        if tau_override is not None and r in tau_override:
-            forced = np.asarray(tau_override[r], dtype=np.int32)
-            b.tau.copy_(LB.to_device(forced, device))
-            tau_use = np.clip(forced, 1, wl.B + 1)
-        s.append_accepted(dev["k_new"], dev["v_new"], b.tau)
-        s.draft_attention(dev["q"], dev["k_blk"], dev["v_blk"], b.out)
+        if fused:
+            runner.round(logits_dev, dev)
+        else:
+            s.verify_greedy(logits_dev, dev["draft"], b.target_tok, b.tau)
+            torch.cuda.synchronize()
+            exact("target_tok", LB.to_host(b.target_tok), tgt_ref)
+            exact("tau", LB.to_host(b.tau), tau_ref)
+            if tau_override is not None and r in tau_override:
+                forced = np.asarray(tau_override[r], dtype=np.int32)
+                b.tau.copy_(LB.to_device(forced, device))
+                tau_use = np.clip(forced, 1, wl.B + 1)
+            s.append_accepted(dev["k_new"], dev["v_new"], b.tau)
+            s.draft_attention(dev["q"], dev["k_blk"], dev["v_blk"], b.out)
         O.append_accepted(ost, inp["k_new"], inp["v_new"], tau_use, heads=heads)
         out_ref = O.draft_attention(ost, inp["q"], inp["k_blk"], inp["v_blk"], pairs=pairs)
         torch.cuda.synchronize()
+        if fused:
+            exact(f"round {r} target_tok", LB.to_host(b.target_tok), tgt_ref)
+            exact(f"round {r} tau", LB.to_host(b.tau), tau_ref)
         stats["tau"].append(tau_ref.copy())
         if check_state_every and (r % check_state_every == 0 or r == rounds - 1):
             compare_state(runner, ost, wl.dtype, heads)
+            if rounds > 32:
+                log(f"[{wl.name}] round {r}: state parity ok ({time.time() - t0:.1f}s)")
         out = LB.to_host(b.out)
         if pairs is None:
             close("out", out, out_ref, wl.dtype)

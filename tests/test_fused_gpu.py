@@ -4,8 +4,8 @@ separate entry points (ls_verify_greedy, then ls_append_accepted).
 The fused call derives tau from the verification's partial keys inside the
 update; it must give the same target tokens, tau and state, bit for bit, as
 the two calls, over rounds that accept every draft, none, and a random mix.
-The oracle parity of the fused path itself is covered by the lockstep tests
-(their rounds use it)."""
+The fused path against the oracle is tests/test_parity_gpu.py's
+full-size and edge-logits cases (lockstep with fused=True)."""
 import numpy as np
 import pytest
 

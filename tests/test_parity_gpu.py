@@ -87,13 +87,70 @@ def test_parity_q3_4b_8k_all_heads():
     H.log(f"mean tau {taus.mean():.2f} (expected {WLM.expected_tau(wl):.2f})")
 
 
-@pytest.mark.parametrize("name", ["q3_8b_32k", "q3_8b_128k"])
+FULL_SIZE_HEADS = {
+    "q3_8b_32k": [(0, 0), (7, 3), (15, 7)],
+    "q3_8b_64k": [(0, 5), (6, 2), (11, 0), (15, 7)],
+    "q3_8b_128k": [(0, 0), (7, 3), (15, 7)],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_SIZE_HEADS))
 def test_parity_full_size_sampled(name):
-    """Full shape, full prefix, bench launch configuration; sampled heads."""
+    """Full shape and prefix, the bench's call sequence (ls_verify_append, then
+    ls_draft_attention) for the configured 256 rounds.  Integers (target_tok,
+    tau, the whole ring, ring_pos, seq_len) are checked every round for every
+    sequence; the fp32 summary state and the slots of the sampled (sequence,
+    KV head) units every 32 rounds and at the end, so the incremental update
+    is held against the oracle over a run of the configuration's length
+    (Fig. 3: initialised over the prefix, then only the retained rows)."""
     wl = WLM.WORKLOADS[name]
-    heads = [(0, 0), (7, 3), (15, 7)]
-    _announce(wl, f"rounds=6 sampled heads={heads}")
-    H.lockstep(wl, 6, heads=heads, check_state_every=2)
+    heads = FULL_SIZE_HEADS[name]
+    _announce(wl, f"fused rounds={wl.rounds} sampled heads={heads}")
+    runner, ost, stats = H.lockstep(wl, wl.rounds, heads=heads, check_state_every=32, fused=True)
+    taus = np.stack(stats["tau"]).astype(np.float64)      # [rounds, C]
+    H.log(f"mean tau {taus.mean():.3f} (expected {WLM.expected_tau(wl):.3f})")
+    # accepted lengths differ across the batch, so the ring offsets diverge
+    assert len(set(ost.seq_len.tolist())) > 1
+    assert abs(taus.mean() - WLM.expected_tau(wl)) < 0.5
+
+
+def _edge_drafts(wl):
+    """Drafts that accept (c + r) mod (B + 1) tokens of the oracle's targets."""
+    def fn(r, target):
+        d = np.empty((wl.C, wl.B), dtype=np.int32)
+        for c in range(wl.C):
+            M = (c + r) % (wl.B + 1)
+            for i in range(wl.B):
+                if i < M:
+                    d[c, i] = target[c, i]
+                elif i == M:
+                    d[c, i] = (target[c, i] + 1) % wl.V
+                else:
+                    d[c, i] = (7 * i + 3 * c) % wl.V
+        return d
+    return fn
+
+
+EDGE = {
+    # the headline's verification shape (C = 16, B = 16, V = 151936: 19 key
+    # chunks per row), a short prefix to keep the case quick
+    "edge_q3_8b": WLM.WORKLOADS["q3_8b_128k"].with_(name="edge_q3_8b", L0=1500, rounds=4),
+    "edge_bf16_small": SMALL["bf16_wrap"].with_(name="edge_bf16_small", V=20000, rounds=4),
+    "edge_f32": SMALL["f32_d32_wrap"].with_(name="edge_f32", V=9000, rounds=4),
+}
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("name", list(EDGE))
+def test_parity_edge_logits(name, fused):
+    """Rows whose maximum is <= 0, +0 / -0 only, all -inf, ties on both sides of
+    an 8192-logit boundary, the maximum in the ragged last chunk, a lone
+    subnormal: through ls_verify_greedy (+ the update and the draft) and
+    through ls_verify_append, every round against the oracle."""
+    wl = EDGE[name]
+    _announce(wl, f"edge logits, {'fused' if fused else 'separate'} calls")
+    H.lockstep(wl, wl.rounds, fused=fused, logits_fn=lambda r: (WLM.edge_logits(wl, r), None),
+               draft_fn=_edge_drafts(wl), heads=[(0, 0), (wl.C - 1, wl.Hkv - 1)])
 
 
 def test_tau_out_of_range_is_clamped_and_flagged():
