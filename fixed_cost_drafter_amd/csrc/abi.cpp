@@ -63,9 +63,9 @@ ls_status check_state(const ls_state* s, const ls_dims& d, int32_t L0) {
 
 extern "C" {
 
-int32_t ls_version(void) { return 103; }
+int32_t ls_version(void) { return 104; }
 
-const char* ls_status_string(ls_status status) {
+const char* ls_status_string(int32_t status) {
   switch (status) {
     case LS_OK: return "ok";
     case LS_ERR_NULL: return "a required pointer is NULL";

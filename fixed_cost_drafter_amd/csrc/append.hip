@@ -216,11 +216,11 @@ __device__ __forceinline__ void append_window(
   static_assert(kThreads > 48, "every row of the block gets a thread");
   const int tid = threadIdx.x;
   const int B1 = B + 1;
-  const int L = seq_len[c];
-  if (W == 0) {  // no window view: only the count advances
-    if (tid == 0) seq_len[c] = L + Tn;
+  if (W == 0) {  // no window view: only the count advances (one thread reads and writes it)
+    if (tid == 0) seq_len[c] += Tn;
     return;
   }
+  const int L = seq_len[c];
   const int G = kThreads / B1, i = tid % B1, g = tid / B1;
   const int pairs = Hkv * V16;
   const int64_t src0 = (int64_t(c) * B1 + i) * Hkv * D;
@@ -271,6 +271,9 @@ __device__ __forceinline__ void append_window(
     }
   }
   if (tid < Tn) ring_pos[int64_t(c) * W + (L + tid) % W] = L + tid;
+  // every thread has read the old length (and used it for its stores) before
+  // it is replaced
+  __syncthreads();
   if (tid == 0) seq_len[c] = L + Tn;
 }
 

@@ -4,8 +4,9 @@
 // speculative-sampling rule:
 //   p_j = softmax(target row j / T), q_j = softmax(drafter row j / T);
 //   draft j is accepted when u_accept[j] * q_j(d_j) < p_j(d_j);
-//   at the first rejection j the emitted token is drawn from max(0, p_j - q_j),
-//   after B acceptances from p_B; the draw is the inverse CDF over the
+//   at the first rejection j the emitted token is drawn from max(0, p_j - q_j)
+//   (from p_j when that residual is zero everywhere), after B acceptances
+//   from p_B; the draw is the inverse CDF over the
 //   vocabulary in index order: the smallest k whose running sum exceeds
 //   u_sample times the total.
 //
@@ -147,10 +148,14 @@ __global__ __launch_bounds__(kThreads) void samp_stats(
   }
 }
 
-// weight of vocabulary entry k in the draw of a record's row
+// weight of vocabulary entry k in the draw of a record's row.  p and q are
+// each rounded before the difference: a fused multiply-subtract would leave
+// the rounding error of one product where p == q, and an identically zero
+// residual must stay zero (the draw then falls back to p_j).
 template <typename Ty>
 __device__ __forceinline__ float draw_weight(const typename Ty::T* rt, const typename Ty::T* rd,
                                              const Record& r, float k2, int k) {
+#pragma clang fp contract(off)
   const float p = exp2_f(Ty::load(rt, k) * k2 - r.mt) * r.izt;
   if (r.bonus) return p;
   const float q = exp2_f(Ty::load(rd, k) * k2 - r.md) * r.izd;
@@ -162,6 +167,7 @@ __device__ __forceinline__ float draw_weight(const typename Ty::T* rt, const typ
 template <typename Ty>
 __device__ __forceinline__ void draw_weights16(const typename Vec16<Ty>::V& vt, const typename Vec16<Ty>::V& vd,
                                                const Record& r, float k2, float* w) {
+#pragma clang fp contract(off)
   using VT = Vec16<Ty>;
 #pragma unroll
   for (int e = 0; e < VT::N; ++e) {
@@ -313,47 +319,64 @@ __global__ __launch_bounds__(kThreads) void samp_decide_sums(
 // registers; a workgroup scan of the thread totals finds the thread whose
 // entries hold the crossing, and that thread walks its registers.  When
 // rounding leaves the threshold past the end, the last entry with weight
-// is drawn (last non-empty chunk, thread, entry).
+// is drawn (last non-empty chunk, thread, entry).  A rejection whose residual
+// max(0, p_j - q_j) is zero everywhere (p_j == q_j: the drafted token had
+// p = q = 0) draws from p_j instead; its chunk sums come from the target
+// row's chunk statistics.
 template <typename Ty>
 __global__ __launch_bounds__(kThreads) void samp_draw(
     const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
     const Record* __restrict__ rec, const float* __restrict__ sums,
-    const float* __restrict__ u_sample, int32_t* __restrict__ tokens, int B, int V, int nsplit,
-    float k2, int vec_ok) {
+    const float2* __restrict__ stats, const float* __restrict__ u_sample,
+    int32_t* __restrict__ tokens, int B, int V, int nsplit, float k2, int vec_ok) {
   using VT = Vec16<Ty>;
   constexpr int SEG = kVerifyChunk / kThreads;  // entries per thread
   constexpr int NV = SEG / VT::N;               // 16-byte vectors per thread
   static_assert(SEG % VT::N == 0, "whole vectors per thread");
-  __shared__ int s_split;
+  __shared__ int s_split, s_bonus;
   __shared__ float s_base, s_thr;
   __shared__ float wtot[kThreads / 64];
   __shared__ int s_first[kThreads / 64], s_last[kThreads / 64];
   const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const Record r = rec[c];
+  Record r = rec[c];
   const typename Ty::T* rt = tl + (int64_t(c) * (B + 1) + r.row) * V;
   const typename Ty::T* rd = dl + (int64_t(c) * B + min(r.row, B - 1)) * V;
   if (tid == 0) {
     const float* sm = sums + int64_t(c) * nsplit;
+    const float2* st = stats + (int64_t(c) * (B + 1) + r.row) * nsplit;
     float total = 0.f;
     for (int k = 0; k < nsplit; ++k) total += sm[k];
+    // an empty residual: draw from p_j, whose chunk k holds
+    // s_k 2^(m_k - mt) / Z of the probability mass
+    const bool from_p = !r.bonus && !(total > 0.f);
+    auto chunk = [&](int k) {
+      return from_p ? (st[k].x == -INFINITY ? 0.f : st[k].y * exp2_f(st[k].x - r.mt) * r.izt) : sm[k];
+    };
+    if (from_p) {
+      total = 0.f;
+      for (int k = 0; k < nsplit; ++k) total += chunk(k);
+    }
     const float thr = u_sample[c] * total;
     float run = 0.f;
     int sp = -1, last = 0;
     for (int k = 0; k < nsplit; ++k) {
-      if (sm[k] > 0.f) last = k;
-      if (sp < 0 && run + sm[k] > thr) sp = k;
-      if (sp < 0) run += sm[k];
+      const float a = chunk(k);
+      if (a > 0.f) last = k;
+      if (sp < 0 && run + a > thr) sp = k;
+      if (sp < 0) run += a;
     }
     if (sp < 0) {  // rounding left the threshold at the very end: the last non-empty chunk
       sp = last;
       run = 0.f;
-      for (int k = 0; k < last; ++k) run += sm[k];
+      for (int k = 0; k < last; ++k) run += chunk(k);
     }
     s_split = sp;
     s_base = run;
     s_thr = thr;
+    s_bonus = from_p ? 1 : r.bonus;
   }
   __syncthreads();
+  r.bonus = s_bonus;
   const int begin = s_split * kVerifyChunk, end = min(V, begin + kVerifyChunk);
   const int k0 = begin + tid * SEG;
   float w[SEG];
@@ -436,8 +459,8 @@ ls_status run(const ls_dims& d, const void* tl, const void* dl, const int32_t* d
   hipLaunchKernelGGL(samp_decide_sums<Ty>, dim3(nsplit, d.C), dim3(kThreads), 0, stream, t, dd, draft,
                      u_accept, stats, rec, tokens, tau, sums, d.C, d.B, d.V, nsplit, k2, vec_ok);
   if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
-  hipLaunchKernelGGL(samp_draw<Ty>, dim3(d.C), dim3(kThreads), 0, stream, t, dd, rec, sums, u_sample,
-                     tokens, d.B, d.V, nsplit, k2, vec_ok);
+  hipLaunchKernelGGL(samp_draw<Ty>, dim3(d.C), dim3(kThreads), 0, stream, t, dd, rec, sums, stats,
+                     u_sample, tokens, d.B, d.V, nsplit, k2, vec_ok);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
 

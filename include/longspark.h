@@ -236,9 +236,11 @@ ls_status ls_verify_attention(const ls_dims* dims, const void* k_cache, const vo
  * The pages do not print the rule; this is the textbook speculative-sampling
  * rule.  p_j = softmax(target row j / T), q_j = softmax(drafter row j / T);
  * draft j is accepted when u_accept[c, j] * q_j(d) < p_j(d); at the first
- * rejection the token is drawn from max(0, p_j - q_j), after B acceptances
- * from p_B, as the smallest k whose running sum exceeds u_sample[c] times
- * the total (inverse CDF over the vocabulary in index order).
+ * rejection the token is drawn from max(0, p_j - q_j) (from p_j when that
+ * residual is zero everywhere, i.e. p_j == q_j and the drafted token had
+ * p = q = 0), after B acceptances from p_B, as the smallest k whose running
+ * sum exceeds u_sample[c] times the total (inverse CDF over the vocabulary
+ * in index order).
  *   target_logits: [C, B+1, V] dtype; draft_logits: [C, B, V] dtype; no NaN.
  *   draft:         [C, B] int32 drafted tokens (each in [0, V)).
  *   temperature:   T > 0 (host value).
@@ -254,8 +256,9 @@ ls_status ls_verify_sampling(const ls_dims* dims, const void* target_logits,
                              int32_t* tau, void* workspace, size_t workspace_bytes,
                              ls_stream stream);
 
-/* Static description of a status code. */
-const char* ls_status_string(ls_status status);
+/* Static description of a status code (any integer: unknown values give
+ * "unknown status"). */
+const char* ls_status_string(int32_t status);
 
 /* Library ABI version (major * 100 + minor). */
 int32_t ls_version(void);

@@ -212,12 +212,14 @@ def _sampling_expectation(tl, dl, draft, T, ua, us, c):
     while j < B:
         d = int(draft[c, j])
         a, b = float(ua[c, j]) * q[j, d], p[j, d]
-        if abs(a - b) <= ACCEPT_EPS * max(a, b, 1e-300):
-            return None
+        if max(a, b) > 0.0 and abs(a - b) <= ACCEPT_EPS * max(a, b):
+            return None     # (0 < 0 is false in any precision: no ambiguity)
         if not a < b:
             break
         j += 1
     w = np.maximum(p[j] - q[j], 0.0) if j < B else p[B]
+    if not np.any(w > 0.0):   # an empty residual: the oracle's rule draws from p_j
+        w = p[j]
     cs = np.cumsum(w)
     thr = float(us[c]) * cs[-1]
     band = DRAW_EPS * cs[-1]
@@ -283,3 +285,38 @@ def test_verify_sampling_equal_distributions_accept_all():
     torch.cuda.synchronize()
     assert LB.to_host(tau).tolist() == [wl.B + 1] * wl.C
     assert np.array_equal(LB.to_host(tokens)[:, :wl.B], inp["draft"])
+
+
+def test_verify_sampling_empty_residual_draws_from_the_target():
+    """Drafter == target except that row 1's drafted token has logit -inf in both:
+    draft 0 is accepted, draft 1 rejected with p = q = 0, the residual
+    max(0, p_1 - q_1) is zero everywhere and the token comes from p_1."""
+    import torch
+    from fixed_cost_drafter_amd import binding as LB
+    wl = SMALL["bf16_s64_ragged"].with_(name="samp_empty_residual", C=5, B=4, V=20001)
+    H.log(f"CASE verify_sampling empty residual C={wl.C} B={wl.B} V={wl.V}")
+    tl, _ = WLM.logits_entry(wl, 3)
+    inp = WLM.sampling_inputs(wl, 3, tl, noise=0.0)
+    x = WLM.bf16_bits_to_f32(tl)
+    draft = inp["draft"].copy()
+    for c in range(wl.C):
+        x[c, 1, draft[c, 1]] = -np.inf
+    tl2 = WLM.f32_to_bf16_bits(x)
+    dl2 = np.ascontiguousarray(tl2[:, :wl.B])
+    ua = np.full((wl.C, wl.B), 0.5, dtype=np.float32)
+    us = np.array([0.0, 0.25, 0.5, 0.75, 0.999], dtype=np.float32)
+    st = _state(wl)
+    tokens = torch.empty((wl.C, wl.B + 1), dtype=torch.int32, device="cuda")
+    tau = torch.empty((wl.C,), dtype=torch.int32, device="cuda")
+    st.verify_sampling(LB.to_device(tl2), LB.to_device(dl2), LB.to_device(draft), 1.0,
+                       LB.to_device(ua), LB.to_device(us), tokens, tau)
+    torch.cuda.synchronize()
+    got_tok, got_tau = LB.to_host(tokens), LB.to_host(tau)
+    ref_tok, ref_tau = O.verify_sampling(tl2, dl2, draft, 1.0, ua, us)
+    assert got_tau.tolist() == ref_tau.tolist() == [2] * wl.C
+    for c in range(wl.C):
+        exp = _sampling_expectation(tl2, dl2, draft, 1.0, ua, us, c)
+        assert exp is not None and exp[0] == 2
+        assert int(got_tok[c, 0]) == int(draft[c, 0])
+        assert int(got_tok[c, 1]) in exp[2], (c, got_tok[c, 1], sorted(exp[2])[:8], ref_tok[c, 1])
+        assert (got_tok[c, 2:] == -1).all()
