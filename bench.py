@@ -217,46 +217,72 @@ def run_gpu(args, wl):
             ts.append(a.elapsed_time(b) * 1e-3)
         return statistics.median(ts)
 
-    def run_rounds(L0, rn=None):
-        """the timed region: args.steps rounds after args.warmup untimed ones"""
+    def bind_all(rn):
+        """every round's calls marshalled once, so the timed loop only issues them"""
+        return [rn.bind_round(pool[r % len(pool)][0], rounds[r], stream) for r in range(n_rounds)]
+
+    def run_rounds(L0, rn=None, passes=args.passes):
+        """``passes`` timed passes of args.steps rounds each (after args.warmup
+        untimed rounds), every pass bracketed by a device synchronisation on
+        both sides; the median pass by wall clock is reported"""
         runner_ = rn if rn is not None else runner
         runner_.init(L0)
+        calls = bind_all(runner_)
         for r in range(args.warmup):
-            runner_.round(pool[r % len(pool)][0], rounds[r])
+            calls[r]()
         torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for r in range(args.warmup, n_rounds):
-            runner_.round(pool[r % len(pool)][0], rounds[r])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return dict(wall_s=time.perf_counter() - t_start, gpu_s=e0.elapsed_time(e1) * 1e-3)
+        res = []
+        for _ in range(passes):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            e0.record(stream)
+            for r in range(args.warmup, n_rounds):
+                calls[r]()
+            t_issue = time.perf_counter()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t_end = time.perf_counter()
+            res.append(dict(wall_s=t_end - t_start, issue_s=t_issue - t_start,
+                            gpu_s=e0.elapsed_time(e1) * 1e-3))
+        res_sorted = sorted(res, key=lambda x: x["wall_s"])
+        med = dict(res_sorted[len(res_sorted) // 2])
+        med["passes_wall_s"] = [x["wall_s"] for x in res]
+        return med
 
     def run_graph(L0):
         """K rounds captured once in a HIP graph, replayed; the same inputs as run_rounds."""
         runner.init(L0)
+        calls = bind_all(runner)
         for r in range(args.warmup):
-            runner.round(pool[r % len(pool)][0], rounds[r])
+            calls[r]()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
+            cap = bind_all_on(runner, side)
             g.capture_begin()
             for r in range(args.warmup, n_rounds):
-                runner.round(pool[r % len(pool)][0], rounds[r])
+                cap[r]()
             g.capture_end()
         torch.cuda.current_stream().wait_stream(side)
         runner.init(L0)  # capture does not execute: replay from the same state
         for r in range(args.warmup):
-            runner.round(pool[r % len(pool)][0], rounds[r])
+            calls[r]()
         torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        g.replay()
-        torch.cuda.synchronize()
-        return dict(wall_s=time.perf_counter() - t_start)
+        walls = []
+        for _ in range(args.passes):
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t_start)
+        return dict(wall_s=statistics.median(walls))
+
+    def bind_all_on(rn, strm):
+        return [rn.bind_round(pool[r % len(pool)][0], rounds[r], strm) for r in range(n_rounds)]
 
     out = {}
     # headline: the workload's own prefix
@@ -387,41 +413,109 @@ def run_gpu(args, wl):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle, as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
-def cpu_baseline(wl, budget_s: float):
-    from oracle import longspark_oracle as O
-    from fixed_cost_drafter_amd import workload as WLM
+_CPU = {}          # inputs of the sample, set before the worker processes fork
+CPU_L_INIT = 1024  # prefix rows the oracle's state starts from (round cost does not depend on it)
+CPU_POOL = 2       # logits tensors cycled by the sample
+CPU_INPUTS = 32    # distinct round inputs cycled by the sample
+
+
+def host_cpus() -> int:
+    """CPUs this process may run on (the box's share, whatever nproc shows), at most 16."""
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
-    L_init = 1024
-    Kp, Vp = WLM.prefix(wl, L0=L_init, threads=4)
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_rounds(seqs, n_rounds):
+    """n_rounds full rounds (verify, append, draft attention) of sequences ``seqs``
+    with the oracle; returns the seconds they took."""
+    from oracle import longspark_oracle as O
+    c0, c1 = seqs
+    wl, u, logl = _CPU["wl"], _CPU["u"], _CPU["logl"]
+    st = O.summary_init(u, logl, _CPU["Kp"][c0:c1], _CPU["Vp"][c0:c1], wl.W)
     t0 = time.perf_counter()
-    st = O.summary_init(WLM.slot_queries(wl), WLM.log_lambda(wl), Kp, Vp, wl.W)
-    t_init = time.perf_counter() - t0
-    n = 0
-    t_rounds = 0.0
-    pool = {}
-    while n < 2 or (t_rounds < budget_s and n < 64):
-        k = n % max(1, WLM.pool_size(wl))
-        if k not in pool:
-            pool[k] = WLM.logits_entry(wl, k)
-        logits, planted = pool[k]
-        inp = WLM.round_inputs(wl, n, planted)
-        t1 = time.perf_counter()
-        _, tau = O.verify_greedy(logits, inp["draft"])
-        O.append_accepted(st, inp["k_new"], inp["v_new"], tau)
-        O.draft_attention(st, inp["q"], inp["k_blk"], inp["v_blk"])
-        t_rounds += time.perf_counter() - t1
-        n += 1
-    init_bytes = wl.C * wl.Hkv * L_init * wl.d * 2 * (2 if wl.dtype == "bf16" else 4)
-    return dict(value=round(n / t_rounds, 3), unit="rounds/s", cores=int(cores), kind="oracle",
-                sample=(f"{n} full rounds (verify + append + draft attention, all {wl.C} "
-                        f"sequences and heads, V={wl.V}) of the {wl.name} shapes, the oracle's "
-                        f"summary initialised over the first {L_init} prefix rows (round cost "
-                        f"does not depend on the prefix); fp64 numpy"),
-                init_gb_per_s=round(init_bytes / t_init / 1e9, 4))
+    for r in range(n_rounds):
+        logits = _CPU["pool"][r % len(_CPU["pool"])][c0:c1]
+        inp = _CPU["inputs"][r % len(_CPU["inputs"])]
+        _, tau = O.verify_greedy(logits, inp["draft"][c0:c1])
+        O.append_accepted(st, inp["k_new"][c0:c1], inp["v_new"][c0:c1], tau)
+        O.draft_attention(st, inp["q"][c0:c1], inp["k_blk"][c0:c1], inp["v_blk"][c0:c1])
+    return time.perf_counter() - t0
+
+
+def _cpu_worker(job):
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):
+        return _cpu_rounds(*job)
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle timed on the host, before anything touches the GPU.
+
+    Single thread: the whole batch in this process with one BLAS thread.
+    All cores: the C sequences are independent, so host_cpus() worker processes
+    (forked now, with no GPU context to inherit) each run the oracle's rounds
+    on their share of the sequences with one BLAS thread; the rate is the
+    rounds of the whole batch over the wall time of the slowest worker.
+    """
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    from fixed_cost_drafter_amd import workload as WLM
+    t_setup = time.perf_counter()
+    Kp, Vp = WLM.prefix(wl, L0=CPU_L_INIT, threads=4)
+    pool, planted = [], []
+    for k in range(CPU_POOL):
+        lg, pl = WLM.logits_entry(wl, k)
+        pool.append(lg)
+        planted.append(pl)
+    _CPU.update(wl=wl, u=WLM.slot_queries(wl), logl=WLM.log_lambda(wl), Kp=Kp, Vp=Vp, pool=pool,
+                inputs=[WLM.round_inputs(wl, r, planted[r % CPU_POOL]) for r in range(CPU_INPUTS)])
+    log(f"cpu_baseline: inputs ready ({time.perf_counter() - t_setup:.1f}s)")
+    # one thread: rounds until about a third of the budget is spent
+    with threadpool_limits(1):
+        n1 = 2
+        t1 = _cpu_rounds((0, wl.C), n1)
+        while t1 < budget_s / 3 and n1 < 64:
+            n1 *= 2
+            t1 = _cpu_rounds((0, wl.C), n1)
+    rate1 = n1 / t1
+    log(f"cpu_baseline: 1 thread {rate1:.3f} rounds/s ({n1} rounds)")
+    workers = min(host_cpus(), wl.C)
+    per = -(-wl.C // workers)
+    jobs_seqs = [(c, min(wl.C, c + per)) for c in range(0, wl.C, per)]
+    workers = len(jobs_seqs)
+    n_par = int(min(wl.rounds, max(8, budget_s * 2 / 3 * rate1 * workers)))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as p:
+        t0 = time.perf_counter()
+        secs = p.map(_cpu_worker, [(js, n_par) for js in jobs_seqs])
+        wall = time.perf_counter() - t0
+    rate_all = n_par / max(secs)
+    log(f"cpu_baseline: {workers} processes {rate_all:.3f} rounds/s ({n_par} rounds, wall {wall:.1f}s)")
+    _CPU.clear()
+    return dict(value=round(rate_all, 3), unit="rounds/s", cores=workers, kind="oracle",
+                sample=(f"{n_par} full rounds (verify + append + draft attention, all {wl.C} sequences "
+                        f"and heads, V={wl.V}) of the {wl.name} shapes on {workers} worker processes "
+                        f"(one BLAS thread each, {per} sequence(s) each; rate = rounds / slowest "
+                        f"worker); the oracle's summary initialised over the first {CPU_L_INIT} prefix "
+                        f"rows (round cost does not depend on the prefix); {CPU_POOL} logits tensors "
+                        f"and {CPU_INPUTS} round inputs cycled; fp64 numpy"),
+                single_thread=dict(value=round(rate1, 3), rounds=n1),
+                host=dict(cpu_model=cpu_model(), cpus_usable=host_cpus(),
+                          nproc=os.cpu_count(), thread_source="worker processes x 1 BLAS thread"))
 
 
 def next_steps(wl, g) -> dict:
@@ -461,9 +555,11 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="q3_8b_128k")
+    ap.add_argument("--passes", type=int, default=5,
+                    help="timed passes of --steps rounds; the median pass is reported")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
     ap.add_argument("--no-cpu", dest="cpu", action="store_false")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-budget", type=float, default=18.0)
     ap.add_argument("--threads", type=int, default=16)
     ap.add_argument("--no-next", dest="next", action="store_false",
                     help="skip the steps beside the round (argmax, boundary, view ablations)")
@@ -488,6 +584,11 @@ def main(argv=None):
         return 2
     from fixed_cost_drafter_amd import workload as WLM
     wl = WLM.WORKLOADS[args.workload]
+    cpu = None
+    if args.cpu:
+        # first, while no process has touched the GPU: the workers fork from here
+        log("timing the oracle on the host (cpu_baseline)")
+        cpu = cpu_baseline(wl, args.cpu_budget)
     g = run_gpu(args, wl)
     main_r = g["main"]
     value = args.steps / main_r["wall_s"]
@@ -545,16 +646,15 @@ def main(argv=None):
         "round_alg_bytes": int(alg["round"]),
         "round_gb_per_s": round(alg["round"] * value / 1e9, 1),
         "gpu_event_ms_per_step": round(main_r["gpu_s"] / args.steps * 1e3, 5),
+        "passes": args.passes,
+        "pass_ms_per_step": [round(w / args.steps * 1e3, 5) for w in main_r["passes_wall_s"]],
+        "host_issue_us_per_round": round(main_r["issue_s"] / args.steps * 1e6, 2),
         "sweep": g["sweep"],
         "graph_rounds_per_s": (round(args.steps / g["graph"]["wall_s"], 1) if "graph" in g else None),
         "state_bytes_per_seq": g["state_bytes_per_seq"],
         "next": next_steps(wl, g) if args.next else None,
     }
-    if args.cpu:
-        log("timing the oracle on the host (cpu_baseline)")
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
-    else:
-        line["cpu_baseline"] = None
+    line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
     return 0
 

@@ -18,7 +18,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liblongspark.so")
+# LONGSPARK_LIB selects another build of the same library (e.g. the host-side
+# sanitizer build of fixed_cost_drafter_amd.sanitize)
+LIB_PATH = os.environ.get("LONGSPARK_LIB") or os.path.join(_HERE, "liblongspark.so")
 
 LS_F32, LS_BF16 = 0, 1
 STATUS = {0: "LS_OK", 1: "LS_ERR_NULL", 2: "LS_ERR_SHAPE", 3: "LS_ERR_DTYPE",
@@ -111,6 +113,25 @@ def _stream(stream) -> int | None:
 def _check(fn: str, status: int):
     if status != 0:
         raise LsError(fn, status)
+
+
+class BoundCall:
+    """One C-ABI call with every argument already marshalled (raw pointers,
+    ctypes references, the stream handle): calling it only crosses into the
+    library and checks the status.  For loops that issue the same calls
+    many times, e.g. a round's calls prepared before a timed region."""
+
+    __slots__ = ("name", "fn", "args")
+
+    def __init__(self, name: str, *args):
+        self.name = name
+        self.fn = getattr(_lib, name)
+        self.args = args
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != 0:
+            raise LsError(self.name, rc)
 
 
 def make_dims(C, Hq, Hkv, d, W, S, B, V, dtype) -> LsDims:
@@ -342,6 +363,16 @@ class DrafterState:
 
     def draft_attention(self, q, k_blk, v_blk, out, stream=None):
         ls_draft_attention(self.dims, self.c_state, q, k_blk, v_blk, out, stream)
+
+    # the round's two calls with their arguments fixed (see BoundCall)
+    def bind_verify_append(self, logits, draft, target_tok, tau, k_new, v_new, stream=None):
+        return BoundCall("ls_verify_append", ctypes.byref(self.dims), ctypes.byref(self.c_state),
+                         _ptr(logits), _ptr(draft), _ptr(target_tok), _ptr(tau), _ptr(k_new),
+                         _ptr(v_new), _stream(stream))
+
+    def bind_draft_attention(self, q, k_blk, v_blk, out, stream=None):
+        return BoundCall("ls_draft_attention", ctypes.byref(self.dims), ctypes.byref(self.c_state),
+                         _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(out), _stream(stream))
 
     def draft_argmax(self, logits, draft_tok, stream=None):
         ls_draft_argmax(self.dims, logits, draft_tok, self.workspace, self.workspace.numel(), stream)

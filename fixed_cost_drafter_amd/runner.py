@@ -57,6 +57,19 @@ class PathRunner:
         s.verify_append(logits, dev["draft"], b.target_tok, b.tau, dev["k_new"], dev["v_new"], stream)
         s.draft_attention(dev["q"], dev["k_blk"], dev["v_blk"], b.out, stream)
 
+    def bind_round(self, logits: torch.Tensor, dev: dict, stream=None):
+        """The calls of round() with their arguments marshalled once; calling the
+        result issues the round.  The tensors must stay alive while it is used."""
+        s, b = self.state, self.buf
+        va = s.bind_verify_append(logits, dev["draft"], b.target_tok, b.tau, dev["k_new"],
+                                  dev["v_new"], stream)
+        da = s.bind_draft_attention(dev["q"], dev["k_blk"], dev["v_blk"], b.out, stream)
+
+        def issue():
+            va()
+            da()
+        return issue
+
     def round_separate(self, logits: torch.Tensor, dev: dict, stream=None):
         """The same round through the three separate entry points."""
         s, b = self.state, self.buf
