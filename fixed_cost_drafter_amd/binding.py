@@ -24,10 +24,11 @@ LIB_PATH = os.environ.get("LONGSPARK_LIB") or os.path.join(_HERE, "liblongspark.
 
 LS_F32, LS_BF16 = 0, 1
 STATUS = {0: "LS_OK", 1: "LS_ERR_NULL", 2: "LS_ERR_SHAPE", 3: "LS_ERR_DTYPE",
-          4: "LS_ERR_WORKSPACE", 5: "LS_ERR_ALIGN", 6: "LS_ERR_HIP"}
+          4: "LS_ERR_WORKSPACE", 5: "LS_ERR_ALIGN", 6: "LS_ERR_HIP", 7: "LS_ERR_SCRATCH"}
 EXPORTS = ("ls_workspace_bytes", "ls_summary_init", "ls_verify_greedy", "ls_append_accepted",
            "ls_draft_attention", "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention",
-           "ls_verify_sampling", "ls_verify_append", "ls_status_string", "ls_version")
+           "ls_verify_sampling", "ls_verify_append", "ls_verify_greedy_noalloc", "ls_status_string",
+           "ls_version")
 
 
 class LsDims(ctypes.Structure):
@@ -69,9 +70,10 @@ def _load() -> ctypes.CDLL:
     lib.ls_verify_attention.argtypes = [D, P, P, I64, P, I32, P, P, P, SZ, P, P]
     lib.ls_verify_sampling.argtypes = [D, P, P, P, ctypes.c_float, P, P, P, P, P, SZ, P]
     lib.ls_verify_append.argtypes = [D, S, P, P, P, P, P, P, P]
+    lib.ls_verify_greedy_noalloc.argtypes = [D, P, P, P, P, P]
     for f in ("ls_summary_init", "ls_verify_greedy", "ls_append_accepted", "ls_draft_attention",
               "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention", "ls_verify_sampling",
-              "ls_verify_append"):
+              "ls_verify_append", "ls_verify_greedy_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ls_status_string.argtypes = [ctypes.c_int]
     lib.ls_status_string.restype = ctypes.c_char_p
@@ -240,6 +242,12 @@ def ls_verify_greedy(dims: LsDims, logits, draft, target_tok, tau, workspace, wo
     _check("ls_verify_greedy", _lib.ls_verify_greedy(
         ctypes.byref(dims), _ptr(logits), _ptr(draft), _ptr(target_tok), _ptr(tau),
         _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def ls_verify_greedy_noalloc(dims: LsDims, logits, draft, target_tok, tau, stream=None):
+    _check("ls_verify_greedy_noalloc", _lib.ls_verify_greedy_noalloc(
+        ctypes.byref(dims), _ptr(logits), _ptr(draft), _ptr(target_tok), _ptr(tau),
+        _stream(stream)))
 
 
 def ls_append_accepted(dims: LsDims, state: LsState, k_new, v_new, tau, stream=None):

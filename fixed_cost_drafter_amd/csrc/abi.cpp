@@ -12,9 +12,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 
-namespace {
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+namespace ls {
 
 ls_status check_dims(const ls_dims* d) {
   if (d == nullptr) return LS_ERR_NULL;
@@ -42,6 +40,14 @@ ls_status check_dims(const ls_dims* d) {
   return LS_OK;
 }
 
+}  // namespace ls
+
+namespace {
+
+using ls::check_dims;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 ls_status check_state(const ls_state* s, const ls_dims& d, int32_t L0) {
   if (s == nullptr) return LS_ERR_NULL;
   if (!s->seq_len || !s->err_flag || !s->workspace) return LS_ERR_NULL;
@@ -63,7 +69,7 @@ ls_status check_state(const ls_state* s, const ls_dims& d, int32_t L0) {
 
 extern "C" {
 
-int32_t ls_version(void) { return 104; }
+int32_t ls_version(void) { return 105; }
 
 const char* ls_status_string(int32_t status) {
   switch (status) {
@@ -74,6 +80,8 @@ const char* ls_status_string(int32_t status) {
     case LS_ERR_WORKSPACE: return "workspace missing or too small";
     case LS_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case LS_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case LS_ERR_SCRATCH:
+      return "the call needs more scratch than the allocation-free entry point's static buffer";
   }
   return "unknown status";
 }

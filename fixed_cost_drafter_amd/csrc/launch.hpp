@@ -9,8 +9,16 @@
 
 namespace ls {
 
+// the sizes every entry point validates (abi.cpp): LS_OK or the status to return
+ls_status check_dims(const ls_dims* d);
+
 ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* draft,
                         int32_t* target_tok, int32_t* tau, char* ws, hipStream_t stream);
+
+// the same, with the C*(B+1)*verify_splits(d) partial keys at `keys`
+ls_status launch_verify_into(const ls_dims& d, const void* logits, const int32_t* draft,
+                             int32_t* target_tok, int32_t* tau, uint64_t* keys,
+                             hipStream_t stream);
 
 // the verification's partial argmax keys only (into the workspace's key area)
 ls_status launch_verify_keys(const ls_dims& d, const void* logits, char* ws, hipStream_t stream);

@@ -300,9 +300,14 @@ ls_status launch_verify_keys(const ls_dims& d, const void* logits, char* ws, hip
 
 ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* draft,
                         int32_t* target_tok, int32_t* tau, char* ws, hipStream_t stream) {
-  const WsLayout lay = ws_layout(d, 1);
-  const int nsplit = lay.vsplit;
-  uint64_t* part = reinterpret_cast<uint64_t*>(ws + lay.verify_part);
+  return launch_verify_into(d, logits, draft, target_tok, tau,
+                            reinterpret_cast<uint64_t*>(ws + ws_layout(d, 1).verify_part), stream);
+}
+
+ls_status launch_verify_into(const ls_dims& d, const void* logits, const int32_t* draft,
+                             int32_t* target_tok, int32_t* tau, uint64_t* part,
+                             hipStream_t stream) {
+  const int nsplit = verify_splits(d);
   const int rows = d.C * (d.B + 1);
   const ls_status st = d.dtype == LS_BF16 ? launch_partials<BF16>(d, logits, rows, part, nsplit, stream)
                                           : launch_partials<F32>(d, logits, rows, part, nsplit, stream);

@@ -71,7 +71,9 @@ typedef enum ls_status {
   LS_ERR_DTYPE = 3,     /* dtype is neither LS_F32 nor LS_BF16               */
   LS_ERR_WORKSPACE = 4, /* workspace missing or smaller than required        */
   LS_ERR_ALIGN = 5,     /* a pointer lacks the required 16-byte alignment    */
-  LS_ERR_HIP = 6        /* the HIP runtime reported an error at launch       */
+  LS_ERR_HIP = 6,       /* the HIP runtime reported an error at launch       */
+  LS_ERR_SCRATCH = 7    /* too large for ls_verify_greedy_noalloc's static
+                           scratch (see there)                              */
 } ls_status;
 
 /* A hipStream_t; NULL selects the default stream. */
@@ -174,6 +176,21 @@ ls_status ls_append_accepted(const ls_dims* dims, const ls_state* state, const v
 ls_status ls_verify_append(const ls_dims* dims, const ls_state* state, const void* logits,
                            const int32_t* draft, int32_t* target_tok, int32_t* tau,
                            const void* k_new, const void* v_new, ls_stream stream);
+
+/* ls_verify_greedy without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * ls_verify_greedy, minus the workspace; it allocates nothing.
+ * Its C*(B+1)*ceil(V/8192) partial argmax keys live in a static 512 KiB
+ * device array that the library holds on each GPU it runs on until the
+ * process ends: at most 65536 keys (e.g. C*(B+1) <= 3449 at V = 151936).
+ * Larger calls return LS_ERR_SCRATCH before anything is launched.  Every
+ * call on one GPU shares that array: calls that overlap on one GPU
+ * (different streams without ordering) race; calls ordered on one stream
+ * are safe (each writes every key it reads, nothing carries over).
+ * LS_ERR_HIP if the array's device address cannot be obtained. */
+ls_status ls_verify_greedy_noalloc(const ls_dims* dims, const void* logits, const int32_t* draft,
+                                   int32_t* target_tok, int32_t* tau, ls_stream stream);
 
 /* Drafter block attention (Fig. 2 (c)).
  *   q:            [C, B, Hq, d] dtype, block queries.

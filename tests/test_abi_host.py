@@ -67,9 +67,9 @@ def test_header_compiles_as_plain_c(tmp_path):
 
 
 def test_version_and_status_strings(LB):
-    assert LB.ls_version() == 104
+    assert LB.ls_version() == 105
     assert LB.ls_status_string(0) == "ok"
-    for s in range(1, 7):
+    for s in range(1, 8):
         assert LB.ls_status_string(s) and LB.ls_status_string(s) != "unknown status"
     assert LB.ls_status_string(99) == "unknown status"
 
@@ -289,3 +289,21 @@ def test_verify_append_validation(LB):
                               None) == 4             # workspace too small
 
 
+
+@no_device
+def test_noalloc_verify_rejects_what_its_static_scratch_cannot_hold(LB):
+    """ls_verify_greedy_noalloc: 65536 partial keys at most (C (B+1) ceil(V/8192));
+    larger calls return LS_ERR_SCRATCH before any HIP call, bad sizes and NULL
+    pointers the usual codes."""
+    L = LB.lib()
+    fake = 1 << 30
+    big = _dims(LB, C=3500)            # 3500 * 17 rows * 19 chunks = 1.13M keys
+    assert L.ls_verify_greedy_noalloc(ctypes.byref(big), fake, fake, fake, fake, None) == 7
+    edge = _dims(LB, C=203)            # 203 * 17 * 19 = 65569 > 65536
+    assert L.ls_verify_greedy_noalloc(ctypes.byref(edge), fake, fake, fake, fake, None) == 7
+    ok = _dims(LB, C=202)              # 202 * 17 * 19 = 65246 keys: fits
+    assert L.ls_verify_greedy_noalloc(ctypes.byref(ok), None, fake, fake, fake, None) == 1
+    assert L.ls_verify_greedy_noalloc(ctypes.byref(_dims(LB, B=0)), fake, fake, fake, fake, None) == 2
+    assert L.ls_verify_greedy_noalloc(None, fake, fake, fake, fake, None) == 1
+    # in range, valid pointers, but no device here: the symbol lookup fails with LS_ERR_HIP
+    assert L.ls_verify_greedy_noalloc(ctypes.byref(ok), fake, fake, fake, fake, None) == 6
