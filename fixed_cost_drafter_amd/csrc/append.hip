@@ -11,14 +11,17 @@
 //   lambda_j are merged by the online-softmax rule; slot = n / l.
 //   seq_len[c] += tau.
 //
-// Grid: C window workgroups (one per sequence: the only reader and writer of
-// seq_len in the launch, so the update needs no second kernel and no
-// device-scope fence), then the summary workgroups.
+// bf16 (d = 128, S = 0, 64 or 128): append_units below, one workgroup per
+// (sequence, KV head, 32-slot tile); the summary merge on MFMA; the window
+// copy shared out among a unit's workgroups.  The length L before the update
+// comes from a snapshot taken by the launch before (the verification's key
+// pass in ls_verify_append, a one-line kernel in ls_append_accepted), so no
+// workgroup reads the seq_len that one of them advances: no device-scope
+// fence, no second kernel after the update.
 //
-// bf16 (d = 128, S = 64 or 128): append_tiles below, the summary merge on
-// MFMA, 32-slot tiles two per workgroup.
-//
-// f32 (append_kernel): one workgroup per (sequence, KV head, 32 slots), LPS
+// f32: C window workgroups (one per sequence: the only reader and writer of
+// seq_len in the launch, after a barrier), then the summary workgroups,
+// append_kernel: one workgroup per (sequence, KV head, 32 slots), LPS
 // lanes per slot (32; at most d).  Lane g of a slot owns 2d/LPS consecutive
 // entries of the slot's [k | v] numerator n (the first half of the lanes the
 // key half, the rest the value half) and keeps them in registers from the
@@ -436,9 +439,10 @@ __global__ __launch_bounds__(block_threads<D>()) void append_kernel(
 // ---------------------------------------------------------------------------
 // bf16, d = 128, S a multiple of 32: the summary merge on MFMA.
 //
-// Workgroup = one unit (sequence, KV head) with its S / 32 tiles of 32 slots,
-// 4 waves per tile.  For the 32 slots j of a tile and the tau new rows i of
-// the unit, with a_ji = u_j.k_i/sqrt(d) + (tau-1-i) ln(lambda_j):
+// Workgroup = one unit (sequence, KV head) and a group of kTPW tiles of 32
+// slots, 4 waves per tile; the S / (32 kTPW) workgroups of a unit are
+// consecutive on one XCD.  For the 32 slots j of a tile and the tau new rows i
+// of the unit, with a_ji = u_j.k_i/sqrt(d) + (tau-1-i) ln(lambda_j):
 //   S^T = K U^T        rows x slots, 32x32x16 MFMA, each wave for itself;
 //   per slot (one lane column): m' = max(m + tau ln(lambda), max_i a_ji),
 //   s = e^(m + tau ln(lambda) - m'), w_ji = e^(a_ji - m'), l' = l s + sum_i w_ji;
@@ -448,13 +452,19 @@ __global__ __launch_bounds__(block_threads<D>()) void append_kernel(
 // about 16 bits of the fp32 weight; l sums the fp32 weights.  The state n is
 // read once into the accumulators and written once; its tiled layout makes
 // each 16-byte load or store of a wave 1 KB contiguous.  The workgroup
-// stages, once for its tiles, all B+1 verified rows of the unit whatever tau
-// is (keys row-major for S^T, [entry][row] for R^T, rows past B+1 zero) and
-// the slot queries, so no load waits for tau; K-steps past tau are skipped
-// and the weights of rows past tau are 0.  The pooled slots leave through LDS
-// as one key tile (operand order) and one value tile ([d][32]) per tile, in
-// 16-byte stores.  The window workgroups of the same launch have the same
-// 256 S / 32 threads (1024 at S = 128), which keeps their stores short.
+// stages all B+1 verified rows of its unit whatever tau is (keys row-major
+// for S^T, [entry][row] for R^T, rows past B+1 zero) and its slot queries,
+// so no load waits for tau; K-steps past tau are skipped and the weights of
+// rows past tau are 0.  The pooled slots leave through LDS as one key tile
+// (operand order) and one value tile ([d][32]) per tile, in 16-byte stores.
+//
+// The window: the unit's workgroups share out the copy of its tau new rows
+// from the staged rows to ring slots (L + i) mod W: keys as 16-byte pieces
+// at their tiled place, values with lanes over rows (neighbouring lanes,
+// neighbouring slots of one tile row).  L is the sequence's length before
+// the call, read from a snapshot that the launch before this one took
+// (len_snap), so no workgroup here reads seq_len; the lead workgroup of the
+// sequence (KV head 0, first tile group) writes ring_pos and seq_len = L + tau.
 // ---------------------------------------------------------------------------
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -464,11 +474,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // rows each lane feeds the N^T product as its B operand.
 __device__ __forceinline__ int tile_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-// kRB: 32-row score blocks (B + 1 <= 32 kRB); kTPW = S / 32 tiles: one
-// workgroup per unit
 // kVerify: tau is not an input but the accepted prefix of the greedy
 // verification whose partial argmax keys are vkeys (nkeys per row): every
-// workgroup derives it for its sequence, and the window workgroup also writes
+// workgroup derives it for its sequence, and the lead workgroup also writes
 // target_tok and tau_out.
 struct VerifyKeys {
   const uint64_t* keys;
@@ -478,15 +486,24 @@ struct VerifyKeys {
   int32_t* tau_out;
 };
 
+// the length snapshot that the separate update takes before its main launch
+__global__ __launch_bounds__(256) void len_snapshot(const int32_t* __restrict__ seq_len,
+                                                    int32_t* __restrict__ snap, int C) {
+  const int c = int(blockIdx.x) * 256 + int(threadIdx.x);
+  if (c < C) snap[c] = seq_len[c];
+}
+
+// kRB: 32-row score blocks (B + 1 <= 32 kRB); kTPW: tiles of 32 slots per
+// workgroup (S / (32 kTPW) workgroups per unit; one when S = 0)
 template <int kRB, int kTPW, bool kVerify>
-__global__ __launch_bounds__(256 * kTPW) void append_tiles(
+__global__ __launch_bounds__(256 * kTPW) void append_units(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    const int32_t* __restrict__ tau_in, VerifyKeys vk, uint16_t* __restrict__ ring_k,
-    uint16_t* __restrict__ ring_v, int32_t* __restrict__ ring_pos, int32_t* __restrict__ seq_len,
-    float* __restrict__ sum_m, float* __restrict__ sum_l, float* __restrict__ sum_n,
-    uint16_t* __restrict__ slot_k, uint16_t* __restrict__ slot_v, const uint16_t* __restrict__ u,
-    const float* __restrict__ log_lambda, int32_t* __restrict__ err_flag, int C, int Hkv, int W,
-    int S, int B) {
+    const int32_t* __restrict__ tau_in, VerifyKeys vk, const int32_t* __restrict__ len_snap,
+    uint16_t* __restrict__ ring_k, uint16_t* __restrict__ ring_v, int32_t* __restrict__ ring_pos,
+    int32_t* __restrict__ seq_len, float* __restrict__ sum_m, float* __restrict__ sum_l,
+    float* __restrict__ sum_n, uint16_t* __restrict__ slot_k, uint16_t* __restrict__ slot_v,
+    const uint16_t* __restrict__ u, const float* __restrict__ log_lambda,
+    int32_t* __restrict__ err_flag, int C, int Hkv, int W, int S, int B) {
   constexpr int D = 128, E = 2 * D;
   constexpr int kThreads = 256 * kTPW;
   constexpr int RP = 32 * kRB;              // staged rows
@@ -498,46 +515,44 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
   uint16_t* KL = lds;                       // [RP][KLS]   verified keys
   uint16_t* RT = KL + RP * KLS;             // [E][RTS]    verified [k | v], transposed
   uint16_t* UL = RT + E * RTS;              // [32 kTPW][KLS] slot queries
-  __shared__ int32_t g_tok[64];              // kVerify: the rows' argmax tokens
+  __shared__ int32_t g_tok[64];             // kVerify: the rows' argmax tokens
   const int tid = threadIdx.x, lane = tid & 63;
-  if (int(blockIdx.x) < C) {
-    const int c = int(blockIdx.x);
-    int Tn;
-    if constexpr (kVerify) {  // tau first: its barrier must not hold the window's loads
-      const int32_t dj = lane < B ? vk.draft[int64_t(c) * B + lane] : 0;
-      accept_rows<kThreads>(vk.keys, vk.nkeys, c, B, g_tok, vk.target_tok);
-      __syncthreads();
-      Tn = accept_tau(g_tok, dj, B);
-      if (tid == 0) vk.tau_out[c] = Tn;
-    } else {
-      Tn = read_tau(tau_in, c, B, err_flag, true);
-    }
-    append_window<BF16, D, kThreads, 8>(k_new, v_new, Tn, ring_k, ring_v, ring_pos, seq_len, c,
-                                         Hkv, W, B);
-    return;
-  }
-  const int unit = int(blockIdx.x) - C;
+  // blocks of one unit are consecutive in the order each XCD receives them
+  // (block b runs on XCD b mod 8): the unit's staged rows come from one L2
+  const int groups = S > 0 ? S / (32 * kTPW) : 1;
+  const int nblk = int(gridDim.x);
+  int bid = int(blockIdx.x);
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int unit = bid / groups, grp = bid % groups;
   const int c = unit / Hkv, h = unit % Hkv;
+  const bool lead = h == 0 && grp == 0;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tl = wave >> 2, q4 = wave & 3;  // tile of the group, entry quarter
-  const int tile = tl;
+  const int tile = grp * kTPW + tl;
   const int ln = lane & 31, hi = lane >> 5;
   const int B1 = B + 1;
+  const bool summ = S > 0;
   const int j = tile * 32 + ln;             // this lane's slot
   const int64_t sidx = int64_t(unit) * S + j;
   // the wave's part of the tile's state (tiled numerator layout):
   // acc[t][4k + r] = n[j][32 (2 q4 + t) + 8k + 4 hi + r]
   float* nt = sum_n + (int64_t(unit) * S + tile * 32) * E + q4 * 2 * 4 * 64 * 4 + lane * 4;
   f32x16 acc[2];
+  float m_old = 0.f, l_old = 0.f, lnl = 0.f;
+  if (summ) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(nt + (t * 4 + k) * 64 * 4);
+      for (int k = 0; k < 4; ++k) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(nt + (t * 4 + k) * 64 * 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[t][4 * k + r] = v[r];
-    }
-  const float m_old = sum_m[sidx], l_old = sum_l[sidx], lnl = log_lambda[j];
+        for (int r = 0; r < 4; ++r) acc[t][4 * k + r] = v[r];
+      }
+    m_old = sum_m[sidx];
+    l_old = sum_l[sidx];
+    lnl = log_lambda[j];
+  }
+  const int L = len_snap[c];
 
   // staging loads: item (16-byte piece of [k | v], row), rows fastest, so the
   // [entry][row] writes of a wave fall on consecutive banks; then the group's
@@ -554,19 +569,20 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
     const int rc = min(row, B1 - 1);  // rows past B+1 load a real row and are zeroed
     x[q] = *reinterpret_cast<const u16x8*>((half ? v_new : k_new) + ((int64_t(c) * B1 + rc) * Hkv + h) * D + 8 * e);
   }
+  if (summ) {
 #pragma unroll
-  for (int q = 0; q < kUItems; ++q) {
-    const int p = q * kThreads + tid, sl = p >> 4, pc = p & 15;
-    const int slot = sl;
-    xu[q] = *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + slot) * D + 8 * pc);
+    for (int q = 0; q < kUItems; ++q) {
+      const int p = q * kThreads + tid, sl = p >> 4, pc = p & 15;
+      xu[q] = *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + grp * 32 * kTPW + sl) * D + 8 * pc);
+    }
   }
   int Tn = 1;
   int32_t dj = 0;
   if constexpr (kVerify) {
     dj = lane < B ? vk.draft[int64_t(c) * B + lane] : 0;
-    accept_rows<kThreads>(vk.keys, vk.nkeys, c, B, g_tok, nullptr);
+    accept_rows<kThreads>(vk.keys, vk.nkeys, c, B, g_tok, lead ? vk.target_tok : nullptr);
   } else {
-    Tn = read_tau(tau_in, c, B, err_flag, false);
+    Tn = read_tau(tau_in, c, B, err_flag, lead);
   }
 #pragma unroll
   for (int q = 0; q < kItems; ++q) {
@@ -577,13 +593,40 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
 #pragma unroll
     for (int r = 0; r < 8; ++r) RT[(half * D + 8 * e + r) * RTS + row] = v[r];
   }
+  if (summ) {
 #pragma unroll
-  for (int q = 0; q < kUItems; ++q) {
-    const int p = q * kThreads + tid, sl = p >> 4, pc = p & 15;
-    *reinterpret_cast<u16x8*>(&UL[sl * KLS + 8 * pc]) = xu[q];
+    for (int q = 0; q < kUItems; ++q) {
+      const int p = q * kThreads + tid, sl = p >> 4, pc = p & 15;
+      *reinterpret_cast<u16x8*>(&UL[sl * KLS + 8 * pc]) = xu[q];
+    }
   }
   __syncthreads();
-  if constexpr (kVerify) Tn = accept_tau(g_tok, dj, B);  // every wave, from the LDS tokens
+  if constexpr (kVerify) {
+    Tn = accept_tau(g_tok, dj, B);  // every wave, from the LDS tokens
+    if (lead && tid == 0) vk.tau_out[c] = Tn;
+  }
+
+  // the window: this workgroup's share of the unit's copies (Tn 16-byte key
+  // pieces, then 128 Tn value elements, lanes over rows), from the staged rows
+  if (W > 0) {
+    const int nk = Tn * (D / 8), n_all = nk + D * Tn;
+    const int per = (n_all + groups - 1) / groups;
+    const int p0 = grp * per, p1 = min(n_all, p0 + per);
+    for (int p = p0 + tid; p < p1; p += kThreads) {
+      if (p < nk) {
+        const int i = p >> 4, e = p & 15;
+        const int slot = (L + i) % W;
+        *reinterpret_cast<u16x8*>(ring_k + key_index(unit, W, D, slot, 8 * e)) =
+            *reinterpret_cast<const u16x8*>(&KL[i * KLS + 8 * e]);
+      } else {
+        const int q = p - nk, dim = q / Tn, i = q - dim * Tn;
+        ring_v[value_index(unit, W, D, (L + i) % W, dim)] = RT[(D + dim) * RTS + i];
+      }
+    }
+    if (lead && tid < Tn) ring_pos[int64_t(c) * W + (L + tid) % W] = L + tid;
+  }
+  if (lead && tid == 0) seq_len[c] = L + Tn;
+  if (!summ) return;
 
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -679,12 +722,14 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
       }
     }
 
+    // non-temporal stores: the state is next read a round later, and the
+    // round's other streams leave nothing of it in L2 by then
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<f32x4*>(nt + (t * 4 + k) * 64 * 4) =
-            f32x4{acc[t][4 * k], acc[t][4 * k + 1], acc[t][4 * k + 2], acc[t][4 * k + 3]};
+        __builtin_nontemporal_store(f32x4{acc[t][4 * k], acc[t][4 * k + 1], acc[t][4 * k + 2], acc[t][4 * k + 3]},
+                                    reinterpret_cast<f32x4*>(nt + (t * 4 + k) * 64 * 4));
     if (q4 == 0 && hi == 0) {
       sum_m[sidx] = m_new;
       sum_l[sidx] = l_new;
@@ -726,20 +771,28 @@ __global__ __launch_bounds__(256 * kTPW) void append_tiles(
 #pragma unroll
   for (int q = 0; q < 2 * P16 * kTPW / kThreads; ++q) {
     const int p = q * kThreads + tid, t2 = p / (2 * P16), r = p % (2 * P16);
-    if (r < P16)
-      reinterpret_cast<uint4*>(slot_k + key_index(unit, S, D, t2 * 32, 0))[r] = src[p];
-    else
-      reinterpret_cast<uint4*>(slot_v + value_index(unit, S, D, t2 * 32, 0))[r - P16] = src[p];
+    const int t_glob = grp * kTPW + t2;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 val = *reinterpret_cast<const u32x4*>(src + p);
+    u32x4* dst = r < P16 ? reinterpret_cast<u32x4*>(slot_k + key_index(unit, S, D, t_glob * 32, 0)) + r
+                         : reinterpret_cast<u32x4*>(slot_v + value_index(unit, S, D, t_glob * 32, 0)) + (r - P16);
+    __builtin_nontemporal_store(val, dst);
   }
 }
 
+#ifndef LS_APPEND_TPW
+#define LS_APPEND_TPW 2
+#endif
+constexpr int kTilesPerGroup = LS_APPEND_TPW;  // tiles of 32 slots per update workgroup
+
 template <int kRB, int kTPW, bool kVerify>
-void launch_tiles(const ls_dims& d, const ls_state& st, const void* k_new, const void* v_new,
-                  const int32_t* tau, const VerifyKeys& vk, hipStream_t stream) {
-  const int units = d.S > 0 ? d.C * d.Hkv : 0;
-  hipLaunchKernelGGL((append_tiles<kRB, kTPW, kVerify>), dim3(unsigned(d.C + units)),
+void launch_units(const ls_dims& d, const ls_state& st, const void* k_new, const void* v_new,
+                  const int32_t* tau, const VerifyKeys& vk, const int32_t* len_snap,
+                  hipStream_t stream) {
+  const int groups = d.S > 0 ? d.S / (32 * kTPW) : 1;
+  hipLaunchKernelGGL((append_units<kRB, kTPW, kVerify>), dim3(unsigned(d.C * d.Hkv * groups)),
                      dim3(256 * kTPW), 0, stream, static_cast<const uint16_t*>(k_new),
-                     static_cast<const uint16_t*>(v_new), tau, vk,
+                     static_cast<const uint16_t*>(v_new), tau, vk, len_snap,
                      static_cast<uint16_t*>(st.ring_k), static_cast<uint16_t*>(st.ring_v),
                      st.ring_pos, st.seq_len, st.sum_m, st.sum_l, st.sum_n,
                      static_cast<uint16_t*>(st.slot_k), static_cast<uint16_t*>(st.slot_v),
@@ -747,18 +800,16 @@ void launch_tiles(const ls_dims& d, const ls_state& st, const void* k_new, const
                      d.S, d.B);
 }
 
-// bf16: the shape's instantiation (S = 0 runs the window part only)
+// bf16: the shape's instantiation (S in {0, 64, 128}: whole tile groups)
 template <bool kVerify>
-void launch_tiles_for(const ls_dims& d, const ls_state& st, const void* k_new, const void* v_new,
-                      const int32_t* tau, const VerifyKeys& vk, hipStream_t stream) {
-  const bool four = d.S != 64;
-  if (d.B + 1 <= 32) {
-    if (four) launch_tiles<1, 4, kVerify>(d, st, k_new, v_new, tau, vk, stream);
-    else launch_tiles<1, 2, kVerify>(d, st, k_new, v_new, tau, vk, stream);
-  } else {
-    if (four) launch_tiles<2, 4, kVerify>(d, st, k_new, v_new, tau, vk, stream);
-    else launch_tiles<2, 2, kVerify>(d, st, k_new, v_new, tau, vk, stream);
-  }
+void launch_units_for(const ls_dims& d, const ls_state& st, const void* k_new, const void* v_new,
+                      const int32_t* tau, const VerifyKeys& vk, const int32_t* len_snap,
+                      hipStream_t stream) {
+  static_assert(64 % (32 * kTilesPerGroup) == 0, "tile groups divide S = 64 and S = 128");
+  if (d.B + 1 <= 32)
+    launch_units<1, kTilesPerGroup, kVerify>(d, st, k_new, v_new, tau, vk, len_snap, stream);
+  else
+    launch_units<2, kTilesPerGroup, kVerify>(d, st, k_new, v_new, tau, vk, len_snap, stream);
 }
 
 template <typename Ty, int D>
@@ -783,7 +834,12 @@ ls_status run(const ls_dims& d, const ls_state& st, const void* k_new, const voi
 ls_status launch_append(const ls_dims& d, const ls_state& st, const void* k_new,
                         const void* v_new, const int32_t* tau, hipStream_t stream) {
   if (d.dtype == LS_BF16) {  // d = 128, S in {0, 64, 128}
-    launch_tiles_for<false>(d, st, k_new, v_new, tau, VerifyKeys{}, stream);
+    // the lengths before the update, then the update (which advances seq_len)
+    int32_t* snap = reinterpret_cast<int32_t*>(static_cast<char*>(st.workspace) + ws_layout(d, 1).len_snap);
+    hipLaunchKernelGGL(len_snapshot, dim3(unsigned(cdiv(d.C, 256))), dim3(256), 0, stream, st.seq_len,
+                       snap, d.C);
+    if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
+    launch_units_for<false>(d, st, k_new, v_new, tau, VerifyKeys{}, snap, stream);
     return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
   }
   switch (d.d) {
@@ -803,12 +859,14 @@ ls_status launch_verify_append(const ls_dims& d, const ls_state& st, const void*
     const ls_status s1 = launch_verify(d, logits, draft, target_tok, tau, ws, stream);
     return s1 != LS_OK ? s1 : launch_append(d, st, k_new, v_new, tau, stream);
   }
-  const ls_status s1 = launch_verify_keys(d, logits, ws, stream);
-  if (s1 != LS_OK) return s1;
+  // the verification's partial keys; the same launch takes the length snapshot
   const WsLayout lay = ws_layout(d, 1);
+  int32_t* snap = reinterpret_cast<int32_t*>(ws + lay.len_snap);
+  const ls_status s1 = launch_verify_keys(d, logits, ws, st.seq_len, snap, stream);
+  if (s1 != LS_OK) return s1;
   const VerifyKeys vk{reinterpret_cast<const uint64_t*>(ws + lay.verify_part), lay.vsplit, draft,
                       target_tok, tau};
-  launch_tiles_for<true>(d, st, k_new, v_new, nullptr, vk, stream);
+  launch_units_for<true>(d, st, k_new, v_new, nullptr, vk, snap, stream);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
 

@@ -134,7 +134,10 @@ constexpr int kVerifyChunk = LS_VERIFY_CHUNK;  // logits per verify workgroup
 // append's staging of B + 1 fp32 rows of [k | v] (d = 128) stays under 64 KB
 // of LDS.
 constexpr int kMaxBlock = 47;
-constexpr int kInitTargetBlocks = 512; // aim of the init grid size
+#ifndef LS_INIT_TARGET_BLOCKS
+#define LS_INIT_TARGET_BLOCKS 512
+#endif
+constexpr int kInitTargetBlocks = LS_INIT_TARGET_BLOCKS; // aim of the init grid size
 constexpr int kInitRowTile = 64;       // rows per init tile (MFMA path)
 
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
@@ -148,6 +151,7 @@ struct WsLayout {
   int64_t samp_stats;                         // float2 (max, sum) [C*(2B+1)*vsplit]
   int64_t samp_seq;                           // per-sequence decision record [C*8] (4-byte words)
   int64_t samp_sums;                          // float [C*vsplit] chunk sums of the drawn row
+  int64_t len_snap;                           // int32 [C] lengths before an update
   int64_t total;
   int vsplit, isplit, init_rows, asplit;
 };
@@ -222,6 +226,7 @@ inline WsLayout ws_layout(const ls_dims& d, int32_t max_L0) {
   w.samp_stats = off; off = align256(off + 8 * int64_t(d.C) * (2 * d.B + 1) * w.vsplit);
   w.samp_seq = off; off = align256(off + 32 * int64_t(d.C));
   w.samp_sums = off; off = align256(off + 4 * int64_t(d.C) * w.vsplit);
+  w.len_snap = off; off = align256(off + 4 * int64_t(d.C));
   w.total = off;
   return w;
 }

@@ -57,9 +57,10 @@ __device__ __host__ inline int64_t part_off(int split, int units, int unit, int 
 // transposed reads (4 rows x 4 chunks per 16 lanes) on distinct banks.
 // Tiles go from global memory straight into LDS (global_load_lds_dwordx4:
 // lane i of an instruction fills the i-th 16 bytes of a 1 KB LDS block, so
-// each lane fetches the chunk that the swizzle places there), double
-// buffered: the next tile streams in while the current one is computed, and
-// one barrier per tile separates the two.
+// each lane fetches the chunk that the swizzle places there), triple
+// buffered: the next two tiles stream in while the current one is computed
+// (with one workgroup per CU, a single tile in flight left the CU waiting on
+// memory latency), and one barrier per tile separates reads from refills.
 // The two row halves of a slot group keep separate (m, l, n) and merge
 // through LDS at the end.
 // ---------------------------------------------------------------------------
@@ -77,18 +78,22 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
   constexpr int KI = TR * RS / 512 / (NT / 64);  // 1 KB blocks of a K (or V) tile per wave
   static_assert(KI >= 1 && KI * (NT / 64) * 512 == TR * RS, "tile blocks must cover the waves");
   // four LDS arrays of at least one slot group's merge record (64 lanes x
-  // m_true, m_run, l, 128 n): tile buffers 0 and 1 ([K rows | V rows] each),
-  // the slot queries, and a spare; after the loop slot group g merges
-  // through array g.  Separate arrays let the compiler see that the tile
-  // streaming into one buffer does not alias the reads of the other.
+  // m_true, m_run, l, 128 n): tile buffers 0, 1 and 2 ([K rows | V rows]
+  // each) and the slot queries; after the loop slot group g merges through
+  // array g.  Separate arrays let the compiler see that the tiles streaming
+  // into two buffers do not alias the reads of the third.
   constexpr int kMergeElems = 64 * 131 * 2;
   constexpr int kBufElems = 2 * TR * RS > kMergeElems ? 2 * TR * RS : kMergeElems;
   constexpr int kUElems = S * KLS > kMergeElems ? S * KLS : kMergeElems;
   static_assert(NG <= 4, "one merge array per slot group");
   __shared__ __attribute__((aligned(16))) uint16_t buf0[kBufElems];
   __shared__ __attribute__((aligned(16))) uint16_t buf1[kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t buf2[kBufElems];
   __shared__ __attribute__((aligned(16))) uint16_t UL[kUElems];  // [S][KLS]: the slot queries
-  __shared__ __attribute__((aligned(16))) uint16_t spare[NG > 3 ? kMergeElems : 8];
+  // s_waitcnt immediates: every load of this wave done / all but the newest
+  // tile's 2 KI loads done (vmcnt in bits 3:0, expcnt and lgkmcnt not waited)
+  static_assert(2 * KI < 16, "one tile's loads fit the low vmcnt field");
+  constexpr int kWaitAll = 0x0F70, kWaitButOne = 0x0F70 | (2 * KI);
   // element offset of 16-byte chunk c of tile row r
   auto chunk_at = [](int r, int c) { return r * RS + ((c ^ tile_swz(r)) << 3); };
 
@@ -167,15 +172,20 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
   // every few tiles as the bias grows by |ln lambda| per row).
   const int ntiles = (r_end - r_begin + TR - 1) / TR;
   auto tile_t0 = [&](int idx) { return r_begin + (ntiles - 1 - idx) * TR; };
-  // one tile computed from buffer cur while the next streams into nxt
+  // one tile computed from buffer cur while the two after it stream in; nxt
+  // (the buffer of tile idx - 1) receives tile idx + 2
   auto tile_step = [&](int idx, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
     const int t0 = tile_t0(idx);
     const int nrows = min(TR, r_end - t0);
     const uint16_t* KL = cur;
     const uint16_t* VL = cur + TR * RS;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's blocks of the tile are in LDS
-    __syncthreads();  // ... and every wave's; the other buffer's reads (tile idx-1) are done
-    if (idx + 1 < ntiles) issue_tile(tile_t0(idx + 1), nxt);  // streams in during this tile
+    // this wave's blocks of tile idx are in LDS (tile idx + 1 may still stream)
+    if (idx + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(kWaitButOne);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __syncthreads();  // ... and every wave's; the reads of tile idx - 1 are done
+    if (idx + 2 < ntiles) issue_tile(tile_t0(idx + 2), nxt);  // streams in during this tile
 
     // S^T for the wave's 32 rows
     f32x16 s = f32x16{};
@@ -272,9 +282,11 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
       }
   };
   if (ntiles > 0) issue_tile(tile_t0(0), buf0);
-  for (int idx = 0; idx < ntiles; idx += 2) {  // even tiles in buffer 0, odd in buffer 1
-    tile_step(idx, buf0, buf1);
+  if (ntiles > 1) issue_tile(tile_t0(1), buf1);
+  for (int idx = 0; idx < ntiles; idx += 3) {  // tile i in buffer i mod 3
+    tile_step(idx, buf0, buf2);
     if (idx + 1 < ntiles) tile_step(idx + 1, buf1, buf0);
+    if (idx + 2 < ntiles) tile_step(idx + 2, buf2, buf1);
   }
 
   // merge the two row halves of each slot group: half 1 leaves (m_true,
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
     lt = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
   }
   __syncthreads();  // the last tile's LDS reads are done
-  float* mg = reinterpret_cast<float*>(sg == 0 ? buf0 : sg == 1 ? buf1 : sg == 2 ? UL : spare);  // [64 lanes][m_true, m_run, l, 128 n]
+  float* mg = reinterpret_cast<float*>(sg == 0 ? buf0 : sg == 1 ? buf1 : sg == 2 ? buf2 : UL);  // [64 lanes][m_true, m_run, l, 128 n]
   if (half == 1) {
     float* dst = mg + lane * 131;
     dst[0] = m_true;

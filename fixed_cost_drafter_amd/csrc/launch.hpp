@@ -20,8 +20,10 @@ ls_status launch_verify_into(const ls_dims& d, const void* logits, const int32_t
                              int32_t* target_tok, int32_t* tau, uint64_t* keys,
                              hipStream_t stream);
 
-// the verification's partial argmax keys only (into the workspace's key area)
-ls_status launch_verify_keys(const ls_dims& d, const void* logits, char* ws, hipStream_t stream);
+// the verification's partial argmax keys only (into the workspace's key area);
+// the same launch copies seq_len into len_snap when len_snap is not null
+ls_status launch_verify_keys(const ls_dims& d, const void* logits, char* ws,
+                             const int32_t* seq_len, int32_t* len_snap, hipStream_t stream);
 
 // greedy verification, then the append of the accepted rows (tau derived by
 // the append from the partial keys in st.workspace)
