@@ -80,10 +80,12 @@ struct Half {
   int pos;  // key halves: ring_pos of key (lane & 31); 0 for the slots
 };
 
-// kt: the chunk's key tile (operand order); pp: 32 ints to read the
-// positions from (the chunk's ring_pos, or any readable 128 bytes for the
-// slots, whose positions are then taken as 0 = occupied).  The position
-// loads first, so the occupancy mask never waits for the operands behind it.
+// The positions read for a slot chunk: slots are always occupied.
+__device__ const int32_t kSlotPos[32] = {};
+
+// kt: the chunk's key tile (operand order); pp: the chunk's 32 positions
+// (its ring_pos, or kSlotPos for the slots).  The position loads first, so
+// the occupancy mask never waits for the operands behind it.
 // No branch around any load: the compiler can then count the loads in
 // flight exactly and wait only for the ones a step needs.
 __device__ __forceinline__ void load_keys(Half& x, const uint16_t* kt, const int32_t* pp, bool ring,
@@ -233,7 +235,6 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
   const uint16_t* sk = slot_k + int64_t(unit) * S * D;
   const uint16_t* sv = slot_v + int64_t(unit) * D * S;
   const int32_t* rp = ring_pos + int64_t(c) * W;
-  const int32_t* any_ints = reinterpret_cast<const int32_t*>(q);  // >= 256 readable bytes
 
   // this wave's window / slot chunks: pidx, pidx + nparts, ...
   const int nmine = ngl > pidx ? (ngl - pidx + nparts - 1) / nparts : 0;
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     const int ch = pidx + j * nparts;
     const bool ring = ch < nring;
     load_keys(x, ring ? rk + int64_t(ch) * 32 * D : sk + int64_t(ch - nring) * 32 * D,
-              ring ? rp + ch * 32 : any_ints, ring, lane);
+              ring ? rp + ch * 32 : kSlotPos, ring, lane);
   };
   auto values_of = [&](Half& x, int j) {
     const int ch = pidx + j * nparts;

@@ -242,3 +242,32 @@ def test_prefix_stride_and_sub_prefix():
                          wl.W)
     H.compare_state(a, ost, wl.dtype)
     del LB
+
+
+@pytest.mark.parametrize("S", [64, 128])
+def test_init_with_large_scores_in_old_rows(S):
+    """An old prefix row whose key is 12 times a slow-decay slot's query scores
+    about 12 ||u||^2 / sqrt(d) ~ 135 for that slot, far above the rows of its
+    split's first (newest) tile, so the init kernel's reference max has to move
+    by ~190 (base 2) late in the split: the lazy rescale of the accumulators.
+    At L0 = 40000 each split holds 5 tiles (320 rows) and the planted rows lie
+    in later tiles of their splits.  The state must match the oracle (which
+    sees the same inputs) like any other init; the slots that the planted rows
+    dominate hold values up to ~48, so the bf16 outputs are held to 2e-2
+    relative to their size (bf16 keeps 2^-9 of it)."""
+    import torch
+    from fixed_cost_drafter_amd.runner import PathRunner
+    wl = WLM.Workload(f"bf16_big_old_score_s{S}", "bf16", C=2, Hq=8, Hkv=2, d=128, L0=40000,
+                      W=64, S=S, B=4, V=1000, rounds=1, p_match=0.8, seed=22)
+    _announce(wl, "planted large scores in old rows")
+    Kp, Vp = WLM.prefix(wl, threads=4)
+    u = WLM.slot_queries(wl)
+    uf = WLM.bf16_bits_to_f32(u)
+    # slots 14 and 15 decay by 1 - 2^-14 and 1 - 2^-15 per row: an old row still counts
+    for c, h, row, j in ((0, 1, 7, 14), (1, 0, 2100, 15)):
+        Kp[c, row, h] = WLM.f32_to_bf16_bits(12.0 * uf[h, j])
+    rn = PathRunner(wl, Kp, Vp)
+    rn.init()
+    torch.cuda.synchronize()
+    ost = O.summary_init(u, WLM.log_lambda(wl), Kp, Vp, wl.W)
+    H.compare_state(rn, ost, wl.dtype, scaled=True)
