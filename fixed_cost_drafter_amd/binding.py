@@ -27,8 +27,8 @@ STATUS = {0: "LS_OK", 1: "LS_ERR_NULL", 2: "LS_ERR_SHAPE", 3: "LS_ERR_DTYPE",
           4: "LS_ERR_WORKSPACE", 5: "LS_ERR_ALIGN", 6: "LS_ERR_HIP", 7: "LS_ERR_SCRATCH"}
 EXPORTS = ("ls_workspace_bytes", "ls_summary_init", "ls_verify_greedy", "ls_append_accepted",
            "ls_draft_attention", "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention",
-           "ls_verify_sampling", "ls_verify_append", "ls_verify_greedy_noalloc", "ls_status_string",
-           "ls_version")
+           "ls_verify_sampling", "ls_verify_append", "ls_verify_append_draft",
+           "ls_verify_greedy_noalloc", "ls_status_string", "ls_version")
 
 
 class LsDims(ctypes.Structure):
@@ -71,9 +71,10 @@ def _load() -> ctypes.CDLL:
     lib.ls_verify_sampling.argtypes = [D, P, P, P, ctypes.c_float, P, P, P, P, P, SZ, P]
     lib.ls_verify_append.argtypes = [D, S, P, P, P, P, P, P, P]
     lib.ls_verify_greedy_noalloc.argtypes = [D, P, P, P, P, P]
+    lib.ls_verify_append_draft.argtypes = [D, S, P, P, P, P, P, P, P, P, P, P, P]
     for f in ("ls_summary_init", "ls_verify_greedy", "ls_append_accepted", "ls_draft_attention",
               "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention", "ls_verify_sampling",
-              "ls_verify_append", "ls_verify_greedy_noalloc"):
+              "ls_verify_append", "ls_verify_greedy_noalloc", "ls_verify_append_draft"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ls_status_string.argtypes = [ctypes.c_int]
     lib.ls_status_string.restype = ctypes.c_char_p
@@ -263,6 +264,14 @@ def ls_verify_append(dims: LsDims, state: LsState, logits, draft, target_tok, ta
         _ptr(tau), _ptr(k_new), _ptr(v_new), _stream(stream)))
 
 
+def ls_verify_append_draft(dims: LsDims, state: LsState, logits, draft, target_tok, tau, k_new,
+                           v_new, q, k_blk, v_blk, out, stream=None):
+    _check("ls_verify_append_draft", _lib.ls_verify_append_draft(
+        ctypes.byref(dims), ctypes.byref(state), _ptr(logits), _ptr(draft), _ptr(target_tok),
+        _ptr(tau), _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(out),
+        _stream(stream)))
+
+
 def ls_draft_attention(dims: LsDims, state: LsState, q, k_blk, v_blk, out, stream=None):
     _check("ls_draft_attention", _lib.ls_draft_attention(
         ctypes.byref(dims), ctypes.byref(state), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(out),
@@ -372,11 +381,22 @@ class DrafterState:
     def draft_attention(self, q, k_blk, v_blk, out, stream=None):
         ls_draft_attention(self.dims, self.c_state, q, k_blk, v_blk, out, stream)
 
+    def verify_append_draft(self, logits, draft, target_tok, tau, k_new, v_new, q, k_blk, v_blk, out,
+                            stream=None):
+        ls_verify_append_draft(self.dims, self.c_state, logits, draft, target_tok, tau, k_new, v_new,
+                               q, k_blk, v_blk, out, stream)
+
     # the round's two calls with their arguments fixed (see BoundCall)
     def bind_verify_append(self, logits, draft, target_tok, tau, k_new, v_new, stream=None):
         return BoundCall("ls_verify_append", ctypes.byref(self.dims), ctypes.byref(self.c_state),
                          _ptr(logits), _ptr(draft), _ptr(target_tok), _ptr(tau), _ptr(k_new),
                          _ptr(v_new), _stream(stream))
+
+    def bind_verify_append_draft(self, logits, draft, target_tok, tau, k_new, v_new, q, k_blk, v_blk,
+                                 out, stream=None):
+        return BoundCall("ls_verify_append_draft", ctypes.byref(self.dims), ctypes.byref(self.c_state),
+                         _ptr(logits), _ptr(draft), _ptr(target_tok), _ptr(tau), _ptr(k_new),
+                         _ptr(v_new), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(out), _stream(stream))
 
     def bind_draft_attention(self, q, k_blk, v_blk, out, stream=None):
         return BoundCall("ls_draft_attention", ctypes.byref(self.dims), ctypes.byref(self.c_state),

@@ -40,6 +40,7 @@
 #include "accept.hpp"
 #include "common.hpp"
 #include "launch.hpp"
+#include "merge_ops.hpp"
 
 namespace ls {
 namespace {
@@ -466,14 +467,6 @@ __global__ __launch_bounds__(block_threads<D>()) void append_kernel(
 // (len_snap), so no workgroup here reads seq_len; the lead workgroup of the
 // sequence (KV head 0, first tile group) writes ring_pos and seq_len = L + tau.
 // ---------------------------------------------------------------------------
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// A-row m of a 32-row score block holds verified row tile_row(m) (bits 2 and
-// 3 of m swapped): the S^T output then gives lanes 0-31 rows 0-7 and 16-23 of
-// the block, lanes 32-63 rows 8-15 and 24-31, which are the 8 consecutive
-// rows each lane feeds the N^T product as its B operand.
-__device__ __forceinline__ int tile_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
-
 // kVerify: tau is not an input but the accepted prefix of the greedy
 // verification whose partial argmax keys are vkeys (nkeys per row): every
 // workgroup derives it for its sequence, and the lead workgroup also writes
@@ -628,143 +621,27 @@ __global__ __launch_bounds__(256 * kTPW) void append_units(
   if (lead && tid == 0) seq_len[c] = L + Tn;
   if (!summ) return;
 
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  float l_new;
-  {
-    // S^T = K U^T; element 8 (s % 2) + e of block s / 2 is verified row 16 s + 8 hi + e
-    f32x16 sc[kRB];
+  // the merge of the wave's two accumulator tiles (merge_ops.hpp)
+  float m_new;
+  const float l_new = merge_wave<kRB, 2>(KL, RT, UL + 32 * tl * KLS, acc, m_old, l_old, lnl, Tn, q4,
+                                         lane, m_new);
+  // non-temporal stores: the state is next read a round later, and the
+  // round's other streams leave nothing of it in L2 by then
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      sc[rb] = f32x16{};
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[(32 * rb + tile_row(ln)) * KLS + 16 * ks + 8 * hi]));
-        const bf16x8 b = as_bf16x8(*reinterpret_cast<const u16x8*>(&UL[(32 * tl + ln) * KLS + 16 * ks + 8 * hi]));
-        sc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, sc[rb], 0, 0, 0);
-      }
-    }
-
-    // softmax of slot j over the new rows in base 2, K-step by K-step (rows
-    // 16 s .. 16 s + 15; steps past tau are skipped); the partner lane
-    // (lane ^ 32) holds the other 8 rows of each step.  x_ji = a_ji log2(e);
-    // a zero decay (ln(lambda) = -inf) enters the bias as -1e30, so every
-    // older row's exponent is hugely negative and 0 * bias never occurs.
-    constexpr float kLog2e = 1.4426950408889634f;
-    const int nks = (Tn + 15) >> 4;
-    const float sc2 = kLog2e / sqrtf(float(D));
-    const float lb2 = fmaxf(lnl, -1e30f) * kLog2e;
-    const float base2 = lnl == -INFINITY ? -INFINITY : fmaf(float(Tn), lnl, m_old) * kLog2e;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int s = 0; s < 2 * kRB; ++s)
-      if (s < nks) {
-        const int rem = Tn - 16 * s - 8 * hi;         // rows e < rem are new rows
-        const float d0 = float(rem - 1);              // distance of e = 0 to row tau-1
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // the distance enters as an exact small integer: row tau-1 gets bias 0 exactly
-          const float x = fmaf(d0 - float(e), lb2, sc[s >> 1][8 * (s & 1) + e] * sc2);
-          sc[s >> 1][8 * (s & 1) + e] = e < rem ? x : -INFINITY;
-          mx = fmaxf(mx, sc[s >> 1][8 * (s & 1) + e]);
-        }
-      }
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    // row tau-1 always counts and has a finite exponent, so m2 is finite and
-    // 2^(-inf - m2) = 0 needs no test
-    const float m2 = fmaxf(base2, mx);
-    const float s_old = __builtin_amdgcn_exp2f(base2 - m2);
-    float lsum = 0.f;
-#pragma unroll
-    for (int s = 0; s < 2 * kRB; ++s)
-      if (s < nks) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float w = __builtin_amdgcn_exp2f(sc[s >> 1][8 * (s & 1) + e] - m2);
-          sc[s >> 1][8 * (s & 1) + e] = w;
-          lsum += w;
-        }
-      }
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
-      lsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    l_new = fmaf(l_old, s_old, lsum);
-    const float m_new = m2 * 0.6931471805599453f;  // back to natural-log units
-
-    // N^T = s N^T + R^T W^T over the K-steps that hold new rows; the weights
-    // as bf16 pairs hi = rne(w), lo = rne(w - hi)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) acc[t] *= s_old;
-#pragma unroll
-    for (int s = 0; s < 2 * kRB; ++s) {
-      if (s < nks) {
-        uint32_t whi[4], wlo[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const f32x2 w2 = {sc[s >> 1][8 * (s & 1) + e], sc[s >> 1][8 * (s & 1) + e + 1]};
-          const bf16x2 h2 = __builtin_convertvector(w2, bf16x2);
-          const f32x2 r2 = w2 - __builtin_convertvector(h2, f32x2);
-          whi[e / 2] = __builtin_bit_cast(uint32_t, h2);
-          wlo[e / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2));
-        }
-        const bf16x8 bhi = __builtin_bit_cast(bf16x8, uint4{whi[0], whi[1], whi[2], whi[3]});
-        const bf16x8 blo = __builtin_bit_cast(bf16x8, uint4{wlo[0], wlo[1], wlo[2], wlo[3]});
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(&RT[((2 * q4 + t) * 32 + ln) * RTS + 16 * s + 8 * hi]));
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bhi, acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, blo, acc[t], 0, 0, 0);
-        }
-      }
-    }
-
-    // non-temporal stores: the state is next read a round later, and the
-    // round's other streams leave nothing of it in L2 by then
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        __builtin_nontemporal_store(f32x4{acc[t][4 * k], acc[t][4 * k + 1], acc[t][4 * k + 2], acc[t][4 * k + 3]},
-                                    reinterpret_cast<f32x4*>(nt + (t * 4 + k) * 64 * 4));
-    if (q4 == 0 && hi == 0) {
-      sum_m[sidx] = m_new;
-      sum_l[sidx] = l_new;
-    }
+    for (int k = 0; k < 4; ++k)
+      __builtin_nontemporal_store(f32x4{acc[t][4 * k], acc[t][4 * k + 1], acc[t][4 * k + 2], acc[t][4 * k + 3]},
+                                  reinterpret_cast<f32x4*>(nt + (t * 4 + k) * 64 * 4));
+  if (q4 == 0 && hi == 0) {
+    sum_m[sidx] = m_new;
+    sum_l[sidx] = l_new;
   }
 
   // pooled slots n / l -> the tile's key tile (operand order) and value tile
-  // [d][32] in LDS, then 16-byte stores of the group's tiles.  A lane's 4
-  // consecutive entries are 4 consecutive dimensions of its slot: one 8-byte
-  // write in the key tile, 4 rows of the value tile.
-  const float il = 1.0f / l_new;
+  // [d][32] in LDS, then 16-byte stores of the group's tiles
   __syncthreads();  // every wave is done with the staged rows
-  {
-    uint16_t* kt = lds + tl * 2 * 32 * D;
-    uint16_t* vt = kt + 32 * D;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int ent = (2 * q4 + t) * 32 + 8 * k + 4 * hi;  // first of the 4 entries
-        const bf16x2 p0 = __builtin_convertvector((f32x2{acc[t][4 * k], acc[t][4 * k + 1]} * il), bf16x2);
-        const bf16x2 p1 = __builtin_convertvector((f32x2{acc[t][4 * k + 2], acc[t][4 * k + 3]} * il), bf16x2);
-        if (q4 < 2) {  // key entries (uniform in the wave)
-          *reinterpret_cast<uint2*>(&kt[key_index(0, 32, D, ln, ent)]) =
-              uint2{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1)};
-        } else {
-          const uint32_t w0 = __builtin_bit_cast(uint32_t, p0), w1 = __builtin_bit_cast(uint32_t, p1);
-          uint16_t* v = vt + (ent - D) * 32 + ln;
-          v[0] = uint16_t(w0);
-          v[32] = uint16_t(w0 >> 16);
-          v[64] = uint16_t(w1);
-          v[96] = uint16_t(w1 >> 16);
-        }
-      }
-  }
+  pooled_to_lds<2>(acc, 1.0f / l_new, q4, lane, lds + tl * 2 * 32 * D, lds + tl * 2 * 32 * D + 32 * D);
   __syncthreads();
   constexpr int P16 = 32 * D * 2 / 16;  // 16-byte pieces per key (or value) tile
   const uint4* src = reinterpret_cast<const uint4*>(lds);

@@ -143,6 +143,9 @@ constexpr int kInitRowTile = 64;       // rows per init tile (MFMA path)
 inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// arrival counters per sequence: one per (KV head, 32-slot tile)
+inline int arrivals_per_seq(const ls_dims& d) { return d.Hkv * int(cdiv(d.S < 1 ? 1 : d.S, 32)); }
+
 struct WsLayout {
   int64_t draft_part;                         // float [C*Hkv*halves * Mpad*(d+2)]
   int64_t verify_part;                        // uint64 keys [C*(B+1)*vsplit]
@@ -152,6 +155,7 @@ struct WsLayout {
   int64_t samp_seq;                           // per-sequence decision record [C*8] (4-byte words)
   int64_t samp_sums;                          // float [C*vsplit] chunk sums of the drawn row
   int64_t len_snap;                           // int32 [C] lengths before an update
+  int64_t arrivals;                           // int32 [C*Hkv*tiles] waves of a (unit, slot tile) past their state reads
   int64_t total;
   int vsplit, isplit, init_rows, asplit;
 };
@@ -227,6 +231,7 @@ inline WsLayout ws_layout(const ls_dims& d, int32_t max_L0) {
   w.samp_seq = off; off = align256(off + 32 * int64_t(d.C));
   w.samp_sums = off; off = align256(off + 4 * int64_t(d.C) * w.vsplit);
   w.len_snap = off; off = align256(off + 4 * int64_t(d.C));
+  w.arrivals = off; off = align256(off + 4 * int64_t(d.C) * arrivals_per_seq(d));
   w.total = off;
   return w;
 }

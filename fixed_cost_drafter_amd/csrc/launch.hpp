@@ -21,9 +21,12 @@ ls_status launch_verify_into(const ls_dims& d, const void* logits, const int32_t
                              hipStream_t stream);
 
 // the verification's partial argmax keys only (into the workspace's key area);
-// the same launch copies seq_len into len_snap when len_snap is not null
+// the same launch copies seq_len into len_snap when len_snap is not null, and
+// then zeroes the arrival counters (arrivals_per_seq per sequence) when
+// arrivals is not null
 ls_status launch_verify_keys(const ls_dims& d, const void* logits, char* ws,
-                             const int32_t* seq_len, int32_t* len_snap, hipStream_t stream);
+                             const int32_t* seq_len, int32_t* len_snap, hipStream_t stream,
+                             int32_t* arrivals = nullptr);
 
 // greedy verification, then the append of the accepted rows (tau derived by
 // the append from the partial keys in st.workspace)
@@ -60,5 +63,14 @@ ls_status launch_init(const ls_dims& d, const ls_state& st, const void* k_prefix
 
 ls_status launch_draft(const ls_dims& d, const ls_state& st, const void* q, const void* k_blk,
                        const void* v_blk, void* out, hipStream_t stream);
+
+// a whole round: verification, update, draft attention (update and draft in
+// one launch where round_fusable, else the separate entry points' launches)
+bool round_fusable(const ls_dims& d);
+ls_status launch_verify_append_draft(const ls_dims& d, const ls_state& st, const void* logits,
+                                     const int32_t* draft, int32_t* target_tok, int32_t* tau,
+                                     const void* k_new, const void* v_new, const void* q,
+                                     const void* k_blk, const void* v_blk, void* out,
+                                     hipStream_t stream);
 
 }  // namespace ls

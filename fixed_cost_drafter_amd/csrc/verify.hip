@@ -154,18 +154,23 @@ __device__ __forceinline__ uint64_t chunk_argmax_bf16(const uint16_t* __restrict
 
 // len_snap (may be null): the first chunk of each sequence's first row also
 // copies seq_len[c] to len_snap[c] (rows_per_seq rows per sequence), the
-// length before the update that the next launch makes
+// length before the update that the next launch makes, and clears the
+// sequence's n_arr arrival counters when `arrivals` is not null
 template <typename Ty>
 __global__ __launch_bounds__(kThreads) void verify_partial(
     const typename Ty::T* __restrict__ logits, uint64_t* __restrict__ part, int V, int nsplit,
     int chunk, int vec_ok, const int32_t* __restrict__ seq_len, int32_t* __restrict__ len_snap,
-    int rows_per_seq) {
+    int rows_per_seq, int32_t* __restrict__ arrivals, int n_arr) {
   using VT = Vec16<Ty>;
   const int split = blockIdx.x;
   const int row = blockIdx.y;  // c * (B+1) + i
   const int tid = threadIdx.x;
-  if (len_snap != nullptr && split == 0 && tid == 0 && row % rows_per_seq == 0)
-    len_snap[row / rows_per_seq] = seq_len[row / rows_per_seq];
+  if (len_snap != nullptr && split == 0 && row % rows_per_seq == 0) {
+    const int c = row / rows_per_seq;
+    if (tid == 0) len_snap[c] = seq_len[c];
+    if (arrivals != nullptr)
+      for (int i = tid; i < n_arr; i += kThreads) arrivals[int64_t(c) * n_arr + i] = 0;
+  }
   const typename Ty::T* x = logits + int64_t(row) * V;
   const int begin = split * chunk;
   const int end = min(V, begin + chunk);
@@ -270,13 +275,13 @@ __global__ __launch_bounds__(kThreads) void argmax_finalize(const uint64_t* __re
 template <typename Ty>
 ls_status launch_partials(const ls_dims& d, const void* logits, int rows, uint64_t* part,
                           int nsplit, hipStream_t stream, const int32_t* seq_len = nullptr,
-                          int32_t* len_snap = nullptr) {
+                          int32_t* len_snap = nullptr, int32_t* arrivals = nullptr) {
   const int esz = Ty::kBytes;
   // 16-byte loads need every row start (and chunk start) 16-byte aligned
   const int vec_ok = ((int64_t(d.V) * esz) % 16 == 0) && ((uintptr_t(logits) & 15) == 0);
   hipLaunchKernelGGL(verify_partial<Ty>, dim3(nsplit, rows), dim3(kThreads), 0, stream,
                      static_cast<const typename Ty::T*>(logits), part, d.V, nsplit, kVerifyChunk,
-                     vec_ok, seq_len, len_snap, d.B + 1);
+                     vec_ok, seq_len, len_snap, d.B + 1, arrivals, arrivals_per_seq(d));
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
 }
 
@@ -298,13 +303,14 @@ ls_status launch_argmax(const ls_dims& d, const void* logits, int32_t* draft_tok
 }
 
 ls_status launch_verify_keys(const ls_dims& d, const void* logits, char* ws,
-                             const int32_t* seq_len, int32_t* len_snap, hipStream_t stream) {
+                             const int32_t* seq_len, int32_t* len_snap, hipStream_t stream,
+                             int32_t* arrivals) {
   const WsLayout lay = ws_layout(d, 1);
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + lay.verify_part);
   const int rows = d.C * (d.B + 1);
   return d.dtype == LS_BF16
-             ? launch_partials<BF16>(d, logits, rows, part, lay.vsplit, stream, seq_len, len_snap)
-             : launch_partials<F32>(d, logits, rows, part, lay.vsplit, stream, seq_len, len_snap);
+             ? launch_partials<BF16>(d, logits, rows, part, lay.vsplit, stream, seq_len, len_snap, arrivals)
+             : launch_partials<F32>(d, logits, rows, part, lay.vsplit, stream, seq_len, len_snap, arrivals);
 }
 
 ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* draft,

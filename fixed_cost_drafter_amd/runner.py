@@ -51,24 +51,26 @@ class PathRunner:
         self.state.summary_init(self.k_prefix, self.v_prefix, L0 or rows, rows, stream)
 
     def round(self, logits: torch.Tensor, dev: dict, stream=None):
-        """One drafting round: verification and update in one call (the update
-        derives tau from the verification's keys), then the draft attention."""
+        """One drafting round in one call (ls_verify_append_draft): verification,
+        update and draft attention, the update and the draft in one launch."""
+        s, b = self.state, self.buf
+        s.verify_append_draft(logits, dev["draft"], b.target_tok, b.tau, dev["k_new"], dev["v_new"],
+                              dev["q"], dev["k_blk"], dev["v_blk"], b.out, stream)
+
+    def round_two_calls(self, logits: torch.Tensor, dev: dict, stream=None):
+        """The same round as verification + update in one call (the update derives
+        tau from the verification's keys), then the draft attention."""
         s, b = self.state, self.buf
         s.verify_append(logits, dev["draft"], b.target_tok, b.tau, dev["k_new"], dev["v_new"], stream)
         s.draft_attention(dev["q"], dev["k_blk"], dev["v_blk"], b.out, stream)
 
     def bind_round(self, logits: torch.Tensor, dev: dict, stream=None):
-        """The calls of round() with their arguments marshalled once; calling the
-        result issues the round.  The tensors must stay alive while it is used."""
+        """round() with its arguments marshalled once; calling the result issues
+        the round.  The tensors must stay alive while it is used."""
         s, b = self.state, self.buf
-        va = s.bind_verify_append(logits, dev["draft"], b.target_tok, b.tau, dev["k_new"],
-                                  dev["v_new"], stream)
-        da = s.bind_draft_attention(dev["q"], dev["k_blk"], dev["v_blk"], b.out, stream)
-
-        def issue():
-            va()
-            da()
-        return issue
+        return s.bind_verify_append_draft(logits, dev["draft"], b.target_tok, b.tau, dev["k_new"],
+                                          dev["v_new"], dev["q"], dev["k_blk"], dev["v_blk"], b.out,
+                                          stream)
 
     def round_separate(self, logits: torch.Tensor, dev: dict, stream=None):
         """The same round through the three separate entry points."""

@@ -192,6 +192,30 @@ ls_status ls_verify_append(const ls_dims* dims, const ls_state* state, const voi
 ls_status ls_verify_greedy_noalloc(const ls_dims* dims, const void* logits, const int32_t* draft,
                                    int32_t* target_tok, int32_t* tau, ls_stream stream);
 
+/* One whole drafting round (Fig. 2: (a) the target verifies the drafted
+ * block, (b) the accepted rows extend the views, (c) the drafter attends
+ * over the views): ls_verify_append followed by ls_draft_attention, in two
+ * launches instead of three.  The update and the draft attention share one
+ * launch; the draft sees the window as updated (the tau new rows in place of
+ * the ones they replace) and the merged slots.
+ *   logits, draft, target_tok, tau, k_new, v_new: as in ls_verify_append.
+ *   q, k_blk, v_blk, out: as in ls_draft_attention (the next block's
+ *       queries and block rows; out is the attention output).
+ * The state, target_tok and tau are bit for bit those of the two calls; out
+ * equals theirs up to the order in which the softmax visits the keys (the
+ * new window rows and the slots are attended as chunks of their own, and
+ * the probabilities enter P.V rounded to bf16 against the running maximum).
+ * The state's workspace also holds per-(sequence, KV head, 32-slot tile)
+ * arrival counters that the launch zeroes and uses (no carry-over between
+ * calls).  Shapes other than bf16, d = 128, S in {64, 128}, B + 1 <= 32,
+ * W a positive multiple of 32 and at most 64 query rows B*Hq/Hkv per KV
+ * head run the two calls' launches. */
+ls_status ls_verify_append_draft(const ls_dims* dims, const ls_state* state, const void* logits,
+                                 const int32_t* draft, int32_t* target_tok, int32_t* tau,
+                                 const void* k_new, const void* v_new, const void* q,
+                                 const void* k_blk, const void* v_blk, void* out,
+                                 ls_stream stream);
+
 /* Drafter block attention (Fig. 2 (c)).
  *   q:            [C, B, Hq, d] dtype, block queries.
  *   k_blk, v_blk: [C, B, Hkv, d] dtype, block keys/values.

@@ -108,16 +108,18 @@ def compare_state(runner, ost: O.OracleState, dtype, heads=None, scaled=False):
 
 def lockstep(wl: WLM.Workload, rounds: int, k_prefix=None, v_prefix=None, heads=None,
              check_state_every=1, runner=None, tau_override=None, device="cuda", fused=False,
-             logits_fn=None, draft_fn=None):
+             logits_fn=None, draft_fn=None, calls=None):
     """Run ``rounds`` rounds on both sides and compare after each.
 
     ``heads`` samples (c, h) pairs for the float checks of large workloads
     (the oracle's summary and attention are computed only there).
     ``tau_override`` (round -> tau array) replaces the verified tau on both
     sides before the append (device-side clamping and the error flag).
-    ``fused`` runs each round as the bench does (runner.round:
-    ls_verify_append, then ls_draft_attention) instead of the three separate
-    entry points; target_tok and tau are then checked after the round.
+    ``calls`` picks the entry points of a round: "separate" (default:
+    ls_verify_greedy, ls_append_accepted, ls_draft_attention), "two"
+    (ls_verify_append, then ls_draft_attention) or "round" (the bench's call,
+    ls_verify_append_draft); ``fused=True`` means "round".  For "two" and
+    "round" target_tok and tau are checked after the round.
     ``logits_fn(r)`` -> (logits, planted or None) replaces the pooled logits;
     ``draft_fn(r, target)`` -> draft [C, B] replaces the round's drafts, built
     from the oracle's target tokens ``target`` (never from GPU output).
@@ -127,7 +129,9 @@ def lockstep(wl: WLM.Workload, rounds: int, k_prefix=None, v_prefix=None, heads=
     from fixed_cost_drafter_amd import binding as LB
     from fixed_cost_drafter_amd.runner import PathRunner, upload_round
 
-    assert not (fused and tau_override), "the fused call derives tau itself"
+    calls = calls or ("round" if fused else "separate")
+    fused = calls != "separate"
+    assert not (fused and tau_override), "the fused calls derive tau themselves"
     t0 = time.time()
     if k_prefix is None:
         k_prefix, v_prefix = WLM.prefix(wl, threads=16)
@@ -172,8 +176,10 @@ def lockstep(wl: WLM.Workload, rounds: int, k_prefix=None, v_prefix=None, heads=
         b = runner.buf
         s = runner.state
         tau_use = tau_ref
-        if fused:
+        if calls == "round":
             runner.round(logits_dev, dev)
+        elif calls == "two":
+            runner.round_two_calls(logits_dev, dev)
         else:
             s.verify_greedy(logits_dev, dev["draft"], b.target_tok, b.tau)
             torch.cuda.synchronize()

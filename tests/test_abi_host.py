@@ -67,7 +67,7 @@ def test_header_compiles_as_plain_c(tmp_path):
 
 
 def test_version_and_status_strings(LB):
-    assert LB.ls_version() == 105
+    assert LB.ls_version() == 106
     assert LB.ls_status_string(0) == "ok"
     for s in range(1, 8):
         assert LB.ls_status_string(s) and LB.ls_status_string(s) != "unknown status"

@@ -79,6 +79,18 @@ def test_parity_small(name):
     assert taus.min() >= 1 and taus.max() <= wl.B + 1
 
 
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small_round(name):
+    """The same cases through the bench's one-call round (ls_verify_append_draft):
+    the fused update + draft kernel where the shape allows it (bf16, S in
+    {64, 128}, B + 1 <= 32: window wrap, short prefix with empty slots, one-row
+    prefix, key parts without window chunks), the two calls' launches
+    otherwise."""
+    wl = SMALL[name]
+    _announce(wl, f"rounds={wl.rounds} one-call round")
+    H.lockstep(wl, wl.rounds, calls="round")
+
+
 def test_parity_q3_4b_8k_all_heads():
     wl = WLM.WORKLOADS["q3_4b_8k"]
     _announce(wl, "rounds=64 (state checked every 8)")
