@@ -28,7 +28,8 @@ STATUS = {0: "LS_OK", 1: "LS_ERR_NULL", 2: "LS_ERR_SHAPE", 3: "LS_ERR_DTYPE",
 EXPORTS = ("ls_workspace_bytes", "ls_summary_init", "ls_verify_greedy", "ls_append_accepted",
            "ls_draft_attention", "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention",
            "ls_verify_sampling", "ls_verify_append", "ls_verify_append_draft",
-           "ls_verify_greedy_noalloc", "ls_status_string", "ls_version")
+           "ls_verify_keys", "ls_update_draft", "ls_verify_greedy_noalloc", "ls_status_string",
+           "ls_version")
 
 
 class LsDims(ctypes.Structure):
@@ -72,9 +73,12 @@ def _load() -> ctypes.CDLL:
     lib.ls_verify_append.argtypes = [D, S, P, P, P, P, P, P, P]
     lib.ls_verify_greedy_noalloc.argtypes = [D, P, P, P, P, P]
     lib.ls_verify_append_draft.argtypes = [D, S, P, P, P, P, P, P, P, P, P, P, P]
+    lib.ls_verify_keys.argtypes = [D, S, P, P]
+    lib.ls_update_draft.argtypes = [D, S, P, P, P, P, P, P, P, P, P, P]
     for f in ("ls_summary_init", "ls_verify_greedy", "ls_append_accepted", "ls_draft_attention",
               "ls_draft_argmax", "ls_gather_boundary", "ls_verify_attention", "ls_verify_sampling",
-              "ls_verify_append", "ls_verify_greedy_noalloc", "ls_verify_append_draft"):
+              "ls_verify_append", "ls_verify_greedy_noalloc", "ls_verify_append_draft",
+              "ls_verify_keys", "ls_update_draft"):
         getattr(lib, f).restype = ctypes.c_int
     lib.ls_status_string.argtypes = [ctypes.c_int]
     lib.ls_status_string.restype = ctypes.c_char_p
@@ -272,6 +276,18 @@ def ls_verify_append_draft(dims: LsDims, state: LsState, logits, draft, target_t
         _stream(stream)))
 
 
+def ls_verify_keys(dims: LsDims, state: LsState, logits, stream=None):
+    _check("ls_verify_keys", _lib.ls_verify_keys(
+        ctypes.byref(dims), ctypes.byref(state), _ptr(logits), _stream(stream)))
+
+
+def ls_update_draft(dims: LsDims, state: LsState, draft, target_tok, tau, k_new, v_new, q, k_blk,
+                    v_blk, out, stream=None):
+    _check("ls_update_draft", _lib.ls_update_draft(
+        ctypes.byref(dims), ctypes.byref(state), _ptr(draft), _ptr(target_tok), _ptr(tau),
+        _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(out), _stream(stream)))
+
+
 def ls_draft_attention(dims: LsDims, state: LsState, q, k_blk, v_blk, out, stream=None):
     _check("ls_draft_attention", _lib.ls_draft_attention(
         ctypes.byref(dims), ctypes.byref(state), _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(out),
@@ -386,7 +402,24 @@ class DrafterState:
         ls_verify_append_draft(self.dims, self.c_state, logits, draft, target_tok, tau, k_new, v_new,
                                q, k_blk, v_blk, out, stream)
 
-    # the round's two calls with their arguments fixed (see BoundCall)
+    def verify_keys(self, logits, stream=None):
+        ls_verify_keys(self.dims, self.c_state, logits, stream)
+
+    def update_draft(self, draft, target_tok, tau, k_new, v_new, q, k_blk, v_blk, out, stream=None):
+        ls_update_draft(self.dims, self.c_state, draft, target_tok, tau, k_new, v_new, q, k_blk, v_blk,
+                        out, stream)
+
+    # the round's calls with their arguments fixed (see BoundCall)
+    def bind_verify_keys(self, logits, stream=None):
+        return BoundCall("ls_verify_keys", ctypes.byref(self.dims), ctypes.byref(self.c_state),
+                         _ptr(logits), _stream(stream))
+
+    def bind_update_draft(self, draft, target_tok, tau, k_new, v_new, q, k_blk, v_blk, out,
+                          stream=None):
+        return BoundCall("ls_update_draft", ctypes.byref(self.dims), ctypes.byref(self.c_state),
+                         _ptr(draft), _ptr(target_tok), _ptr(tau), _ptr(k_new), _ptr(v_new), _ptr(q),
+                         _ptr(k_blk), _ptr(v_blk), _ptr(out), _stream(stream))
+
     def bind_verify_append(self, logits, draft, target_tok, tau, k_new, v_new, stream=None):
         return BoundCall("ls_verify_append", ctypes.byref(self.dims), ctypes.byref(self.c_state),
                          _ptr(logits), _ptr(draft), _ptr(target_tok), _ptr(tau), _ptr(k_new),

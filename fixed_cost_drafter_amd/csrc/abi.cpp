@@ -69,7 +69,7 @@ ls_status check_state(const ls_state* s, const ls_dims& d, int32_t L0) {
 
 extern "C" {
 
-int32_t ls_version(void) { return 106; }
+int32_t ls_version(void) { return 107; }
 
 const char* ls_status_string(int32_t status) {
   switch (status) {
@@ -214,6 +214,33 @@ ls_status ls_verify_append_draft(const ls_dims* dims, const ls_state* state, con
     return LS_ERR_ALIGN;
   return ls::launch_verify_append_draft(*dims, *state, logits, draft, target_tok, tau, k_new, v_new,
                                         q, k_blk, v_blk, out, static_cast<hipStream_t>(stream));
+}
+
+ls_status ls_verify_keys(const ls_dims* dims, const ls_state* state, const void* logits,
+                         ls_stream stream) {
+  ls_status st = check_dims(dims);
+  if (st != LS_OK) return st;
+  st = check_state(state, *dims, 1);
+  if (st != LS_OK) return st;
+  if (!logits) return LS_ERR_NULL;
+  return ls::launch_round_keys(*dims, *state, logits, static_cast<hipStream_t>(stream));
+}
+
+ls_status ls_update_draft(const ls_dims* dims, const ls_state* state, const int32_t* draft,
+                          int32_t* target_tok, int32_t* tau, const void* k_new, const void* v_new,
+                          const void* q, const void* k_blk, const void* v_blk, void* out,
+                          ls_stream stream) {
+  ls_status st = check_dims(dims);
+  if (st != LS_OK) return st;
+  st = check_state(state, *dims, 1);
+  if (st != LS_OK) return st;
+  if (!draft || !target_tok || !tau || !k_new || !v_new || !q || !k_blk || !v_blk || !out)
+    return LS_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(q) || !aligned16(k_blk) ||
+      !aligned16(v_blk) || !aligned16(out))
+    return LS_ERR_ALIGN;
+  return ls::launch_update_draft(*dims, *state, draft, target_tok, tau, k_new, v_new, q, k_blk, v_blk,
+                                 out, static_cast<hipStream_t>(stream));
 }
 
 ls_status ls_draft_attention(const ls_dims* dims, const ls_state* state, const void* q,

@@ -728,6 +728,23 @@ ls_status launch_append(const ls_dims& d, const ls_state& st, const void* k_new,
   return LS_ERR_SHAPE;
 }
 
+ls_status launch_append_from_keys(const ls_dims& d, const ls_state& st, const int32_t* draft,
+                                  int32_t* target_tok, int32_t* tau, const void* k_new,
+                                  const void* v_new, hipStream_t stream) {
+  char* ws = static_cast<char*>(st.workspace);
+  if (d.dtype != LS_BF16) {  // f32: finish the verification, then the update
+    const ls_status s1 = launch_verify_finalize(d, draft, target_tok, tau, ws, stream);
+    return s1 != LS_OK ? s1 : launch_append(d, st, k_new, v_new, tau, stream);
+  }
+  // the update derives tau from the keys; L from the key pass's snapshot
+  const WsLayout lay = ws_layout(d, 1);
+  const VerifyKeys vk{reinterpret_cast<const uint64_t*>(ws + lay.verify_part), lay.vsplit, draft,
+                      target_tok, tau};
+  launch_units_for<true>(d, st, k_new, v_new, nullptr, vk,
+                         reinterpret_cast<const int32_t*>(ws + lay.len_snap), stream);
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+}
+
 ls_status launch_verify_append(const ls_dims& d, const ls_state& st, const void* logits,
                                const int32_t* draft, int32_t* target_tok, int32_t* tau,
                                const void* k_new, const void* v_new, hipStream_t stream) {
@@ -737,14 +754,9 @@ ls_status launch_verify_append(const ls_dims& d, const ls_state& st, const void*
     return s1 != LS_OK ? s1 : launch_append(d, st, k_new, v_new, tau, stream);
   }
   // the verification's partial keys; the same launch takes the length snapshot
-  const WsLayout lay = ws_layout(d, 1);
-  int32_t* snap = reinterpret_cast<int32_t*>(ws + lay.len_snap);
-  const ls_status s1 = launch_verify_keys(d, logits, ws, st.seq_len, snap, stream);
-  if (s1 != LS_OK) return s1;
-  const VerifyKeys vk{reinterpret_cast<const uint64_t*>(ws + lay.verify_part), lay.vsplit, draft,
-                      target_tok, tau};
-  launch_units_for<true>(d, st, k_new, v_new, nullptr, vk, snap, stream);
-  return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+  const ls_status s1 = launch_verify_keys(d, logits, ws, st.seq_len,
+                                          reinterpret_cast<int32_t*>(ws + ws_layout(d, 1).len_snap), stream);
+  return s1 != LS_OK ? s1 : launch_append_from_keys(d, st, draft, target_tok, tau, k_new, v_new, stream);
 }
 
 }  // namespace ls

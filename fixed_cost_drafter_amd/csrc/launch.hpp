@@ -64,9 +64,26 @@ ls_status launch_init(const ls_dims& d, const ls_state& st, const void* k_prefix
 ls_status launch_draft(const ls_dims& d, const ls_state& st, const void* q, const void* k_blk,
                        const void* v_blk, void* out, hipStream_t stream);
 
-// a whole round: verification, update, draft attention (update and draft in
-// one launch where round_fusable, else the separate entry points' launches)
+// the verification's second half over the keys in the workspace
+// (target_tok, tau)
+ls_status launch_verify_finalize(const ls_dims& d, const int32_t* draft, int32_t* target_tok,
+                                 int32_t* tau, const char* ws, hipStream_t stream);
+// the update over the keys in the workspace (a key pass took the snapshot):
+// tau and target_tok derived on the way, as in launch_verify_append
+ls_status launch_append_from_keys(const ls_dims& d, const ls_state& st, const int32_t* draft,
+                                  int32_t* target_tok, int32_t* tau, const void* k_new,
+                                  const void* v_new, hipStream_t stream);
+
+// a whole round: the key pass (round_keys: partial keys, length snapshot,
+// zeroed arrival counters), then update + draft attention (update_draft: one
+// launch where round_fusable, else the separate entry points' launches)
 bool round_fusable(const ls_dims& d);
+ls_status launch_round_keys(const ls_dims& d, const ls_state& st, const void* logits,
+                            hipStream_t stream);
+ls_status launch_update_draft(const ls_dims& d, const ls_state& st, const int32_t* draft,
+                              int32_t* target_tok, int32_t* tau, const void* k_new,
+                              const void* v_new, const void* q, const void* k_blk,
+                              const void* v_blk, void* out, hipStream_t stream);
 ls_status launch_verify_append_draft(const ls_dims& d, const ls_state& st, const void* logits,
                                      const int32_t* draft, int32_t* target_tok, int32_t* tau,
                                      const void* k_new, const void* v_new, const void* q,

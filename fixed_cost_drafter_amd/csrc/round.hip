@@ -3,9 +3,9 @@
 // views are updated with the accepted rows, (c) the drafter attends over the
 // views; Fig. 3: only the newly retained rows enter the summary).
 //
-// ls_verify_append_draft = the verification's key pass (verify.hip, which
-// also takes the length snapshot and zeroes the arrival counters), then
-// update_draft below: the same results as ls_verify_append followed by
+// ls_verify_append_draft = the verification's key pass (ls_verify_keys:
+// verify.hip, which also takes the length snapshot and zeroes the arrival
+// counters), then update_draft below (ls_update_draft): the same results as ls_verify_append followed by
 // ls_draft_attention, in two launches instead of three.  The state comes out
 // bit for bit as from the update kernel (the same merge, merge_ops.hpp); the
 // attention output equals the draft kernel's up to the order in which the
@@ -28,13 +28,14 @@
 // Every workgroup of the unit merges every tile from the state as it was
 // before the round (its drafters need all pooled tiles); tile t's state is
 // written by the last of the unit's R waves that merged it to finish (a
-// counter per (unit, tile)): a wave that starts late must not read a tile
-// that a sibling has already updated.  Nobody waits: the others skip the
-// stores.  Slot tile t goes out from the workgroup with t % R == ridx (the
-// pooled tiles are identical in all of them).  The lead workgroup of the
-// sequence writes target_tok, tau, ring_pos and seq_len = L + tau (L from
-// the snapshot: no workgroup here reads seq_len).  The key parts of the 8
-// waves merge in LDS as in the draft kernel.
+// counter per (unit, tile), which that wave sets back to zero): a wave
+// that starts late must not read a tile that a sibling has already updated.
+// Nobody waits: the others skip the stores.  Slot tile t goes out from the
+// workgroup with t % R == ridx (the pooled tiles are identical in all of
+// them).  The lead workgroup of the sequence writes target_tok, tau,
+// ring_pos and seq_len = L + tau (L from the snapshot: no workgroup here
+// reads seq_len).  The key parts of the 8 waves merge in LDS as in the
+// draft kernel.
 #include "accept.hpp"
 #include "common.hpp"
 #include "draft_ops.hpp"
@@ -58,7 +59,7 @@ struct RoundKeys {          // the verification's partial keys and its outputs
   const int32_t* draft;
   int32_t* target_tok;
   int32_t* tau_out;
-  int32_t* arrivals;        // [C*Hkv*S/32], zero at launch
+  int32_t* arrivals;        // [C*Hkv*S/32], zero at launch; zero again at exit
 };
 
 // kTiles: S / 32 slot tiles (2 or 4) = updater waves.  nd_total: the window
@@ -141,6 +142,9 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
   // the unit's B+1 verified rows (row-major keys KL, transposed [k | v] RT,
   // rows past B+1 zero) and its S slot queries UL; the rows' argmax tokens
   // into g_tok.  Every thread takes part; the caller then meets a barrier.
+  // (Requesting these before the role's large loads does not bring that
+  // barrier forward: the first ~7 us of the kernel are the whole grid's
+  // initial requests, about 200 KB per CU, arriving at the memory's rate.)
   constexpr int kItems = RP * (E / 8) / kThreads;
   static_assert(kItems * kThreads == RP * (E / 8), "whole passes");
   constexpr int kUItems = S * (D / 8) / kThreads;
@@ -277,6 +281,10 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
     uint16_t* kt = pool + tl * 2 * 32 * D;
     pooled_to_lds<8>(acc, 1.0f / l_new, 0, lane, kt, kt + 32 * D);
     const bool writer = R == 1 || __builtin_amdgcn_readfirstlane(before) == R - 1;
+    // the last arrival also rearms the counter for the next launch
+    if (R > 1 && writer && lane == 0)
+      __hip_atomic_store(rk.arrivals + int64_t(unit) * kTiles + tl, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     if (writer) {  // every sibling's wave for this tile has read the old state
 #pragma unroll
       for (int t = 0; t < 8; ++t)
@@ -446,23 +454,26 @@ bool round_fusable(const ls_dims& d) {
          d.W >= 32 && d.W % 32 == 0 && draft_row_splits(d) <= 2;
 }
 
-ls_status launch_verify_append_draft(const ls_dims& d, const ls_state& st, const void* logits,
-                                     const int32_t* draft, int32_t* target_tok, int32_t* tau,
-                                     const void* k_new, const void* v_new, const void* q,
-                                     const void* k_blk, const void* v_blk, void* out,
-                                     hipStream_t stream) {
-  if (!round_fusable(d)) {  // the two entry points' launches
-    const ls_status s1 = launch_verify_append(d, st, logits, draft, target_tok, tau, k_new, v_new, stream);
+ls_status launch_round_keys(const ls_dims& d, const ls_state& st, const void* logits,
+                            hipStream_t stream) {
+  char* ws = static_cast<char*>(st.workspace);
+  const WsLayout lay = ws_layout(d, 1);
+  return launch_verify_keys(d, logits, ws, st.seq_len, reinterpret_cast<int32_t*>(ws + lay.len_snap),
+                            stream, reinterpret_cast<int32_t*>(ws + lay.arrivals));
+}
+
+ls_status launch_update_draft(const ls_dims& d, const ls_state& st, const int32_t* draft,
+                              int32_t* target_tok, int32_t* tau, const void* k_new,
+                              const void* v_new, const void* q, const void* k_blk,
+                              const void* v_blk, void* out, hipStream_t stream) {
+  if (!round_fusable(d)) {  // the update over the keys, then the draft kernel
+    const ls_status s1 = launch_append_from_keys(d, st, draft, target_tok, tau, k_new, v_new, stream);
     return s1 != LS_OK ? s1 : launch_draft(d, st, q, k_blk, v_blk, out, stream);
   }
   char* ws = static_cast<char*>(st.workspace);
   const WsLayout lay = ws_layout(d, 1);
-  int32_t* snap = reinterpret_cast<int32_t*>(ws + lay.len_snap);
-  int32_t* arrivals = reinterpret_cast<int32_t*>(ws + lay.arrivals);
-  const ls_status s1 = launch_verify_keys(d, logits, ws, st.seq_len, snap, stream, arrivals);
-  if (s1 != LS_OK) return s1;
   const RoundKeys rk{reinterpret_cast<const uint64_t*>(ws + lay.verify_part), lay.vsplit, draft,
-                     target_tok, tau, arrivals};
+                     target_tok, tau, reinterpret_cast<int32_t*>(ws + lay.arrivals)};
   const int units = d.C * d.Hkv;
   const int tiles = d.S / 32, nring = d.W / 32;
   // the updaters take up to LS_ROUND_UPD_WIN window chunks each, as long as
@@ -470,7 +481,8 @@ ls_status launch_verify_append_draft(const ls_dims& d, const ls_state& st, const
   const int nd_total = nring - std::min(kRoundUpdWin * tiles, std::max(0, nring - (kKPW - tiles)));
   auto kernel = d.S == 128 ? update_draft<4> : update_draft<2>;
   hipLaunchKernelGGL(kernel, dim3(unsigned(units * draft_row_splits(d))), dim3(64 * kKPW), 0, stream,
-                     rk, snap, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+                     rk, reinterpret_cast<const int32_t*>(ws + lay.len_snap),
+                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_blk),
                      static_cast<const uint16_t*>(v_blk), static_cast<uint16_t*>(st.ring_k),
                      static_cast<uint16_t*>(st.ring_v), st.ring_pos, st.seq_len, st.sum_m, st.sum_l,
@@ -478,6 +490,17 @@ ls_status launch_verify_append_draft(const ls_dims& d, const ls_state& st, const
                      static_cast<const uint16_t*>(st.u), st.log_lambda, static_cast<uint16_t*>(out),
                      d.Hq, d.Hkv, d.W, d.B, units, nd_total);
   return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+}
+
+ls_status launch_verify_append_draft(const ls_dims& d, const ls_state& st, const void* logits,
+                                     const int32_t* draft, int32_t* target_tok, int32_t* tau,
+                                     const void* k_new, const void* v_new, const void* q,
+                                     const void* k_blk, const void* v_blk, void* out,
+                                     hipStream_t stream) {
+  const ls_status s1 = launch_round_keys(d, st, logits, stream);
+  return s1 != LS_OK ? s1
+                     : launch_update_draft(d, st, draft, target_tok, tau, k_new, v_new, q, k_blk,
+                                           v_blk, out, stream);
 }
 
 }  // namespace ls

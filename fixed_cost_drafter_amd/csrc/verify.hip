@@ -319,6 +319,14 @@ ls_status launch_verify(const ls_dims& d, const void* logits, const int32_t* dra
                             reinterpret_cast<uint64_t*>(ws + ws_layout(d, 1).verify_part), stream);
 }
 
+ls_status launch_verify_finalize(const ls_dims& d, const int32_t* draft, int32_t* target_tok,
+                                 int32_t* tau, const char* ws, hipStream_t stream) {
+  hipLaunchKernelGGL(verify_finalize, dim3(d.C), dim3(kFinalizeThreads), 0, stream,
+                     reinterpret_cast<const uint64_t*>(ws + ws_layout(d, 1).verify_part), draft,
+                     target_tok, tau, d.B, verify_splits(d));
+  return hipGetLastError() == hipSuccess ? LS_OK : LS_ERR_HIP;
+}
+
 ls_status launch_verify_into(const ls_dims& d, const void* logits, const int32_t* draft,
                              int32_t* target_tok, int32_t* tau, uint64_t* part,
                              hipStream_t stream) {

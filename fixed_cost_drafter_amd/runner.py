@@ -72,6 +72,21 @@ class PathRunner:
                                           dev["v_new"], dev["q"], dev["k_blk"], dev["v_blk"], b.out,
                                           stream)
 
+    def round_split(self, logits: torch.Tensor, dev: dict, stream=None):
+        """round() as its two launches called one by one: ls_verify_keys (the
+        pass over the logits), then ls_update_draft."""
+        s, b = self.state, self.buf
+        s.verify_keys(logits, stream)
+        s.update_draft(dev["draft"], b.target_tok, b.tau, dev["k_new"], dev["v_new"], dev["q"],
+                       dev["k_blk"], dev["v_blk"], b.out, stream)
+
+    def bind_round_split(self, logits: torch.Tensor, dev: dict, stream=None):
+        """round_split() marshalled once: (key pass, update + draft) callables."""
+        s, b = self.state, self.buf
+        return (s.bind_verify_keys(logits, stream),
+                s.bind_update_draft(dev["draft"], b.target_tok, b.tau, dev["k_new"], dev["v_new"],
+                                    dev["q"], dev["k_blk"], dev["v_blk"], b.out, stream))
+
     def round_separate(self, logits: torch.Tensor, dev: dict, stream=None):
         """The same round through the three separate entry points."""
         s, b = self.state, self.buf

@@ -206,15 +206,38 @@ ls_status ls_verify_greedy_noalloc(const ls_dims* dims, const void* logits, cons
  * new window rows and the slots are attended as chunks of their own, and
  * the probabilities enter P.V rounded to bf16 against the running maximum).
  * The state's workspace also holds per-(sequence, KV head, 32-slot tile)
- * arrival counters that the launch zeroes and uses (no carry-over between
- * calls).  Shapes other than bf16, d = 128, S in {64, 128}, B + 1 <= 32,
+ * arrival counters that the key pass zeroes and the update leaves at zero
+ * (no carry-over between calls).  Shapes other than bf16, d = 128, S in {64, 128}, B + 1 <= 32,
  * W a positive multiple of 32 and at most 64 query rows B*Hq/Hkv per KV
- * head run the two calls' launches. */
+ * head run the two calls' launches.  Equal to ls_verify_keys followed by
+ * ls_update_draft on the same stream. */
 ls_status ls_verify_append_draft(const ls_dims* dims, const ls_state* state, const void* logits,
                                  const int32_t* draft, int32_t* target_tok, int32_t* tau,
                                  const void* k_new, const void* v_new, const void* q,
                                  const void* k_blk, const void* v_blk, void* out,
                                  ls_stream stream);
+
+/* The two launches of ls_verify_append_draft as calls of their own, for a
+ * caller that wants to place other work between them.
+ * ls_verify_keys: the verification's pass over the logits (Fig. 2 (a)): the
+ *   per-chunk argmax keys of the C*(B+1) rows go to the state's workspace,
+ *   together with the lengths seq_len as they stand (the update appends at
+ *   those lengths) and zeroed arrival counters.  Reads logits only; changes
+ *   no state.  LS_ERR_NULL if logits is null.
+ * ls_update_draft: the rest of the round (Fig. 2 (a) acceptance, (b), (c))
+ *   from what the last ls_verify_keys on this state's workspace left there:
+ *   target_tok, tau, the update and the draft attention, as
+ *   ls_verify_append_draft.  Arguments as there, minus logits.  A second
+ *   call without a new key pass appends the same accepted rows at the same
+ *   lengths again (the ring rows and lengths come out the same, the summary
+ *   merges them once more); the results are unspecified if no key pass ran
+ *   on the workspace since it was allocated. */
+ls_status ls_verify_keys(const ls_dims* dims, const ls_state* state, const void* logits,
+                         ls_stream stream);
+ls_status ls_update_draft(const ls_dims* dims, const ls_state* state, const int32_t* draft,
+                          int32_t* target_tok, int32_t* tau, const void* k_new, const void* v_new,
+                          const void* q, const void* k_blk, const void* v_blk, void* out,
+                          ls_stream stream);
 
 /* Drafter block attention (Fig. 2 (c)).
  *   q:            [C, B, Hq, d] dtype, block queries.

@@ -67,7 +67,7 @@ def test_header_compiles_as_plain_c(tmp_path):
 
 
 def test_version_and_status_strings(LB):
-    assert LB.ls_version() == 106
+    assert LB.ls_version() == 107
     assert LB.ls_status_string(0) == "ok"
     for s in range(1, 8):
         assert LB.ls_status_string(s) and LB.ls_status_string(s) != "unknown status"
@@ -288,6 +288,40 @@ def test_verify_append_validation(LB):
     assert L.ls_verify_append(ctypes.byref(d), ctypes.byref(small), 16, 16, 16, 16, 16, 16,
                               None) == 4             # workspace too small
 
+
+
+@no_device
+def test_round_entry_validation(LB):
+    """The one-call round and its two halves check dims, state and every
+    pointer they take, before any launch."""
+    d = _dims(LB)
+    L = LB.lib()
+    st = _fake_state(LB, d, LB.ls_workspace_bytes(d, 1))
+    one = lambda *a: L.ls_verify_append_draft(ctypes.byref(d), ctypes.byref(st), *a, None)
+    upd = lambda *a: L.ls_update_draft(ctypes.byref(d), ctypes.byref(st), *a, None)
+    ok = [16] * 10
+    for i in range(10):  # logits, draft, target_tok, tau, k_new, v_new, q, k_blk, v_blk, out
+        args = list(ok)
+        args[i] = None
+        assert one(*args) == 1, i
+        if i > 0:
+            assert upd(*args[1:]) == 1, i
+    for i in (4, 5, 6, 7, 8, 9):  # the 16-byte rows: k_new, v_new, q, k_blk, v_blk, out
+        args = list(ok)
+        args[i] = 24
+        assert one(*args) == 5, i
+        assert upd(*args[1:]) == 5, i
+    assert L.ls_verify_keys(ctypes.byref(d), ctypes.byref(st), None, None) == 1
+    assert L.ls_verify_keys(None, ctypes.byref(st), 16, None) == 1
+    empty = LB.LsState()
+    assert L.ls_verify_keys(ctypes.byref(d), ctypes.byref(empty), 16, None) == 1
+    small = _fake_state(LB, d, 256)
+    assert L.ls_verify_keys(ctypes.byref(d), ctypes.byref(small), 16, None) == 4
+    assert L.ls_update_draft(ctypes.byref(d), ctypes.byref(small), *ok[1:], None) == 4
+    assert L.ls_verify_append_draft(ctypes.byref(d), ctypes.byref(small), *ok, None) == 4
+    bad = _dims(LB, B=48)
+    assert L.ls_verify_keys(ctypes.byref(bad), ctypes.byref(st), 16, None) == 2
+    assert L.ls_update_draft(ctypes.byref(bad), ctypes.byref(st), *ok[1:], None) == 2
 
 
 @no_device

@@ -105,3 +105,78 @@ def test_round_matches_two_calls(name):
               f"unequal {float(np.mean(diff > 0)):.4f}")
         assert float(diff.max()) <= H.BF16_ABS, f"round {r}: max diff {float(diff.max()):.3e}"
         assert float(diff.mean()) <= 1e-3, f"round {r}: mean diff {float(diff.mean()):.3e}"
+
+
+@pytest.mark.parametrize("name", ["bf16_wrap", "bf16_s128_short", "bf16_halves", "f32_d32_wrap", "q3_8b_32k"])
+def test_split_round_matches_one_call(name):
+    """ls_verify_keys then ls_update_draft against ls_verify_append_draft:
+    the same launches, so everything matches bit for bit, the output too
+    (f32_d32_wrap: the shapes the fused kernel does not take, where both run
+    the separate kernels)."""
+    import torch
+    from fixed_cost_drafter_amd import binding as LB
+    from fixed_cost_drafter_amd.runner import PathRunner, upload_round
+    wl = SMALL[name] if name in SMALL else WLM.WORKLOADS[name].with_(L0=3000)
+    rounds = 5
+    _announce(wl, f"split round vs one call x {rounds}")
+    Kp, Vp = WLM.prefix(wl, threads=8)
+    one, two = PathRunner(wl, Kp, Vp), PathRunner(wl, Kp, Vp)
+    one.init()
+    two.init()
+    for r in range(rounds):
+        logits, planted = WLM.logits_entry(wl, r % WLM.pool_size(wl))
+        dev = upload_round(WLM.round_inputs(wl, r, planted))
+        lg = LB.to_device(logits)
+        one.round(lg, dev)
+        two.round_split(lg, dev)
+        torch.cuda.synchronize()
+        for k in ("tau", "target_tok", "out"):
+            H.exact(f"round {r} {k}", LB.to_host(getattr(one.buf, k)), LB.to_host(getattr(two.buf, k)))
+        a, b = one.snapshot(), two.snapshot()
+        for k in a:
+            H.exact(f"round {r} {k}", a[k], b[k])
+
+
+@pytest.mark.parametrize("name", ["bf16_s128_short", "q3_8b_32k"])
+def test_update_draft_repeats_without_a_key_pass(name):
+    """Two ls_update_draft calls after one key pass: the second merges the
+    same accepted rows into the summary once more at the same lengths.  The
+    reference replays that second update from a restored state: the state
+    after the first update, with the lengths put back, and a fresh key pass
+    (the same logits give the same keys).  The shapes have two workgroups
+    per KV head, so the second call's state writes need the arrival counters
+    that the first call left at zero."""
+    import torch
+    from fixed_cost_drafter_amd import binding as LB
+    from fixed_cost_drafter_amd.runner import PathRunner, upload_round
+    wl = SMALL[name] if name in SMALL else WLM.WORKLOADS[name].with_(L0=3000)
+    assert wl.B * wl.Hq // wl.Hkv > 32, "two workgroups per KV head"
+    _announce(wl, "update_draft twice after one key pass")
+    Kp, Vp = WLM.prefix(wl, threads=8)
+    twice, ref = PathRunner(wl, Kp, Vp), PathRunner(wl, Kp, Vp)
+    twice.init()
+    ref.init()
+    logits, planted = WLM.logits_entry(wl, 0)
+    dev = upload_round(WLM.round_inputs(wl, 0, planted))
+    lg = LB.to_device(logits)
+    s, b = twice.state, twice.buf
+    s.verify_keys(lg)
+    upd = lambda st, bf: st.update_draft(dev["draft"], bf.target_tok, bf.tau, dev["k_new"], dev["v_new"],
+                                         dev["q"], dev["k_blk"], dev["v_blk"], bf.out)
+    upd(s, b)
+    torch.cuda.synchronize()
+    first = twice.snapshot()
+    seq0 = LB.to_host(ref.state.seq_len)
+    upd(s, b)
+    torch.cuda.synchronize()
+    after = twice.snapshot()
+    assert not np.array_equal(first["sum_n"], after["sum_n"]), "the second update wrote no summary"
+    back = dict(first)
+    back["seq_len"] = seq0
+    ref.restore(back)
+    ref.round_split(lg, dev)
+    torch.cuda.synchronize()
+    want = ref.snapshot()
+    for k in after:
+        H.exact(k, after[k], want[k])
+    H.exact("out", LB.to_host(twice.buf.out), LB.to_host(ref.buf.out))
