@@ -108,8 +108,8 @@ FULL_SIZE_HEADS = {
 
 @pytest.mark.parametrize("name", list(FULL_SIZE_HEADS))
 def test_parity_full_size_sampled(name):
-    """Full shape and prefix, the bench's call sequence (ls_verify_append, then
-    ls_draft_attention) for the configured 256 rounds.  Integers (target_tok,
+    """Full shape and prefix, the bench's call (ls_verify_append_draft) for the
+    configured 256 rounds.  Integers (target_tok,
     tau, the whole ring, ring_pos, seq_len) are checked every round for every
     sequence; the fp32 summary state and the slots of the sampled (sequence,
     KV head) units every 32 rounds and at the end, so the incremental update
@@ -117,8 +117,8 @@ def test_parity_full_size_sampled(name):
     (Fig. 3: initialised over the prefix, then only the retained rows)."""
     wl = WLM.WORKLOADS[name]
     heads = FULL_SIZE_HEADS[name]
-    _announce(wl, f"fused rounds={wl.rounds} sampled heads={heads}")
-    runner, ost, stats = H.lockstep(wl, wl.rounds, heads=heads, check_state_every=32, fused=True)
+    _announce(wl, f"one-call rounds={wl.rounds} sampled heads={heads}")
+    runner, ost, stats = H.lockstep(wl, wl.rounds, heads=heads, check_state_every=32, calls="round")
     taus = np.stack(stats["tau"]).astype(np.float64)      # [rounds, C]
     H.log(f"mean tau {taus.mean():.3f} (expected {WLM.expected_tau(wl):.3f})")
     # accepted lengths differ across the batch, so the ring offsets diverge
@@ -152,16 +152,17 @@ EDGE = {
 }
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("calls", ["separate", "two", "round"])
 @pytest.mark.parametrize("name", list(EDGE))
-def test_parity_edge_logits(name, fused):
+def test_parity_edge_logits(name, calls):
     """Rows whose maximum is <= 0, +0 / -0 only, all -inf, ties on both sides of
     an 8192-logit boundary, the maximum in the ragged last chunk, a lone
-    subnormal: through ls_verify_greedy (+ the update and the draft) and
-    through ls_verify_append, every round against the oracle."""
+    subnormal: through ls_verify_greedy (+ the update and the draft), through
+    ls_verify_append (+ the draft) and through ls_verify_append_draft, every
+    round against the oracle."""
     wl = EDGE[name]
-    _announce(wl, f"edge logits, {'fused' if fused else 'separate'} calls")
-    H.lockstep(wl, wl.rounds, fused=fused, logits_fn=lambda r: (WLM.edge_logits(wl, r), None),
+    _announce(wl, f"edge logits, calls={calls}")
+    H.lockstep(wl, wl.rounds, calls=calls, logits_fn=lambda r: (WLM.edge_logits(wl, r), None),
                draft_fn=_edge_drafts(wl), heads=[(0, 0), (wl.C - 1, wl.Hkv - 1)])
 
 
