@@ -190,6 +190,13 @@ def summarize_traffic(fetch_dir: str, write_dir: str, command: str) -> dict:
         factor = CALIB_BYTES / max(calib)
         out[f"{key}_scale"] = round(factor, 4)
         out[f"{key}_calibration_raw_bytes"] = max(calib)
+        # a second point: the 64 MiB copies of the streaming reference (each
+        # reads and writes 64 MiB), if the run made them; their scale should
+        # match the 512 MiB copy's
+        small = sorted(v for v in calib if v < 0.5 * max(calib))
+        if small:
+            out[f"{key}_scale_64MiB"] = round((64 << 20) / small[len(small) // 2], 4)
+            out[f"{key}_calibration_64MiB_dispatches"] = len(small)
         for name, vs in vals.items():
             short = name.replace("(anonymous namespace)::", "").replace("void ", "").split("(")[0]
             ent = out["kernels"].setdefault(short, {})

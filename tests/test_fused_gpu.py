@@ -57,7 +57,8 @@ def test_verify_append_matches_separate_calls(name):
         H.exact(f"round {r} out", LB.to_host(fused.buf.out), LB.to_host(sep.buf.out))
 
 
-@pytest.mark.parametrize("name", ["bf16_wrap", "bf16_s128_short", "bf16_halves", "bf16_l1", "q3_8b_32k"])
+@pytest.mark.parametrize("name", ["bf16_wrap", "bf16_s128_short", "bf16_halves", "bf16_l1", "bf16_s64_r2",
+                                  "bf16_w32_full", "q3_8b_32k"])
 def test_round_matches_two_calls(name):
     """ls_verify_append_draft (update and draft in one launch) against
     ls_verify_append + ls_draft_attention: target tokens, tau and the whole

@@ -1,9 +1,12 @@
 """One drafting round captured in a HIP graph and replayed.
 
-A caller may capture verify -> append -> draft once and replay it every
-round.  The round's kernels take all sizes from their arguments and tau from
-device memory, and no call records a memset, so a replay must do exactly what
-the eager calls do.  The replays here run with the program's own eager work
+A caller may capture the round (ls_verify_append_draft: the key pass, then
+the update and the draft attention) once and replay it every round.  The
+round's kernels take all sizes from their arguments and tau from device
+memory, and no call records a memset (the key pass zeroes the arrival
+counters with its own stores), so a replay must do exactly what the eager
+calls do.  bf16_s128_short has two workgroups per KV head, so its replays
+also exercise the arrival counters.  The replays here run with the program's own eager work
 and synchronisations between them, and every replay is compared bit for bit
 with an eager run of the same rounds.
 """
@@ -17,7 +20,7 @@ from tests.test_parity_gpu import SMALL, _announce
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["bf16_halves", "bf16_wrap", "f32_d32_wrap"])
+@pytest.mark.parametrize("name", ["bf16_halves", "bf16_wrap", "bf16_s128_short", "f32_d32_wrap"])
 def test_graph_replay_matches_eager(name):
     import torch
     from fixed_cost_drafter_amd import binding as LB

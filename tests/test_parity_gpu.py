@@ -67,6 +67,16 @@ SMALL = {
     "bf16_s128_b40": WLM.Workload(
         "bf16_s128_b40", "bf16", C=2, Hq=2, Hkv=2, d=128, L0=90, W=128, S=128, B=40, V=1504,
         rounds=5, p_match=0.92, seed=20),
+    # S = 64 with B*G = 48 query rows: two workgroups per KV head in the
+    # one-call round's 2-tile kernel (the arrival counters), a wrapping ring
+    "bf16_s64_r2": WLM.Workload(
+        "bf16_s64_r2", "bf16", C=3, Hq=16, Hkv=4, d=128, L0=200, W=64, S=64, B=12, V=5000,
+        rounds=8, p_match=0.8, seed=22),
+    # B + 1 = W = 32: a fully accepted block replaces the whole window in one
+    # round (every window slot masked, the new rows are the window)
+    "bf16_w32_full": WLM.Workload(
+        "bf16_w32_full", "bf16", C=2, Hq=2, Hkv=2, d=128, L0=70, W=32, S=128, B=31, V=3000,
+        rounds=6, p_match=0.97, seed=23),
 }
 
 
