@@ -181,3 +181,38 @@ def test_update_draft_repeats_without_a_key_pass(name):
     for k in after:
         H.exact(k, after[k], want[k])
     H.exact("out", LB.to_host(twice.buf.out), LB.to_host(ref.buf.out))
+
+
+def _random_round_shapes(n, seed=2024):
+    """Seeded bf16 shapes that the one-call round's fused kernel takes: W a
+    multiple of 32 from 32 to 256, S in {64, 128}, 1 <= B <= min(31, W - 1),
+    B * G <= 64 query rows per KV head (one or two workgroups), C and the
+    prefix length (shorter than the window, or wrapping it) varied."""
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < n:
+        W = 32 * int(rng.integers(1, 9))
+        S = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(1, min(31, W - 1) + 1))
+        if B * G > 64 or (len(shapes) % 2 == 1 and B * G <= 32):
+            continue  # every other shape has two workgroups per KV head
+        C = int(rng.integers(1, 5))
+        L0 = int(rng.integers(1, 3 * W))
+        V = int(rng.choice([1000, 4096, 9001]))
+        shapes.append(WLM.Workload(
+            f"rand{len(shapes)}", "bf16", C=C, Hq=Hkv * G, Hkv=Hkv, d=128, L0=L0, W=W, S=S, B=B, V=V,
+            rounds=4, p_match=float(rng.choice([0.5, 0.85, 0.97])), seed=100 + len(shapes)))
+    return shapes
+
+
+RANDOM_ROUND = _random_round_shapes(20)
+
+
+@pytest.mark.parametrize("wl", RANDOM_ROUND, ids=[w.name for w in RANDOM_ROUND])
+def test_round_random_shapes_against_the_oracle(wl):
+    """The one-call round against the oracle, every round and the whole state,
+    over seeded random shapes that its fused kernel takes."""
+    _announce(wl, f"G={wl.Hq // wl.Hkv} rows/head={wl.B * wl.Hq // wl.Hkv} rounds={wl.rounds} one-call round")
+    H.lockstep(wl, wl.rounds, calls="round")
