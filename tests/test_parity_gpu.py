@@ -294,3 +294,46 @@ def test_init_with_large_scores_in_old_rows(S):
     torch.cuda.synchronize()
     ost = O.summary_init(u, WLM.log_lambda(wl), Kp, Vp, wl.W)
     H.compare_state(rn, ost, wl.dtype, scaled=True)
+
+
+def _random_shapes(n, seed=77):
+    """Seeded shapes across the whole accepted range, both dtypes: bf16 (d = 128,
+    S in {0, 64, 128}, W = 0 or a multiple of 32, B up to 47, up to 64 query
+    rows per KV head) and f32 (d in {16, 32, 64, 128}, any S <= 40, any W);
+    W = 0 or S = 0 switch a view off; the window is at least B + 1 rows."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        dt = "bf16" if len(out) % 3 else "f32"
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 48))
+        if dt == "bf16":
+            d, S = 128, int(rng.choice([0, 64, 128]))
+            W = 32 * int(rng.integers(0, 9))
+            if B * G > 64:
+                continue
+        else:
+            d, S = int(rng.choice([16, 32, 64, 128])), int(rng.integers(0, 41))
+            W = int(rng.integers(0, 49))
+        if W and W < B + 1:
+            continue
+        C = int(rng.integers(1, 5))
+        L0 = int(rng.integers(1, 3 * max(W, 32)))
+        V = int(rng.choice([300, 4096, 9001, 20001]))
+        out.append(WLM.Workload(f"any{len(out)}_{dt}", dt, C=C, Hq=Hkv * G, Hkv=Hkv, d=d, L0=L0, W=W, S=S,
+                                B=B, V=V, rounds=3, p_match=float(rng.choice([0.5, 0.9])),
+                                seed=300 + len(out)))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(15)
+
+
+@pytest.mark.parametrize("calls", ["separate", "two", "round"])
+@pytest.mark.parametrize("wl", RANDOM_SHAPES, ids=[w.name for w in RANDOM_SHAPES])
+def test_parity_random_shapes(wl, calls):
+    """Every entry-point sequence of a round against the oracle, every round and
+    the whole state, over seeded random shapes across the accepted range."""
+    _announce(wl, f"G={wl.Hq // wl.Hkv} rounds={wl.rounds} calls={calls}")
+    H.lockstep(wl, wl.rounds, calls=calls)
