@@ -196,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void samp_decide_sums(
   constexpr int kW = kThreads / 64;
   constexpr int kRows = (kMaxBlock + 1 + kW - 1) / kW;  // rows per wave
   static_assert(kRows <= 64, "a lane per row for the gathers");
-  __shared__ float pt[64], qd[64], mt[64], izt[64], md[64], izd[64];
+  __shared__ float pt[64], qd[64], mt[64], izt[64], md[64], izd[64], ua[64];
   __shared__ Record s_rec;
   __shared__ int s_js;
   const int split = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63,
@@ -214,6 +214,9 @@ __global__ __launch_bounds__(kThreads) void samp_decide_sums(
     if (j <= B && lane < nsplit) ts[i] = stats[(int64_t(c) * (B + 1) + j) * nsplit + lane];
     if (j < B && lane < nsplit) ds[i] = stats[(int64_t(nt) + int64_t(c) * B + j) * nsplit + lane];
   }
+  // the acceptance draws, one per lane, for thread 0's rule below (one
+  // round trip instead of a dependent load per drafted position)
+  if (tid < B) ua[tid] = u_accept[int64_t(c) * B + tid];
   float xt = 0.f, xd = 0.f;
   {
     const int j = wave + kW * lane;
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void samp_decide_sums(
   __syncthreads();
   if (tid == 0) {
     int j = 0;
-    while (j < B && u_accept[int64_t(c) * B + j] * qd[j] < pt[j]) ++j;
+    while (j < B && ua[j] * qd[j] < pt[j]) ++j;
     s_js = j;
     Record r;
     r.row = j;
@@ -323,6 +326,9 @@ __global__ __launch_bounds__(kThreads) void samp_decide_sums(
 // max(0, p_j - q_j) is zero everywhere (p_j == q_j: the drafted token had
 // p = q = 0) draws from p_j instead; its chunk sums come from the target
 // row's chunk statistics.
+// at most 2^20 logits per row (checked by the ABI): the chunks of a row
+constexpr int kMaxChunks = ((1 << 20) + kVerifyChunk - 1) / kVerifyChunk;
+
 template <typename Ty>
 __global__ __launch_bounds__(kThreads) void samp_draw(
     const typename Ty::T* __restrict__ tl, const typename Ty::T* __restrict__ dl,
@@ -335,15 +341,24 @@ __global__ __launch_bounds__(kThreads) void samp_draw(
   static_assert(SEG % VT::N == 0, "whole vectors per thread");
   __shared__ int s_split, s_bonus;
   __shared__ float s_base, s_thr;
+  __shared__ float s_sm[kMaxChunks];
+  __shared__ float2 s_st[kMaxChunks];
   __shared__ float wtot[kThreads / 64];
   __shared__ int s_first[kThreads / 64], s_last[kThreads / 64];
   const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Record r = rec[c];
   const typename Ty::T* rt = tl + (int64_t(c) * (B + 1) + r.row) * V;
   const typename Ty::T* rd = dl + (int64_t(c) * B + min(r.row, B - 1)) * V;
+  // the chunk sums and the drawn row's chunk statistics, loaded in parallel
+  // for thread 0's scan (which adds them in chunk order, as before)
+  for (int k = tid; k < nsplit; k += kThreads) {
+    s_sm[k] = sums[int64_t(c) * nsplit + k];
+    s_st[k] = stats[(int64_t(c) * (B + 1) + r.row) * nsplit + k];
+  }
+  __syncthreads();
   if (tid == 0) {
-    const float* sm = sums + int64_t(c) * nsplit;
-    const float2* st = stats + (int64_t(c) * (B + 1) + r.row) * nsplit;
+    const float* sm = s_sm;
+    const float2* st = s_st;
     float total = 0.f;
     for (int k = 0; k < nsplit; ++k) total += sm[k];
     // an empty residual: draw from p_j, whose chunk k holds
