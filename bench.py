@@ -816,9 +816,13 @@ def main(argv=None):
             kernels[name]["mfma_util_counter"] = round(cnt["MfmaUtil"] / 100.0, 4)
     d = kernels[dominant]
     traffic = load_traffic(dominant)
+    ref = g["stream_reference"].get("copy_64MiB_gb_per_s")
     roof = dict(kernel=dominant, bound="hbm", achieved=d["gb_per_s"], peak=HBM_PEAK_GBS,
                 unit="GB/s", frac=d["hbm_frac"], traffic=traffic,
-                mfma_frac_algorithmic=d.get("mfma_frac"), mfma_util_counter=d.get("mfma_util_counter"))
+                mfma_frac_algorithmic=d.get("mfma_frac"), mfma_util_counter=d.get("mfma_util_counter"),
+                # beside the datasheet peak: the same rate over what a plain library copy
+                # of the round's scale reaches on this GPU (stream_reference)
+                frac_of_stream_reference=round(d["gb_per_s"] / ref, 4) if ref else None)
     line = {
         "metric": "draft rounds/s at concurrency 16, prefix 32K–128K; % HBM/MFMA peak",
         "value": round(value, 1),
