@@ -5,10 +5,12 @@ the verification's partial keys inside the update; it must give the same
 target tokens, tau, state and draft output, bit for bit, as ls_verify_greedy
 then ls_append_accepted.  ls_verify_append_draft (the whole round in one call)
 must match ls_verify_append + ls_draft_attention bit for bit in everything but
-the attention output, which differs only in summation order.  Each runs over
-rounds that accept every draft, none, and a random mix.  The fused paths
-against the oracle are tests/test_parity_gpu.py's small round-mode,
-full-size and edge-logits cases."""
+the attention output, which differs only in the order the softmax visits the
+keys; its halves (ls_verify_keys, ls_update_draft) must match it bit for bit.
+Each runs over rounds that accept every draft, none, and a random mix.  The
+one-call round also meets the oracle here on seeded random shapes; the fused
+paths against the oracle are otherwise tests/test_parity_gpu.py's small
+round-mode, random-shape, full-size and edge-logits cases."""
 import numpy as np
 import pytest
 
