@@ -1,0 +1,103 @@
+"""Host-side logic of bench.py, on the CPU: the algorithmic bytes it prices
+the kernels with, its rocprofv3 counter summaries (on synthetic counter
+files) and its refusal of more than one GPU."""
+import csv
+import os
+
+import pytest
+
+import bench
+from fixed_cost_drafter_amd import workload as WLM
+
+
+def test_algorithmic_bytes_are_the_shapes_closed_forms():
+    """At the 128K workload every per-call figure is the sum of the arrays the
+    step must touch, written out from the shapes."""
+    wl = WLM.WORKLOADS["q3_8b_128k"]
+    tau = 3.0
+    a = bench.algorithmic(wl, tau, wl.L0)
+    C, Hq, Hkv, d, W, S, B, V = wl.C, wl.Hq, wl.Hkv, wl.d, wl.W, wl.S, wl.B, wl.V
+    units = C * Hkv
+    # logits once, the drafts, and the target tokens + tau words
+    assert a["verify"] == C * (B + 1) * V * 2 + C * B * 4 + C * (B + 2) * 4
+    # fp32 (m, l, n) read and written, bf16 slots written, tau rows read and
+    # written to the ring, the slot queries read once
+    state = units * S * (2 * d + 2) * 4
+    slots = units * S * d * 2 * 2
+    rows = C * tau * Hkv * d * 2 * 2
+    assert a["append"] == pytest.approx(2 * state + slots + 2 * rows + Hkv * S * d * 2)
+    # every key and value of the three views, the queries and the output, the
+    # window positions
+    assert a["draft"] == units * (W + S + B) * d * 2 * 2 + 2 * C * B * Hq * d * 2 + C * W * 4
+    assert a["draft"] == 80_805_888
+    # one launch: the merged slots are not read back
+    assert a["update_draft"] == pytest.approx(a["append"] + a["draft"] - slots)
+    assert a["round"] == pytest.approx(a["verify"] + a["update_draft"])
+    assert a["draft_flop"] == units * 4 * B * (Hq // Hkv) * (W + S + B) * d
+    assert a["init"] == units * wl.L0 * d * 2 * 2
+    assert a["init_flop"] == units * wl.L0 * 6 * S * d
+
+
+def _counter_csv(path, rows):
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for kernel, counter, value in rows:
+            w.writerow(dict(Kernel_Name=kernel, Counter_Name=counter, Counter_Value=value))
+
+
+def test_traffic_summary_scales_by_the_calibration_copies(tmp_path):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled so the 512 MiB copy
+    reads and writes 512 MiB; the 64 MiB copies give the second point; an
+    entry point's bytes are the sum over its kernels."""
+    neg = "void at::native::vectorized_elementwise_kernel<8, at::native::neg_kernel_cuda(...)"
+    # this part's FETCH_SIZE counts half of a copy's reads; WRITE_SIZE all
+    fetch = [(neg, "FETCH_SIZE", 256 * 1024)] + [(neg, "FETCH_SIZE", 32 * 1024)] * 3
+    write = [(neg, "WRITE_SIZE", 512 * 1024)] + [(neg, "WRITE_SIZE", 64 * 1024)] * 3
+    for k, f_kib, w_kib in (("void ls::(anonymous namespace)::verify_partial<ls::BF16>(...)", 40000, 100),
+                            ("void ls::(anonymous namespace)::update_draft<4>(...)", 48000, 27000)):
+        fetch += [(k, "FETCH_SIZE", f_kib)] * 2
+        write += [(k, "WRITE_SIZE", w_kib)] * 2
+    _counter_csv(tmp_path / "f", fetch)
+    _counter_csv(tmp_path / "w", write)
+    t = bench.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "cmd")
+    assert t["fetch_scale"] == pytest.approx(2.0)
+    assert t["write_scale"] == pytest.approx(1.0)
+    assert t["fetch_scale_64MiB"] == pytest.approx(2.0)
+    assert t["write_scale_64MiB"] == pytest.approx(1.0)
+    assert t["fetch_calibration_64MiB_dispatches"] == 3
+    ud = t["entry_points"]["update_draft"]
+    assert ud["fetch_bytes"] == round(48000 * 1024 * 2.0)
+    assert ud["write_bytes"] == round(27000 * 1024)
+    rd = t["entry_points"]["round"]  # verify_partial + update_draft
+    assert rd["fetch_bytes"] == round((40000 + 48000) * 1024 * 2.0)
+    assert rd["write_bytes"] == round((100 + 27000) * 1024)
+    assert sorted(rd["kernels"]) == ["ls::update_draft<4>", "ls::verify_partial<ls::BF16>"]
+    assert rd["source_hash"] == bench.source_hash(bench.KERNEL_SOURCES["round"])
+
+
+def test_traffic_summary_needs_the_calibration_copy(tmp_path):
+    _counter_csv(tmp_path / "f", [("void ls::x(...)", "FETCH_SIZE", 1)])
+    _counter_csv(tmp_path / "w", [("void ls::x(...)", "WRITE_SIZE", 1)])
+    with pytest.raises(SystemExit):
+        bench.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "cmd")
+
+
+def test_counter_summary_means_per_dispatch(tmp_path):
+    k = "void ls::(anonymous namespace)::update_draft<4>(...)"
+    _counter_csv(tmp_path / "a", [(k, "MfmaUtil", 6.0), (k, "MfmaUtil", 8.0), (k, "GRBM_GUI_ACTIVE", 100.0),
+                                  (k, "GRBM_GUI_ACTIVE", 300.0)])
+    _counter_csv(tmp_path / "b", [(k, "SQ_WAVES", 2048.0), (k, "SQ_WAVES", 2048.0)])
+    c = bench.summarize_counters([str(tmp_path / "a"), str(tmp_path / "b")], "cmd")
+    ent = c["entry_points"]["update_draft"]
+    assert ent["kernel"] == "ls::update_draft<4>"
+    assert ent["MfmaUtil"] == pytest.approx(7.0)
+    assert ent["GRBM_GUI_ACTIVE"] == pytest.approx(200.0)
+    assert ent["SQ_WAVES"] == pytest.approx(2048.0)
+    assert c["kernels"]["ls::update_draft<4>"]["dispatches"] == 2
+
+
+def test_more_than_one_gpu_is_refused(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
