@@ -218,3 +218,21 @@ def test_round_random_shapes_against_the_oracle(wl):
     over seeded random shapes that its fused kernel takes."""
     _announce(wl, f"G={wl.Hq // wl.Hkv} rows/head={wl.B * wl.Hq // wl.Hkv} rounds={wl.rounds} one-call round")
     H.lockstep(wl, wl.rounds, calls="round")
+
+
+MINIMAL_ROUND = {
+    # one drafted token, one query row per KV head, a one-row prefix
+    "min_b1_g1": WLM.Workload("min_b1_g1", "bf16", C=1, Hq=1, Hkv=1, d=128, L0=1, W=32, S=64, B=1,
+                              V=1000, rounds=6, p_match=0.5, seed=41),
+    # one drafted token, eight query heads per KV head, a prefix that wraps the window
+    "min_b1_g8": WLM.Workload("min_b1_g8", "bf16", C=2, Hq=16, Hkv=2, d=128, L0=1000, W=32, S=128, B=1,
+                              V=1000, rounds=6, p_match=0.5, seed=42),
+}
+
+
+@pytest.mark.parametrize("name", list(MINIMAL_ROUND))
+def test_round_minimal_shapes_against_the_oracle(name):
+    """The one-call round at the smallest shapes its fused kernel takes."""
+    wl = MINIMAL_ROUND[name]
+    _announce(wl, f"rounds={wl.rounds} one-call round")
+    H.lockstep(wl, wl.rounds, calls="round")
