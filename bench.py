@@ -715,7 +715,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="q3_8b_128k")
+    ap.add_argument("--workload", default="q3_8b_128k",
+                    help="a named workload (fixed_cost_drafter_amd/configs/<name>.json) or a JSON file")
     ap.add_argument("--passes", type=int, default=5,
                     help="timed passes of --steps rounds; the median pass is reported")
     ap.add_argument("--heat", type=int, default=400,
@@ -755,7 +756,7 @@ def main(argv=None):
               "Run with --gpus 1.", file=sys.stderr)
         return 2
     from fixed_cost_drafter_amd import workload as WLM
-    wl = WLM.WORKLOADS[args.workload]
+    wl = WLM.resolve_workload(args.workload)
     cpu = None
     if args.cpu:
         # first, while no process has touched the GPU: the workers fork from here

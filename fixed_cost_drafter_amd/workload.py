@@ -20,6 +20,9 @@ depends only on the shapes.
 """
 from __future__ import annotations
 
+import dataclasses
+import json
+import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, replace
 
@@ -59,26 +62,36 @@ class Workload:
         return replace(self, **kw)
 
 
-WORKLOADS = {
-    # tiny fp32 case: 1 sequence, 2 query heads on 1 KV head, d=16
-    "tiny_f32": Workload("tiny_f32", "f32", C=1, Hq=2, Hkv=1, d=16, L0=64, W=16, S=4, B=4,
-                         V=32, rounds=8, p_match=0.7, seed=20260929,
-                         lambdas=(1.0, 0.9, 0.5, 0.1)),
-    # Qwen3-4B-shaped tapped layer, one sequence, 8K prefix
-    "q3_4b_8k": Workload("q3_4b_8k", "bf16", C=1, Hq=32, Hkv=8, d=128, L0=8192, W=512, S=64,
-                         B=16, V=151936, rounds=64, p_match=0.8, seed=20260930,
-                         logits_pool=8),
-    # Qwen3-8B-shaped tapped layer at concurrency 16
-    "q3_8b_32k": Workload("q3_8b_32k", "bf16", C=16, Hq=32, Hkv=8, d=128, L0=32768, W=1024,
-                          S=128, B=16, V=151936, rounds=256, p_match=0.8, seed=20260931,
-                          logits_pool=8),
-    "q3_8b_64k": Workload("q3_8b_64k", "bf16", C=16, Hq=32, Hkv=8, d=128, L0=65536, W=1024,
-                          S=128, B=16, V=151936, rounds=256, p_match=0.75, seed=20260932,
-                          logits_pool=8),
-    "q3_8b_128k": Workload("q3_8b_128k", "bf16", C=16, Hq=32, Hkv=8, d=128, L0=131072,
-                           W=1024, S=128, B=16, V=151936, rounds=256, p_match=0.7,
-                           seed=20260933, logits_pool=8),
-}
+CONFIG_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "configs")
+CONFIG_NAMES = ("tiny_f32", "q3_4b_8k", "q3_8b_32k", "q3_8b_64k", "q3_8b_128k")
+
+
+def load_workload(path: str) -> Workload:
+    """A workload from its JSON file: the Workload fields by name (lambdas a
+    list, empty for the default decays); an "about" text is allowed."""
+    with open(path) as f:
+        cfg = json.load(f)
+    cfg.pop("about", None)
+    fields = {f.name for f in dataclasses.fields(Workload)}
+    unknown = set(cfg) - fields
+    if unknown:
+        raise ValueError(f"{path}: unknown workload fields {sorted(unknown)}")
+    cfg["lambdas"] = tuple(float(x) for x in cfg.get("lambdas", ()))
+    return Workload(**cfg)
+
+
+def resolve_workload(name_or_path: str) -> Workload:
+    """A named workload (configs/<name>.json) or the JSON file at a path."""
+    if name_or_path in WORKLOADS:
+        return WORKLOADS[name_or_path]
+    if os.path.isfile(name_or_path):
+        return load_workload(name_or_path)
+    raise KeyError(f"no workload {name_or_path!r}: not one of {sorted(WORKLOADS)} and not a file")
+
+
+# the five workloads: tiny fp32; Qwen3-4B-shaped, one sequence, 8K prefix;
+# Qwen3-8B-shaped at concurrency 16 with 32K, 64K and 128K prefixes
+WORKLOADS = {n: load_workload(os.path.join(CONFIG_DIR, n + ".json")) for n in CONFIG_NAMES}
 SWEEP_L0 = (4096, 16384, 32768, 65536, 131072)
 
 

@@ -55,3 +55,31 @@ def test_lambda_rule_and_state_bytes():
     assert np.isneginf(WLM.log_lambda(wl)[0])
     # ring 4 MiB + fp32 summary ~1 MiB + bf16 slots 0.5 MiB per sequence
     assert 5.4 * 2 ** 20 < WLM.state_bytes(wl) < 5.6 * 2 ** 20
+
+
+def test_named_workloads_come_from_their_config_files(tmp_path):
+    """The five workloads are the JSON files under configs/; a file of one's
+    own loads the same way, and unknown fields are refused."""
+    import json
+    import os
+    from fixed_cost_drafter_amd import workload as WLM
+    assert sorted(WLM.WORKLOADS) == sorted(WLM.CONFIG_NAMES)
+    for name in WLM.CONFIG_NAMES:
+        path = os.path.join(WLM.CONFIG_DIR, name + ".json")
+        assert WLM.load_workload(path) == WLM.WORKLOADS[name]
+        assert WLM.resolve_workload(name) is WLM.WORKLOADS[name]
+    h = WLM.WORKLOADS["q3_8b_128k"]
+    assert (h.C, h.Hq, h.Hkv, h.d, h.L0, h.W, h.S, h.B, h.V) == (16, 32, 8, 128, 131072, 1024, 128, 16, 151936)
+    own = dict(name="own", dtype="bf16", C=2, Hq=8, Hkv=2, d=128, L0=300, W=64, S=64, B=5, V=2000,
+               rounds=3, p_match=0.8, seed=5, lambdas=[1.0] * 64, about="a test shape")
+    p = tmp_path / "own.json"
+    p.write_text(json.dumps(own))
+    wl = WLM.resolve_workload(str(p))
+    assert wl.C == 2 and wl.lambdas == tuple([1.0] * 64) and wl.logits_pool == 0
+    own["Q"] = 1
+    p.write_text(json.dumps(own))
+    import pytest
+    with pytest.raises(ValueError):
+        WLM.load_workload(str(p))
+    with pytest.raises(KeyError):
+        WLM.resolve_workload("no_such_workload")
