@@ -33,7 +33,8 @@
  *
  * Supported shapes: Hq % Hkv == 0; 1 <= B <= 47; 1 <= V <= 2^20;
  *   C*(B+1) <= 65535; W >= 0 with B+1 <= W when W > 0; S >= 0.
- *   LS_F32 : d in {16, 32, 64, 128}, S <= 256, B*Hq/Hkv <= 64.
+ *   LS_F32 : d in {16, 32, 64, 128}, S <= 256 (any number of query rows
+ *            B*Hq/Hkv per KV head).
  *   LS_BF16: d == 128, S in {0, 64, 128}, W % 32 == 0, B*Hq/Hkv <= 64.
  * W = 0 switches the window view off and S = 0 the summary view (the view
  * ablations of Table 5, cost side): the drafter then attends to the other

@@ -72,6 +72,10 @@ SMALL = {
     "bf16_s64_r2": WLM.Workload(
         "bf16_s64_r2", "bf16", C=3, Hq=16, Hkv=4, d=128, L0=200, W=64, S=64, B=12, V=5000,
         rounds=8, p_match=0.8, seed=22),
+    # f32 has no limit on query rows per KV head: G = 8, B = 20 (160 rows)
+    "f32_many_rows": WLM.Workload(
+        "f32_many_rows", "f32", C=2, Hq=8, Hkv=1, d=16, L0=50, W=40, S=8, B=20, V=500,
+        rounds=4, p_match=0.9, seed=24),
     # B + 1 = W = 32: a fully accepted block replaces the whole window in one
     # round (every window slot masked, the new rows are the window)
     "bf16_w32_full": WLM.Workload(
