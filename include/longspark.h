@@ -32,7 +32,8 @@
  *     stream, or ordered with events).
  *
  * Supported shapes: Hq % Hkv == 0; 1 <= B <= 47; 1 <= V <= 2^20;
- *   C*(B+1) <= 65535; W >= 0 with B+1 <= W when W > 0; S >= 0.
+ *   C*(B+1) <= 65535; W >= 0 with B+1 <= W when W > 0; S >= 0;
+ *   C*Hkv*S <= 2^30.
  *   LS_F32 : d in {16, 32, 64, 128}, S <= 256 (any number of query rows
  *            B*Hq/Hkv per KV head).
  *   LS_BF16: d == 128, S in {0, 64, 128}, W % 32 == 0, B*Hq/Hkv <= 64.
