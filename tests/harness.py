@@ -117,9 +117,10 @@ def lockstep(wl: WLM.Workload, rounds: int, k_prefix=None, v_prefix=None, heads=
     sides before the append (device-side clamping and the error flag).
     ``calls`` picks the entry points of a round: "separate" (default:
     ls_verify_greedy, ls_append_accepted, ls_draft_attention), "two"
-    (ls_verify_append, then ls_draft_attention) or "round" (the bench's call,
-    ls_verify_append_draft); ``fused=True`` means "round".  For "two" and
-    "round" target_tok and tau are checked after the round.
+    (ls_verify_append, then ls_draft_attention), "round" (the bench's call,
+    ls_verify_append_draft) or "mixed" (round, two, separate in turn on the
+    same state); ``fused=True`` means "round".  For "two" and "round"
+    target_tok and tau are checked after the round.
     ``logits_fn(r)`` -> (logits, planted or None) replaces the pooled logits;
     ``draft_fn(r, target)`` -> draft [C, B] replaces the round's drafts, built
     from the oracle's target tokens ``target`` (never from GPU output).
@@ -130,8 +131,8 @@ def lockstep(wl: WLM.Workload, rounds: int, k_prefix=None, v_prefix=None, heads=
     from fixed_cost_drafter_amd.runner import PathRunner, upload_round
 
     calls = calls or ("round" if fused else "separate")
-    fused = calls != "separate"
-    assert not (fused and tau_override), "the fused calls derive tau themselves"
+    assert calls in ("separate", "two", "round", "mixed"), calls
+    assert not (calls != "separate" and tau_override), "the fused calls derive tau themselves"
     t0 = time.time()
     if k_prefix is None:
         k_prefix, v_prefix = WLM.prefix(wl, threads=16)
@@ -176,9 +177,12 @@ def lockstep(wl: WLM.Workload, rounds: int, k_prefix=None, v_prefix=None, heads=
         b = runner.buf
         s = runner.state
         tau_use = tau_ref
-        if calls == "round":
+        # "mixed": the three call sequences in turn on one state
+        mode = ("round", "two", "separate")[r % 3] if calls == "mixed" else calls
+        fused = mode != "separate"
+        if mode == "round":
             runner.round(logits_dev, dev)
-        elif calls == "two":
+        elif mode == "two":
             runner.round_two_calls(logits_dev, dev)
         else:
             s.verify_greedy(logits_dev, dev["draft"], b.target_tok, b.tau)

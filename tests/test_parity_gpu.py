@@ -105,6 +105,17 @@ def test_parity_small_round(name):
     H.lockstep(wl, wl.rounds, calls="round")
 
 
+@pytest.mark.parametrize("name", ["bf16_s64_r2", "bf16_s128_short", "bf16_b47", "f32_d32_wrap"])
+def test_parity_mixed_entry_points(name):
+    """One state driven by the three call sequences in turn (the one-call
+    round, ls_verify_append + draft, the separate calls), against the oracle
+    every round: each leaves the state as the next one expects it (slot
+    tiles, lengths, ring, arrival counters)."""
+    wl = SMALL[name].with_(rounds=max(SMALL[name].rounds, 9))
+    _announce(wl, f"rounds={wl.rounds} mixed entry points")
+    H.lockstep(wl, wl.rounds, calls="mixed")
+
+
 def test_parity_q3_4b_8k_all_heads():
     wl = WLM.WORKLOADS["q3_4b_8k"]
     _announce(wl, "rounds=64 (state checked every 8)")
