@@ -236,3 +236,16 @@ def test_round_minimal_shapes_against_the_oracle(name):
     wl = MINIMAL_ROUND[name]
     _announce(wl, f"rounds={wl.rounds} one-call round")
     H.lockstep(wl, wl.rounds, calls="round")
+
+
+def test_round_when_sibling_workgroups_run_apart():
+    """C = 48 units of 64 query rows: 768 workgroups for 256 CUs, so the two
+    workgroups of a (sequence, KV head) run in different waves of the
+    dispatch and the second starts after the first has finished.  The state
+    must still be merged exactly once (the arrival counters pick the writer);
+    checked against the oracle on sampled heads, every round."""
+    wl = WLM.Workload("siblings_apart", "bf16", C=48, Hq=32, Hkv=8, d=128, L0=600, W=256, S=128, B=16,
+                      V=4096, rounds=4, p_match=0.8, seed=43)
+    assert wl.B * wl.Hq // wl.Hkv == 64 and wl.C * wl.Hkv * 2 >= 3 * 256
+    _announce(wl, "one-call round, sibling workgroups in different dispatch waves")
+    H.lockstep(wl, wl.rounds, calls="round", heads=[(0, 0), (17, 3), (47, 7)])
