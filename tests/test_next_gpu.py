@@ -25,6 +25,7 @@ ARGMAX_CASES = {
     "bf16_l1": SMALL["bf16_l1"],                 # V = 1001: scalar path and a ragged chunk
     "bf16_s64_ragged": SMALL["bf16_s64_ragged"],  # V = 20001: two chunks + tail
     "q3_8b": WLM.WORKLOADS["q3_8b_128k"],        # C = 16, B = 16, V = 151936
+    "bf16_vmax": SMALL["bf16_vmax"],              # V = 2^20: 128 chunks per row
 }
 
 
@@ -233,6 +234,10 @@ SAMPLING_CASES = {
     "bf16_small_T07": (SMALL["bf16_s64_ragged"].with_(name="samp_bf16_t07", C=6, B=5, V=20001), 0.7),
     "f32_tiny": (WLM.WORKLOADS["tiny_f32"].with_(name="samp_f32", C=4, B=4), 1.0),
     "q3_8b_full": (WLM.WORKLOADS["q3_8b_128k"], 1.0),
+    # V = 2^20: 128 chunks per row, more than one lane's share (64) in the
+    # decision's statistics merge
+    "bf16_vmax_T1": (SMALL["bf16_vmax"], 1.0),
+    "f32_vmax_T1": (SMALL["f32_vmax"], 1.0),
 }
 
 

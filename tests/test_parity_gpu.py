@@ -72,6 +72,14 @@ SMALL = {
     "bf16_s64_r2": WLM.Workload(
         "bf16_s64_r2", "bf16", C=3, Hq=16, Hkv=4, d=128, L0=200, W=64, S=64, B=12, V=5000,
         rounds=8, p_match=0.8, seed=22),
+    # the largest vocabulary, V = 2^20: 128 logit chunks per row (16-lane
+    # key reductions over 8 keys each)
+    "bf16_vmax": WLM.Workload(
+        "bf16_vmax", "bf16", C=2, Hq=4, Hkv=2, d=128, L0=100, W=32, S=64, B=4, V=1 << 20,
+        rounds=3, p_match=0.8, seed=25),
+    "f32_vmax": WLM.Workload(
+        "f32_vmax", "f32", C=2, Hq=2, Hkv=1, d=16, L0=30, W=8, S=4, B=4, V=1 << 20,
+        rounds=3, p_match=0.8, seed=26, lambdas=(1.0, 0.9, 0.5, 0.1)),
     # f32 has no limit on query rows per KV head: G = 8, B = 20 (160 rows)
     "f32_many_rows": WLM.Workload(
         "f32_many_rows", "f32", C=2, Hq=8, Hkv=1, d=16, L0=50, W=40, S=8, B=20, V=500,
