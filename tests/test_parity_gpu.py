@@ -80,6 +80,10 @@ SMALL = {
     "f32_vmax": WLM.Workload(
         "f32_vmax", "f32", C=2, Hq=2, Hkv=1, d=16, L0=30, W=8, S=4, B=4, V=1 << 20,
         rounds=3, p_match=0.8, seed=26, lambdas=(1.0, 0.9, 0.5, 0.1)),
+    # the largest f32 summary, S = 256 slots (8 tiles of 32), d = 64
+    "f32_s256": WLM.Workload(
+        "f32_s256", "f32", C=2, Hq=4, Hkv=2, d=64, L0=150, W=24, S=256, B=6, V=700,
+        rounds=4, p_match=0.8, seed=27),
     # f32 has no limit on query rows per KV head: G = 8, B = 20 (160 rows)
     "f32_many_rows": WLM.Workload(
         "f32_many_rows", "f32", C=2, Hq=8, Hkv=1, d=16, L0=50, W=40, S=8, B=20, V=500,
