@@ -20,7 +20,7 @@
 //    the rows are staged, merges the tile with the tau new rows, attends over
 //    the pooled tile straight from its own LDS output, then over its share
 //    of the window chunks (the last chunks of the ring).  Updater S/32-1
-//    also takes the chunk of new rows, updater S/32-2 (or 0) the verified
+//    also takes the chunk of new rows, updater S/32-2 (or 0) the block
 //    block.  The updaters copy the new rows into the ring.
 //  * the other waves, the drafters: request their first window chunk at once
 //    and run through their chunks (the old rows; the slots (L + i) mod W,
@@ -82,19 +82,23 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
   static_assert(KPW == 8 && ND >= 1, "updaters and drafters");
   // LDS: the draft kernel's per-wave slots (key-part merge at the end),
   // overlaid until then by the pooled slot tiles, the staged rows, the slot
-  // queries and the verified block's values
+  // queries and the block rows (k_blk, v_blk) the drafter attends over
   constexpr int kRedFloats = 2 * 34 * 64;
   constexpr int kSlotElems = (kBlkElems > 2 * kRedFloats) ? kBlkElems : 2 * kRedFloats;
   constexpr int kPool = kTiles * 2 * 32 * D;        // pooled key and value tiles
   constexpr int kKL = kPool, kRT = kKL + RP * KLS, kUL = kRT + E * RTS, kBL = kUL + S * KLS;
-  constexpr int kEnd = kBL + kBlkElems;
-  static_assert(kEnd <= KPW * kSlotElems, "the round's staging fits the draft's LDS");
-  __shared__ __attribute__((aligned(16))) uint16_t lds[KPW * kSlotElems];
+  constexpr int kKB = kBL + kBlkElems;
+  constexpr int kEnd = kKB + RP * KLS;
+  constexpr int kLdsElems = kEnd > KPW * kSlotElems ? kEnd : KPW * kSlotElems;
+  static_assert(kLdsElems * 2 + 64 * 4 <= 160 * 1024, "one workgroup's LDS");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
   __shared__ int32_t g_tok[64];
   uint16_t* pool = lds;
   uint16_t* KL = lds + kKL;
   uint16_t* RT = lds + kRT;
   uint16_t* UL = lds + kUL;
+  uint16_t* BV = lds + kBL;  // the block's value rows [32][kBVS]
+  uint16_t* KB = lds + kKB;  // and its key rows [32][KLS] (rows past B repeat row B-1)
 
   const int unit = blockIdx.x % units, ridx = blockIdx.x / units;
   const int R = int(gridDim.x) / units;
@@ -140,8 +144,9 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
   };
 
   // the unit's B+1 verified rows (row-major keys KL, transposed [k | v] RT,
-  // rows past B+1 zero) and its S slot queries UL; the rows' argmax tokens
-  // into g_tok.  Every thread takes part; the caller then meets a barrier.
+  // rows past B+1 zero), its S slot queries UL and the drafted block's B rows
+  // (row-major KB and BV); the verified rows' argmax tokens into g_tok.
+  // Every thread takes part; the caller then meets a barrier.
   // (Requesting these before the role's large loads does not bring that
   // barrier forward: the first ~7 us of the kernel are the whole grid's
   // initial requests, about 200 KB per CU, arriving at the memory's rate.)
@@ -149,8 +154,10 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
   static_assert(kItems * kThreads == RP * (E / 8), "whole passes");
   constexpr int kUItems = S * (D / 8) / kThreads;
   static_assert(kUItems * kThreads == S * (D / 8), "whole passes");
+  constexpr int kBItems = 2 * RP * (D / 8) / kThreads;  // block keys, then values
+  static_assert(kBItems * kThreads == 2 * RP * (D / 8), "whole passes");
   auto stage = [&]() {
-    u16x8 x[kItems], xu[kUItems];
+    u16x8 x[kItems], xu[kUItems], xb[kBItems];
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
       const int p = it * kThreads + tid, row = p % RP, pc = p / RP;
@@ -162,6 +169,12 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
     for (int it = 0; it < kUItems; ++it) {
       const int p = it * kThreads + tid, sl = p >> 4, pc = p & 15;
       xu[it] = *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + sl) * D + 8 * pc);
+    }
+#pragma unroll
+    for (int it = 0; it < kBItems; ++it) {
+      const int p = it * kThreads + tid, half = p / (RP * (D / 8)), row = (p >> 4) % RP, pc = p & 15;
+      const int key = min(row, B - 1);  // rows past B load a real row; their scores are masked
+      xb[it] = *reinterpret_cast<const u16x8*>((half ? vb : kb) + ((int64_t(c) * B + key) * Hkv + h) * D + 8 * pc);
     }
     accept_rows<kThreads>(rk.keys, rk.nkeys, c, B, g_tok, lead ? rk.target_tok : nullptr);
 #pragma unroll
@@ -177,6 +190,11 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
     for (int it = 0; it < kUItems; ++it) {
       const int p = it * kThreads + tid, sl = p >> 4, pc = p & 15;
       *reinterpret_cast<u16x8*>(&UL[sl * KLS + 8 * pc]) = xu[it];
+    }
+#pragma unroll
+    for (int it = 0; it < kBItems; ++it) {
+      const int p = it * kThreads + tid, half = p / (RP * (D / 8)), row = (p >> 4) % RP, pc = p & 15;
+      *reinterpret_cast<u16x8*>(half ? &BV[row * kBVS + 8 * pc] : &KB[row * KLS + 8 * pc]) = xb[it];
     }
   };
 
@@ -334,28 +352,18 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
       lds_chunk(xk, xv, valid8, false);
     }
     if (kq == (kTiles > 1 ? kTiles - 2 : 0)) {
-      // the verified block (one chunk: B <= 31): its key operands straight
-      // from the caller's rows, its value rows transposed through LDS
+      // the drafted block (one chunk: B <= 31), staged with the verified
+      // rows: key operands from its row-major keys (as the new rows), value
+      // operands by transposed reads of its row-major values
       typedef short i16x4 __attribute__((ext_vector_type(4)));
       typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
       Half bk, xv;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int key = min(chunk_key(ln, mb), B - 1);
-          bk.r[mb * 4 + ks] = *reinterpret_cast<const u16x8*>(kb + ((int64_t(c) * B + key) * Hkv + h) * D + ks * 32 + kg * 8);
-        }
-      uint16_t* bv = lds + kBL;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int piece = lane + 64 * i, row = piece >> 4, col = (piece & 15) * 8;
-        const int key = min(row, B - 1);
-        *reinterpret_cast<u16x8*>(bv + row * kBVS + col) =
-            *reinterpret_cast<const u16x8*>(vb + ((int64_t(c) * B + key) * Hkv + h) * D + col);
-      }
-      __builtin_amdgcn_wave_barrier();
-      const uint16_t* rd = bv + (8 * kg + (ln >> 2)) * kBVS + 4 * (ln & 3);
+        for (int ks = 0; ks < 4; ++ks)
+          bk.r[mb * 4 + ks] = *reinterpret_cast<const u16x8*>(&KB[chunk_key(ln, mb) * KLS + ks * 32 + kg * 8]);
+      const uint16_t* rd = BV + (8 * kg + (ln >> 2)) * kBVS + 4 * (ln & 3);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(rd + 16 * db));
