@@ -93,6 +93,7 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
   static_assert(kLdsElems * 2 + 64 * 4 <= 160 * 1024, "one workgroup's LDS");
   __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
   __shared__ int32_t g_tok[64];
+  __shared__ int32_t upd_lds_done;  // updaters past their last read of the staged rows / pooled tiles
   uint16_t* pool = lds;
   uint16_t* KL = lds + kKL;
   uint16_t* RT = lds + kRT;
@@ -157,6 +158,7 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
   constexpr int kBItems = 2 * RP * (D / 8) / kThreads;  // block keys, then values
   static_assert(kBItems * kThreads == 2 * RP * (D / 8), "whole passes");
   auto stage = [&]() {
+    if (tid == 0) upd_lds_done = 0;  // read only after the staging barrier
     u16x8 x[kItems], xu[kUItems], xb[kBItems];
 #pragma unroll
     for (int it = 0; it < kItems; ++it) {
@@ -374,6 +376,11 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
       const uint32_t valid8 = nvalid >= 8 ? 0xFFu : nvalid <= 0 ? 0u : ((1u << nvalid) - 1u);
       lds_chunk(bk, xv, valid8, false);
     }
+    // this wave reads no more LDS until the key-part merge: count it out, so
+    // that the waves that finish first can fill their merge slots (which
+    // overlay the staged rows and the pooled tiles) without waiting for all
+    // (one lane: the count is of waves)
+    if (lane == 0) __hip_atomic_fetch_add(&upd_lds_done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     Half hk, hv;  // the window chunks last (requested here: no registers to hold them earlier)
     if (nmine > 0) {
       keys_of(hk, 0);
@@ -395,8 +402,10 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
     window(hk, hv, Tn);
   }
 
-  // merge the key parts (as the draft kernel), after every wave is done with
-  // the LDS chunks that the merge slots overlay
+  // merge the key parts (as the draft kernel).  Each wave fills its merge
+  // slot as soon as its keys are done and every updater has counted out of
+  // the LDS chunks that the slots overlay (normally long before; the wait is
+  // bounded so that no wave can stay in it), then one barrier.
   float lt[2];
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
@@ -407,7 +416,10 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
   auto red_at = [&](int k, int rg, int e) {
     return reinterpret_cast<float*>(lds + k * kSlotElems) + (rg * 34 + e) * 64 + lane;
   };
-  __syncthreads();
+  for (int spin = 0; spin < (1 << 16); ++spin) {
+    if (__hip_atomic_load(&upd_lds_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= kTiles) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
     *red_at(kq, rg, 0) = st[rg].m;
@@ -418,34 +430,39 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
       for (int r = 0; r < 4; ++r) *red_at(kq, rg, 2 + mb * 4 + r) = st[rg].o[mb][r];
   }
   __syncthreads();
-  constexpr int kPer = 16 / KPW;  // pieces per wave
-  float pm[kPer][KPW], pl[kPer][KPW], po[kPer][KPW][4];
+  constexpr int kPer = 16 / KPW;  // pieces per wave, all in one row group
+  static_assert(8 % kPer == 0, "a wave's pieces share their row group");
+  const int rgw = (kq * kPer) >> 3;
+  float pm[KPW], pl[KPW], wk[KPW], po[kPer][KPW][4];
 #pragma unroll
-  for (int pc = 0; pc < kPer; ++pc) {
-    const int piece = kq * kPer + pc, rg = piece >> 3, mb = piece & 7;
-#pragma unroll
-    for (int k = 0; k < KPW; ++k) {
-      pm[pc][k] = *red_at(k, rg, 0);
-      pl[pc][k] = *red_at(k, rg, 1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) po[pc][k][r] = *red_at(k, rg, 2 + mb * 4 + r);
-    }
+  for (int k = 0; k < KPW; ++k) {
+    pm[k] = *red_at(k, rgw, 0);
+    pl[k] = *red_at(k, rgw, 1);
   }
 #pragma unroll
   for (int pc = 0; pc < kPer; ++pc) {
-    const int piece = kq * kPer + pc, rg = piece >> 3, mb = piece & 7;
-    const int row = ridx * 32 + rg * 16 + ln;
-    float mx = -INFINITY;
+    const int mb = (kq * kPer + pc) & 7;
 #pragma unroll
-    for (int k = 0; k < KPW; ++k) mx = fmaxf(mx, pm[pc][k]);
+    for (int k = 0; k < KPW; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) po[pc][k][r] = *red_at(k, rgw, 2 + mb * 4 + r);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KPW; ++k) mx = fmaxf(mx, pm[k]);
+#pragma unroll
+  for (int k = 0; k < KPW; ++k) wk[k] = pm[k] == -INFINITY ? 0.f : exp2_f(pm[k] - mx);
+#pragma unroll
+  for (int pc = 0; pc < kPer; ++pc) {
+    const int mb = (kq * kPer + pc) & 7;
+    const int row = ridx * 32 + rgw * 16 + ln;
     float l = 0.f;
     f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KPW; ++k) {
-      const float wk = pm[pc][k] == -INFINITY ? 0.f : exp2_f(pm[pc][k] - mx);
-      l = fmaf(pl[pc][k], wk, l);
+      l = fmaf(pl[k], wk[k], l);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = fmaf(po[pc][k][r], wk, o[r]);
+      for (int r = 0; r < 4; ++r) o[r] = fmaf(po[pc][k][r], wk[k], o[r]);
     }
     if (row >= M) continue;
     const float il = 1.0f / l;
