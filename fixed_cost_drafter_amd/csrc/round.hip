@@ -413,8 +413,15 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
     lt[rg] += __shfl_xor(lt[rg], 16, 64);
     lt[rg] += __shfl_xor(lt[rg], 32, 64);
   }
-  auto red_at = [&](int k, int rg, int e) {
+  // wave k's merge slot, per row group rg: m and l (64 lanes each), then
+  // the 8 output pieces with each lane's 4 values contiguous (16-byte LDS
+  // accesses, a wave's 1 KB contiguous)
+  auto ml_at = [&](int k, int rg, int e) {
     return reinterpret_cast<float*>(lds + k * kSlotElems) + (rg * 34 + e) * 64 + lane;
+  };
+  auto o_at = [&](int k, int rg, int mb) {
+    return reinterpret_cast<f32x4*>(reinterpret_cast<float*>(lds + k * kSlotElems) + (rg * 34 + 2) * 64) +
+           mb * 64 + lane;
   };
   for (int spin = 0; spin < (1 << 16); ++spin) {
     if (__hip_atomic_load(&upd_lds_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= kTiles) break;
@@ -422,30 +429,27 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
   }
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
-    *red_at(kq, rg, 0) = st[rg].m;
-    *red_at(kq, rg, 1) = lt[rg];
+    *ml_at(kq, rg, 0) = st[rg].m;
+    *ml_at(kq, rg, 1) = lt[rg];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) *red_at(kq, rg, 2 + mb * 4 + r) = st[rg].o[mb][r];
+    for (int mb = 0; mb < 8; ++mb) *o_at(kq, rg, mb) = st[rg].o[mb];
   }
   __syncthreads();
   constexpr int kPer = 16 / KPW;  // pieces per wave, all in one row group
   static_assert(8 % kPer == 0, "a wave's pieces share their row group");
   const int rgw = (kq * kPer) >> 3;
-  float pm[KPW], pl[KPW], wk[KPW], po[kPer][KPW][4];
+  float pm[KPW], pl[KPW], wk[KPW];
+  f32x4 po[kPer][KPW];
 #pragma unroll
   for (int k = 0; k < KPW; ++k) {
-    pm[k] = *red_at(k, rgw, 0);
-    pl[k] = *red_at(k, rgw, 1);
+    pm[k] = *ml_at(k, rgw, 0);
+    pl[k] = *ml_at(k, rgw, 1);
   }
 #pragma unroll
   for (int pc = 0; pc < kPer; ++pc) {
     const int mb = (kq * kPer + pc) & 7;
 #pragma unroll
-    for (int k = 0; k < KPW; ++k)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) po[pc][k][r] = *red_at(k, rgw, 2 + mb * 4 + r);
+    for (int k = 0; k < KPW; ++k) po[pc][k] = *o_at(k, rgw, mb);
   }
   float mx = -INFINITY;
 #pragma unroll
