@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -49,12 +50,23 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with whitespace runs collapsed, so
+    that a comment or layout edit leaves a kernel's hash unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(rel) -> str:
+    """Hash of the code (not the comments) of a kernel's sources and the
+    shared headers: recorded with each profile, compared before a profile's
+    figures are reported for the kernel as it now is."""
     h = hashlib.sha256()
     rels = rel if isinstance(rel, tuple) else (rel,)
     for p in (*rels, "fixed_cost_drafter_amd/csrc/common.hpp", "fixed_cost_drafter_amd/csrc/accept.hpp"):
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -35,7 +35,8 @@
 // them).  The lead workgroup of the sequence writes target_tok, tau,
 // ring_pos and seq_len = L + tau (L from the snapshot: no workgroup here
 // reads seq_len).  The key parts of the 8 waves merge in LDS as in the
-// draft kernel.
+// draft kernel; a wave fills its merge slot as soon as it is done and the
+// updaters have counted themselves out of the LDS that the slots overlay.
 #include "accept.hpp"
 #include "common.hpp"
 #include "draft_ops.hpp"

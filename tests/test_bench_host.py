@@ -101,3 +101,14 @@ def test_counter_summary_means_per_dispatch(tmp_path):
 def test_more_than_one_gpu_is_refused(capsys):
     assert bench.main(["--gpus", "2"]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_source_hash_follows_code_not_comments():
+    """A profile stays valid across comment and layout edits of its kernel's
+    sources, and goes stale with any change of the code itself."""
+    code = "__global__ void k(int* p) {\n  p[0] = 1;  // store\n}\n"
+    commented = "/* a kernel */\n__global__ void k(int* p) {\n    p[0] = 1;  // the one store\n}\n"
+    changed = "__global__ void k(int* p) {\n  p[0] = 2;  // store\n}\n"
+    assert bench._code_only(code) == bench._code_only(commented)
+    assert bench._code_only(code) != bench._code_only(changed)
+    assert len(bench.source_hash(bench.KERNEL_SOURCES["round"])) == 16
