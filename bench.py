@@ -155,6 +155,31 @@ def stream_reference(dev, reps=20) -> dict:
     return out
 
 
+def mfma_reference(dev, n=8192, reps=10) -> dict:
+    """What a tuned library bf16 GEMM (torch.mm, n x n x n, contiguous
+    operands) reaches on this GPU: the practical dense-MFMA ceiling beside the
+    2.5 PFLOP/s datasheet peak.  Events over reps back-to-back products.  Run
+    after every other timing: its power draw lowers the clock of what follows."""
+    import torch
+    a = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    b = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    e1.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    tf = 2.0 * n ** 3 / t / 1e12
+    del a, b, c
+    return dict(gemm=f"{n}x{n}x{n} bf16 torch.mm", tflop_per_s=round(tf, 1),
+                frac_of_peak=round(tf / MFMA_BF16_PEAK_TFS, 4))
+
+
 def load_traffic(kernel: str):
     """HBM bytes per call of an entry point from the committed PMC summary, if current."""
     if not os.path.exists(TRAFFIC_JSON):
@@ -775,6 +800,8 @@ def main(argv=None):
         log("timing the oracle on the host (cpu_baseline)")
         cpu = cpu_baseline(wl, args.cpu_budget)
     g = run_gpu(args, wl)
+    g["mfma_reference"] = mfma_reference("cuda")
+    log(f"MFMA reference: {g['mfma_reference']}")
     main_r = g["main"]
     value = args.steps / main_r["wall_s"]
     mean_tau = WLM.expected_tau(wl)
@@ -820,7 +847,10 @@ def main(argv=None):
     kernels["init"] = dict(avg_us=round(init_s * 1e6, 2), alg_bytes=int(alg["init"]),
                            gb_per_s=round(init_bw, 1), hbm_frac=round(init_bw / HBM_PEAK_GBS, 4),
                            tflop_per_s=round(alg["init_flop"] / init_s / 1e12, 1),
-                           mfma_frac=round(alg["init_flop"] / init_s / 1e12 / MFMA_BF16_PEAK_TFS, 4))
+                           mfma_frac=round(alg["init_flop"] / init_s / 1e12 / MFMA_BF16_PEAK_TFS, 4),
+                           # the same rate over what a library bf16 GEMM reaches here
+                           frac_of_mfma_reference=round(alg["init_flop"] / init_s / 1e12 /
+                                                        g["mfma_reference"]["tflop_per_s"], 4))
     for name in ("draft", "init", "update_draft"):
         cnt = load_counters(name)
         if cnt and "MfmaUtil" in cnt:
@@ -861,6 +891,7 @@ def main(argv=None):
         "pass_gpu_ms_per_step": [round(w / args.steps * 1e3, 5) for w in main_r["passes_gpu_s"]],
         "heat_rounds": args.heat,
         "stream_reference": g["stream_reference"],
+        "mfma_reference": g["mfma_reference"],
         "host_issue_us_per_round": round(main_r["issue_s"] / args.steps * 1e6, 2),
         "sweep": g["sweep"],
         "graph_rounds_per_s": (round(args.steps / g["graph"]["wall_s"], 1) if "graph" in g else None),
