@@ -72,7 +72,7 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
   static_assert(16 % KPW == 0, "the merge deals 16 (row group, dimension block) pieces to the waves");
   // one LDS slot per wave, touched only by that wave until the merge: first
   // its block chunk (if it owns one), then its (m, l, O) partial
-  constexpr int kRedFloats = 2 * 34 * 64;  // [row group][m, l, O[32]][lane]
+  constexpr int kRedFloats = 2 * 34 * 64;  // per row group: m[64], l[64], O[8 pieces][64 lanes][4]
   constexpr int kSlotElems = (kBlkElems > 2 * kRedFloats) ? kBlkElems : 2 * kRedFloats;
   static_assert(KPW * kSlotElems * 2 <= 160 * 1024, "the wave slots must fit the LDS");
   __shared__ __attribute__((aligned(16))) uint16_t lds[KPW * kSlotElems];
@@ -222,9 +222,10 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
   if (nmine > 0) step(false, nmine - 1);
 
   // merge the key parts: each wave leaves (m, l, O) in its own slot as soon
-  // as its chunks are done (element-major, lanes contiguous: every access is
-  // 64 consecutive floats); after one barrier each wave combines 16 / KPW of
-  // the 16 (row group, dimension block) pieces
+  // as its chunks are done (per row group: m and l with the lanes contiguous,
+  // then the 8 output pieces with each lane's 4 values contiguous, so every
+  // access is a wave's 256 bytes or 1 KB in a row); after one barrier each
+  // wave combines 16 / KPW of the 16 (row group, dimension block) pieces
   float lt[2];
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
@@ -232,49 +233,56 @@ __global__ __launch_bounds__(64 * KPW, 1) void draft_direct(
     lt[rg] += __shfl_xor(lt[rg], 16, 64);
     lt[rg] += __shfl_xor(lt[rg], 32, 64);
   }
-  auto red_at = [&](int k, int rg, int e) {
+  auto ml_at = [&](int k, int rg, int e) {
     return reinterpret_cast<float*>(lds + k * kSlotElems) + (rg * 34 + e) * 64 + lane;
+  };
+  auto o_at = [&](int k, int rg, int mb) {
+    return reinterpret_cast<f32x4*>(reinterpret_cast<float*>(lds + k * kSlotElems) + (rg * 34 + 2) * 64) +
+           mb * 64 + lane;
   };
 #pragma unroll
   for (int rg = 0; rg < 2; ++rg) {
-    *red_at(kq, rg, 0) = st[rg].m;
-    *red_at(kq, rg, 1) = lt[rg];
+    *ml_at(kq, rg, 0) = st[rg].m;
+    *ml_at(kq, rg, 1) = lt[rg];
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) *red_at(kq, rg, 2 + mb * 4 + r) = st[rg].o[mb][r];
+    for (int mb = 0; mb < 8; ++mb) *o_at(kq, rg, mb) = st[rg].o[mb];
   }
   __syncthreads();
-  constexpr int kPer = 16 / KPW;  // pieces per wave
+  constexpr int kPer = 16 / KPW;  // pieces per wave, all in one row group
+  static_assert(8 % kPer == 0, "a wave's pieces share their row group");
+  const int rgw = (kq * kPer) >> 3;
   // every read of the wave's pieces is issued before the arithmetic, so the
-  // LDS round trips overlap instead of forming a chain per key part
-  float pm[kPer][KPW], pl[kPer][KPW], po[kPer][KPW][4];
+  // LDS round trips overlap instead of forming a chain per key part; the
+  // parts' (m, l) and weights serve both pieces
+  float pm[KPW], pl[KPW], wk[KPW];
+  f32x4 po[kPer][KPW];
 #pragma unroll
-  for (int pc = 0; pc < kPer; ++pc) {
-    const int piece = kq * kPer + pc, rg = piece >> 3, mb = piece & 7;
-#pragma unroll
-    for (int k = 0; k < KPW; ++k) {
-      pm[pc][k] = *red_at(k, rg, 0);
-      pl[pc][k] = *red_at(k, rg, 1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) po[pc][k][r] = *red_at(k, rg, 2 + mb * 4 + r);
-    }
+  for (int k = 0; k < KPW; ++k) {
+    pm[k] = *ml_at(k, rgw, 0);
+    pl[k] = *ml_at(k, rgw, 1);
   }
 #pragma unroll
   for (int pc = 0; pc < kPer; ++pc) {
-    const int piece = kq * kPer + pc, rg = piece >> 3, mb = piece & 7;
-    const int row = ridx * 32 + rg * 16 + ln;
-    float mx = -INFINITY;
+    const int mb = (kq * kPer + pc) & 7;
 #pragma unroll
-    for (int k = 0; k < KPW; ++k) mx = fmaxf(mx, pm[pc][k]);
+    for (int k = 0; k < KPW; ++k) po[pc][k] = *o_at(k, rgw, mb);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KPW; ++k) mx = fmaxf(mx, pm[k]);
+#pragma unroll
+  for (int k = 0; k < KPW; ++k) wk[k] = pm[k] == -INFINITY ? 0.f : exp2_f(pm[k] - mx);
+#pragma unroll
+  for (int pc = 0; pc < kPer; ++pc) {
+    const int mb = (kq * kPer + pc) & 7;
+    const int row = ridx * 32 + rgw * 16 + ln;
     float l = 0.f;
     f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KPW; ++k) {
-      const float wk = pm[pc][k] == -INFINITY ? 0.f : exp2_f(pm[pc][k] - mx);
-      l = fmaf(pl[pc][k], wk, l);
+      l = fmaf(pl[k], wk[k], l);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = fmaf(po[pc][k][r], wk, o[r]);
+      for (int r = 0; r < 4; ++r) o[r] = fmaf(po[pc][k][r], wk[k], o[r]);
     }
     if (row >= M) continue;
     if (ksplit == 1) {  // the whole key list: write the output
