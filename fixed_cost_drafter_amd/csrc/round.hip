@@ -20,8 +20,9 @@
 //    the rows are staged, merges the tile with the tau new rows, attends over
 //    the pooled tile straight from its own LDS output, then over its share
 //    of the window chunks (the last chunks of the ring).  Updater S/32-1
-//    also takes the chunk of new rows, updater S/32-2 (or 0) the block
-//    block.  The updaters copy the new rows into the ring.
+//    also takes the chunk of new rows, updater S/32-2 (or 0) the chunk of
+//    block rows (k_blk, v_blk; staged in LDS with the verified rows).  The
+//    updaters copy the new rows into the ring.
 //  * the other waves, the drafters: request their first window chunk at once
 //    and run through their chunks (the old rows; the slots (L + i) mod W,
 //    i < tau, that the new rows replace are masked, as are empty ones).
