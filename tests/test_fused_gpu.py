@@ -238,6 +238,30 @@ def test_round_minimal_shapes_against_the_oracle(name):
     H.lockstep(wl, wl.rounds, calls="round")
 
 
+MAXIMAL_ROUND = {
+    # the largest block the fused kernel takes (B + 1 = 32 verified rows, a
+    # 31-row block chunk), every draft accepted: tau = 32 every round, so the
+    # chunk of new rows is full and the 64-row window wraps every other round;
+    # 62 query rows per KV head (two workgroups)
+    "max_b31_g2_all": WLM.Workload("max_b31_g2_all", "bf16", C=2, Hq=8, Hkv=4, d=128, L0=100, W=64,
+                                   S=128, B=31, V=3000, rounds=6, p_match=1.0, seed=43),
+    # the same block at one query row per draft and KV head (one workgroup),
+    # a long window and mostly accepted drafts
+    "max_b31_g1": WLM.Workload("max_b31_g1", "bf16", C=3, Hq=2, Hkv=2, d=128, L0=700, W=256, S=64,
+                               B=31, V=3000, rounds=6, p_match=0.97, seed=44),
+}
+
+
+@pytest.mark.parametrize("name", list(MAXIMAL_ROUND))
+def test_round_largest_block_against_the_oracle(name):
+    """The one-call round at the largest block its fused kernel takes."""
+    wl = MAXIMAL_ROUND[name]
+    _announce(wl, f"rounds={wl.rounds} one-call round")
+    _, _, stats = H.lockstep(wl, wl.rounds, calls="round")
+    if wl.p_match == 1.0:
+        assert all((t == wl.B + 1).all() for t in stats["tau"]), "every draft accepted"
+
+
 def test_round_when_sibling_workgroups_run_apart():
     """C = 48 units of 64 query rows: 768 workgroups for 256 CUs, so the two
     workgroups of a (sequence, KV head) run in different waves of the
