@@ -267,25 +267,6 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
     const float m_old = sum_m[sidx], l_old = sum_l[sidx], lnl = log_lambda[j];
     stage();
     __syncthreads();  // staging complete
-    // count this wave in for tile tl as soon as its state loads have
-    // returned: the count only has to follow this wave's reads of the old
-    // state (the empty asm takes every register they filled, so the atomic
-    // cannot be issued before all of them are in), and its reply is needed
-    // only after the merge, which hides the round trip
-    int32_t before = 0;
-    if (R > 1) {
-      int one = 1;
-      asm volatile("" : "+v"(one)
-                   : "v"(acc[0]), "v"(acc[1]), "v"(acc[2]), "v"(acc[3]), "v"(acc[4]), "v"(acc[5]),
-                     "v"(acc[6]), "v"(acc[7]), "v"(m_old), "v"(l_old));
-      // an address the compiler cannot prove uniform: it then issues the
-      // atomic as it stands instead of a wave-level rewrite that reads the
-      // reply at once (the reply is waited for where it is used)
-      typedef __attribute__((address_space(1))) int32_t global_i32;
-      global_i32* ap = (global_i32*)(rk.arrivals + int64_t(unit) * kTiles + tl);
-      asm volatile("" : "+v"(ap));
-      if (lane == 0) before = __hip_atomic_fetch_add(ap, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
     const int Tn = accept_tau(g_tok, dj, B);
     if (lead && tid == 0) rk.tau_out[c] = Tn;
     // the window: this workgroup's share of the unit's copies (Tn 16-byte
@@ -313,7 +294,20 @@ __global__ __launch_bounds__(64 * kKPW, 1) void update_draft(
     float m_new;
     const float l_new = merge_wave<1, 8>(KL, RT, UL + 32 * tl * KLS, acc, m_old, l_old, lnl, Tn, 0,
                                          lane, m_new);
-    // the counter's reply, after the pooled tile is in LDS
+    // this wave has used its state loads: count it in for tile tl (the
+    // empty asm makes the increment depend on the merged accumulators, and so
+    // on every state load, so the atomic cannot be issued before they are
+    // in); the reply is read after the pooled tile is in LDS
+    int32_t before = 0;
+    if (R > 1) {
+      int one = 1;
+      asm volatile("" : "+v"(one)
+                   : "v"(acc[0]), "v"(acc[1]), "v"(acc[2]), "v"(acc[3]), "v"(acc[4]), "v"(acc[5]),
+                     "v"(acc[6]), "v"(acc[7]), "v"(l_new));
+      if (lane == 0)
+        before = __hip_atomic_fetch_add(rk.arrivals + int64_t(unit) * kTiles + tl, one, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    }
     uint16_t* kt = pool + tl * 2 * 32 * D;
     pooled_to_lds<8>(acc, 1.0f / l_new, 0, lane, kt, kt + 32 * D);
     const bool writer = R == 1 || __builtin_amdgcn_readfirstlane(before) == R - 1;
