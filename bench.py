@@ -747,61 +747,11 @@ def next_steps(wl, g) -> dict:
     return res
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--workload", default="q3_8b_128k",
-                    help="a named workload (fixed_cost_drafter_amd/configs/<name>.json) or a JSON file")
-    ap.add_argument("--passes", type=int, default=5,
-                    help="timed passes of --steps rounds; the median pass is reported")
-    ap.add_argument("--heat", type=int, default=400,
-                    help="untimed rounds between the summary init and the warmup rounds")
-    ap.add_argument("--no-sweep", dest="sweep", action="store_false")
-    ap.add_argument("--no-cpu", dest="cpu", action="store_false")
-    ap.add_argument("--cpu-budget", type=float, default=18.0)
-    ap.add_argument("--threads", type=int, default=16)
-    ap.add_argument("--no-next", dest="next", action="store_false",
-                    help="skip the steps beside the round (argmax, boundary, view ablations)")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the K rounds captured in one HIP graph")
-    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="summarise two rocprofv3 --pmc csv runs into the traffic table and exit")
-    ap.add_argument("--traffic-command", default="",
-                    help="the command the counter runs were made with (recorded in the table)")
-    ap.add_argument("--counters", nargs="+", metavar="DIR",
-                    help="summarise rocprofv3 --pmc csv runs (e.g. MfmaUtil) into profiles/counters.json and exit")
-    args = ap.parse_args(argv)
-    if args.counters:
-        t = summarize_counters(args.counters, args.traffic_command)
-        os.makedirs(os.path.dirname(COUNTERS_JSON), exist_ok=True)
-        with open(COUNTERS_JSON, "w") as f:
-            json.dump(t, f, indent=1, sort_keys=True)
-        print(json.dumps(t["entry_points"]))
-        return 0
-    if args.traffic:
-        t = summarize_traffic(args.traffic[0], args.traffic[1], args.traffic_command)
-        os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
-        with open(TRAFFIC_JSON, "w") as f:
-            json.dump(t, f, indent=1, sort_keys=True)
-        print(json.dumps(t["entry_points"]))
-        return 0
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the drafting "
-              "state shards by sequence or KV head with no exchange; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
-        return 2
+def result_line(args, wl, g: dict, cpu) -> dict:
+    """The one JSON line from the GPU measurements ``g`` (run_gpu's result plus
+    the MFMA reference) and the oracle's CPU rate: the metric, the roofline of
+    the round's longest kernel and every entry point's own figures."""
     from fixed_cost_drafter_amd import workload as WLM
-    wl = WLM.resolve_workload(args.workload)
-    cpu = None
-    if args.cpu:
-        # first, while no process has touched the GPU: the workers fork from here
-        log("timing the oracle on the host (cpu_baseline)")
-        cpu = cpu_baseline(wl, args.cpu_budget)
-    g = run_gpu(args, wl)
-    g["mfma_reference"] = mfma_reference("cuda")
-    log(f"MFMA reference: {g['mfma_reference']}")
     main_r = g["main"]
     value = args.steps / main_r["wall_s"]
     mean_tau = WLM.expected_tau(wl)
@@ -899,6 +849,65 @@ def main(argv=None):
         "next": next_steps(wl, g) if args.next else None,
     }
     line["cpu_baseline"] = cpu
+    return line
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="q3_8b_128k",
+                    help="a named workload (fixed_cost_drafter_amd/configs/<name>.json) or a JSON file")
+    ap.add_argument("--passes", type=int, default=5,
+                    help="timed passes of --steps rounds; the median pass is reported")
+    ap.add_argument("--heat", type=int, default=400,
+                    help="untimed rounds between the summary init and the warmup rounds")
+    ap.add_argument("--no-sweep", dest="sweep", action="store_false")
+    ap.add_argument("--no-cpu", dest="cpu", action="store_false")
+    ap.add_argument("--cpu-budget", type=float, default=18.0)
+    ap.add_argument("--threads", type=int, default=16)
+    ap.add_argument("--no-next", dest="next", action="store_false",
+                    help="skip the steps beside the round (argmax, boundary, view ablations)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the K rounds captured in one HIP graph")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc csv runs into the traffic table and exit")
+    ap.add_argument("--traffic-command", default="",
+                    help="the command the counter runs were made with (recorded in the table)")
+    ap.add_argument("--counters", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc csv runs (e.g. MfmaUtil) into profiles/counters.json and exit")
+    args = ap.parse_args(argv)
+    if args.counters:
+        t = summarize_counters(args.counters, args.traffic_command)
+        os.makedirs(os.path.dirname(COUNTERS_JSON), exist_ok=True)
+        with open(COUNTERS_JSON, "w") as f:
+            json.dump(t, f, indent=1, sort_keys=True)
+        print(json.dumps(t["entry_points"]))
+        return 0
+    if args.traffic:
+        t = summarize_traffic(args.traffic[0], args.traffic[1], args.traffic_command)
+        os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+        with open(TRAFFIC_JSON, "w") as f:
+            json.dump(t, f, indent=1, sort_keys=True)
+        print(json.dumps(t["entry_points"]))
+        return 0
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the drafting "
+              "state shards by sequence or KV head with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+    from fixed_cost_drafter_amd import workload as WLM
+    wl = WLM.resolve_workload(args.workload)
+    cpu = None
+    if args.cpu:
+        # first, while no process has touched the GPU: the workers fork from here
+        log("timing the oracle on the host (cpu_baseline)")
+        cpu = cpu_baseline(wl, args.cpu_budget)
+    g = run_gpu(args, wl)
+    g["mfma_reference"] = mfma_reference("cuda")
+    log(f"MFMA reference: {g['mfma_reference']}")
+    line = result_line(args, wl, g, cpu)
     print(json.dumps(line), flush=True)
     return 0
 

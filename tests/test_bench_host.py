@@ -112,3 +112,52 @@ def test_source_hash_follows_code_not_comments():
     assert bench._code_only(code) == bench._code_only(commented)
     assert bench._code_only(code) != bench._code_only(changed)
     assert len(bench.source_hash(bench.KERNEL_SOURCES["round"])) == 16
+
+
+def _synthetic_measurements():
+    """A run_gpu-shaped result with round-number timings (seconds)."""
+    main = dict(wall_s=20 * 41e-6, gpu_s=20 * 40e-6, issue_s=20 * 10e-6,
+                passes_wall_s=[20 * 41e-6] * 5, passes_gpu_s=[20 * 40e-6] * 5)
+    kern = dict(verify_s=17e-6, append_s=12e-6, draft_s=16e-6, update_draft_s=26e-6,
+                draft_cold_s=28e-6, draft_warm_single_s=18.5e-6, update_draft_event_s=28.5e-6,
+                verify_keys_s=14e-6, round_split_s=40e-6, verify_append_s=24e-6)
+    return dict(main=main, kern=kern, init_s=2.5e-3, sweep={}, state_bytes_per_seq=5_779_464,
+                stream_reference=dict(copy_64MiB_gb_per_s=6800.0, copy_512MiB_gb_per_s=6250.0),
+                mfma_reference=dict(gemm="8192x8192x8192 bf16 torch.mm", tflop_per_s=1100.0,
+                                    frac_of_peak=0.44))
+
+
+def test_result_line_keeps_the_contract():
+    """The JSON line's required fields and its arithmetic, from synthetic
+    measurements: whole-job rounds/s, the roofline of the longest kernel
+    (algorithmic bytes / its time against the 8 TB/s peak) and the oracle's
+    CPU rate, all JSON-serialisable."""
+    import argparse
+    import json
+    wl = WLM.WORKLOADS["q3_8b_128k"]
+    args = argparse.Namespace(steps=20, warmup=5, passes=5, heat=400, next=False)
+    cpu = dict(value=50.0, unit="rounds/s", cores=16, kind="oracle", sample="synthetic")
+    line = bench.result_line(args, wl, _synthetic_measurements(), cpu)
+    json.loads(json.dumps(line))
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in line, key
+    assert line["n_gpus"] == 1 and line["steps"] == 20 and line["warmup"] == 5
+    assert line["unit"] == "rounds/s" and line["higher_is_better"] is True
+    assert line["vs_baseline"] is None and line["data"] == "synthetic"
+    assert line["config"]["workload"] == "q3_8b_128k"
+    assert line["value"] == pytest.approx(1 / 41e-6, rel=1e-3)
+    assert line["ms_per_step"] == pytest.approx(0.041, rel=1e-3)
+    roof = line["roofline"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert key in roof, key
+    alg = bench.algorithmic(wl, WLM.expected_tau(wl), wl.L0)
+    assert roof["kernel"] == "update_draft" and roof["bound"] == "hbm" and roof["unit"] == "GB/s"
+    assert roof["peak"] == 8000.0
+    assert roof["achieved"] == pytest.approx(alg["update_draft"] / 26e-6 / 1e9, abs=0.1)
+    assert roof["frac"] == pytest.approx(roof["achieved"] / 8000.0, abs=1e-4)
+    assert roof["frac_of_stream_reference"] == pytest.approx(roof["achieved"] / 6800.0, abs=1e-4)
+    assert line["cpu_baseline"] == cpu
+    init = line["kernels"]["init"]
+    assert init["frac_of_mfma_reference"] == pytest.approx(alg["init_flop"] / 2.5e-3 / 1e12 / 1100.0, abs=1e-4)
