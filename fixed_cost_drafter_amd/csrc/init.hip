@@ -12,14 +12,18 @@
 // contiguous ranges; one workgroup streams its range once (token-major
 // [C, rows, Hkv, d] input, 256-byte row segments) and writes an (m, l, n)
 // partial.  The bf16 d=128 kernel runs both contractions on MFMA
-// (v_mfma_f32_32x32x16_bf16): S^T = K U^T per 64-row tile, then the online
+// (v_mfma_f32_32x32x16_bf16): S^T = K U^T per tile, then the online
 // softmax in registers, then n^T += [K|V]^T P^T with P rounded to bf16 (l
 // sums the same rounded weights, so n/l stays an exact weighted mean of the
 // inputs).  Tiles run newest first, so each slot's maximum (the distance
 // bias favours new rows) is met early and the lazy rescale rarely fires.
+// Its splits are counted back from the newest row (InitPlan): the newest
+// ~12K rows pool every slot, older rows only the slower-decaying half, once
+// the faster half's weights there are shown negligible (see the kernel).
 // The f32 kernel is a plain LDS-tiled loop for small shapes.
-// Phase 2 (init_finalize): merges the partials (associative max-rescale),
-// writes the state and the slots, fills the ring, sets seq_len and err_flag.
+// Phase 2 (init_finalize): merges the partials (associative max-rescale;
+// an empty partial has weight 0), writes the state and the slots, fills the
+// ring, sets seq_len and err_flag.
 #include <algorithm>
 
 #include "common.hpp"
@@ -37,14 +41,29 @@ __device__ __host__ inline int64_t part_off(int split, int units, int unit, int 
 }
 
 // ---------------------------------------------------------------------------
-// MFMA partial kernel, bf16, d = 128, S = 32 * NG slots.  2 * NG waves:
-// wave w owns slots 32 (w % NG) .. +31 and row half w / NG (rows 0-31 or
-// 32-63) of every 64-row tile, two waves share a SIMD, and both products run
-// on v_mfma_f32_32x32x16_bf16:
+// MFMA partial kernel, bf16, d = 128, S = 32 * NG slots, 2 * NG waves (two
+// per SIMD), both products on v_mfma_f32_32x32x16_bf16.
+//  * NQ = 2, near splits (the newest rows): every slot.  Wave w owns slot
+//    group w % NG (32 slots) and row half w / NG of every 64-row tile.
+//  * NQ = 4, far splits (older rows): the slots are ranked by ln lambda and
+//    only the slower-decaying half (NG / 2 groups) is pooled.  Wave w owns
+//    pooled group w % (NG / 2) and row quarter w / (NG / 2) of every 128-row
+//    tile, so a tile costs each wave what a near tile does and the split's
+//    rows go by at twice the rate.  The faster half is then bounded: a slot's
+//    maximum m_j is at least its score on the newest row t, and |u.k| <=
+//    |u| |k| (Cauchy-Schwarz), so every row p of the split has
+//      a_jp - m_j <= |u_j| (max_p |k_p| + |k_t|) / sqrt(d) - (t - p) |ln lambda_j|.
+//    When that is below -48 for every slot of the faster half (rows at least
+//    ~10K back for unit-scale keys and lambda <= 1 - 2^-7), the split records
+//    those slots as empty (m = -inf, l = 0): the weights left out are below
+//    e^-48 of the slot's largest, far under fp32 resolution even summed over
+//    2^31 rows.  Otherwise it sets the split's flag, and a second launch
+//    (kRest) pools the faster half of the flagged splits.
+// Operands (both cases, rows counted inside the wave's 32-row group):
 //   S^T[row][slot] = K U^T over the wave's 32 rows: A = 32 rows x 16 dims
 //     from the row-major K tile, B = U^T (8 k-steps, read from LDS).
 //     A-row m = 8j + 4h + r (j < 4, h < 2, r < 4) reads row 16(j/2) + 8h +
-//     4(j%2) + r of the half, so that the output lane (slot, half h) holds
+//     4(j%2) + r of the group, so that the output lane (slot, half h) holds
 //     rows 8h..8h+7 and 16+8h..16+8h+7 in order: exactly the 8-row
 //     k-slices of the P^T operand of the second product.
 //   n^T[dim][slot] += [K|V]^T P^T per 16-row k-step: A = 32 dims x 16 rows,
@@ -57,69 +76,104 @@ __device__ __host__ inline int64_t part_off(int split, int units, int unit, int 
 // transposed reads (4 rows x 4 chunks per 16 lanes) on distinct banks.
 // Tiles go from global memory straight into LDS (global_load_lds_dwordx4:
 // lane i of an instruction fills the i-th 16 bytes of a 1 KB LDS block, so
-// each lane fetches the chunk that the swizzle places there), triple
-// buffered: the next two tiles stream in while the current one is computed
-// (with one workgroup per CU, a single tile in flight left the CU waiting on
-// memory latency), and one barrier per tile separates reads from refills.
-// The two row halves of a slot group keep separate (m, l, n) and merge
-// through LDS at the end.
+// each lane fetches the chunk that the swizzle places there), and the next
+// tile streams in while one is computed, with one barrier per tile between
+// reads and refills.  (That barrier's fence waits for all of a wave's loads,
+// so the near kernel's third buffer holds no second tile in flight; it is
+// the merge space of a slot group.)  The row groups of a slot group keep
+// separate (m, l, n) and merge through LDS at the end.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int tile_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
-template <int NG>
+template <int NG, int NQ, bool kRest = false>
 __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp, int64_t rows_stride,
-    int L0, int rows_per_split, int nsplit, const uint16_t* __restrict__ u,
-    const float* __restrict__ log_lambda, int Hkv, float* __restrict__ part) {
+    int L0, InitPlan plan, int split0, int nspl, const uint16_t* __restrict__ u,
+    const float* __restrict__ log_lambda, int Hkv, float* __restrict__ part,
+    int32_t* __restrict__ rest_flag) {
   typedef float f32x16 __attribute__((ext_vector_type(16)));
-  constexpr int D = 128, S = 32 * NG, NT = 128 * NG, TR = 64;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  constexpr bool kFar = NQ == 4;
+  static_assert(NQ == 2 || (NQ == 4 && NG % 2 == 0), "near: every slot group; far: half of them");
+  static_assert(kFar || !kRest, "only far splits leave a rest");
+  constexpr int D = 128, S = 32 * NG, NT = 128 * NG, NA = 2 * NG / NQ, TR = 32 * NQ;
   constexpr int KLS = D + 8;   // slot-query row stride (bf16 elements)
   constexpr int RS = D;        // K / V tile row stride: 256 bytes, swizzled chunks
   constexpr int KI = TR * RS / 512 / (NT / 64);  // 1 KB blocks of a K (or V) tile per wave
   static_assert(KI >= 1 && KI * (NT / 64) * 512 == TR * RS, "tile blocks must cover the waves");
-  // four LDS arrays of at least one slot group's merge record (64 lanes x
-  // m_true, m_run, l, 128 n): tile buffers 0, 1 and 2 ([K rows | V rows]
-  // each) and the slot queries; after the loop slot group g merges through
-  // array g.  Separate arrays let the compiler see that the tiles streaming
-  // into two buffers do not alias the reads of the third.
-  constexpr int kMergeElems = 64 * 131 * 2;
+  // merge records: 64 lanes x (m_true, m_run, l, 128 n).  Near: four LDS
+  // arrays of at least one record each, tile buffers 0, 1, 2 ([K rows | V
+  // rows] each) and the slot queries, and slot group g merges through array
+  // g.  Far: two tile buffers of at least two records each, and the row
+  // quarters of pooled group g merge through buffer g.  Separate arrays let
+  // the compiler see that the tiles streaming into one buffer do not alias
+  // the reads of another.
+  constexpr int kRecFloats = 64 * 131;
+  constexpr int kMergeElems = (kFar ? 2 : 1) * kRecFloats * 2;
   constexpr int kBufElems = 2 * TR * RS > kMergeElems ? 2 * TR * RS : kMergeElems;
-  constexpr int kUElems = S * KLS > kMergeElems ? S * KLS : kMergeElems;
+  constexpr int kUElems = kFar ? NA * 32 * KLS : (S * KLS > kMergeElems ? S * KLS : kMergeElems);
   static_assert(NG <= 4, "one merge array per slot group");
   __shared__ __attribute__((aligned(16))) uint16_t buf0[kBufElems];
   __shared__ __attribute__((aligned(16))) uint16_t buf1[kBufElems];
-  __shared__ __attribute__((aligned(16))) uint16_t buf2[kBufElems];
-  __shared__ __attribute__((aligned(16))) uint16_t UL[kUElems];  // [S][KLS]: the slot queries
+  __shared__ __attribute__((aligned(16))) uint16_t buf2[kFar ? 8 : kBufElems];
+  __shared__ __attribute__((aligned(16))) uint16_t UL[kUElems];  // [pooled slots][KLS]: their queries
+  __shared__ int32_t s_order[kFar ? S : 1];  // far: the slot of each rank by ln lambda
+  __shared__ float s_red[kFar ? 2 * (NT / 64) : 1];  // far: per-wave key bounds
   // s_waitcnt immediates: every load of this wave done / all but the newest
   // tile's 2 KI loads done (vmcnt in bits 3:0, expcnt and lgkmcnt not waited)
-  static_assert(2 * KI < 16, "one tile's loads fit the low vmcnt field");
-  constexpr int kWaitAll = 0x0F70, kWaitButOne = 0x0F70 | (2 * KI);
+  static_assert(kFar || 2 * KI < 16, "one tile's loads fit the low vmcnt field");
+  constexpr int kWaitAll = 0x0F70, kWaitButOne = 0x0F70 | ((2 * KI) & 15);
   // element offset of 16-byte chunk c of tile row r
   auto chunk_at = [](int r, int c) { return r * RS + ((c ^ tile_swz(r)) << 3); };
 
-  const int split = blockIdx.x % nsplit;
-  const int unit = blockIdx.x / nsplit;  // c * Hkv + h
+  const int split = split0 + int(blockIdx.x) % nspl;
+  const int unit = int(blockIdx.x) / nspl;  // c * Hkv + h
   const int h = unit % Hkv;
   const int c = unit / Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int sg = wave % NG, half = wave / NG;  // slot group, row half
+  const int sgl = wave % NA, q = wave / NA;  // pooled slot group, row group
   const int m32 = lane & 31, hh = lane >> 5;
-  const int r_begin = split * rows_per_split;
-  const int r_end = min(L0, r_begin + rows_per_split);
+  // the split's rows, counted back from the newest
+  int r_begin, r_end;
+  if (split < plan.n_near) {
+    r_end = L0 - split * plan.near_rows;
+    r_begin = max(0, r_end - plan.near_rows);
+  } else {
+    r_end = L0 - plan.n_near * plan.near_rows - (split - plan.n_near) * plan.far_rows;
+    r_begin = max(0, r_end - plan.far_rows);
+  }
   const int t_newest = L0 - 1;
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
   const float k2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
+  float* pb = part + part_off(split, int(gridDim.x) / nspl, unit, S, D);
+  // far: one flag per (split, unit), set when the faster half is still to pool
+  int32_t* flag = nullptr;
+  if constexpr (kFar) flag = rest_flag + int64_t(split - plan.n_near) * (int(gridDim.x) / nspl) + unit;
+  if constexpr (kRest)
+    if (*flag == 0) return;
 
-  // slot queries, read per tile as the B operand (lane (slot m32, hh) takes
-  // u[slot][16ks + 8hh .. +7]) from LDS: registers go to the accumulators
-  const int slot = sg * 32 + m32;
-  const float lnl2 = log_lambda[slot] * kLog2e;  // -inf stays -inf (lambda = 0)
-  for (int p = tid; p < S * 16; p += NT)
-    *reinterpret_cast<u16x8*>(&UL[(p >> 4) * KLS + (p & 15) * 8]) =
-        *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + (p >> 4)) * D + (p & 15) * 8);
-  // the tile row read by this lane as A-row m32 of its half
-  const int prow = half * 32 + 16 * (m32 >> 4) + 8 * ((m32 >> 2) & 1) + 4 * ((m32 >> 3) & 1) + (m32 & 3);
+  if constexpr (kFar) {
+    // rank the slots by ln lambda, ascending, ties by index (the integer
+    // image of the bits orders every float, NaN included)
+    auto key = [&](int i) {
+      const int b = __float_as_int(log_lambda[i]);
+      return b >= 0 ? b : b ^ 0x7fffffff;
+    };
+    for (int j = tid; j < S; j += NT) {
+      const int kj = key(j);
+      int r = 0;
+      for (int i = 0; i < S; ++i) {
+        const int ki = key(i);
+        r += (ki < kj) || (ki == kj && i < j);
+      }
+      s_order[r] = j;
+    }
+  }
+
+  // the tile row read by this lane as A-row m32 of its row group
+  const int prow = q * 32 + 16 * (m32 >> 4) + 8 * ((m32 >> 2) & 1) + 4 * ((m32 >> 3) & 1) + (m32 & 3);
   // LDS element offsets, the same for every tile:
   //  score operand k-step ks: chunk 2 ks + hh of row prow of the K tile;
   //  P.V operands: in 16-lane group g = lane / 16 reader lane r reads
@@ -133,7 +187,7 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) sc_off[ks] = chunk_at(prow, 2 * ks + hh);
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int tr_row = half * 32 + 8 * (g4 >> 1) + (r16 >> 2);
+  const int tr_row = q * 32 + 8 * (g4 >> 1) + (r16 >> 2);
   const int c0 = 2 * (g4 & 1) + ((r16 & 3) >> 1);
   int pv_base[2], pv_blk[4];
 #pragma unroll
@@ -141,12 +195,6 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
     pv_base[u] = (tr_row + 4 * u) * RS + ((c0 ^ (((tr_row >> 2) + u) & 3)) << 3) + 4 * (r16 & 1);
 #pragma unroll
   for (int k = 0; k < 4; ++k) pv_blk[k] = (k ^ (tr_row & 3)) << 5;
-
-  float m_run = -INFINITY, l_run = 0.f;  // reference max (may lag) and weight sum
-  float m_true = -INFINITY;               // exact running max
-  f32x16 acc[8];  // n^T block db: lane (slot m32, hh) holds dims 32db + 8j + 4hh + r at [4j + r]
-#pragma unroll
-  for (int db = 0; db < 8; ++db) acc[db] = f32x16{};
 
   // tile t0 -> LDS buffer b: wave w's block j holds K (or V) rows
   // 4(KI w + j) .. +3; lane i of it lands at 16-byte position p = 64 (KI w + j)
@@ -172,167 +220,313 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
   // every few tiles as the bias grows by |ln lambda| per row).
   const int ntiles = (r_end - r_begin + TR - 1) / TR;
   auto tile_t0 = [&](int idx) { return r_begin + (ntiles - 1 - idx) * TR; };
-  // one tile computed from buffer cur while the two after it stream in; nxt
-  // (the buffer of tile idx - 1) receives tile idx + 2
-  auto tile_step = [&](int idx, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
-    const int t0 = tile_t0(idx);
-    const int nrows = min(TR, r_end - t0);
-    const uint16_t* KL = cur;
-    const uint16_t* VL = cur + TR * RS;
-    // this wave's blocks of tile idx are in LDS (tile idx + 1 may still stream)
-    if (idx + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(kWaitButOne);
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-    __syncthreads();  // ... and every wave's; the reads of tile idx - 1 are done
-    if (idx + 2 < ntiles) issue_tile(tile_t0(idx + 2), nxt);  // streams in during this tile
+  float kn_max = 0.f;  // far: the largest squared norm of this lane's half of its rows' keys
 
-    // S^T for the wave's 32 rows
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 a = as_bf16x8(*reinterpret_cast<const u16x8*>(&KL[sc_off[ks]]));
-      const bf16x8 b = as_bf16x8(*reinterpret_cast<const u16x8*>(&UL[slot * KLS + ks * 16 + hh * 8]));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
+  {
+    // far: the slower half (ranks S/2 .. S-1), or in kRest the faster half
+    const int gbase = kFar && !kRest ? NG - NA : 0;
+    if (kFar) __syncthreads();  // the ranking is done
+    const int slot = kFar ? s_order[32 * (gbase + sgl) + m32] : sgl * 32 + m32;
+    const int urow = sgl * 32 + m32;  // the slot's row in UL
+    const float lnl2 = log_lambda[slot] * kLog2e;  // -inf stays -inf (lambda = 0)
+    // the slot queries of the pooled groups, read per tile as the B operand
+    // (lane (slot m32, hh) takes u[slot][16ks + 8hh .. +7]) from LDS:
+    // registers go to the accumulators
+    for (int p = tid; p < NA * 32 * 16; p += NT) {
+      const int row = p >> 4;
+      const int sj = kFar ? s_order[32 * gbase + row] : row;
+      *reinterpret_cast<u16x8*>(&UL[row * KLS + (p & 15) * 8]) =
+          *reinterpret_cast<const u16x8*>(u + (int64_t(h) * S + sj) * D + (p & 15) * 8);
     }
 
-    // online softmax per slot over the half (base 2).  Element 4j + r is
-    // tile row 32 half + 16(j/2) + 8hh + 4(j%2) + r, at distance
-    // t_newest - t0 - row >= 1 except in the tile holding the newest row or
-    // the ragged tail, which take the exact per-row path.
-    float tmax = -INFINITY;
-    if (t0 + TR <= t_newest && nrows == TR) {
-      const float dk = float(t_newest - t0 - 32 * half - 8 * hh);
+    float m_run = -INFINITY, l_run = 0.f;  // reference max (may lag) and weight sum
+    float m_true = -INFINITY;               // exact running max
+    f32x16 acc[8];  // n^T block db: lane (slot m32, hh) holds dims 32db + 8j + 4hh + r at [4j + r]
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = i >> 2, r = i & 3;
-        const float bias = (dk - float(16 * (j >> 1) + 4 * (j & 1) + r)) * lnl2;
-        const float a = fmaf(s[i], k2, bias);
-        s[i] = a;
-        tmax = fmaxf(tmax, a);
+    for (int db = 0; db < 8; ++db) acc[db] = f32x16{};
+
+    // one tile computed from buffer cur while the next ones stream in; nxt
+    // (the buffer of tile idx - 1) receives tile idx + 2 (near) or idx + 1 (far)
+    auto tile_step = [&](int idx, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
+      const int t0 = tile_t0(idx);
+      const int nrows = min(TR, r_end - t0);
+      const uint16_t* KL = cur;
+      const uint16_t* VL = cur + TR * RS;
+      if constexpr (kFar) {
+        __builtin_amdgcn_s_waitcnt(kWaitAll);  // this wave's blocks of tile idx are in LDS
+        __syncthreads();  // ... and every wave's; the reads of tile idx - 1 are done
+        if (idx + 1 < ntiles) issue_tile(tile_t0(idx + 1), nxt);  // streams in during this tile
+      } else {
+        // this wave's blocks of tile idx are in LDS (tile idx + 1 may still stream)
+        if (idx + 1 < ntiles)
+          __builtin_amdgcn_s_waitcnt(kWaitButOne);
+        else
+          __builtin_amdgcn_s_waitcnt(kWaitAll);
+        __syncthreads();  // ... and every wave's; the reads of tile idx - 1 are done
+        if (idx + 2 < ntiles) issue_tile(tile_t0(idx + 2), nxt);  // streams in during this tile
+      }
+
+      // S^T for the wave's 32 rows (far: and the squared norm of the lane's
+      // half of its row's key, from the same operand)
+      f32x16 s = f32x16{};
+      float kn = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u16x8 araw = *reinterpret_cast<const u16x8*>(&KL[sc_off[ks]]);
+        const bf16x8 b = as_bf16x8(*reinterpret_cast<const u16x8*>(&UL[urow * KLS + ks * 16 + hh * 8]));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(araw), b, s, 0, 0, 0);
+        if constexpr (kFar) {
+          const uint4 w4 = __builtin_bit_cast(uint4, araw);
+          const uint32_t wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bf16x2 x2 = __builtin_bit_cast(bf16x2, wv[i]);
+            kn = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, kn, false);
+          }
+        }
+      }
+      if constexpr (kFar) kn_max = fmaxf(kn_max, kn);
+
+      // online softmax per slot over the row group (base 2).  Element 4j + r
+      // is tile row 32 q + 16(j/2) + 8hh + 4(j%2) + r, at distance
+      // t_newest - t0 - row >= 1 except in the tile holding the newest row or
+      // the ragged tail, which take the exact per-row path.
+      float tmax = -INFINITY;
+      if (t0 + TR <= t_newest && nrows == TR) {
+        const float dk = float(t_newest - t0 - 32 * q - 8 * hh);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = i >> 2, r = i & 3;
+          const float bias = (dk - float(16 * (j >> 1) + 4 * (j & 1) + r)) * lnl2;
+          const float a = fmaf(s[i], k2, bias);
+          s[i] = a;
+          tmax = fmaxf(tmax, a);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = i >> 2, r = i & 3;
+          const int row = 32 * q + 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + r;
+          const int dist = t_newest - (t0 + row);
+          const float bias = dist == 0 ? 0.f : float(dist) * lnl2;
+          float a = fmaf(s[i], k2, bias);
+          if (row >= nrows) a = -INFINITY;
+          s[i] = a;
+          tmax = fmaxf(tmax, a);
+        }
+      }
+      // the slot's max over the two lane halves (the other rows)
+      {
+        const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+      }
+      // lazy rescale: the reference max moves only when some slot's max grows
+      // by more than 8 e-folds (weights stay <= e^8), so the 128-register
+      // accumulator rescale is skipped in the steady state
+      m_true = fmaxf(m_true, tmax);
+      if (__any(tmax > m_run + 8.f * kLog2e)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float scale = m_run == -INFINITY ? 0.f : exp2_f(m_run - m_new);
+        m_run = m_new;
+        l_run *= scale;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) acc[db] *= scale;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      // weights rounded to bf16 in pairs; l sums the same rounded weights;
+      // elements 8t..8t+7 are the P^T operand of k-step t
+      const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
+      bf16x8 pk[2];
+      float lsum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        uint32_t pw[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const f32x2 e2 = {exp2_f(s[8 * t + 2 * qq] - m_use), exp2_f(s[8 * t + 2 * qq + 1] - m_use)};
+          const bf16x2 b2 = __builtin_convertvector(e2, bf16x2);
+          pw[qq] = __builtin_bit_cast(uint32_t, b2);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(b2, ones, lsum, false);
+        }
+        pk[t] = as_bf16x8(__builtin_bit_cast(u16x8, uint4{pw[0], pw[1], pw[2], pw[3]}));
+      }
+      l_run += lsum;
+
+      // n^T[dim][slot] += [K|V]^T[dim][row] P^T[row][slot], 16 rows per k-step.
+      // A operand of dimension block db: lane l takes dimension 32db + l % 32
+      // and rows 8(l/32) .. +7 of the k-step as two transposed 4-row reads
+      // (offsets above): lane 4a + b of a 16-lane group receives element b of
+      // the reads of lanes a, a+4, a+8, a+12, which cover 4 consecutive rows.
+      typedef short i16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const uint16_t* tile = (db < 4 ? KL : VL) + 16 * t * RS + pv_blk[db & 3];
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + pv_base[0]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + pv_base[1]));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[t], acc[db], 0, 0, 0);
+        }
+    };
+    if constexpr (kFar) {
+      if (ntiles > 0) issue_tile(tile_t0(0), buf0);
+      for (int idx = 0; idx < ntiles; idx += 2) {  // tile i in buffer i mod 2
+        tile_step(idx, buf0, buf1);
+        if (idx + 1 < ntiles) tile_step(idx + 1, buf1, buf0);
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int j = i >> 2, r = i & 3;
-        const int row = 32 * half + 16 * (j >> 1) + 8 * hh + 4 * (j & 1) + r;
-        const int dist = t_newest - (t0 + row);
-        const float bias = dist == 0 ? 0.f : float(dist) * lnl2;
-        float a = fmaf(s[i], k2, bias);
-        if (row >= nrows) a = -INFINITY;
-        s[i] = a;
-        tmax = fmaxf(tmax, a);
+      if (ntiles > 0) issue_tile(tile_t0(0), buf0);
+      if (ntiles > 1) issue_tile(tile_t0(1), buf1);
+      for (int idx = 0; idx < ntiles; idx += 3) {  // tile i in buffer i mod 3
+        tile_step(idx, buf0, buf2);
+        if (idx + 1 < ntiles) tile_step(idx + 1, buf1, buf0);
+        if (idx + 2 < ntiles) tile_step(idx + 2, buf2, buf1);
       }
     }
-    // the slot's max over the two lane halves (the other rows)
+
+    float lt = l_run;  // the slot's weight sum over both lane halves
     {
-      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax), false, false);
-      tmax = fmaxf(__uint_as_float(x32[0]), __uint_as_float(x32[1]));
+      const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
+      lt = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
     }
-    // lazy rescale: the reference max moves only when some slot's max grows
-    // by more than 8 e-folds (weights stay <= e^8), so the 128-register
-    // accumulator rescale is skipped in the steady state
-    m_true = fmaxf(m_true, tmax);
-    if (__any(tmax > m_run + 8.f * kLog2e)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float scale = m_run == -INFINITY ? 0.f : exp2_f(m_run - m_new);
-      m_run = m_new;
-      l_run *= scale;
+    __syncthreads();  // the last tile's LDS reads are done
+    float* nrow = pb + 2 * S + int64_t(slot) * 2 * D;
+    if constexpr (!kFar) {
+      // merge the two row halves of each slot group: half 1 leaves (m_true,
+      // m_run, l, n) in LDS, half 0 takes the exact max of both and rescales
+      float* mg = reinterpret_cast<float*>(sgl == 0 ? buf0 : sgl == 1 ? buf1 : sgl == 2 ? buf2 : UL);
+      if (q == 1) {
+        float* dst = mg + lane * 131;
+        dst[0] = m_true;
+        dst[1] = m_run;
+        dst[2] = lt;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) acc[db] *= scale;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    // weights rounded to bf16 in pairs; l sums the same rounded weights;
-    // elements 8t..8t+7 are the P^T operand of k-step t
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 ones = {__bf16(1.0f), __bf16(1.0f)};
-    bf16x8 pk[2];
-    float lsum = 0.f;
+        for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      uint32_t pw[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x2 e2 = {exp2_f(s[8 * t + 2 * q] - m_use), exp2_f(s[8 * t + 2 * q + 1] - m_use)};
-        const bf16x2 b2 = __builtin_convertvector(e2, bf16x2);
-        pw[q] = __builtin_bit_cast(uint32_t, b2);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(b2, ones, lsum, false);
+          for (int i = 0; i < 16; ++i) dst[3 + db * 16 + i] = acc[db][i];
       }
-      pk[t] = as_bf16x8(__builtin_bit_cast(u16x8, uint4{pw[0], pw[1], pw[2], pw[3]}));
-    }
-    l_run += lsum;
+      __syncthreads();
+      if (q == 1) return;
+      const float* src = mg + lane * 131;
+      const float mt = fmaxf(m_true, src[0]);  // the state's m: the exact max of all rows
+      const float w0 = m_run == -INFINITY ? 0.f : exp2_f(m_run - mt);
+      const float w1 = src[1] == -INFINITY ? 0.f : exp2_f(src[1] - mt);
+      lt = fmaf(lt, w0, src[2] * w1);
 
-    // n^T[dim][slot] += [K|V]^T[dim][row] P^T[row][slot], 16 rows per k-step.
-    // A operand of dimension block db: lane l takes dimension 32db + l % 32
-    // and rows 8(l/32) .. +7 of the k-step as two transposed 4-row reads
-    // (offsets above): lane 4a + b of a 16-lane group receives element b of
-    // the reads of lanes a, a+4, a+8, a+12, which cover 4 consecutive rows.
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const uint16_t* tile = (db < 4 ? KL : VL) + 16 * t * RS + pv_blk[db & 3];
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + pv_base[0]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + pv_base[1]));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[t], acc[db], 0, 0, 0);
+      // write the partial: lane (slot, hh) holds n[slot][32db + 8j + 4hh + r];
+      // each block is combined and stored in turn
+      if (hh == 0) {
+        pb[slot] = mt * kLn2;  // natural units, as the state keeps m
+        pb[S + slot] = lt;
       }
-  };
-  if (ntiles > 0) issue_tile(tile_t0(0), buf0);
-  if (ntiles > 1) issue_tile(tile_t0(1), buf1);
-  for (int idx = 0; idx < ntiles; idx += 3) {  // tile i in buffer i mod 3
-    tile_step(idx, buf0, buf2);
-    if (idx + 1 < ntiles) tile_step(idx + 1, buf1, buf0);
-    if (idx + 2 < ntiles) tile_step(idx + 2, buf2, buf1);
-  }
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f32x4 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = fmaf(acc[db][4 * j + r], w0, src[3 + db * 16 + 4 * j + r] * w1);
+          *reinterpret_cast<f32x4*>(nrow + db * 32 + 8 * j + 4 * hh) = o;
+        }
+    } else {
+      // merge the four row quarters of each pooled group in two rounds
+      // through records 0 and 1 of buffer sgl: quarters 2, 3 into 0, 1, then
+      // quarter 1 into 0
+      float* rec = reinterpret_cast<float*>(sgl == 0 ? buf0 : buf1) + lane * 131;
+      auto put = [&](float* dst) __attribute__((always_inline)) {
+        dst[0] = m_true;
+        dst[1] = m_run;
+        dst[2] = lt;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) dst[3 + db * 16 + i] = acc[db][i];
+      };
+      auto take = [&](const float* src) __attribute__((always_inline)) {
+        const float mt = fmaxf(m_true, src[0]);
+        const float w0 = m_run == -INFINITY ? 0.f : exp2_f(m_run - mt);
+        const float w1 = src[1] == -INFINITY ? 0.f : exp2_f(src[1] - mt);
+        lt = fmaf(lt, w0, src[2] * w1);
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] = fmaf(acc[db][i], w0, src[3 + db * 16 + i] * w1);
+        m_true = mt;
+        m_run = mt;
+      };
+      if (q >= 2) put(rec + (q - 2) * kRecFloats);
+      __syncthreads();
+      if (q < 2) take(rec + q * kRecFloats);
+      __syncthreads();
+      if (q == 1) put(rec);
+      __syncthreads();
+      if (q == 0) {
+        take(rec);
+        if (hh == 0) {
+          pb[slot] = m_true * kLn2;
+          pb[S + slot] = lt;
+        }
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            f32x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = acc[db][4 * j + r];
+            *reinterpret_cast<f32x4*>(nrow + db * 32 + 8 * j + 4 * hh) = o;
+          }
+      }
+      if constexpr (kRest) return;
 
-  // merge the two row halves of each slot group: half 1 leaves (m_true,
-  // m_run, l, n) in LDS, half 0 takes the exact max of both and rescales
-  float lt = l_run;
-  {
-    const auto x32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt), false, false);
-    lt = __uint_as_float(x32[0]) + __uint_as_float(x32[1]);
-  }
-  __syncthreads();  // the last tile's LDS reads are done
-  float* mg = reinterpret_cast<float*>(sg == 0 ? buf0 : sg == 1 ? buf1 : sg == 2 ? buf2 : UL);  // [64 lanes][m_true, m_run, l, 128 n]
-  if (half == 1) {
-    float* dst = mg + lane * 131;
-    dst[0] = m_true;
-    dst[1] = m_run;
-    dst[2] = lt;
+      // the bound on the faster half (above): the largest key norm of the
+      // split, bounded by the sum of the largest squared norms of the two
+      // interleaved dimension halves (lane halves hh), and the newest row's
+      float kb = kn_max;
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
+      for (int o = 16; o >= 1; o >>= 1) kb = fmaxf(kb, __shfl_xor(kb, o, 64));
+      if (m32 == 0) s_red[2 * wave + hh] = kb;
+      __syncthreads();
+      if (wave == 0) {
+        float k0 = 0.f, k1 = 0.f;
+        for (int w = 0; w < NT / 64; ++w) {
+          k0 = fmaxf(k0, s_red[2 * w]);
+          k1 = fmaxf(k1, s_red[2 * w + 1]);
+        }
+        const uint32_t kt = *reinterpret_cast<const uint32_t*>(
+            kp + ((int64_t(c) * rows_stride + t_newest) * Hkv + h) * D + 2 * lane);
+        const bf16x2 kt2 = __builtin_bit_cast(bf16x2, kt);
+        const float ktn = wave_sum(__builtin_amdgcn_fdot2_f32_bf16(kt2, kt2, 0.f, false));
+        bool ok = true;
+        if (lane < 32 * NA) {  // the faster half: ranks 0 .. 32 NA - 1
+          const int j = s_order[lane];
+          float un = 0.f;
+          for (int e = 0; e < D; e += 8) {
+            const uint4 x = *reinterpret_cast<const uint4*>(u + (int64_t(h) * S + j) * D + e);
+            const uint32_t xv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[3 + db * 16 + i] = acc[db][i];
-  }
-  __syncthreads();
-  if (half == 1) return;
-  const float* src = mg + lane * 131;
-  const float mt = fmaxf(m_true, src[0]);  // the state's m: the exact max of all rows
-  const float w0 = m_run == -INFINITY ? 0.f : exp2_f(m_run - mt);
-  const float w1 = src[1] == -INFINITY ? 0.f : exp2_f(src[1] - mt);
-  lt = fmaf(lt, w0, src[2] * w1);
-
-  // write the partial: lane (slot, hh) holds n[slot][32db + 8j + 4hh + r];
-  // each block is combined and stored in turn
-  float* pb = part + part_off(split, gridDim.x / nsplit, unit, S, D);
-  if (hh == 0) {
-    pb[slot] = mt * kLn2;  // natural units, as the state keeps m
-    pb[S + slot] = lt;
-  }
-  float* nrow = pb + 2 * S + int64_t(slot) * 2 * D;
-#pragma unroll
-  for (int db = 0; db < 8; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f32x4 o;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = fmaf(acc[db][4 * j + r], w0, src[3 + db * 16 + 4 * j + r] * w1);
-      *reinterpret_cast<f32x4*>(nrow + db * 32 + 8 * j + 4 * hh) = o;
+            for (int i = 0; i < 4; ++i) {
+              const bf16x2 x2 = __builtin_bit_cast(bf16x2, xv[i]);
+              un = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, un, false);
+            }
+          }
+          // 1 + 2^-10 covers the rounding of the norms; NaN fails
+          const float bound =
+              sqrtf(un) * (sqrtf(k0 + k1) + sqrtf(ktn)) * (0.08838834764831845f * (1.f + 0x1p-10f)) + 48.f;
+          const float decay = float(L0 - r_end) * -log_lambda[j];
+          ok = decay >= bound;
+        }
+        const bool all_ok = __ballot(!ok) == 0;
+        if (lane == 0) *flag = all_ok ? 0 : 1;
+        if (all_ok && lane < 32 * NA) {
+          const int j = s_order[lane];
+          pb[j] = -INFINITY;  // an empty partial: the merge gives it weight 0
+          pb[S + j] = 0.f;
+        }
+      }
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -477,7 +671,7 @@ __global__ __launch_bounds__(kThreads) void init_finalize(
     for (int s = 0; s < nsplit; ++s) {
       const float* pn = part + part_off(s, units, unit, S, D) + 2 * S + int64_t(j) * 2 * D + e;
       const float w = wsm[s * SPB + jj];  // (partials are only 4-byte aligned for odd S)
-      a += f32x4{pn[0], pn[1], pn[2], pn[3]} * w;
+      if (w != 0.f) a += f32x4{pn[0], pn[1], pn[2], pn[3]} * w;  // an empty partial holds no n
     }
     *reinterpret_cast<f32x4*>(sum_n + n_index(ntiled, unit, S, D, j, e)) = a;
     const float il = s_inv_l[jj];
@@ -602,24 +796,38 @@ ls_status run_f32(const ls_dims& d, const ls_state& st, const void* kp, const vo
 ls_status launch_init(const ls_dims& d, const ls_state& st, const void* kp, const void* vp,
                       int32_t L0, int64_t rows_stride, hipStream_t stream) {
   const WsLayout lay = ws_layout(d, L0);
-  const int rows = init_rows_per_split(d, L0);
-  const int nsplit = int(cdiv(L0, rows));
   float* part = reinterpret_cast<float*>(static_cast<char*>(st.workspace) + lay.init_part);
   if (d.dtype == LS_BF16) {
-    const dim3 grid(d.C * d.Hkv * nsplit);
+    const InitPlan plan = init_plan(d, L0);
+    if (plan.nsplit() > lay.isplit) return LS_ERR_SHAPE;  // the workspace bound must cover the plan
+    const int units = d.C * d.Hkv;
     const uint16_t* k16 = static_cast<const uint16_t*>(kp);
     const uint16_t* v16 = static_cast<const uint16_t*>(vp);
     const uint16_t* u16 = static_cast<const uint16_t*>(st.u);
+    // near splits 0 .. n_near - 1, then far splits n_near .. nsplit - 1: the
+    // slower half of the slots, then the faster half where its bound failed
+    int32_t* rest = reinterpret_cast<int32_t*>(static_cast<char*>(st.workspace) + lay.init_flag);
+    auto run = [&](auto near, auto far, auto rest_k, int threads) {
+      hipLaunchKernelGGL(near, dim3(units * plan.n_near), dim3(threads), 0, stream, k16, v16, rows_stride, L0,
+                         plan, 0, plan.n_near, u16, st.log_lambda, d.Hkv, part, rest);
+      if (plan.n_far > 0) {
+        hipLaunchKernelGGL(far, dim3(units * plan.n_far), dim3(threads), 0, stream, k16, v16, rows_stride,
+                           L0, plan, plan.n_near, plan.n_far, u16, st.log_lambda, d.Hkv, part, rest);
+        hipLaunchKernelGGL(rest_k, dim3(units * plan.n_far), dim3(threads), 0, stream, k16, v16,
+                           rows_stride, L0, plan, plan.n_near, plan.n_far, u16, st.log_lambda, d.Hkv,
+                           part, rest);
+      }
+    };
     if (d.S == 128)
-      hipLaunchKernelGGL((init_mfma32_partial<4>), grid, dim3(512), 0, stream, k16, v16,
-                         rows_stride, L0, rows, nsplit, u16, st.log_lambda, d.Hkv, part);
+      run(init_mfma32_partial<4, 2>, init_mfma32_partial<4, 4>, init_mfma32_partial<4, 4, true>, 512);
     else if (d.S == 64)
-      hipLaunchKernelGGL((init_mfma32_partial<2>), grid, dim3(256), 0, stream, k16, v16,
-                         rows_stride, L0, rows, nsplit, u16, st.log_lambda, d.Hkv, part);
+      run(init_mfma32_partial<2, 2>, init_mfma32_partial<2, 4>, init_mfma32_partial<2, 4, true>, 256);
     // S = 0: no summary to pool; the finalize fills the window only
     if (hipGetLastError() != hipSuccess) return LS_ERR_HIP;
-    return finalize<BF16, 128>(d, st, part, nsplit, kp, vp, L0, rows_stride, stream);
+    return finalize<BF16, 128>(d, st, part, plan.nsplit(), kp, vp, L0, rows_stride, stream);
   }
+  const int rows = init_rows_per_split(d, L0);
+  const int nsplit = int(cdiv(L0, rows));
   switch (d.d) {
     case 16: return run_f32<16>(d, st, kp, vp, L0, rows_stride, part, rows, nsplit, stream);
     case 32: return run_f32<32>(d, st, kp, vp, L0, rows_stride, part, rows, nsplit, stream);

@@ -323,6 +323,66 @@ def test_init_with_large_scores_in_old_rows(S):
     H.compare_state(rn, ost, wl.dtype, scaled=True)
 
 
+# the init's far splits: rows at least ~12K back from the newest pool only
+# the slower-decaying half of the slots once the faster half is bounded (for
+# prefixes of at least ~24K rows).  50000 rows at C*Hkv = 4: 64 near splits of
+# 192 rows, then 59 far splits of 640 rows (the oldest holds 592: a ragged tile)
+FAR = {
+    "far_s128": WLM.Workload("bf16_far_s128", "bf16", C=2, Hq=4, Hkv=2, d=128, L0=50000, W=64,
+                             S=128, B=4, V=1000, rounds=1, p_match=0.8, seed=31),
+    "far_s64": WLM.Workload("bf16_far_s64", "bf16", C=2, Hq=4, Hkv=2, d=128, L0=50000, W=64,
+                            S=64, B=4, V=1000, rounds=1, p_match=0.8, seed=32),
+}
+
+
+@pytest.mark.parametrize("name", list(FAR))
+def test_init_far_splits(name):
+    """Unit-scale keys: every far split shows the faster half's weights below
+    e^-48 of their maximum and leaves it out; the state (m, l, n, slots,
+    window) must match the oracle's full sums over every row."""
+    import torch
+    from fixed_cost_drafter_amd.runner import PathRunner
+    wl = FAR[name]
+    _announce(wl, "init with far splits")
+    Kp, Vp = WLM.prefix(wl, threads=4)
+    rn = PathRunner(wl, Kp, Vp)
+    rn.init()
+    torch.cuda.synchronize()
+    ost = O.summary_init(WLM.slot_queries(wl), WLM.log_lambda(wl), Kp, Vp, wl.W)
+    H.compare_state(rn, ost, wl.dtype)
+
+
+@pytest.mark.parametrize("name", list(FAR))
+def test_init_far_splits_rest(name):
+    """Old rows (12,500 and 15,000 back, in far splits) whose key is 180 times
+    the unit query of slot 7 (lambda = 1 - 2^-7, the slowest of the faster
+    half): its score there, ~180 |u_7| / sqrt(d) ~ 180, outweighs the 98
+    (118) nats of decay, so that row dominates slot 7.  The key norm breaks
+    the far split's bound, the split is flagged and the second far launch
+    pools the faster half; a split that left it out would give slot 7 a value
+    far from the oracle's.  Slot 7 then holds values up to ~60, so the bf16
+    outputs are held to 2e-2 relative to their size."""
+    import torch
+    from fixed_cost_drafter_amd.runner import PathRunner
+    wl = FAR[name].with_(seed=FAR[name].seed + 10)
+    _announce(wl, "init with far splits, planted rows that fail the bound")
+    Kp, Vp = WLM.prefix(wl, threads=4)
+    u = WLM.slot_queries(wl)
+    uf = WLM.bf16_bits_to_f32(u).astype(np.float64)
+    t = wl.L0 - 1
+    for c, h, back in ((0, 0, 12500), (1, 1, 12500), (1, 0, 15000)):
+        uj = uf[h, 7]
+        Kp[c, t - back, h] = WLM.f32_to_bf16_bits((180.0 * uj / np.linalg.norm(uj)).astype(np.float32))
+    rn = PathRunner(wl, Kp, Vp)
+    rn.init()
+    torch.cuda.synchronize()
+    ost = O.summary_init(u, WLM.log_lambda(wl), Kp, Vp, wl.W)
+    # the planted rows do dominate slot 7 in the oracle's sums
+    for c, h, back in ((0, 0, 12500), (1, 1, 12500), (1, 0, 15000)):
+        assert ost.m[c, h, 7] > 15.0, (c, h, ost.m[c, h, 7])
+    H.compare_state(rn, ost, wl.dtype, scaled=True)
+
+
 def _random_shapes(n, seed=77):
     """Seeded shapes across the whole accepted range, both dtypes: bf16 (d = 128,
     S in {0, 64, 128}, W = 0 or a multiple of 32, B up to 47, up to 64 query
