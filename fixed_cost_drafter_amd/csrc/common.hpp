@@ -246,6 +246,20 @@ inline InitPlan init_plan(const ls_dims& d, int32_t L0) {
   const int64_t R = std::max(round_up(cdiv(L, want), kInitRowTile), int64_t(kInitRowTile));
   return InitPlan{int(R), int(cdiv(L, R)), 0, 0};
 }
+// rows [*r_begin, *r_end) of split `split` (0 = the newest rows) of a plan
+__host__ __device__ inline void init_split_rows(const InitPlan& p, int L0, int split, int* r_begin,
+                                                int* r_end) {
+  int e, n;
+  if (split < p.n_near) {
+    e = L0 - split * p.near_rows;
+    n = p.near_rows;
+  } else {
+    e = L0 - p.n_near * p.near_rows - (split - p.n_near) * p.far_rows;
+    n = p.far_rows;
+  }
+  *r_end = e;
+  *r_begin = e - n > 0 ? e - n : 0;
+}
 // an upper bound of init_plan(d, L0).nsplit() over 1 <= L0 <= max_L0
 inline int init_split_bound(const ls_dims& d, int32_t max_L0) {
   const int64_t units = int64_t(d.C) * d.Hkv;

@@ -137,13 +137,7 @@ __global__ __launch_bounds__(128 * NG, 1) void init_mfma32_partial(
   const int m32 = lane & 31, hh = lane >> 5;
   // the split's rows, counted back from the newest
   int r_begin, r_end;
-  if (split < plan.n_near) {
-    r_end = L0 - split * plan.near_rows;
-    r_begin = max(0, r_end - plan.near_rows);
-  } else {
-    r_end = L0 - plan.n_near * plan.near_rows - (split - plan.n_near) * plan.far_rows;
-    r_begin = max(0, r_end - plan.far_rows);
-  }
+  init_split_rows(plan, L0, split, &r_begin, &r_end);
   const int t_newest = L0 - 1;
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
   const float k2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
