@@ -63,7 +63,7 @@ int main() {
   for (int dt : {LS_BF16, LS_F32})
     for (int S : {0, 4, 64, 128})
       for (int dd : {16, 128})
-        for (int C : {1, 2, 16})
+        for (int C : {1, 2, 16, 64})
           for (int Hkv : {1, 2, 8}) {
             ls_dims d{};
             d.C = C;
