@@ -1,5 +1,5 @@
 """The summary init's split plan (near and far splits, the workspace bound),
-checked on the host by tests/init_plan_check.cpp over ~390K (shape, prefix
+checked on the host by tests/init_plan_check.cpp over ~520K (shape, prefix
 length) pairs: exact coverage of the prefix rows, far rows at least the near
 distance back, split sizes, and a workspace bound that grows with the prefix.
 No GPU: the check calls host code of csrc/common.hpp only."""
