@@ -42,7 +42,7 @@ __device__ __host__ inline int64_t part_off(int split, int units, int unit, int 
 
 // ---------------------------------------------------------------------------
 // MFMA partial kernel, bf16, d = 128, S = 32 * NG slots, 2 * NG waves (two
-// per SIMD), both products on v_mfma_f32_32x32x16_bf16.
+// per SIMD at S = 128), both products on v_mfma_f32_32x32x16_bf16.
 //  * NQ = 2, near splits (the newest rows): every slot.  Wave w owns slot
 //    group w % NG (32 slots) and row half w / NG of every 64-row tile.
 //  * NQ = 4, far splits (older rows): the slots are ranked by ln lambda and
