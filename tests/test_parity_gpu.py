@@ -383,6 +383,38 @@ def test_init_far_splits_rest(name):
     H.compare_state(rn, ost, wl.dtype, scaled=True)
 
 
+FAR_LAMBDAS = {
+    # lambda = 1 everywhere: no decay, so no far split can bound its faster
+    # half (the decay term is 0) and every one is pooled again in the
+    # second far launch
+    "all_one": (1.0,) * 64,
+    # lambda = 0 and 0.5 in the faster half (always bounded: lambda = 0
+    # weighs only the newest row), 0.999 and 1 in the slower half
+    "zero_half_one": (0.0,) * 16 + (0.5,) * 16 + (0.999,) * 16 + (1.0,) * 16,
+    # the faster half ranked from the end of the slot list: decays in
+    # descending order
+    "descending": tuple(1.0 - 2.0 ** -(15 - (j % 16)) for j in range(64)),
+}
+
+
+@pytest.mark.parametrize("name", list(FAR_LAMBDAS))
+def test_init_far_splits_lambda_edges(name):
+    """Far splits with decays at the ends of the range and in any slot order,
+    S = 64, 30000 rows: the state must match the oracle's sums over every row."""
+    import torch
+    from fixed_cost_drafter_amd.runner import PathRunner
+    wl = WLM.Workload(f"bf16_far_lambda_{name}", "bf16", C=2, Hq=4, Hkv=2, d=128, L0=30000,
+                      W=64, S=64, B=4, V=1000, rounds=1, p_match=0.8, seed=35,
+                      lambdas=FAR_LAMBDAS[name])
+    _announce(wl, "init with far splits, edge decays")
+    Kp, Vp = WLM.prefix(wl, threads=4)
+    rn = PathRunner(wl, Kp, Vp)
+    rn.init()
+    torch.cuda.synchronize()
+    ost = O.summary_init(WLM.slot_queries(wl), WLM.log_lambda(wl), Kp, Vp, wl.W)
+    H.compare_state(rn, ost, wl.dtype)
+
+
 def _random_shapes(n, seed=77):
     """Seeded shapes across the whole accepted range, both dtypes: bf16 (d = 128,
     S in {0, 64, 128}, W = 0 or a multiple of 32, B up to 47, up to 64 query
