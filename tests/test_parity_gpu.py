@@ -128,10 +128,15 @@ def test_parity_mixed_entry_points(name):
     H.lockstep(wl, wl.rounds, calls="mixed")
 
 
-def test_parity_q3_4b_8k_all_heads():
+@pytest.mark.parametrize("calls", ["separate", "round"])
+def test_parity_q3_4b_8k_all_heads(calls):
+    """The 4B-shaped workload (C = 1, 8K prefix, W = 512, S = 64, V = 151936)
+    for its configured 64 rounds, every KV head, through the separate calls
+    and through the one-call round (at S = 64 its fused kernel runs two slot
+    tiles per workgroup, two workgroups per KV head)."""
     wl = WLM.WORKLOADS["q3_4b_8k"]
-    _announce(wl, "rounds=64 (state checked every 8)")
-    _, _, stats = H.lockstep(wl, wl.rounds, check_state_every=8)
+    _announce(wl, f"rounds=64 (state checked every 8), calls={calls}")
+    _, _, stats = H.lockstep(wl, wl.rounds, check_state_every=8, calls=calls)
     taus = np.concatenate(stats["tau"]).astype(float)
     H.log(f"mean tau {taus.mean():.2f} (expected {WLM.expected_tau(wl):.2f})")
 
